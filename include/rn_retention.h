@@ -1,0 +1,161 @@
+/*
+ * rn_retention.h — C ABI of the multi-scale retention forward pass on MI355X (gfx950).
+ *
+ * Retention (RetNet, "Retentive Network") maps q, k, v to
+ *     O_t = alpha * sum_{s<=t} gamma^(t-s) * Re[(q_t e^{i p_t theta})(k_s e^{i p_s theta})^dagger] v_s
+ * (hwhale.com RetNet notes: closed form of O_n after diagonalising A; definition of
+ * Q = (XW_Q) ⊙ Θ, K = (XW_K) ⊙ conj(Θ), D_nm = gamma^(n-m) for n >= m).
+ * Three algebraically equal forms are exported — parallel, chunkwise and one
+ * recurrent (decode) step — plus the per-head GroupNorm with the swish gate.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout (row-major, contiguous, the argument comments of the ParallelRetention /
+ * RecurrentRetention / ChunkwiseRetention listings on the hwhale.com notes):
+ *     q, k        [B, H, N, d_k]
+ *     v, gate,out [B, H, N, d_v]
+ *     state       [B, H, d_k, d_v]   always float32
+ * Rotation: coordinates (2j, 2j+1) form one complex number (sdkjxy.cn walkthrough,
+ * "Retention 機制": elements taken two by two as real and imaginary parts); pair j at
+ * absolute position p is multiplied by e^{+i p theta_j}; k is conjugated in the
+ * score. Positions are p_t = pos0 + t with 0-based t. The angle p*theta_j is formed
+ * and reduced modulo 2*pi in float64 on the device before the float32 sine/cosine.
+ * alpha (qk_scale) multiplies the score; it never enters the recurrent state, so
+ * states are interchangeable between the chunkwise and recurrent entry points.
+ *
+ * Ownership: every tensor argument is a DEVICE pointer owned by the caller; the
+ * library never allocates device memory on these paths (the chunkwise entry point
+ * takes a caller-owned workspace). gamma and theta (in rn_desc) are HOST arrays
+ * read during the call. gn_weight / gn_bias are DEVICE arrays [H*d_v] or NULL.
+ * Asynchrony: each call enqueues kernels on `stream` (a hipStream_t; NULL = the
+ * null stream) and returns without synchronising; device faults surface at the
+ * caller's next synchronisation.
+ * Errors: arguments are validated on the host before any HIP call, so an invalid
+ * call launches nothing and touches no device memory. Return codes only (no
+ * printing, no abort); rn_last_error() gives a thread-local message.
+ * NaN/Inf in inputs propagate; they are never masked.
+ * Overlapping calls that share a workspace or a state buffer race.
+ */
+#ifndef RN_RETENTION_H
+#define RN_RETENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t rn_status;
+#define RN_OK               0
+#define RN_ERR_INVALID_ARG (-1) /* null pointer, size < 1, odd d_k, chunk < 1, bad flags, eps < 0 ... */
+#define RN_ERR_UNSUPPORTED (-2) /* valid but outside what is built: d_k > 256, d_v > 512, N > 2^30 ... */
+#define RN_ERR_HIP         (-3) /* HIP runtime / launch error; text via rn_last_error() */
+#define RN_ERR_WORKSPACE   (-4) /* workspace NULL or smaller than rn_chunkwise_workspace_bytes() */
+
+typedef int32_t rn_dtype;
+#define RN_F32  0   /* IEEE float32 */
+#define RN_BF16 1   /* bfloat16 (upper half of a float32) */
+
+/* flags */
+#define RN_NORM_D_ROW (1u << 0) /* parallel only: D_nm / sqrt(sum_{i<=n} D_ni)  (hwhale notes, 2nd rescaling) */
+#define RN_NORM_R_ROW (1u << 1) /* parallel only: R_nm / max(|sum_{i<=n} R_ni|, 1) (hwhale notes, 3rd rescaling) */
+#define RN_EPI_GN     (1u << 2) /* per-(token, head) GroupNorm over d_v (hwhale notes, multi-head paragraph) */
+#define RN_EPI_GATE   (1u << 3) /* out = GN(.) * swish(gate); requires RN_EPI_GN (m0nads notes, swish gate) */
+#define RN_FORCE_GENERIC (1u << 8) /* use the plain (non-MFMA) kernels; for testing and unusual shapes */
+
+typedef struct rn_desc {
+    int32_t B;             /* batch, >= 1 */
+    int32_t H;             /* heads, 1..128 */
+    int32_t N;             /* tokens; must be 1 for rn_retention_recurrent_step */
+    int32_t d_k;           /* query/key head dim: even, 2..256 */
+    int32_t d_v;           /* value head dim: 1..512 */
+    rn_dtype in_dtype;     /* dtype of q, k, v, gate */
+    rn_dtype out_dtype;    /* dtype of out; accumulation is always float32 */
+    uint32_t flags;        /* RN_* flags above */
+    int64_t pos0;          /* absolute position of token 0 (the step's position for decode), >= 0 */
+    float qk_scale;        /* alpha; finite */
+    float gn_eps;          /* GroupNorm epsilon, >= 0 (used with RN_EPI_GN) */
+    const float* gamma;    /* HOST [H]: per-head decay, 0 < gamma <= 1 (hwhale notes: one gamma per head) */
+    const float* theta;    /* HOST [d_k/2]: one angle per coordinate pair, finite */
+    const float* gn_weight;/* DEVICE [H*d_v] GroupNorm scale, or NULL (= 1) */
+    const float* gn_bias;  /* DEVICE [H*d_v] GroupNorm shift, or NULL (= 0) */
+} rn_desc;
+
+/*
+ * Parallel form: O = ((alpha * Qh Kh^T) ⊙ D) V with the optional row rescalings,
+ * then the optional GroupNorm / gate epilogue.
+ * (hwhale notes: parallel-form equation, the ParallelRetention listing and the list
+ * of three rescalings; rescalings are applied in the listed order as per-row
+ * scalars: c_t = 1/sqrt(sum_{m<=t} gamma^m) for RN_NORM_D_ROW, then division by
+ * max(|signed row sum of R|, 1) for RN_NORM_R_ROW.)
+ * q, k: [B,H,N,d_k]; v: [B,H,N,d_v]; gate: [B,H,N,d_v] (required iff RN_EPI_GATE,
+ * else ignored); out: [B,H,N,d_v] in out_dtype. No state: the parallel form starts
+ * from S = 0.
+ */
+rn_status rn_retention_parallel(const rn_desc* desc, const void* q, const void* k,
+                                const void* v, const void* gate, void* out, void* stream);
+
+/*
+ * Bytes of device workspace rn_retention_chunkwise needs for `desc` (independent of
+ * N). Returns 0 for an invalid descriptor.
+ */
+size_t rn_chunkwise_workspace_bytes(const rn_desc* desc, int32_t chunk);
+
+/*
+ * Chunkwise recurrent form (hwhale notes: chunkwise equation with
+ * xi_j = gamma^(j+1), and the ChunkwiseRetention listing; m0nads notes,
+ * "Chunkwise representation"). For chunk i of length L (the last may be shorter):
+ *   O_[i]   = alpha * ((Qh Kh^T ⊙ D) V + (Qh S_i) ⊙ xi),  xi_j = gamma^(j+1)
+ *   S_{i+1} = gamma^L S_i + sum_j gamma^(L-1-j) Kh_j^T V_j
+ * then the optional GroupNorm / gate epilogue per token. The result does not
+ * depend on `chunk` beyond rounding (every chunk length gives the same O and
+ * S_final); the kernels carry the state at a granularity of their own.
+ * state_in:  [B,H,d_k,d_v] float32 initial state S_0, or NULL for zeros.
+ * state_out: [B,H,d_k,d_v] float32 final state, or NULL to discard; may equal
+ *            state_in (updated in place).
+ * workspace: device buffer of at least rn_chunkwise_workspace_bytes(desc, chunk)
+ *            bytes, 256-byte aligned; contents on entry are ignored.
+ * RN_NORM_D_ROW / RN_NORM_R_ROW are rejected (parallel form only).
+ */
+rn_status rn_retention_chunkwise(const rn_desc* desc, int32_t chunk, const void* q,
+                                 const void* k, const void* v, const void* gate,
+                                 const float* state_in, float* state_out, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent (decode) step at absolute position desc->pos0 (desc->N must be 1):
+ *   S <- gamma S + Kh^T v   (in place),   o = alpha Qh S,   optional GN / gate.
+ * (hwhale notes: recurrent equations and the RecurrentRetention listing, which
+ * includes the current token and sums over d_k.)
+ * q, k: [B,H,1,d_k]; v, gate, out: [B,H,1,d_v]; state: [B,H,d_k,d_v] float32 in/out.
+ */
+rn_status rn_retention_recurrent_step(const rn_desc* desc, const void* q, const void* k,
+                                      const void* v, const void* gate, float* state,
+                                      void* out, void* stream);
+
+/*
+ * Standalone per-head GroupNorm (+ swish gate):
+ *   y = (x - mean) / sqrt(var + eps) * w + b over the d_v channels of each (b,h,t),
+ *   out = y * g * sigmoid(g) if gate != NULL, else y.
+ * (hwhale notes, multi-head paragraph: GroupNorm per head; m0nads notes, "Gated
+ * Multi-Scale Retention": swish gate.) x, gate, out: [B,H,N,d_v]; x and gate in
+ * in_dtype, out in out_dtype; w, b: DEVICE [H*d_v] or NULL. out may equal x when
+ * both dtypes match.
+ */
+rn_status rn_groupnorm_gate(int32_t B, int32_t H, int32_t N, int32_t d_v,
+                            rn_dtype in_dtype, rn_dtype out_dtype, const void* x,
+                            const void* gate, const float* w, const float* b, float eps,
+                            void* out, void* stream);
+
+/* Static name of a status code. */
+const char* rn_status_str(rn_status s);
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* rn_last_error(void);
+/* Library version, e.g. "0.1.0". */
+const char* rn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RN_RETENTION_H */

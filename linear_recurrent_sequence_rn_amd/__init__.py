@@ -1,0 +1,256 @@
+"""Multi-scale retention (RetNet) forward pass on MI355X — Python binding.
+
+A thin ctypes layer over ``librn_retention.so`` (C ABI in include/rn_retention.h).
+Functions carry the C names; they only marshal arguments: check tensors, allocate
+outputs with torch, pass device pointers and the current HIP stream. Every step of
+the computation runs in the library's HIP kernels. There is no CPU fallback: if the
+library is missing, importing this package raises.
+
+Build the library with ``python -m linear_recurrent_sequence_rn_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from pathlib import Path
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+__all__ = [
+    "RN_OK", "RN_ERR_INVALID_ARG", "RN_ERR_UNSUPPORTED", "RN_ERR_HIP", "RN_ERR_WORKSPACE",
+    "RN_F32", "RN_BF16", "RN_NORM_D_ROW", "RN_NORM_R_ROW", "RN_EPI_GN", "RN_EPI_GATE",
+    "RN_FORCE_GENERIC", "RnError", "RnDesc", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
+    "rn_retention_parallel", "rn_retention_chunkwise", "rn_retention_recurrent_step",
+    "rn_groupnorm_gate", "rn_chunkwise_workspace_bytes", "rn_version", "make_desc",
+]
+
+LIB_PATH = Path(__file__).resolve().parent / "librn_retention.so"
+
+RN_OK, RN_ERR_INVALID_ARG, RN_ERR_UNSUPPORTED, RN_ERR_HIP, RN_ERR_WORKSPACE = 0, -1, -2, -3, -4
+RN_F32, RN_BF16 = 0, 1
+RN_NORM_D_ROW, RN_NORM_R_ROW, RN_EPI_GN, RN_EPI_GATE = 1, 2, 4, 8
+RN_FORCE_GENERIC = 1 << 8
+
+EXPORTED_SYMBOLS = (
+    "rn_retention_parallel", "rn_chunkwise_workspace_bytes", "rn_retention_chunkwise",
+    "rn_retention_recurrent_step", "rn_groupnorm_gate", "rn_status_str", "rn_last_error",
+    "rn_version",
+)
+
+
+class RnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_status_name(status)}: {msg}")
+        self.status = status
+
+
+class RnDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("flags", ctypes.c_uint32), ("pos0", ctypes.c_int64),
+        ("qk_scale", ctypes.c_float), ("gn_eps", ctypes.c_float),
+        ("gamma", ctypes.POINTER(ctypes.c_float)), ("theta", ctypes.POINTER(ctypes.c_float)),
+        ("gn_weight", ctypes.c_void_p), ("gn_bias", ctypes.c_void_p),
+    ]
+
+
+def _load():
+    if not LIB_PATH.exists():
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m linear_recurrent_sequence_rn_amd.build`")
+    L = ctypes.CDLL(str(LIB_PATH))
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    D = ctypes.POINTER(RnDesc)
+    L.rn_retention_parallel.argtypes = [D, vp, vp, vp, vp, vp, vp]
+    L.rn_retention_parallel.restype = i32
+    L.rn_chunkwise_workspace_bytes.argtypes = [D, i32]
+    L.rn_chunkwise_workspace_bytes.restype = sz
+    L.rn_retention_chunkwise.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.rn_retention_chunkwise.restype = i32
+    L.rn_retention_recurrent_step.argtypes = [D, vp, vp, vp, vp, vp, vp, vp]
+    L.rn_retention_recurrent_step.restype = i32
+    L.rn_groupnorm_gate.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                    ctypes.c_float, vp, vp]
+    L.rn_groupnorm_gate.restype = i32
+    L.rn_status_str.argtypes = [i32]
+    L.rn_status_str.restype = ctypes.c_char_p
+    L.rn_last_error.argtypes = []
+    L.rn_last_error.restype = ctypes.c_char_p
+    L.rn_version.argtypes = []
+    L.rn_version.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def _status_name(s: int) -> str:
+    return lib.rn_status_str(s).decode()
+
+
+def _check(status: int):
+    if status != RN_OK:
+        raise RnError(status, lib.rn_last_error().decode())
+
+
+def rn_version() -> str:
+    return lib.rn_version().decode()
+
+
+_DT = {torch.float32: RN_F32, torch.bfloat16: RN_BF16}
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t not in _DT:
+        raise TypeError(f"unsupported dtype {t}; use float32 or bfloat16")
+    return _DT[t]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def make_desc(B: int, H: int, N: int, d_k: int, d_v: int, in_dtype: int, out_dtype: int,
+              gamma: Sequence[float], theta: Sequence[float], *, flags: int = 0, pos0: int = 0,
+              qk_scale: float = 1.0, gn_eps: float = 1e-5, gn_weight=None, gn_bias=None):
+    """Builds an rn_desc; returns (desc, keepalive) — keep both alive across the call."""
+    g = np.ascontiguousarray(np.asarray(gamma, dtype=np.float32))
+    th = np.ascontiguousarray(np.asarray(theta, dtype=np.float32))
+    d = RnDesc()
+    d.B, d.H, d.N, d.d_k, d.d_v = B, H, N, d_k, d_v
+    d.in_dtype, d.out_dtype, d.flags, d.pos0 = in_dtype, out_dtype, flags, pos0
+    d.qk_scale, d.gn_eps = qk_scale, gn_eps
+    d.gamma = g.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    d.theta = th.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    d.gn_weight = None if gn_weight is None else gn_weight.data_ptr()
+    d.gn_bias = None if gn_bias is None else gn_bias.data_ptr()
+    return d, (g, th, gn_weight, gn_bias)
+
+
+def _flags(norm_d, norm_r, gn, gate, force_generic):
+    f = 0
+    if norm_d: f |= RN_NORM_D_ROW
+    if norm_r: f |= RN_NORM_R_ROW
+    if gn: f |= RN_EPI_GN
+    if gate is not None: f |= RN_EPI_GATE
+    if force_generic: f |= RN_FORCE_GENERIC
+    return f
+
+
+def _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos0, qk_scale, gn_eps, gn_weight, gn_bias):
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError(f"expected q,k [B,H,N,d_k] and v [B,H,N,d_v]; got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    if len(gamma) != H or len(theta) != dk // 2:
+        raise ValueError(f"need gamma[{H}] and theta[{dk // 2}]")
+    od = q.dtype if out_dtype is None else out_dtype
+    for t in (gn_weight, gn_bias):
+        if t is not None:
+            _ptr(t)
+            if t.dtype != torch.float32 or t.numel() != H * dv:
+                raise ValueError("gn_weight/gn_bias must be float32 with H*d_v elements")
+    d, keep = make_desc(B, H, N, dk, dv, _dtype_code(q.dtype), _dtype_code(od), gamma, theta,
+                        flags=flags, pos0=pos0, qk_scale=qk_scale, gn_eps=gn_eps,
+                        gn_weight=gn_weight, gn_bias=gn_bias)
+    return d, keep, od
+
+
+def rn_retention_parallel(q, k, v, gamma, theta, *, gate=None, out=None, out_dtype=None,
+                          pos0=0, qk_scale=1.0, norm_d=False, norm_r=False, gn=False,
+                          gn_eps=1e-5, gn_weight=None, gn_bias=None, force_generic=False):
+    """Parallel form; returns out [B,H,N,d_v]."""
+    flags = _flags(norm_d, norm_r, gn, gate, force_generic)
+    d, keep, od = _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos0, qk_scale, gn_eps,
+                            gn_weight, gn_bias)
+    if out is None:
+        out = torch.empty(v.shape, dtype=od, device=v.device)
+    _check(lib.rn_retention_parallel(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
+                                     _ptr(out), _stream(q)))
+    return out
+
+
+def rn_chunkwise_workspace_bytes(q, v, gamma, theta, chunk, *, gn=False, gate=None,
+                                 out_dtype=None, force_generic=False) -> int:
+    B, H, N, dk = q.shape
+    flags = _flags(False, False, gn, gate, force_generic)
+    od = q.dtype if out_dtype is None else out_dtype
+    d, keep = make_desc(B, H, N, dk, v.shape[-1], _dtype_code(q.dtype), _dtype_code(od), gamma,
+                        theta, flags=flags)
+    return int(lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), chunk))
+
+
+def rn_retention_chunkwise(q, k, v, gamma, theta, chunk, *, gate=None, state_in=None,
+                           state_out=None, out=None, out_dtype=None, workspace=None, pos0=0,
+                           qk_scale=1.0, gn=False, gn_eps=1e-5, gn_weight=None, gn_bias=None,
+                           force_generic=False):
+    """Chunkwise form; returns (out, state_out). ``state_out`` may be a tensor (written),
+    True (allocated), or None/False (discarded)."""
+    flags = _flags(False, False, gn, gate, force_generic)
+    d, keep, od = _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos0, qk_scale, gn_eps,
+                            gn_weight, gn_bias)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty(v.shape, dtype=od, device=v.device)
+    if state_out is True:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif state_out is False:
+        state_out = None
+    for s in (state_in, state_out):
+        if s is not None and (s.dtype != torch.float32 or tuple(s.shape) != (B, H, dk, dv)):
+            raise ValueError("states must be float32 [B,H,d_k,d_v]")
+    need = int(lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), chunk))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib.rn_retention_chunkwise(ctypes.byref(d), chunk, _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(gate), _ptr(state_in), _ptr(state_out), _ptr(out),
+                                      _ptr(workspace), workspace.numel(), _stream(q)))
+    return out, state_out
+
+
+def rn_retention_recurrent_step(q, k, v, gamma, theta, state, pos, *, gate=None, out=None,
+                                out_dtype=None, qk_scale=1.0, gn=False, gn_eps=1e-5,
+                                gn_weight=None, gn_bias=None):
+    """One decode step at position ``pos``; ``state`` [B,H,d_k,d_v] float32 is updated in
+    place. q, k: [B,H,1,d_k]; v: [B,H,1,d_v]. Returns out [B,H,1,d_v]."""
+    flags = _flags(False, False, gn, gate, False)
+    d, keep, od = _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos, qk_scale, gn_eps,
+                            gn_weight, gn_bias)
+    if state.dtype != torch.float32 or tuple(state.shape) != (q.shape[0], q.shape[1], q.shape[3], v.shape[3]):
+        raise ValueError("state must be float32 [B,H,d_k,d_v]")
+    if out is None:
+        out = torch.empty(v.shape, dtype=od, device=v.device)
+    _check(lib.rn_retention_recurrent_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
+                                           _ptr(state), _ptr(out), _stream(q)))
+    return out
+
+
+def rn_groupnorm_gate(x, gate=None, weight=None, bias=None, eps=1e-5, *, out=None, out_dtype=None):
+    """Per-head GroupNorm over the last axis of x [B,H,N,d_v] (+ swish gate)."""
+    B, H, N, dv = x.shape
+    od = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(x.shape, dtype=od, device=x.device)
+    if gate is not None and (gate.shape != x.shape or gate.dtype != x.dtype):
+        raise ValueError("gate must match x in shape and dtype")
+    _check(lib.rn_groupnorm_gate(B, H, N, dv, _dtype_code(x.dtype), _dtype_code(od), _ptr(x),
+                                 _ptr(gate), _ptr(weight), _ptr(bias), eps, _ptr(out), _stream(x)))
+    return out

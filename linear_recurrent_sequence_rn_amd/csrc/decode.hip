@@ -1,0 +1,133 @@
+// One recurrent retention step (decode): S <- gamma S + Kh^T v in place, o = alpha Qh S
+// (hwhale notes: recurrent equations and the RecurrentRetention listing).
+//
+// HBM-bound: the float32 state is read and written once per step; everything else is
+// a few KB. One 256-thread block owns one (b, h) state of d_k x d_v floats. Thread
+// (group g, column vector c) owns columns [c*VEC, c*VEC+VEC) of rows g, g+G, g+2G, ...
+// so each row is read and written by consecutive lanes in 16-byte pieces (a wave
+// covers 1 KB of one row per instruction). The rows of a thread are processed in
+// batches of kBatch independent loads to keep enough bytes in flight, with
+// non-temporal hints because the state (1 GB for batch 128 x 16 heads) is far larger
+// than the last-level cache and is not re-read within the step.
+#include "rn_device.h"
+#include "rn_kernels.h"
+
+namespace rn {
+namespace {
+
+constexpr int kBatch = 8;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int IN, int OUT, int VEC>
+__global__ void __launch_bounds__(256) decode_step(CallArgs a, const void* q, const void* k,
+                                                   const void* v, const void* gate, float* state,
+                                                   void* out) {
+  __shared__ float qh[kMaxDk];
+  __shared__ float kh[kMaxDk];
+  __shared__ float vv[kMaxDv];
+  __shared__ float part[256 * 4];
+  __shared__ float orow[kMaxDv];
+  __shared__ float red[4];
+  const int bh = blockIdx.x;
+  const int h = bh % a.H;
+  const int dk = a.dk, dv = a.dv;
+  for (int j = threadIdx.x; j < dk / 2; j += 256) {
+    float c, s;
+    angle_cs(a.pos0, a.ap.theta[j], &c, &s);
+    const int64_t o = static_cast<int64_t>(bh) * dk + 2 * j;
+    float q0 = Elem<IN>::load(q, o), q1 = Elem<IN>::load(q, o + 1);
+    float k0 = Elem<IN>::load(k, o), k1 = Elem<IN>::load(k, o + 1);
+    qh[2 * j] = q0 * c - q1 * s;
+    qh[2 * j + 1] = q0 * s + q1 * c;
+    kh[2 * j] = k0 * c - k1 * s;
+    kh[2 * j + 1] = k0 * s + k1 * c;
+  }
+  for (int c = threadIdx.x; c < dv; c += 256) vv[c] = Elem<IN>::load(v, static_cast<int64_t>(bh) * dv + c);
+  __syncthreads();
+
+  const float g = a.hp.gamma[h];
+  const int nq = dv / VEC;                 // column vectors per row
+  const int G = nq >= 256 ? 1 : 256 / nq;  // row groups
+  const int tid = threadIdx.x;
+  // A slot is one (row group, column vector); a thread owns one slot, or two when a
+  // row has more than 256 column vectors (odd d_v above 256).
+  for (int slot = tid; slot < G * nq; slot += 256) {
+    const int cq = slot % nq, grp = slot / nq;
+    float acc[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+    float vr[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) vr[i] = vv[cq * VEC + i];
+    float* S = state + static_cast<int64_t>(bh) * dk * dv + cq * VEC;
+    for (int d0 = grp; d0 < dk; d0 += G * kBatch) {
+      float sv[kBatch][VEC];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int d = d0 + u * G;
+        if (d < dk) {
+          if constexpr (VEC == 4) {
+            f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + static_cast<int64_t>(d) * dv));
+            sv[u][0] = x.x; sv[u][1] = x.y; sv[u][2] = x.z; sv[u][3] = x.w;
+          } else {
+            sv[u][0] = __builtin_nontemporal_load(S + static_cast<int64_t>(d) * dv);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int d = d0 + u * G;
+        if (d < dk) {
+          const float kd = kh[d], qd = qh[d];
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) {
+            float s = fmaf(g, sv[u][i], kd * vr[i]);
+            sv[u][i] = s;
+            acc[i] = fmaf(qd, s, acc[i]);
+          }
+          if constexpr (VEC == 4) {
+            f32x4 x = {sv[u][0], sv[u][1], sv[u][2], sv[u][3]};
+            __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(S + static_cast<int64_t>(d) * dv));
+          } else {
+            __builtin_nontemporal_store(sv[u][0], S + static_cast<int64_t>(d) * dv);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) part[grp * dv + cq * VEC + i] = acc[i];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < dv; c += 256) {
+    float s = 0.f;
+    for (int gg = 0; gg < G; ++gg) s += part[gg * dv + c];
+    orow[c] = a.alpha * s;
+  }
+  __syncthreads();
+  row_epilogue256<IN, OUT>(orow, dv, a, h, gate, static_cast<int64_t>(bh) * dv, out, red);
+}
+
+template <int IN, int OUT>
+hipError_t launch_t(const CallArgs& a, const void* q, const void* k, const void* v,
+                    const void* gate, float* state, void* out, hipStream_t st) {
+  dim3 grid(a.B * a.H);
+  if (a.dv % 4 == 0 && a.dv / 4 <= 256)
+    hipLaunchKernelGGL((decode_step<IN, OUT, 4>), grid, dim3(256), 0, st, a, q, k, v, gate, state, out);
+  else
+    hipLaunchKernelGGL((decode_step<IN, OUT, 1>), grid, dim3(256), 0, st, a, q, k, v, gate, state, out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_step(const CallArgs& a, int in_dt, int out_dt, const void* q,
+                              const void* k, const void* v, const void* gate, float* state,
+                              void* out, hipStream_t st) {
+  if (in_dt == RN_F32)
+    return out_dt == RN_F32 ? launch_t<RN_F32, RN_F32>(a, q, k, v, gate, state, out, st)
+                            : launch_t<RN_F32, RN_BF16>(a, q, k, v, gate, state, out, st);
+  return out_dt == RN_F32 ? launch_t<RN_BF16, RN_F32>(a, q, k, v, gate, state, out, st)
+                          : launch_t<RN_BF16, RN_BF16>(a, q, k, v, gate, state, out, st);
+}
+
+}  // namespace rn

@@ -1,0 +1,197 @@
+// C ABI of the retention library: host-side validation and kernel dispatch.
+// Every argument is checked before the first HIP call, so an invalid call launches
+// nothing; failures return a status and leave a thread-local message.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "rn_kernels.h"
+#include "rn_retention.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+rn_status fail(rn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+rn_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return RN_OK;
+  return fail(RN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+enum class Form { kParallel, kChunkwise, kStep };
+
+constexpr uint32_t kKnownFlags =
+    RN_NORM_D_ROW | RN_NORM_R_ROW | RN_EPI_GN | RN_EPI_GATE | RN_FORCE_GENERIC;
+
+bool dtype_ok(rn_dtype d) { return d == RN_F32 || d == RN_BF16; }
+
+// Validates a descriptor for one form; fills the kernel argument block.
+rn_status check_desc(const rn_desc* d, Form form, rn::CallArgs* a) {
+  if (!d) return fail(RN_ERR_INVALID_ARG, "desc is NULL");
+  if (d->B < 1 || d->H < 1 || d->N < 1 || d->d_k < 1 || d->d_v < 1)
+    return fail(RN_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d H=%d N=%d d_k=%d d_v=%d)", d->B,
+                d->H, d->N, d->d_k, d->d_v);
+  if (d->d_k % 2) return fail(RN_ERR_INVALID_ARG, "d_k=%d must be even (coordinate pairs)", d->d_k);
+  if (d->d_k > rn::kMaxDk) return fail(RN_ERR_UNSUPPORTED, "d_k=%d > %d", d->d_k, rn::kMaxDk);
+  if (d->d_v > rn::kMaxDv) return fail(RN_ERR_UNSUPPORTED, "d_v=%d > %d", d->d_v, rn::kMaxDv);
+  if (d->H > rn::kMaxHeads) return fail(RN_ERR_UNSUPPORTED, "H=%d > %d", d->H, rn::kMaxHeads);
+  if (d->B > 65535) return fail(RN_ERR_UNSUPPORTED, "B=%d > 65535", d->B);
+  if (form == Form::kStep && d->N != 1)
+    return fail(RN_ERR_INVALID_ARG, "recurrent step needs N == 1 (got %d)", d->N);
+  if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype))
+    return fail(RN_ERR_INVALID_ARG, "unknown dtype (in=%d out=%d)", d->in_dtype, d->out_dtype);
+  if (d->flags & ~kKnownFlags) return fail(RN_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
+  if ((d->flags & RN_EPI_GATE) && !(d->flags & RN_EPI_GN))
+    return fail(RN_ERR_INVALID_ARG, "RN_EPI_GATE requires RN_EPI_GN");
+  if (form != Form::kParallel && (d->flags & (RN_NORM_D_ROW | RN_NORM_R_ROW)))
+    return fail(RN_ERR_INVALID_ARG, "row rescalings apply to the parallel form only");
+  if (d->pos0 < 0 || d->pos0 > (int64_t(1) << 40))
+    return fail(RN_ERR_INVALID_ARG, "pos0=%lld outside [0, 2^40]", (long long)d->pos0);
+  if (!std::isfinite(d->qk_scale)) return fail(RN_ERR_INVALID_ARG, "qk_scale is not finite");
+  if ((d->flags & RN_EPI_GN) && !(d->gn_eps >= 0.f && std::isfinite(d->gn_eps)))
+    return fail(RN_ERR_INVALID_ARG, "gn_eps must be finite and >= 0");
+  if (!d->gamma || !d->theta) return fail(RN_ERR_INVALID_ARG, "gamma/theta is NULL");
+  std::memset(a, 0, sizeof(*a));
+  for (int h = 0; h < d->H; ++h) {
+    const float g = d->gamma[h];
+    if (!(g > 0.f && g <= 1.f)) return fail(RN_ERR_INVALID_ARG, "gamma[%d]=%g not in (0, 1]", h, g);
+    a->hp.gamma[h] = g;
+    a->hp.log2g[h] = static_cast<float>(std::log2(static_cast<double>(g)));
+  }
+  for (int j = 0; j < d->d_k / 2; ++j) {
+    if (!std::isfinite(d->theta[j])) return fail(RN_ERR_INVALID_ARG, "theta[%d] is not finite", j);
+    a->ap.theta[j] = d->theta[j];
+  }
+  a->B = d->B; a->H = d->H; a->N = d->N; a->dk = d->d_k; a->dv = d->d_v;
+  a->pos0 = d->pos0;
+  a->alpha = d->qk_scale;
+  a->eps = d->gn_eps;
+  a->flags = d->flags;
+  a->gn_w = d->gn_weight;
+  a->gn_b = d->gn_bias;
+  return RN_OK;
+}
+
+rn_status check_ptrs(const rn_desc* d, const void* q, const void* k, const void* v,
+                     const void* gate, const void* out) {
+  if (!q || !k || !v || !out) return fail(RN_ERR_INVALID_ARG, "q/k/v/out pointer is NULL");
+  if ((d->flags & RN_EPI_GATE) && !gate) return fail(RN_ERR_INVALID_ARG, "RN_EPI_GATE needs a gate");
+  return RN_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t generic_ws_bytes(const rn_desc* d) {
+  return align256(size_t(d->B) * d->H * d->d_k * d->d_v * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rn_version(void) { return "0.1.0"; }
+
+const char* rn_last_error(void) { return g_err; }
+
+const char* rn_status_str(rn_status s) {
+  switch (s) {
+    case RN_OK: return "RN_OK";
+    case RN_ERR_INVALID_ARG: return "RN_ERR_INVALID_ARG";
+    case RN_ERR_UNSUPPORTED: return "RN_ERR_UNSUPPORTED";
+    case RN_ERR_HIP: return "RN_ERR_HIP";
+    case RN_ERR_WORKSPACE: return "RN_ERR_WORKSPACE";
+    default: return "RN_ERR_UNKNOWN";
+  }
+}
+
+rn_status rn_retention_parallel(const rn_desc* desc, const void* q, const void* k, const void* v,
+                                const void* gate, void* out, void* stream) {
+  rn::CallArgs a;
+  rn_status s = check_desc(desc, Form::kParallel, &a);
+  if (s != RN_OK) return s;
+  if ((s = check_ptrs(desc, q, k, v, gate, out)) != RN_OK) return s;
+  g_err[0] = 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(rn::launch_generic_parallel(a, desc->in_dtype, desc->out_dtype, q, k, v,
+                                                gate, out, st),
+                    "parallel launch");
+}
+
+size_t rn_chunkwise_workspace_bytes(const rn_desc* desc, int32_t chunk) {
+  rn::CallArgs a;
+  if (chunk < 1 || check_desc(desc, Form::kChunkwise, &a) != RN_OK) return 0;
+  return generic_ws_bytes(desc);
+}
+
+rn_status rn_retention_chunkwise(const rn_desc* desc, int32_t chunk, const void* q, const void* k,
+                                 const void* v, const void* gate, const float* state_in,
+                                 float* state_out, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  rn::CallArgs a;
+  rn_status s = check_desc(desc, Form::kChunkwise, &a);
+  if (s != RN_OK) return s;
+  if (chunk < 1) return fail(RN_ERR_INVALID_ARG, "chunk=%d must be >= 1", chunk);
+  if ((s = check_ptrs(desc, q, k, v, gate, out)) != RN_OK) return s;
+  const size_t need = rn_chunkwise_workspace_bytes(desc, chunk);
+  if (!workspace || workspace_bytes < need)
+    return fail(RN_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(RN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  a.chunk = chunk;
+  g_err[0] = 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(rn::launch_generic_chunkwise(a, desc->in_dtype, desc->out_dtype, q, k, v,
+                                                 gate, state_in, state_out, out,
+                                                 static_cast<float*>(workspace), st),
+                    "chunkwise launch");
+}
+
+rn_status rn_retention_recurrent_step(const rn_desc* desc, const void* q, const void* k,
+                                      const void* v, const void* gate, float* state, void* out,
+                                      void* stream) {
+  rn::CallArgs a;
+  rn_status s = check_desc(desc, Form::kStep, &a);
+  if (s != RN_OK) return s;
+  if ((s = check_ptrs(desc, q, k, v, gate, out)) != RN_OK) return s;
+  if (!state) return fail(RN_ERR_INVALID_ARG, "state pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(state) % 16)
+    return fail(RN_ERR_INVALID_ARG, "state must be 16-byte aligned");
+  g_err[0] = 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(rn::launch_decode_step(a, desc->in_dtype, desc->out_dtype, q, k, v, gate,
+                                           state, out, st),
+                    "recurrent step launch");
+}
+
+rn_status rn_groupnorm_gate(int32_t B, int32_t H, int32_t N, int32_t d_v, rn_dtype in_dtype,
+                            rn_dtype out_dtype, const void* x, const void* gate, const float* w,
+                            const float* b, float eps, void* out, void* stream) {
+  if (B < 1 || H < 1 || N < 1 || d_v < 1)
+    return fail(RN_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d H=%d N=%d d_v=%d)", B, H, N, d_v);
+  if (d_v > rn::kMaxDv) return fail(RN_ERR_UNSUPPORTED, "d_v=%d > %d", d_v, rn::kMaxDv);
+  if (int64_t(B) * H * N > (int64_t(1) << 33))
+    return fail(RN_ERR_UNSUPPORTED, "B*H*N too large");
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+    return fail(RN_ERR_INVALID_ARG, "unknown dtype (in=%d out=%d)", in_dtype, out_dtype);
+  if (!x || !out) return fail(RN_ERR_INVALID_ARG, "x/out pointer is NULL");
+  if (!(eps >= 0.f && std::isfinite(eps))) return fail(RN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (out == x && in_dtype != out_dtype)
+    return fail(RN_ERR_INVALID_ARG, "in-place GroupNorm needs in_dtype == out_dtype");
+  g_err[0] = 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(rn::launch_groupnorm_gate(B, H, N, d_v, in_dtype, out_dtype, x, gate, w, b,
+                                              eps, out, st),
+                    "groupnorm launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,23 @@
+// Host-side launchers of the retention kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "rn_device.h"
+
+namespace rn {
+
+hipError_t launch_generic_parallel(const CallArgs& a, int in_dt, int out_dt, const void* q,
+                                   const void* k, const void* v, const void* gate, void* out,
+                                   hipStream_t st);
+hipError_t launch_generic_chunkwise(const CallArgs& a, int in_dt, int out_dt, const void* q,
+                                    const void* k, const void* v, const void* gate,
+                                    const float* s_in, float* s_out, void* out, float* ws,
+                                    hipStream_t st);
+hipError_t launch_decode_step(const CallArgs& a, int in_dt, int out_dt, const void* q,
+                              const void* k, const void* v, const void* gate, float* state,
+                              void* out, hipStream_t st);
+hipError_t launch_groupnorm_gate(int B, int H, int N, int dv, int in_dt, int out_dt,
+                                 const void* x, const void* gate, const float* w, const float* b,
+                                 float eps, void* out, hipStream_t st);
+
+}  // namespace rn

@@ -1,0 +1,143 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+symbol the header declares, and rejects invalid arguments before any HIP call.
+Pointers passed here are never dereferenced: validation fails first."""
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import linear_recurrent_sequence_rn_amd as rn
+
+ROOT = Path(__file__).resolve().parents[1]
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+def header_symbols():
+    txt = "\n".join(p.read_text() for p in (ROOT / "include").glob("*.h"))
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(rn_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_header_declares_the_boundary():
+    syms = header_symbols()
+    for s in ("rn_retention_parallel", "rn_retention_chunkwise", "rn_retention_recurrent_step",
+              "rn_groupnorm_gate"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol():
+    so = ctypes.CDLL(str(rn.LIB_PATH))
+    for s in header_symbols():
+        assert hasattr(so, s), s
+    assert set(header_symbols()) == set(rn.EXPORTED_SYMBOLS)
+
+
+def test_version_and_status_strings():
+    assert re.match(r"\d+\.\d+\.\d+", rn.rn_version())
+    assert rn.lib.rn_status_str(rn.RN_ERR_WORKSPACE) == b"RN_ERR_WORKSPACE"
+    assert rn.lib.rn_status_str(-99) == b"RN_ERR_UNKNOWN"
+
+
+def desc(**kw):
+    p = dict(B=1, H=2, N=8, d_k=16, d_v=16, in_dtype=rn.RN_BF16, out_dtype=rn.RN_F32,
+             gamma=[0.9, 0.8], theta=np.ones(8), flags=0, pos0=0, qk_scale=1.0, gn_eps=1e-5)
+    p.update(kw)
+    g, th = p.pop("gamma"), p.pop("theta")
+    B, H, N, dk, dv, i, o = (p.pop(x) for x in ("B", "H", "N", "d_k", "d_v", "in_dtype", "out_dtype"))
+    return rn.make_desc(B, H, N, dk, dv, i, o, g, th, **p)
+
+
+def par(d, gate=FAKE):
+    return rn.lib.rn_retention_parallel(ctypes.byref(d), FAKE, FAKE, FAKE, gate, FAKE, None)
+
+
+def chk(d, chunk=4, ws_bytes=1 << 30, ws=FAKE):
+    return rn.lib.rn_retention_chunkwise(ctypes.byref(d), chunk, FAKE, FAKE, FAKE, FAKE, None,
+                                         None, FAKE, ws, ws_bytes, None)
+
+
+def step(d, state=FAKE):
+    return rn.lib.rn_retention_recurrent_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, state,
+                                              FAKE, None)
+
+
+BAD_DESCS = [
+    (dict(B=0), rn.RN_ERR_INVALID_ARG),
+    (dict(N=0), rn.RN_ERR_INVALID_ARG),
+    (dict(d_k=15, theta=np.ones(7)), rn.RN_ERR_INVALID_ARG),
+    (dict(d_k=258, theta=np.ones(129)), rn.RN_ERR_UNSUPPORTED),
+    (dict(d_v=513), rn.RN_ERR_UNSUPPORTED),
+    (dict(H=129, gamma=np.full(129, 0.9)), rn.RN_ERR_UNSUPPORTED),
+    (dict(in_dtype=7), rn.RN_ERR_INVALID_ARG),
+    (dict(out_dtype=-1), rn.RN_ERR_INVALID_ARG),
+    (dict(flags=1 << 20), rn.RN_ERR_INVALID_ARG),
+    (dict(flags=rn.RN_EPI_GATE), rn.RN_ERR_INVALID_ARG),          # gate without GN
+    (dict(gamma=[0.9, 0.0]), rn.RN_ERR_INVALID_ARG),
+    (dict(gamma=[0.9, 1.5]), rn.RN_ERR_INVALID_ARG),
+    (dict(gamma=[float("nan"), 0.5]), rn.RN_ERR_INVALID_ARG),
+    (dict(theta=np.r_[np.ones(7), np.inf]), rn.RN_ERR_INVALID_ARG),
+    (dict(qk_scale=float("inf")), rn.RN_ERR_INVALID_ARG),
+    (dict(flags=rn.RN_EPI_GN, gn_eps=-1.0), rn.RN_ERR_INVALID_ARG),
+    (dict(pos0=-1), rn.RN_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_DESCS)
+def test_invalid_descriptors_rejected_everywhere(kw, code):
+    d, keep = desc(**kw)
+    assert par(d) == code, rn.lib.rn_last_error()
+    assert rn.lib.rn_last_error() != b""
+    assert chk(d) == code
+    d1, keep1 = desc(**{**kw, "N": 1} if "N" not in kw else kw)
+    assert step(d1) == code
+    assert rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), 4) == 0
+
+
+def test_null_desc_and_pointers():
+    assert rn.lib.rn_retention_parallel(None, FAKE, FAKE, FAKE, None, FAKE, None) == rn.RN_ERR_INVALID_ARG
+    d, keep = desc()
+    assert rn.lib.rn_retention_parallel(ctypes.byref(d), None, FAKE, FAKE, None, FAKE, None) == rn.RN_ERR_INVALID_ARG
+    assert rn.lib.rn_retention_parallel(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, None) == rn.RN_ERR_INVALID_ARG
+    d, keep = desc(flags=rn.RN_EPI_GN | rn.RN_EPI_GATE)
+    assert par(d, gate=None) == rn.RN_ERR_INVALID_ARG     # gate flag without a gate tensor
+
+
+def test_chunkwise_specific_errors():
+    d, keep = desc()
+    assert chk(d, chunk=0) == rn.RN_ERR_INVALID_ARG
+    need = rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), 4)
+    assert need > 0
+    assert chk(d, ws_bytes=need - 1) == rn.RN_ERR_WORKSPACE
+    assert chk(d, ws=None) == rn.RN_ERR_WORKSPACE
+    d, keep = desc(flags=rn.RN_NORM_D_ROW)
+    assert chk(d) == rn.RN_ERR_INVALID_ARG                 # rescalings: parallel form only
+    d, keep = desc(flags=rn.RN_NORM_R_ROW, N=1)
+    assert step(d) == rn.RN_ERR_INVALID_ARG
+
+
+def test_workspace_independent_of_sequence_length():
+    sizes = set()
+    for N in (64, 8192, 65536):
+        d, keep = desc(N=N, d_k=256, d_v=512, theta=np.ones(128), H=16, gamma=np.full(16, 0.9))
+        sizes.add(rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), 256))
+    assert len(sizes) == 1 and sizes.pop() > 0
+
+
+def test_step_specific_errors():
+    d, keep = desc(N=2)
+    assert step(d) == rn.RN_ERR_INVALID_ARG                # decode takes one token
+    d, keep = desc(N=1)
+    assert step(d, state=None) == rn.RN_ERR_INVALID_ARG
+    assert step(d, state=ctypes.c_void_p(0x1004)) == rn.RN_ERR_INVALID_ARG  # misaligned
+
+
+def test_groupnorm_errors():
+    f = rn.lib.rn_groupnorm_gate
+    assert f(0, 1, 1, 8, rn.RN_F32, rn.RN_F32, FAKE, None, None, None, 1e-5, FAKE, None) == rn.RN_ERR_INVALID_ARG
+    assert f(1, 1, 1, 600, rn.RN_F32, rn.RN_F32, FAKE, None, None, None, 1e-5, FAKE, None) == rn.RN_ERR_UNSUPPORTED
+    assert f(1, 1, 1, 8, 5, rn.RN_F32, FAKE, None, None, None, 1e-5, FAKE, None) == rn.RN_ERR_INVALID_ARG
+    assert f(1, 1, 1, 8, rn.RN_F32, rn.RN_F32, None, None, None, None, 1e-5, FAKE, None) == rn.RN_ERR_INVALID_ARG
+    assert f(1, 1, 1, 8, rn.RN_F32, rn.RN_F32, FAKE, None, None, None, -1.0, FAKE, None) == rn.RN_ERR_INVALID_ARG
+    assert f(1, 1, 1, 8, rn.RN_F32, rn.RN_BF16, FAKE, None, None, None, 1e-5, FAKE, None) == rn.RN_ERR_INVALID_ARG  # in place, dtype change

@@ -1,0 +1,212 @@
+"""GPU parity: the HIP kernels against the fp64 oracle on the same seeded inputs.
+
+Tolerances:
+  * float32 arithmetic paths: per (b, h) slice, ||gpu - ref||_inf <= 1e-4 ||ref||_inf
+    (raw outputs, GroupNorm outputs and final states alike).
+  * bf16 MFMA paths: 2e-2 max-abs after GroupNorm (fp32 output); raw outputs and
+    states at a relative bound derived from bf16 operand rounding (see each test).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def rn():
+    import linear_recurrent_sequence_rn_amd as m
+    return m
+
+
+def rel_inf(gpu, ref):
+    """max over (b,h) of ||gpu - ref||_inf / ||ref||_inf."""
+    g = O.to64(gpu)
+    r = O.to64(ref)
+    err = np.abs(g - r).reshape(r.shape[0], r.shape[1], -1).max(-1)
+    nrm = np.abs(r).reshape(r.shape[0], r.shape[1], -1).max(-1)
+    return float((err / np.maximum(nrm, 1e-30)).max())
+
+
+def dev(x):
+    return None if x is None else x.to(DEV)
+
+
+def inputs(name, **kw):
+    w = W.WORKLOADS[name]
+    x = W.make_inputs(w, **kw)
+    return w, x
+
+
+# ---- tiny workload: float32, all three forms, raw and GroupNorm ----------------------
+
+@pytest.mark.parametrize("gn", [False, True])
+def test_tiny_parallel_fp32(gn):
+    w, x = inputs("tiny")
+    out = rn().rn_retention_parallel(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"],
+                                     gn=gn, gn_eps=w.gn_eps)
+    ref = O.brute_force(x["q"], x["k"], x["v"], x["gamma"], x["theta"])
+    ref = O.apply_epilogue(ref, gn=gn, eps=w.gn_eps)
+    assert rel_inf(out.cpu(), ref) <= 1e-4
+
+
+@pytest.mark.parametrize("gn", [False, True])
+@pytest.mark.parametrize("chunk", [16, 5, 64, 1])
+def test_tiny_chunkwise_fp32(gn, chunk):
+    w, x = inputs("tiny")
+    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
+                                         x["theta"], chunk, state_out=True, gn=gn, gn_eps=w.gn_eps)
+    ref = O.brute_force(x["q"], x["k"], x["v"], x["gamma"], x["theta"])
+    _, Sref = O.recurrent(x["q"], x["k"], x["v"], x["gamma"], x["theta"])
+    assert rel_inf(out.cpu(), O.apply_epilogue(ref, gn=gn, eps=w.gn_eps)) <= 1e-4
+    assert rel_inf(S.cpu(), Sref) <= 1e-4
+
+
+@pytest.mark.parametrize("gn", [False, True])
+def test_tiny_recurrent_fp32(gn):
+    w, x = inputs("tiny")
+    B, H, N, dk = x["q"].shape
+    dv = x["v"].shape[-1]
+    S = torch.zeros(B, H, dk, dv, device=DEV)
+    outs = []
+    for t in range(N):
+        sl = slice(t, t + 1)
+        outs.append(rn().rn_retention_recurrent_step(dev(x["q"][:, :, sl].contiguous()),
+                                                     dev(x["k"][:, :, sl].contiguous()),
+                                                     dev(x["v"][:, :, sl].contiguous()),
+                                                     x["gamma"], x["theta"], S, t, gn=gn,
+                                                     gn_eps=w.gn_eps))
+    out = torch.cat(outs, 2).cpu()
+    ref = O.brute_force(x["q"], x["k"], x["v"], x["gamma"], x["theta"])
+    _, Sref = O.recurrent(x["q"], x["k"], x["v"], x["gamma"], x["theta"])
+    assert rel_inf(out, O.apply_epilogue(ref, gn=gn, eps=w.gn_eps)) <= 1e-4
+    assert rel_inf(S.cpu(), Sref) <= 1e-4
+
+
+def test_tiny_parallel_rescaled_fp32():
+    """The parallel form with the 1.3B workload's flags: alpha = 1/sqrt(d_k), D and R row
+    normalisation, GroupNorm."""
+    w, x = inputs("tiny")
+    a = 1.0 / 4.0
+    for nd, nr in ((True, False), (False, True), (True, True)):
+        out = rn().rn_retention_parallel(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
+                                         x["theta"], qk_scale=a, norm_d=nd, norm_r=nr)
+        ref = O.parallel(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 0, a, nd, nr)
+        assert rel_inf(out.cpu(), ref) <= 1e-4, (nd, nr)
+    out = rn().rn_retention_parallel(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"],
+                                     qk_scale=a, norm_d=True, norm_r=True, gn=True)
+    ref = O.group_norm(O.parallel(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 0, a, True, True))
+    assert rel_inf(out.cpu(), ref) <= 1e-4
+
+
+def test_tiny_state_in_pos0_gate_affine_fp32():
+    """Initial state, a nonzero start position, ragged chunks, the swish gate and a GN affine."""
+    w = W.WORKLOADS["tiny"]
+    x = W.make_inputs(W.Workload(**{**w.__dict__, "gate": True, "state_std": 0.3}))
+    B, H, N, dk = x["q"].shape
+    dv = x["v"].shape[-1]
+    gw = torch.randn(H * dv, generator=torch.Generator().manual_seed(5))
+    gb = torch.randn(H * dv, generator=torch.Generator().manual_seed(6))
+    pos0 = 70000
+    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
+                                         x["theta"], 7, gate=dev(x["gate"]),
+                                         state_in=dev(x["state"]), state_out=True, pos0=pos0,
+                                         gn=True, gn_weight=dev(gw), gn_bias=dev(gb))
+    raw, Sref = O.chunkwise(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 7, pos0, 1.0, x["state"])
+    ref = O.groupnorm_gate(raw, x["gate"], 1e-5, gw.reshape(H, dv), gb.reshape(H, dv))
+    assert rel_inf(out.cpu(), ref) <= 1e-4
+    assert rel_inf(S.cpu(), Sref) <= 1e-4
+
+
+# ---- decode step ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_steps_match_oracle(dtype):
+    """Reduced-batch decode workload (6.7B head shape): 6 steps in place from a random
+    state at positions near 65536; every output and the final state."""
+    w = W.Workload(**{**W.WORKLOADS["decode_6p7b"].__dict__, "B": 3, "dtype": dtype})
+    S0 = W.initial_state(w)
+    S = dev(S0.clone())
+    Sref = S0
+    for i in range(6):
+        pos = 65536 - 6 + i
+        x = W.make_decode_step_inputs(w, i)
+        out = rn().rn_retention_recurrent_step(dev(x["q"]), dev(x["k"]), dev(x["v"]), w.gamma(),
+                                               w.theta(), S, pos, out_dtype=torch.float32)
+        o_ref, Sref = O.recurrent_step(x["q"], x["k"], x["v"], w.gamma(), w.theta(), pos, 1.0, Sref)
+        assert rel_inf(out.cpu()[:, :, 0], o_ref) <= 1e-4
+    assert rel_inf(S.cpu(), Sref) <= 1e-4
+
+
+def test_decode_full_batch_sampled():
+    """Full decode shape (batch 128, 16 heads, 256 x 512 state): one step, checked on 16
+    sampled (b, h) pairs, in the launch configuration the benchmark uses."""
+    w = W.WORKLOADS["decode_6p7b"]
+    S0 = W.initial_state(w)
+    S = dev(S0)
+    x = W.make_decode_step_inputs(w, 0)
+    out = rn().rn_retention_recurrent_step(dev(x["q"]), dev(x["k"]), dev(x["v"]), w.gamma(),
+                                           w.theta(), S, 0, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, 128, 16), rng.integers(0, 16, 16))]
+    Sg = S.cpu()
+    for b, h in pairs:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        o_ref, s_ref = O.recurrent_step(x["q"][sl], x["k"][sl], x["v"][sl], w.gamma()[h:h + 1],
+                                        w.theta(), 0, 1.0, S0[sl])
+        assert rel_inf(out.cpu()[sl][:, :, 0], o_ref) <= 1e-4
+        assert rel_inf(Sg[sl], s_ref) <= 1e-4
+
+
+def test_decode_gn_gate_bf16_out():
+    w = W.Workload(**{**W.WORKLOADS["decode_6p7b"].__dict__, "B": 2})
+    S0 = W.initial_state(w)
+    x = W.make_decode_step_inputs(w, 3)
+    g = torch.randn(2, 16, 1, 512, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    S = dev(S0.clone())
+    out = rn().rn_retention_recurrent_step(dev(x["q"]), dev(x["k"]), dev(x["v"]), w.gamma(),
+                                           w.theta(), S, 17, gate=dev(g), gn=True)
+    o_ref, _ = O.recurrent_step(x["q"], x["k"], x["v"], w.gamma(), w.theta(), 17, 1.0, S0)
+    ref = O.groupnorm_gate(o_ref[:, :, None], g)
+    d = np.abs(O.to64(out.cpu()) - ref)
+    # bf16 output: GN values are O(1); allow the bar plus half a bf16 ulp of the reference
+    assert (d <= 2e-2 + np.abs(ref) * 2.0 ** -8).all()
+
+
+# ---- standalone GroupNorm + gate ----------------------------------------------------
+
+@pytest.mark.parametrize("dt,dv", [(torch.float32, 512), (torch.bfloat16, 512), (torch.float32, 37),
+                                   (torch.bfloat16, 100)])
+def test_groupnorm_gate(dt, dv):
+    gen = torch.Generator().manual_seed(dv)
+    x = (torch.randn(2, 3, 5, dv, generator=gen) * 3 + 1).to(dt)
+    g = torch.randn(2, 3, 5, dv, generator=gen).to(dt)
+    w = torch.randn(3 * dv, generator=gen)
+    b = torch.randn(3 * dv, generator=gen)
+    out = rn().rn_groupnorm_gate(dev(x), dev(g), dev(w), dev(b), 1e-5, out_dtype=torch.float32)
+    ref = O.groupnorm_gate(x, g, 1e-5, w.reshape(3, dv), b.reshape(3, dv))
+    assert rel_inf(out.cpu(), ref) <= 1e-4
+    out2 = rn().rn_groupnorm_gate(dev(x), None, None, None, 1e-5, out_dtype=torch.float32)
+    assert rel_inf(out2.cpu(), O.group_norm(x, 1e-5)) <= 1e-4
+
+
+# ---- generic path with bf16 inputs ---------------------------------------------------
+
+def test_generic_bf16_inputs_fp32_accuracy():
+    """The plain kernels compute in float32 from bf16 inputs: 1e-4 relative holds."""
+    w = W.Workload("g", "all", B=2, H=3, N=45, d_k=32, d_v=24, dtype="bf16", chunk=8, seed=21)
+    x = W.make_inputs(w)
+    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
+                                         x["theta"], 8, state_out=True, out_dtype=torch.float32,
+                                         pos0=3, force_generic=True)
+    ref, Sref = O.chunkwise(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 8, 3)
+    assert rel_inf(out.cpu(), ref) <= 1e-4
+    assert rel_inf(S.cpu(), Sref) <= 1e-4
+    out = rn().rn_retention_parallel(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"],
+                                     out_dtype=torch.float32, pos0=3, force_generic=True)
+    assert rel_inf(out.cpu(), O.parallel(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 3)) <= 1e-4
