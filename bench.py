@@ -1,0 +1,185 @@
+"""Benchmark of the retention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one chunkwise forward of the 6.7B-shaped training workload (B=2, H=16,
+N=8192, d_k=256, d_v=512, chunk 256, bf16 q/k/v/gate, GroupNorm + swish gate, bf16
+output, float32 final state) with inputs resident in HBM. The line also carries the
+decode step time of the 6.7B-shaped decode workload (batch 128, 16 heads, float32
+state updated in place; 1024 sequential steps timed back to back).
+
+Prints one JSON line. `roofline` describes the fused chunkwise kernel: its average
+duration is measured with HIP events recorded on the stream it runs on; achieved
+bandwidth = compulsory HBM bytes / duration. `cpu_baseline` times the fp64 oracle on
+a bounded sample (one head of the same workload) on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def chunkwise_work(B, H, N, dk, dv, C):
+    """Algorithmic flops and compulsory HBM bytes of one chunkwise forward with
+    GroupNorm + gate: causal intra-chunk pairs (C+1)(dk+dv) per token, cross term and
+    state carry 2*dk*dv each per token; bytes: q, k, v, gate read, out written (bf16),
+    final state written (fp32)."""
+    th = B * H * N
+    flops = th * ((C + 1) * (dk + dv) + 4 * dk * dv)
+    bytes_ = th * 2 * (dk + dk + dv + dv + dv) + B * H * dk * dv * 4
+    return flops, bytes_
+
+
+def decode_work(B, H, dk, dv):
+    flops = 5 * B * H * dk * dv
+    bytes_ = B * H * dk * dv * 4 * 2 + B * H * (dk + dk + dv) * 2 + B * H * dv * 4
+    return flops, bytes_
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the retention heads shard over GPUs without communication, so the "
+              "whole-job figure is N times the one-GPU figure, which is not measured here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import linear_recurrent_sequence_rn_amd as rn
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.WORKLOADS["chunkwise_6p7b"]
+    x = W.make_inputs(w)
+    q, k, v, gate = (x[n].to(dev) for n in ("q", "k", "v", "gate"))
+    gamma, theta = x["gamma"], x["theta"]
+    out = torch.empty_like(v)
+    S_out = torch.empty(w.B, w.H, w.d_k, w.d_v, dtype=torch.float32, device=dev)
+    nws = rn.rn_chunkwise_workspace_bytes(q, v, gamma, theta, w.chunk, gn=True, gate=gate)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+    def step():
+        rn.rn_retention_chunkwise(q, k, v, gamma, theta, w.chunk, gate=gate, gn=True,
+                                  gn_eps=w.gn_eps, state_out=S_out, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    kern_s = float(np.mean(durs_ms)) / 1e3
+    tokens = w.B * w.N
+    value = tokens * args.steps / wall
+    flops, bytes_ = chunkwise_work(w.B, w.H, w.N, w.d_k, w.d_v, w.chunk)
+    gbs = bytes_ / kern_s / 1e9
+    tfl = flops / kern_s / 1e12
+
+    rec = {
+        "metric": "retention tokens/s (chunkwise fwd N=8192) + decode step us; % of roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "chunkwise_6p7b: B=2 H=16 N=8192 d_k=256 d_v=512 chunk=256, "
+                               "bf16 in/out, GroupNorm+swish gate, fp32 final state",
+                   "global_batch": w.B, "seq_len": w.N, "heads": w.H, "d_k": w.d_k, "d_v": w.d_v,
+                   "chunk": w.chunk},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "chunkwise_fused", "kernel_ms": kern_s * 1e3,
+                     "algorithmic_bytes": bytes_, "algorithmic_flops": flops,
+                     "mfma_tflops": tfl, "mfma_frac": tfl / BF16_PEAK_TFLOPS},
+    }
+
+    # ---- decode step ---------------------------------------------------------------
+    if not args.no_decode:
+        wd = W.WORKLOADS["decode_6p7b"]
+        state = W.initial_state(wd).to(dev)
+        n_in = 32
+        ins = [W.make_decode_step_inputs(wd, i) for i in range(n_in)]
+        ins = [{kk: t.to(dev) for kk, t in d.items()} for d in ins]
+        dout = torch.empty(wd.B, wd.H, 1, wd.d_v, dtype=torch.float32, device=dev)
+        g_d, th_d = wd.gamma(), wd.theta()
+        for i in range(3):
+            d = ins[i % n_in]
+            rn.rn_retention_recurrent_step(d["q"], d["k"], d["v"], g_d, th_d, state, i, out=dout)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.decode_steps):
+            d = ins[i % n_in]
+            rn.rn_retention_recurrent_step(d["q"], d["k"], d["v"], g_d, th_d, state, i, out=dout)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        step_us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+        dfl, dby = decode_work(wd.B, wd.H, wd.d_k, wd.d_v)
+        rec["decode_step_us"] = step_us
+        rec["decode"] = {"workload": "decode_6p7b: batch 128, H=16, d_k=256, d_v=512, fp32 state in place, "
+                                     f"{args.decode_steps} sequential steps",
+                         "tokens_per_s": wd.B / (step_us * 1e-6),
+                         "achieved_GBs": dby / (step_us * 1e-6) / 1e9,
+                         "hbm_frac": dby / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         "algorithmic_bytes": dby}
+        del state
+
+    # ---- CPU baseline: the fp64 oracle on one head of the same workload --------------
+    if not args.no_cpu_baseline:
+        import oracle as O
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            cores = len(os.sched_getaffinity(0))
+        sl = (slice(0, 1), slice(0, 1))
+        t0 = time.perf_counter()
+        raw, _ = O.chunkwise(x["q"][sl], x["k"][sl], x["v"][sl], gamma[:1], theta, w.chunk)
+        O.groupnorm_gate(raw, x["gate"][sl], w.gn_eps)
+        t1 = time.perf_counter() - t0
+        heads = w.B * w.H
+        rec["cpu_baseline"] = {"value": tokens / (t1 * heads), "unit": "tokens/s", "cores": cores,
+                               "kind": "oracle",
+                               "sample": f"1 of {heads} heads of chunkwise_6p7b (N=8192, chunk 256, "
+                                         f"GroupNorm+gate) in fp64 took {t1:.2f} s; scaled x{heads}"}
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

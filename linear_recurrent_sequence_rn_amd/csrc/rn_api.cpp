@@ -127,9 +127,14 @@ rn_status rn_retention_parallel(const rn_desc* desc, const void* q, const void* 
                     "parallel launch");
 }
 
+static bool use_mfma_chunkwise(const rn_desc* d, const rn::CallArgs& a) {
+  return !(d->flags & RN_FORCE_GENERIC) && rn::chunkwise_mfma_supported(a, d->in_dtype);
+}
+
 size_t rn_chunkwise_workspace_bytes(const rn_desc* desc, int32_t chunk) {
   rn::CallArgs a;
   if (chunk < 1 || check_desc(desc, Form::kChunkwise, &a) != RN_OK) return 0;
+  if (use_mfma_chunkwise(desc, a)) return align256(rn::chunkwise_mfma_ws_bytes(a));
   return generic_ws_bytes(desc);
 }
 
@@ -150,6 +155,10 @@ rn_status rn_retention_chunkwise(const rn_desc* desc, int32_t chunk, const void*
   a.chunk = chunk;
   g_err[0] = 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (use_mfma_chunkwise(desc, a))
+    return hip_status(rn::launch_chunkwise_mfma(a, desc->out_dtype, q, k, v, gate, state_in,
+                                                state_out, out, workspace, workspace_bytes, st),
+                      "chunkwise (MFMA) launch");
   return hip_status(rn::launch_generic_chunkwise(a, desc->in_dtype, desc->out_dtype, q, k, v,
                                                  gate, state_in, state_out, out,
                                                  static_cast<float*>(workspace), st),

@@ -20,4 +20,12 @@ hipError_t launch_groupnorm_gate(int B, int H, int N, int dv, int in_dt, int out
                                  const void* x, const void* gate, const float* w, const float* b,
                                  float eps, void* out, hipStream_t st);
 
+// Fused MFMA chunkwise kernel (bf16 inputs, d_k = 256, d_v in {64,128,256,512}).
+bool chunkwise_mfma_supported(const CallArgs& a, int in_dt);
+size_t chunkwise_mfma_ws_bytes(const CallArgs& a);
+hipError_t launch_chunkwise_mfma(const CallArgs& a, int out_dt, const void* q, const void* k,
+                                 const void* v, const void* gate, const float* s_in,
+                                 float* s_out, void* out, void* ws, size_t ws_bytes,
+                                 hipStream_t st);
+
 }  // namespace rn

@@ -1,0 +1,173 @@
+"""GPU parity of the fused MFMA chunkwise kernel (bf16 q/k/v, d_k = 256).
+
+Tolerances (bf16 operands, fp32 accumulation):
+  * raw outputs and final states: per (b, h), ||gpu - ref||_inf <= 1e-2 ||ref||_inf.
+    Qh, Kh, the bf16 copy of the state used by the cross term and the decayed scores
+    are each rounded to bf16 (relative 2^-9); an output is a sum of many such terms of
+    mixed sign, so the error of one element is ~2^-9 of the typical magnitude, about
+    2e-3 of the slice maximum; 1e-2 leaves a 5x margin.
+  * after GroupNorm (fp32 output): max-abs 2e-2; with the gate, 2e-2 * max(1, |swish(g)|).
+  * bf16 output: the same bound plus half a bf16 ulp of the reference.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def rn():
+    import linear_recurrent_sequence_rn_amd as m
+    return m
+
+
+def rel_inf(gpu, ref):
+    g, r = O.to64(gpu), O.to64(ref)
+    err = np.abs(g - r).reshape(r.shape[0], r.shape[1], -1).max(-1)
+    nrm = np.abs(r).reshape(r.shape[0], r.shape[1], -1).max(-1)
+    return float((err / np.maximum(nrm, 1e-30)).max())
+
+
+def dev(x):
+    return None if x is None else x.to(DEV)
+
+
+def wl(**kw):
+    base = dict(name="t", form="chunkwise", B=1, H=2, N=200, d_k=256, d_v=512, dtype="bf16",
+                chunk=64, gamma_kind="wide", qkv_std=1 / 16, seed=31)
+    base.update(kw)
+    return W.Workload(**base)
+
+
+def check_gated(out, ref, gate):
+    sw = np.abs(O.swish(gate)) if gate is not None else 1.0
+    bound = 2e-2 * np.maximum(1.0, sw)
+    d = np.abs(O.to64(out) - ref)
+    if out.dtype == torch.bfloat16:
+        bound = bound + np.abs(ref) * 2.0 ** -8
+    assert (d <= bound).all(), float((d / bound).max())
+
+
+def ws_for(q, v, gamma, theta, chunk, **kw):
+    n = rn().rn_chunkwise_workspace_bytes(q, v, gamma, theta, chunk, **kw)
+    return torch.zeros(n, dtype=torch.uint8, device=DEV)
+
+
+def counters(ws, heads):
+    c = ws[: heads * 256].view(torch.int32).reshape(heads, 64).cpu().numpy()
+    return c
+
+
+@pytest.mark.parametrize("N,pos0", [(200, 0), (64, 5), (1, 70000), (129, 3)])
+def test_raw_output_and_state(N, pos0):
+    w = wl(N=N, state_std=0.05)
+    x = W.make_inputs(w)
+    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
+                                         x["theta"], 64, state_in=dev(x["state"]), state_out=True,
+                                         out_dtype=torch.float32, pos0=pos0)
+    ref, Sref = O.chunkwise(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 64, pos0, 1.0, x["state"])
+    assert rel_inf(out.cpu(), ref) <= 1e-2
+    assert rel_inf(S.cpu(), Sref) <= 1e-2
+
+
+def test_gn_gate_affine_fp32_and_bf16_out():
+    w = wl(N=333, gate=True)
+    x = W.make_inputs(w)
+    H, dv = 2, 512
+    gw = torch.randn(H * dv, generator=torch.Generator().manual_seed(3)) * 0.5 + 1
+    gb = torch.randn(H * dv, generator=torch.Generator().manual_seed(4)) * 0.1
+    raw, _ = O.chunkwise(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 256)
+    ref = O.groupnorm_gate(raw, x["gate"], 1e-5, gw.reshape(H, dv), gb.reshape(H, dv))
+    for od in (torch.float32, torch.bfloat16):
+        out, _ = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
+                                             x["theta"], 256, gate=dev(x["gate"]), gn=True,
+                                             gn_weight=dev(gw), gn_bias=dev(gb), out_dtype=od)
+        check_gated(out.cpu(), ref, x["gate"])
+
+
+@pytest.mark.parametrize("dv", [64, 128, 256])
+def test_value_dims(dv):
+    w = wl(d_v=dv, N=150, H=3)
+    x = W.make_inputs(w)
+    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
+                                         x["theta"], 32, state_out=True, out_dtype=torch.float32)
+    ref, Sref = O.chunkwise(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 32)
+    assert rel_inf(out.cpu(), ref) <= 1e-2
+    assert rel_inf(S.cpu(), Sref) <= 1e-2
+    out, _ = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
+                                         x["theta"], 32, gn=True, out_dtype=torch.float32)
+    check_gated(out.cpu(), O.group_norm(ref), None)
+
+
+def test_exchange_diagnostics_and_determinism():
+    """Every slice of a head reports the same XCD (the L2 exchange path is the one in
+    use), no wait hit its time limit, and two runs agree bit for bit."""
+    w = wl(N=300, H=4, gate=True)
+    x = W.make_inputs(w)
+    args = (dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"], 64)
+    ws = ws_for(args[0], args[2], x["gamma"], x["theta"], 64, gn=True, gate=x["gate"])
+    outs = []
+    for _ in range(2):
+        o, s = rn().rn_retention_chunkwise(*args, gate=dev(x["gate"]), gn=True, state_out=True,
+                                           workspace=ws)
+        outs.append((o.cpu(), s.cpu()))
+    torch.cuda.synchronize()
+    c = counters(ws, 4)
+    print("xcc per slice:", c[:, 8:16].tolist(), "mask:", c[:, 3].tolist())
+    assert (c[:, 4] == 0).all(), "an exchange wait hit its time limit"
+    assert all(bin(int(m)).count("1") == 1 for m in c[:, 3]), "slices of a head span XCDs"
+    assert (c[:, 0] == 8 * 5).all() and (c[:, 1] == 8 * 5).all()   # 5 blocks x 8 slices
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_more_heads_than_one_launch():
+    """48 heads x 8 slices exceed one co-resident launch: the heads run in groups."""
+    w = wl(B=3, H=16, N=70)
+    x = W.make_inputs(w)
+    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
+                                         x["theta"], 64, state_out=True, out_dtype=torch.float32)
+    ref, Sref = O.chunkwise(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 64)
+    assert rel_inf(out.cpu(), ref) <= 1e-2
+    assert rel_inf(S.cpu(), Sref) <= 1e-2
+
+
+def test_6p7b_training_shape_sampled_heads():
+    """The 6.7B-shaped training workload (B=2, H=16, N=8192, chunk 256, GroupNorm + gate)
+    in the launch configuration the benchmark times; three sampled heads checked in full
+    against the oracle (outputs and final states)."""
+    w = W.WORKLOADS["chunkwise_6p7b"]
+    x = W.make_inputs(w)
+    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
+                                         x["theta"], w.chunk, gate=dev(x["gate"]), gn=True,
+                                         state_out=True, out_dtype=torch.float32)
+    out, S = out.cpu(), S.cpu()
+    assert torch.isfinite(out).all()
+    for b, h in ((0, 0), (1, 15), (0, 9)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        raw, Sref = O.chunkwise(x["q"][sl], x["k"][sl], x["v"][sl], x["gamma"][h:h + 1], x["theta"],
+                                w.chunk)
+        check_gated(out[sl], O.groupnorm_gate(raw, x["gate"][sl]), x["gate"][sl])
+        assert rel_inf(S[sl], Sref) <= 1e-2
+
+
+def test_long_sequence_sampled_head():
+    """Long-sequence workload (B=1, H=16, N=65536, chunk 512, GroupNorm): head 11 checked
+    in full; workspace stays the N-independent size."""
+    w = W.WORKLOADS["chunkwise_long"]
+    x = W.make_inputs(w)
+    n64 = rn().rn_chunkwise_workspace_bytes(x["q"][:, :, :64], x["v"][:, :, :64], x["gamma"], x["theta"], 512, gn=True)
+    nfull = rn().rn_chunkwise_workspace_bytes(x["q"], x["v"], x["gamma"], x["theta"], 512, gn=True)
+    assert n64 == nfull
+    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
+                                         x["theta"], w.chunk, gn=True, state_out=True,
+                                         out_dtype=torch.float32)
+    out, S = out.cpu(), S.cpu()
+    h = 11
+    sl = (slice(0, 1), slice(h, h + 1))
+    raw, Sref = O.chunkwise(x["q"][sl], x["k"][sl], x["v"][sl], x["gamma"][h:h + 1], x["theta"], 2048)
+    check_gated(out[sl], O.group_norm(raw), None)
+    assert rel_inf(S[sl], Sref) <= 1e-2
