@@ -7,16 +7,24 @@
 // accumulator registers for the whole sequence) and walks the sequence in blocks of
 // 64 tokens. Inside the workgroup the four waves split d_k into quarters: wave w
 // keeps S[64w:64w+64, slice] and computes the quarter's partial products, which are
-// summed through LDS. Per block and wave (16x16x32 bf16 MFMA, fp32 accumulate):
+// summed through LDS. Per block and wave (16x16x32 f16 MFMA, fp32 accumulate):
 //   cross   acc  = xi ⊙ (Qh_w S_w)                 (Qh_w: 64 x 64 quarter of Qh)
 //   scores  P_w  = alpha (Kh_w Qh_w^T ⊙ D)^T       (partial over the quarter)
 //   intra   acc += P_w V
 //   carry   S_w  = gamma^L S_w + (zeta ⊙ Kh_w)^T V
 // The output is the sum of the four waves' acc; GroupNorm (+ gate) follows.
 //
+// Operand precision. q, k, v arrive in bf16; the rotation runs in float32 and every
+// MFMA operand (Qh, Kh, V, the decayed scores, the state copy used by the cross term)
+// is rounded to IEEE half. bf16 values are exact in half within its range, and half
+// keeps 3 more significand bits than bf16, which is what holds the error after
+// GroupNorm well inside 2e-2 (bf16 operands put it near 2.6e-2 on RetNet-shaped data).
+// Precondition of this path: operands within half's range (|x| < 65504); values
+// outside it need the plain float32 kernels (RN_FORCE_GENERIC).
+//
 // Sharing between the slices of one head. Every slice needs the whole rotated block
 // of q and k. Each of the nS workgroups rotates 64/nS rows of the NEXT block and
-// writes Qh, Kh and (zeta ⊙ Kh)^T in bf16 to a ring of 4 block slots in the
+// writes Qh, Kh and (zeta ⊙ Kh)^T in half to a ring of 4 block slots in the
 // workspace; a per-head counter says how many row groups are published. GroupNorm
 // statistics (per-row mean and centred sum of squares of each slice) go through a
 // second counter, and the normalisation of block j waits for them while block j+1
@@ -31,14 +39,17 @@
 // Ring safety: consuming block j needs every slice to have published block j, which
 // they do at their iteration j-1; so no workgroup is more than one block ahead of
 // another, and with 4 slots the slot a workgroup overwrites (block j+1) is never one
-// that a slower workgroup can still read (blocks j-1 and j).
+// that a slower workgroup can still read (blocks j-1 and j). Statistics of block j are
+// read at iteration j+1 and their slot is rewritten at iteration j+4, by which time
+// every slice has passed iteration j+2.
 #include "rn_device.h"
 #include "rn_kernels.h"
 
 namespace rn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -57,14 +68,28 @@ constexpr int kMaxWgPerLaunch = 4096;
 constexpr uint64_t kWaitTicks = 100000000ull;  // 1 s of the 100 MHz wall clock
 
 // counter words
-// counter words per head; words [8, 16) record the XCD of each slice (diagnostics)
-enum { kReady = 0, kStatReady = 1, kArrive = 2, kXccMask = 3, kError = 4, kXccOfSlice = 8 };
+// Counter words per head. Publication counts are kept per ring slot: slot s counts the
+// row groups published for blocks s, s+4, s+8, ...; block j is complete when word
+// kReady + j%4 reaches nS*(j/4 + 1). (A single running count per head would not do: a
+// workgroup that is one block ahead adds its next publication to the same count and
+// can complete it while a slower slice has not yet published the block being waited
+// for.) The same holds for the GroupNorm statistics (kStat + j%4). Words [8, 16)
+// record the XCD of each slice (diagnostics).
+enum { kArrive = 2, kXccMask = 3, kError = 4, kXccOfSlice = 8, kReady = 16, kStat = 20 };
 
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 u) { return __builtin_bit_cast(f16x8, u); }
+
+// Round-to-nearest-even float32 pair -> packed f16 (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2 v;
+  v[0] = static_cast<_Float16>(lo);
+  v[1] = static_cast<_Float16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 __device__ __forceinline__ uint32_t xcc_id() {
   // HW_REG_XCC_ID (id 20), bits [3:0]
@@ -252,7 +277,7 @@ chunkwise_fused(Params P) {
           x1 = __uint_as_float(wv & 0xffff0000u);
         }
         const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
-        *reinterpret_cast<uint32_t*>(dst + size_t(rr) * kDK + 2 * pp) = pack_bf16x2(y0, y1);
+        *reinterpret_cast<uint32_t*>(dst + size_t(rr) * kDK + 2 * pp) = pack_f16x2(y0, y1);
         const float zeta = (rr < Lb) ? exp2f(lg * float(Lb - 1 - rr)) : 0.f;
         z0[u] = y0 * zeta;
         z1[u] = y1 * zeta;
@@ -264,15 +289,15 @@ chunkwise_fused(Params P) {
         u32x4 t0, t1;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          t0[u] = pack_bf16x2(z0[2 * u], z0[2 * u + 1]);
-          t1[u] = pack_bf16x2(z1[2 * u], z1[2 * u + 1]);
+          t0[u] = pack_f16x2(z0[2 * u], z0[2 * u + 1]);
+          t1[u] = pack_f16x2(z1[2 * u], z1[2 * u + 1]);
         }
         *reinterpret_cast<u32x4*>(dstT + size_t(2 * pp) * kT + r_lo + r8) = t0;
         *reinterpret_cast<u32x4*>(dstT + size_t(2 * pp + 1) * kT + r_lo + r8) = t1;
       }
     }
     store_fence_release(agent);
-    signal_count(cnt, kReady);
+    signal_count(cnt, kReady + jb % kRing);
   };
 
   float o_prev[16];
@@ -361,40 +386,46 @@ chunkwise_fused(Params P) {
         else
           rv[i] = u32x2{0u, 0u};
       }
+      float fv[4][4];   // [row i][column j] as float32
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fv[i][0] = __uint_as_float(rv[i][0] << 16);
+        fv[i][1] = __uint_as_float(rv[i][0] & 0xffff0000u);
+        fv[i][2] = __uint_as_float(rv[i][1] << 16);
+        fv[i][3] = __uint_as_float(rv[i][1] & 0xffff0000u);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int wi = j >> 1;
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
         u32x2 o;
-        o[0] = __builtin_amdgcn_perm(rv[1][wi], rv[0][wi], sel);
-        o[1] = __builtin_amdgcn_perm(rv[3][wi], rv[2][wi], sel);
+        o[0] = pack_f16x2(fv[0][j], fv[1][j]);
+        o[1] = pack_f16x2(fv[2][j], fv[3][j]);
         *reinterpret_cast<u32x2*>(&sm.vt[d0 + j][s0]) = o;
       }
     }
-    wait_count(cnt, kReady, uint32_t(nS) * uint32_t(jb + 1), agent);  // includes a barrier
+    wait_count(cnt, kReady + jb % kRing, uint32_t(nS) * uint32_t(jb / kRing + 1), agent);  // + barrier
 
     const uint32_t slot_off = ring_off + static_cast<uint32_t>((jb % kRing) * 3 * kSlotElems * sizeof(uint16_t));
     const uint32_t kh_off = slot_off + static_cast<uint32_t>(kSlotElems * sizeof(uint16_t));
     const uint32_t kt_off = slot_off + static_cast<uint32_t>(2 * kSlotElems * sizeof(uint16_t));
 
     // ---- cross term: acc[m][b] = Qh[16m.., dk quarter] · S_w -------------------------
-    bf16x8 qf[4][2];
+    f16x8 qf[4][2];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        qf[m][c] = as_bf16x8(ld_sc0_b128(wsr, slot_off + static_cast<uint32_t>(((16 * m + l16) * kDK + 64 * w + 32 * c + 8 * g) * 2)));
-    bf16x8 sf[2][4];
+        qf[m][c] = as_f16x8(ld_sc0_b128(wsr, slot_off + static_cast<uint32_t>(((16 * m + l16) * kDK + 64 * w + 32 * c + 8 * g) * 2)));
+    f16x8 sf[2][4];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         u32x4 u;
-        u[0] = pack_bf16x2(Sacc[2 * c][tb][0], Sacc[2 * c][tb][1]);
-        u[1] = pack_bf16x2(Sacc[2 * c][tb][2], Sacc[2 * c][tb][3]);
-        u[2] = pack_bf16x2(Sacc[2 * c + 1][tb][0], Sacc[2 * c + 1][tb][1]);
-        u[3] = pack_bf16x2(Sacc[2 * c + 1][tb][2], Sacc[2 * c + 1][tb][3]);
-        sf[c][tb] = as_bf16x8(u);
+        u[0] = pack_f16x2(Sacc[2 * c][tb][0], Sacc[2 * c][tb][1]);
+        u[1] = pack_f16x2(Sacc[2 * c][tb][2], Sacc[2 * c][tb][3]);
+        u[2] = pack_f16x2(Sacc[2 * c + 1][tb][0], Sacc[2 * c + 1][tb][1]);
+        u[3] = pack_f16x2(Sacc[2 * c + 1][tb][2], Sacc[2 * c + 1][tb][3]);
+        sf[c][tb] = as_f16x8(u);
       }
     f32x4 acc[4][4];
 #pragma unroll
@@ -412,16 +443,16 @@ chunkwise_fused(Params P) {
 
     // ---- scores: P^T tiles (s-tile i, t-tile m), e = i/2 <= m/2 ----------------------
     // K rows for tile i: A-row l16 <-> s = 32e + 8(l16>>2) + 4(i&1) + (l16&3)
-    bf16x8 kf[4][2];
+    f16x8 kf[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = 32 * (i >> 1) + 8 * (l16 >> 2) + 4 * (i & 1) + (l16 & 3);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        kf[i][c] = as_bf16x8(ld_sc0_b128(wsr, kh_off + static_cast<uint32_t>((s * kDK + 64 * w + 32 * c + 8 * g) * 2)));
+        kf[i][c] = as_f16x8(ld_sc0_b128(wsr, kh_off + static_cast<uint32_t>((s * kDK + 64 * w + 32 * c + 8 * g) * 2)));
     }
     // P A-fragments for the PV product: pf[m][e]
-    bf16x8 pf[4][2];
+    f16x8 pf[4][2];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -448,20 +479,20 @@ chunkwise_fused(Params P) {
           pt[hh] = z;
         }
         u32x4 u;
-        u[0] = pack_bf16x2(pt[0][0], pt[0][1]);
-        u[1] = pack_bf16x2(pt[0][2], pt[0][3]);
-        u[2] = pack_bf16x2(pt[1][0], pt[1][1]);
-        u[3] = pack_bf16x2(pt[1][2], pt[1][3]);
-        pf[m][e] = as_bf16x8(u);
+        u[0] = pack_f16x2(pt[0][0], pt[0][1]);
+        u[1] = pack_f16x2(pt[0][2], pt[0][3]);
+        u[2] = pack_f16x2(pt[1][0], pt[1][1]);
+        u[3] = pack_f16x2(pt[1][2], pt[1][3]);
+        pf[m][e] = as_f16x8(u);
       }
 
     // ---- V fragments (B operand, k = s): vf[e][b] -------------------------------
-    bf16x8 vf[2][4];
+    f16x8 vf[2][4];
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
-        vf[e][tb] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.vt[16 * tb + l16][32 * e + 8 * g]));
+        vf[e][tb] = as_f16x8(*reinterpret_cast<const u32x4*>(&sm.vt[16 * tb + l16][32 * e + 8 * g]));
 
     // ---- intra term -------------------------------------------------------------
 #pragma unroll
@@ -514,19 +545,19 @@ chunkwise_fused(Params P) {
         *reinterpret_cast<u32x2*>(sp) = u32x2{__float_as_uint(mu), __float_as_uint(m2)};
       }
       store_fence_release(agent);
-      signal_count(cnt, kStatReady);
+      signal_count(cnt, kStat + jb % kRing);
     }
 
     // ---- state carry: S_w = gamma^Lb S_w + (zeta ⊙ Kh)^T V ---------------------------
     {
       const float gL = exp2f(lg * float(Lb));
-      bf16x8 ktf[4][2];
+      f16x8 ktf[4][2];
 #pragma unroll
       for (int ta = 0; ta < 4; ++ta) {
         const int dk = 64 * w + 32 * (ta >> 1) + 8 * (l16 >> 2) + 4 * (ta & 1) + (l16 & 3);
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-          ktf[ta][e] = as_bf16x8(ld_sc0_b128(wsr, kt_off + static_cast<uint32_t>((dk * kT + 32 * e + 8 * g) * 2)));
+          ktf[ta][e] = as_f16x8(ld_sc0_b128(wsr, kt_off + static_cast<uint32_t>((dk * kT + 32 * e + 8 * g) * 2)));
       }
 #pragma unroll
       for (int ta = 0; ta < 4; ++ta)
@@ -542,7 +573,7 @@ chunkwise_fused(Params P) {
     // ---- normalise and store the previous block (its statistics are complete) --------
     if (use_gn) {
       if (prev_row >= 0) {
-        wait_count(cnt, kStatReady, uint32_t(nS) * uint32_t(jb), agent);
+        wait_count(cnt, kStat + (jb - 1) % kRing, uint32_t(nS) * uint32_t((jb - 1) / kRing + 1), agent);
         finalize(jb - 1, o_prev);
       }
 #pragma unroll
@@ -554,7 +585,7 @@ chunkwise_fused(Params P) {
     __syncthreads();  // LDS buffers are reused by the next block
   }
   if (use_gn && prev_row >= 0) {
-    wait_count(cnt, kStatReady, uint32_t(nS) * uint32_t(P.nb), agent);
+    wait_count(cnt, kStat + (P.nb - 1) % kRing, uint32_t(nS) * uint32_t((P.nb - 1) / kRing + 1), agent);
     finalize(P.nb - 1, o_prev);
   }
 

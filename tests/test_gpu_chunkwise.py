@@ -1,11 +1,12 @@
 """GPU parity of the fused MFMA chunkwise kernel (bf16 q/k/v, d_k = 256).
 
-Tolerances (bf16 operands, fp32 accumulation):
+Tolerances (half-precision MFMA operands, fp32 accumulation):
   * raw outputs and final states: per (b, h), ||gpu - ref||_inf <= 1e-2 ||ref||_inf.
-    Qh, Kh, the bf16 copy of the state used by the cross term and the decayed scores
-    are each rounded to bf16 (relative 2^-9); an output is a sum of many such terms of
-    mixed sign, so the error of one element is ~2^-9 of the typical magnitude, about
-    2e-3 of the slice maximum; 1e-2 leaves a 5x margin.
+    Qh, Kh, V, the copy of the state used by the cross term and the decayed scores are
+    each rounded to IEEE half (relative 2^-11); an output is a sum of many such terms
+    of mixed sign, so the error of one element is a few 2^-11 of the typical magnitude
+    (4e-4 of the slice maximum measured on the tiny-to-6.7B shapes); 1e-2 is the bound
+    a bf16-operand kernel would need, kept as the raw-output bar.
   * after GroupNorm (fp32 output): max-abs 2e-2; with the gate, 2e-2 * max(1, |swish(g)|).
   * bf16 output: the same bound plus half a bf16 ulp of the reference.
 """
@@ -120,7 +121,9 @@ def test_exchange_diagnostics_and_determinism():
     print("xcc per slice:", c[:, 8:16].tolist(), "mask:", c[:, 3].tolist())
     assert (c[:, 4] == 0).all(), "an exchange wait hit its time limit"
     assert all(bin(int(m)).count("1") == 1 for m in c[:, 3]), "slices of a head span XCDs"
-    assert (c[:, 0] == 8 * 5).all() and (c[:, 1] == 8 * 5).all()   # 5 blocks x 8 slices
+    # 5 blocks x 8 slices, two runs on one workspace (counters are cleared per launch):
+    # ring slots 0..3 count blocks {0,4}, {1}, {2}, {3}
+    assert c[:, 16:20].tolist() == [[16, 8, 8, 8]] * 4 and c[:, 20:24].tolist() == [[16, 8, 8, 8]] * 4
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
@@ -162,9 +165,11 @@ def test_long_sequence_sampled_head():
     n64 = rn().rn_chunkwise_workspace_bytes(x["q"][:, :, :64], x["v"][:, :, :64], x["gamma"], x["theta"], 512, gn=True)
     nfull = rn().rn_chunkwise_workspace_bytes(x["q"], x["v"], x["gamma"], x["theta"], 512, gn=True)
     assert n64 == nfull
-    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
-                                         x["theta"], w.chunk, gn=True, state_out=True,
-                                         out_dtype=torch.float32)
+    args = (dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"], w.chunk)
+    out, S = rn().rn_retention_chunkwise(*args, gn=True, state_out=True, out_dtype=torch.float32)
+    out2, S2 = rn().rn_retention_chunkwise(*args, gn=True, state_out=True, out_dtype=torch.float32)
+    assert torch.equal(out, out2) and torch.equal(S, S2), "runs differ: exchange race"
+    del out2, S2
     out, S = out.cpu(), S.cpu()
     h = 11
     sl = (slice(0, 1), slice(h, h + 1))
