@@ -54,6 +54,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only", choices=["chunkwise", "decode", "copy"], default=None,
+                    help="run one workload only (for profiling); 'copy' times a plain 1 GiB "
+                         "device copy, the reference for the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -70,6 +73,22 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only == "copy":
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "copy_GBs": 2 * src.numel() * 4 / dt / 1e9}))
+        return
+    if args.only == "decode":
+        args.no_cpu_baseline = True
     w = W.WORKLOADS["chunkwise_6p7b"]
     x = W.make_inputs(w)
     q, k, v, gate = (x[n].to(dev) for n in ("q", "k", "v", "gate"))
@@ -83,6 +102,8 @@ def main():
         rn.rn_retention_chunkwise(q, k, v, gamma, theta, w.chunk, gate=gate, gn=True,
                                   gn_eps=w.gn_eps, state_out=S_out, out=out, workspace=ws)
 
+    if args.only == "decode":
+        args.steps = args.warmup = 1
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -130,6 +151,8 @@ def main():
     }
 
     # ---- decode step ---------------------------------------------------------------
+    if args.only == "chunkwise":
+        args.no_decode = True
     if not args.no_decode:
         wd = W.WORKLOADS["decode_6p7b"]
         state = W.initial_state(wd).to(dev)
