@@ -40,6 +40,14 @@ def chunkwise_work(B, H, N, dk, dv, C):
     return flops, bytes_
 
 
+def parallel_work(B, H, N, dk, dv):
+    """Causal pairs only: N(N+1)/2 (q.k and p.v) per head; bytes: q, k, v read and out
+    written once (bf16)."""
+    flops = B * H * N * (N + 1) * (dk + dv)
+    bytes_ = B * H * N * 2 * (dk + dk + dv + dv)
+    return flops, bytes_
+
+
 def decode_work(B, H, dk, dv):
     flops = 5 * B * H * dk * dv
     bytes_ = B * H * dk * dv * 4 * 2 + B * H * (dk + dk + dv) * 2 + B * H * dv * 4
@@ -54,7 +62,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["chunkwise", "decode", "copy"], default=None,
+    ap.add_argument("--no-parallel", action="store_true")
+    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "copy"], default=None,
                     help="run one workload only (for profiling); 'copy' times a plain 1 GiB "
                          "device copy, the reference for the HBM byte counters")
     args = ap.parse_args()
@@ -87,7 +96,7 @@ def main():
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "copy_GBs": 2 * src.numel() * 4 / dt / 1e9}))
         return
-    if args.only == "decode":
+    if args.only in ("decode", "parallel"):
         args.no_cpu_baseline = True
     w = W.WORKLOADS["chunkwise_6p7b"]
     x = W.make_inputs(w)
@@ -102,7 +111,7 @@ def main():
         rn.rn_retention_chunkwise(q, k, v, gamma, theta, w.chunk, gate=gate, gn=True,
                                   gn_eps=w.gn_eps, state_out=S_out, out=out, workspace=ws)
 
-    if args.only == "decode":
+    if args.only in ("decode", "parallel"):
         args.steps = args.warmup = 1
     for _ in range(args.warmup):
         step()
@@ -150,8 +159,46 @@ def main():
                      "mfma_tflops": tfl, "mfma_frac": tfl / BF16_PEAK_TFLOPS},
     }
 
+    # ---- parallel form, 1.3B shape (secondary record) --------------------------------
+    if args.only in ("chunkwise", "decode"):
+        args.no_parallel = True
+    if args.only == "parallel":
+        args.no_decode = True
+    if not args.no_parallel:
+        del q, k, v, gate, out, ws
+        wp = W.WORKLOADS["parallel_1p3b"]
+        xp = W.make_inputs(wp)
+        qp, kp, vp = (xp[n].to(dev) for n in ("q", "k", "v"))
+        outp = torch.empty_like(vp)
+        wsp = torch.empty(rn.rn_parallel_workspace_bytes(qp, vp, xp["gamma"], xp["theta"], norm_d=True,
+                                                         norm_r=True, gn=True), dtype=torch.uint8, device=dev)
+
+        def pstep():
+            rn.rn_retention_parallel(qp, kp, vp, xp["gamma"], xp["theta"], out=outp, workspace=wsp,
+                                     qk_scale=wp.qk_scale, norm_d=True, norm_r=True, gn=True)
+
+        for _ in range(3):
+            pstep()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            pstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ps = e0.elapsed_time(e1) / reps / 1e3
+        pfl, pby = parallel_work(wp.B, wp.H, wp.N, wp.d_k, wp.d_v)
+        rec["parallel"] = {"workload": "parallel_1p3b: B=8 H=8 N=2048 d_k=256 d_v=512, alpha=1/16, "
+                                       "D and R row normalisation, GroupNorm, bf16 in/out",
+                           "ms": ps * 1e3, "tokens_per_s": wp.B * wp.N / ps,
+                           "mfma_tflops": pfl / ps / 1e12, "mfma_frac": pfl / ps / 1e12 / BF16_PEAK_TFLOPS,
+                           "algorithmic_flops": pfl, "algorithmic_bytes": pby,
+                           "hbm_frac": pby / ps / 1e9 / HBM_PEAK_GBS}
+        del xp, qp, kp, vp, outp, wsp
+
     # ---- decode step ---------------------------------------------------------------
-    if args.only == "chunkwise":
+    if args.only in ("chunkwise", "parallel"):
         args.no_decode = True
     if not args.no_decode:
         wd = W.WORKLOADS["decode_6p7b"]

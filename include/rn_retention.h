@@ -83,6 +83,14 @@ typedef struct rn_desc {
 } rn_desc;
 
 /*
+ * Bytes of device workspace rn_retention_parallel needs for `desc` (0 for an invalid
+ * descriptor or when the call needs none). The MFMA path stores the rotated q and k
+ * and the blocked, transposed v in half precision there: 2*B*H*ceil(N/64)*64*(2*d_k + d_v)
+ * bytes, linear in N.
+ */
+size_t rn_parallel_workspace_bytes(const rn_desc* desc);
+
+/*
  * Parallel form: O = ((alpha * Qh Kh^T) ⊙ D) V with the optional row rescalings,
  * then the optional GroupNorm / gate epilogue.
  * (hwhale notes: parallel-form equation, the ParallelRetention listing and the list
@@ -91,10 +99,12 @@ typedef struct rn_desc {
  * max(|signed row sum of R|, 1) for RN_NORM_R_ROW.)
  * q, k: [B,H,N,d_k]; v: [B,H,N,d_v]; gate: [B,H,N,d_v] (required iff RN_EPI_GATE,
  * else ignored); out: [B,H,N,d_v] in out_dtype. No state: the parallel form starts
- * from S = 0.
+ * from S = 0. workspace: device buffer of at least rn_parallel_workspace_bytes(desc)
+ * bytes, 256-byte aligned (may be NULL when that size is 0); contents ignored.
  */
 rn_status rn_retention_parallel(const rn_desc* desc, const void* q, const void* k,
-                                const void* v, const void* gate, void* out, void* stream);
+                                const void* v, const void* gate, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace rn_retention_chunkwise needs for `desc` (independent of

@@ -6,7 +6,7 @@ outputs with torch, pass device pointers and the current HIP stream. Every step 
 the computation runs in the library's HIP kernels. There is no CPU fallback: if the
 library is missing, importing this package raises.
 
-Build the library with ``python -m linear_recurrent_sequence_rn_amd.build``.
+Build the library with ``python linear_recurrent_sequence_rn_amd/build.py``.
 """
 from __future__ import annotations
 
@@ -23,7 +23,8 @@ __all__ = [
     "RN_F32", "RN_BF16", "RN_NORM_D_ROW", "RN_NORM_R_ROW", "RN_EPI_GN", "RN_EPI_GATE",
     "RN_FORCE_GENERIC", "RnError", "RnDesc", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
     "rn_retention_parallel", "rn_retention_chunkwise", "rn_retention_recurrent_step",
-    "rn_groupnorm_gate", "rn_chunkwise_workspace_bytes", "rn_version", "make_desc",
+    "rn_groupnorm_gate", "rn_chunkwise_workspace_bytes", "rn_parallel_workspace_bytes",
+    "rn_version", "make_desc",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "librn_retention.so"
@@ -34,7 +35,7 @@ RN_NORM_D_ROW, RN_NORM_R_ROW, RN_EPI_GN, RN_EPI_GATE = 1, 2, 4, 8
 RN_FORCE_GENERIC = 1 << 8
 
 EXPORTED_SYMBOLS = (
-    "rn_retention_parallel", "rn_chunkwise_workspace_bytes", "rn_retention_chunkwise",
+    "rn_parallel_workspace_bytes", "rn_retention_parallel", "rn_chunkwise_workspace_bytes", "rn_retention_chunkwise",
     "rn_retention_recurrent_step", "rn_groupnorm_gate", "rn_status_str", "rn_last_error",
     "rn_version",
 )
@@ -61,11 +62,13 @@ class RnDesc(ctypes.Structure):
 def _load():
     if not LIB_PATH.exists():
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m linear_recurrent_sequence_rn_amd.build`")
+                          "`python linear_recurrent_sequence_rn_amd/build.py`")
     L = ctypes.CDLL(str(LIB_PATH))
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     D = ctypes.POINTER(RnDesc)
-    L.rn_retention_parallel.argtypes = [D, vp, vp, vp, vp, vp, vp]
+    L.rn_parallel_workspace_bytes.argtypes = [D]
+    L.rn_parallel_workspace_bytes.restype = sz
+    L.rn_retention_parallel.argtypes = [D, vp, vp, vp, vp, vp, vp, sz, vp]
     L.rn_retention_parallel.restype = i32
     L.rn_chunkwise_workspace_bytes.argtypes = [D, i32]
     L.rn_chunkwise_workspace_bytes.restype = sz
@@ -174,17 +177,32 @@ def _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos0, qk_scale, gn_eps, g
 
 
 def rn_retention_parallel(q, k, v, gamma, theta, *, gate=None, out=None, out_dtype=None,
-                          pos0=0, qk_scale=1.0, norm_d=False, norm_r=False, gn=False,
-                          gn_eps=1e-5, gn_weight=None, gn_bias=None, force_generic=False):
+                          workspace=None, pos0=0, qk_scale=1.0, norm_d=False, norm_r=False,
+                          gn=False, gn_eps=1e-5, gn_weight=None, gn_bias=None,
+                          force_generic=False):
     """Parallel form; returns out [B,H,N,d_v]."""
     flags = _flags(norm_d, norm_r, gn, gate, force_generic)
     d, keep, od = _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos0, qk_scale, gn_eps,
                             gn_weight, gn_bias)
     if out is None:
         out = torch.empty(v.shape, dtype=od, device=v.device)
+    need = int(lib.rn_parallel_workspace_bytes(ctypes.byref(d)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nws = 0 if workspace is None else workspace.numel()
     _check(lib.rn_retention_parallel(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
-                                     _ptr(out), _stream(q)))
+                                     _ptr(out), _ptr(workspace), nws, _stream(q)))
     return out
+
+
+def rn_parallel_workspace_bytes(q, v, gamma, theta, *, norm_d=False, norm_r=False, gn=False,
+                                gate=None, out_dtype=None, force_generic=False) -> int:
+    B, H, N, dk = q.shape
+    flags = _flags(norm_d, norm_r, gn, gate, force_generic)
+    od = q.dtype if out_dtype is None else out_dtype
+    d, keep = make_desc(B, H, N, dk, v.shape[-1], _dtype_code(q.dtype), _dtype_code(od), gamma,
+                        theta, flags=flags)
+    return int(lib.rn_parallel_workspace_bytes(ctypes.byref(d)))
 
 
 def rn_chunkwise_workspace_bytes(q, v, gamma, theta, chunk, *, gn=False, gate=None,

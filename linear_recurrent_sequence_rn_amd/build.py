@@ -1,6 +1,8 @@
 """Builds librn_retention.so in-tree with hipcc for gfx950.
 
-    python -m linear_recurrent_sequence_rn_amd.build
+    python linear_recurrent_sequence_rn_amd/build.py
+
+(Run as a script: importing the package loads the library, which may not exist yet.)
 
 Every HIP source under csrc/ is compiled to an object under _build/ and linked into
 linear_recurrent_sequence_rn_amd/librn_retention.so. Always recompiles.

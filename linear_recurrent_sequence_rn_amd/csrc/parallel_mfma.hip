@@ -1,0 +1,412 @@
+// Parallel retention with MFMA for bf16 q/k/v, d_k = 256, d_v = 512
+// (hwhale notes: parallel-form equation, ParallelRetention listing and the list of
+// three rescalings).
+//
+// Two kernels.
+//  1. prep: rotates q (scaled by alpha) and k once into half precision, row-major, and
+//     writes v transposed per 64-row block (V^T[block][d_v][64]) in half, into the
+//     caller's workspace. Rotating k here instead of in the main kernel avoids redoing
+//     it for every query block that reads the key block (32 x on average at N = 2048).
+//  2. main: one 512-thread workgroup (8 waves) per (head, 128-row query block), walking
+//     the 64-row key blocks that have causal pairs with it. Each key block of Kh is
+//     copied once into LDS (buffer loads with the lds modifier, two buffers, two blocks
+//     ahead). Wave w computes the scores of query rows 16w..16w+15 against the 64 keys
+//     (16x16x32 f16 MFMA over all of d_k), applies gamma^(t-s) and the causal mask,
+//     accumulates the signed row sums for the R normalisation and writes the scores to
+//     LDS in half (two buffers: the scores of block kb+1 are computed while block kb is
+//     multiplied with V); every wave then multiplies all 128 score rows with its 64
+//     columns of V. At the end each row is scaled by c_t = 1/sqrt(sum_{m<=t} gamma^m)
+//     (D normalisation) and 1/max(c_t |rowsum|, 1) (R normalisation), then GroupNorm
+//     (+ gate) over the 512 columns, whose sums are combined across the waves in LDS.
+// Query blocks are launched from the last (most key blocks) to the first, and each head's
+// blocks all go to one XCD.
+#include "rn_device.h"
+#include "rn_kernels.h"
+
+namespace rn {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kT = 64;      // rows per block
+constexpr int kDK = 256;
+constexpr int kDV = 512;
+constexpr int kPLd = 72;    // LDS row stride (half) of the score block
+
+__device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 u) { return __builtin_bit_cast(f16x8, u); }
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2 v;
+  v[0] = static_cast<_Float16>(lo);
+  v[1] = static_cast<_Float16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           static_cast<int>(bytes > 0 ? bytes : 0), 0x00020000);
+}
+__device__ __forceinline__ u32x4 ld_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void st_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, 0);
+}
+
+// Workspace per head: Qh [Np][256], Kh [Np][256], Vt [Np/64][512][64], all half,
+// with Np = N rounded up to 64 (rows past N are zero).
+struct Ws {
+  size_t q, k, v, head;   // element offsets within a head, and elements per head
+};
+__host__ __device__ inline Ws ws_layout(int N) {
+  const size_t np = size_t((N + kT - 1) / kT) * kT;
+  Ws w;
+  w.q = 0;
+  w.k = np * kDK;
+  w.v = 2 * np * kDK;
+  w.head = 2 * np * kDK + np * kDV;
+  return w;
+}
+
+// ---- prep: one 256-thread block per (64-row block, head) ------------------------------
+// bf16 inputs only. q and k: thread = (group of 4 coordinate pairs = 16 bytes, group of
+// 8 rows); 16-byte loads, angles by recurrence along the rows. v: thread = 8 rows x 8
+// columns, transposed in registers and written as 8 rows of V^T (16 bytes each).
+__global__ void __launch_bounds__(256) parallel_prep(CallArgs a, const uint16_t* q,
+                                                     const uint16_t* k, const uint16_t* v,
+                                                     uint16_t* ws) {
+  const int jb = blockIdx.x, bh = blockIdx.y;
+  const int N = a.N, tid = threadIdx.x;
+  const Ws L = ws_layout(N);
+  uint16_t* base = ws + size_t(bh) * L.head;
+  const int row0 = jb * kT;
+  const int64_t bytes_qk = int64_t(N) * kDK * 2, bytes_v = int64_t(N) * kDV * 2;
+  const __amdgpu_buffer_rsrc_t rq = range_rsrc(q + size_t(bh) * N * kDK, bytes_qk);
+  const __amdgpu_buffer_rsrc_t rk = range_rsrc(k + size_t(bh) * N * kDK, bytes_qk);
+  const __amdgpu_buffer_rsrc_t rv = range_rsrc(v + size_t(bh) * N * kDV, bytes_v);
+  {
+    const int pg = tid & 31, rg = tid >> 5;     // pairs 4pg..4pg+3, rows 8rg..8rg+7
+    float cs[4], sn[4], c1[4], s1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float th = a.ap.theta[4 * pg + i];
+      angle_cs(1, th, &c1[i], &s1[i]);
+      angle_cs(a.pos0 + row0 + 8 * rg, th, &cs[i], &sn[i]);
+    }
+    const float al = a.alpha;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = row0 + 8 * rg + u;
+      const uint32_t off = static_cast<uint32_t>((t * kDK + 8 * pg) * 2);
+      const u32x4 xq = ld_b128(rq, off), xk = ld_b128(rk, off);   // zero past N
+      u32x4 oq, ok;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float q0 = __uint_as_float(xq[i] << 16), q1 = __uint_as_float(xq[i] & 0xffff0000u);
+        const float k0 = __uint_as_float(xk[i] << 16), k1 = __uint_as_float(xk[i] & 0xffff0000u);
+        oq[i] = pack_f16x2(al * (q0 * cs[i] - q1 * sn[i]), al * (q0 * sn[i] + q1 * cs[i]));
+        ok[i] = pack_f16x2(k0 * cs[i] - k1 * sn[i], k0 * sn[i] + k1 * cs[i]);
+        const float cn = cs[i] * c1[i] - sn[i] * s1[i];
+        sn[i] = cs[i] * s1[i] + sn[i] * c1[i];
+        cs[i] = cn;
+      }
+      *reinterpret_cast<u32x4*>(base + L.q + size_t(t) * kDK + 8 * pg) = oq;
+      *reinterpret_cast<u32x4*>(base + L.k + size_t(t) * kDK + 8 * pg) = ok;
+    }
+  }
+  // v: 8x8 tiles; 64 x 512 block = 512 tiles, 2 per thread
+  uint16_t* vt = base + L.v + size_t(jb) * kDV * kT;
+#pragma unroll
+  for (int rep = 0; rep < 2; ++rep) {
+    const int tile = tid + 256 * rep;
+    const int cg = tile & 63, sg = tile >> 6;     // columns 8cg..8cg+7, rows 8sg..8sg+7
+    float f[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4 x = ld_b128(rv, static_cast<uint32_t>(((row0 + 8 * sg + i) * kDV + 8 * cg) * 2));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[i][2 * j] = __uint_as_float(x[j] << 16);
+        f[i][2 * j + 1] = __uint_as_float(x[j] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = pack_f16x2(f[2 * i][j], f[2 * i + 1][j]);
+      *reinterpret_cast<u32x4*>(vt + size_t(8 * cg + j) * kT + 8 * sg) = o;
+    }
+  }
+}
+
+// ---- main -------------------------------------------------------------------------------
+constexpr int kQ = 128;       // query rows per workgroup
+constexpr int kWaves = 8;     // 512 threads
+
+struct alignas(16) PShared {
+  u32x4 kh[2][kT * kDK / 8];     // two key blocks, half, 16-byte units (swizzled)
+  uint16_t p[2][kQ][kPLd];       // scores of two key blocks, half
+  float red[kWaves][kQ];         // per-wave row partials for the GroupNorm statistics
+  float rs[kQ];                  // signed row sums of the scores
+  float mean[kQ], rstd[kQ];      // GroupNorm statistics per row
+};
+
+// Unit u (16 bytes = 8 halves, u in [0, 32)) of key row s sits at LDS unit
+// 32 s + (u ^ (s & 31)): the 16 rows a 16-lane group reads for one fragment then fall
+// into 16 different 4-bank groups.
+__device__ __forceinline__ int kh_unit(int s, int u) { return 32 * s + (u ^ (s & 31)); }
+
+template <int OUT>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
+  const int N = a.N, nb = (N + kT - 1) / kT, nq = (N + kQ - 1) / kQ;
+  const int BH = a.B * a.H;
+  // Workgroups are dispatched round-robin over the 8 XCDs (id mod 8). XCD x owns the
+  // heads bh = x (mod 8), so their key/value blocks are only ever read through its L2,
+  // and walks them heaviest query block first (longest-job-first over that XCD's CUs).
+  const int hpx = (BH + 7) / 8;   // heads per XCD
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int bh = 8 * (j % hpx) + xcd;
+  const int qb = nq - 1 - j / hpx;
+  if (bh >= BH) return;
+  const int h = bh % a.H;
+  const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, g = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const Ws L = ws_layout(N);
+  const uint16_t* base = ws + size_t(bh) * L.head;
+  const int64_t np = int64_t(nb) * kT;
+  const __amdgpu_buffer_rsrc_t rq = range_rsrc(base + L.q, np * kDK * 2);
+  const __amdgpu_buffer_rsrc_t rk = range_rsrc(base + L.k, np * kDK * 2);
+  const __amdgpu_buffer_rsrc_t rv = range_rsrc(base + L.v, np * kDV * 2);
+  __shared__ PShared sm;
+
+  const float lg = a.hp.log2g[h];
+  const int kb_end = min(2 * qb + 1, nb - 1);   // last key block with a causal pair
+
+  // key block kb -> LDS buffer `buf`: each wave copies 4 KB (4 x 64 lanes x 16 B)
+  auto stage_k = [&](int kb, int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = (w * 4 + j) * 64 + l;             // LDS unit this lane fills
+      const int s = p >> 5, u = (p & 31) ^ (s & 31);  // key row and 16-byte unit
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void*)(&sm.kh[buf][(w * 4 + j) * 64]), 16,
+          static_cast<uint32_t>(((kb * kT + s) * kDK + 8 * u) * 2), 0, 0, 0);
+    }
+  };
+
+  // this wave's 16 query rows (A operand: row t, k = dk)
+  const int t_row = qb * kQ + 16 * w + l16;
+  f16x8 qf[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    qf[c] = as_f16x8(ld_b128(rq, static_cast<uint32_t>((t_row * kDK + 32 * c + 8 * g) * 2)));
+
+  float rsum[4] = {0.f, 0.f, 0.f, 0.f};   // partial signed sums of rows 16w + 4g + r
+
+  // scores of key block kb (in LDS buffer kb % 2) -> sm.p[kb % 2], half
+  auto scores = [&](int kb) {
+    const int buf = kb & 1;
+    f32x4 sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = 16 * i + l16;        // key row (B operand column)
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        z = mfma(qf[c], as_f16x8(sm.kh[buf][kh_unit(s, 4 * c + g)]), z);
+      sc[i] = z;
+    }
+    // D layout: row t = 16w + 4g + r, column s = 16i + l16
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = (qb * kQ + 16 * w + 4 * g + r) - (kb * kT + 16 * i + l16);
+        const float val = (d >= 0) ? sc[i][r] * exp2f(lg * float(d)) : 0.f;
+        rsum[r] += val;
+        sm.p[buf][16 * w + 4 * g + r][16 * i + l16] =
+            __builtin_bit_cast(uint16_t, static_cast<_Float16>(val));
+      }
+  };
+
+  // output accumulators: all 128 rows (8 t-tiles) x this wave's 64 columns (4 tiles)
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: key block 0 -> scores 0; key block 1 staged
+  stage_k(0, 0);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (kb_end >= 1) stage_k(1, 1);
+  scores(0);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int kb = 0; kb <= kb_end; ++kb) {
+    // scores(kb) are in sm.p[kb%2]; key block kb+1 is in sm.kh[(kb+1)%2]
+    if (kb + 2 <= kb_end) stage_k(kb + 2, kb & 1);
+    const uint32_t vblk = static_cast<uint32_t>(kb) * kDV * kT;
+    f16x8 vf[2][4];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int dv = 64 * w + 16 * n + l16;
+        vf[e][n] = as_f16x8(ld_b128(rv, (vblk + static_cast<uint32_t>(dv * kT + 32 * e + 8 * g)) * 2));
+      }
+    if (kb + 1 <= kb_end) scores(kb + 1);
+    // O[:, this wave's columns] += P(kb) V(kb): A = P (row t, k = s), B = V^T (col dv, k = s)
+    const int buf = kb & 1;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const f16x8 pf = as_f16x8(*reinterpret_cast<const u32x4*>(&sm.p[buf][16 * m + l16][32 * e + 8 * g]));
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[m][n] = mfma(pf, vf[e][n], acc[m][n]);
+      }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // ---- row scalars ------------------------------------------------------------------
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float x = rsum[r];
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 4, 64);
+    x += __shfl_xor(x, 8, 64);
+    if (l16 == 0) sm.rs[16 * w + 4 * g + r] = x;
+  }
+  __syncthreads();
+  const bool any_norm = a.flags & (RN_NORM_D_ROW | RN_NORM_R_ROW);
+  if (any_norm) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tl = 16 * m + 4 * g + r;
+        const int t = qb * kQ + tl;
+        double ct = 1.0;
+        if (a.flags & RN_NORM_D_ROW) {
+          const double gm = a.hp.gamma[h];
+          const double G = (gm == 1.0) ? double(t + 1) : -expm1(double(t + 1) * log(gm)) / (1.0 - gm);
+          ct = 1.0 / sqrt(G);
+        }
+        double sc = ct;
+        if (a.flags & RN_NORM_R_ROW) sc = ct / fmax(fabs(ct * double(sm.rs[tl])), 1.0);
+        const float f = static_cast<float>(sc);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[m][n][r] *= f;
+      }
+  }
+
+  // ---- GroupNorm over the 512 columns of each row (8 waves x 64) ---------------------
+  const bool gn = a.flags & RN_EPI_GN;
+  const bool gt = a.flags & RN_EPI_GATE;
+  auto row_partial = [&](auto f) {   // sum over this wave's 64 columns of f(value, m, r)
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = 0.f;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) x += f(acc[m][n][r], m, r);
+        x += __shfl_xor(x, 1, 64);
+        x += __shfl_xor(x, 2, 64);
+        x += __shfl_xor(x, 4, 64);
+        x += __shfl_xor(x, 8, 64);
+        if (l16 == 0) sm.red[w][16 * m + 4 * g + r] = x;
+      }
+  };
+  if (gn) {
+    row_partial([](float v, int, int) { return v; });
+    __syncthreads();
+    if (tid < kQ) {
+      float x = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) x += sm.red[ww][tid];
+      sm.mean[tid] = x * (1.0f / kDV);
+    }
+    __syncthreads();
+    row_partial([&](float v, int m, int r) {
+      const float d = v - sm.mean[16 * m + 4 * g + r];
+      return d * d;
+    });
+    __syncthreads();
+    if (tid < kQ) {
+      float x = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) x += sm.red[ww][tid];
+      sm.rstd[tid] = 1.0f / sqrtf(x * (1.0f / kDV) + a.eps);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise, gate, store (each lane: 4 consecutive rows x 1 column) ----
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int col = 64 * w + 16 * n + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = qb * kQ + 16 * m + 4 * g + r;
+        if (t >= N) continue;
+        float y = acc[m][n][r];
+        const int64_t off = (int64_t(bh) * N + t) * kDV + col;
+        if (gn) {
+          const int tl = 16 * m + 4 * g + r;
+          y = (y - sm.mean[tl]) * sm.rstd[tl];
+          if (a.gn_w) y *= a.gn_w[h * kDV + col];
+          if (a.gn_b) y += a.gn_b[h * kDV + col];
+          if (gt) y *= swishf(Elem<RN_BF16>::load(gate, off));
+        }
+        Elem<OUT>::store(out, off, y);
+      }
+    }
+}
+
+}  // namespace
+
+bool parallel_mfma_supported(const CallArgs& a, int in_dt) {
+  return in_dt == RN_BF16 && a.dk == kDK && a.dv == kDV;
+}
+
+size_t parallel_mfma_ws_bytes(const CallArgs& a) {
+  return size_t(a.B) * a.H * ws_layout(a.N).head * sizeof(uint16_t);
+}
+
+hipError_t launch_parallel_mfma(const CallArgs& a, int out_dt, const void* q, const void* k,
+                                const void* v, const void* gate, void* out, void* ws,
+                                hipStream_t st) {
+  const int nb = (a.N + kT - 1) / kT;
+  const int BH = a.B * a.H;
+  uint16_t* w = static_cast<uint16_t*>(ws);
+  hipLaunchKernelGGL(parallel_prep, dim3(nb, BH), dim3(256), 0, st, a,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nq = (a.N + kQ - 1) / kQ;
+  const dim3 grid(static_cast<unsigned>(nq) * 8 * ((BH + 7) / 8));
+  if (out_dt == RN_BF16)
+    hipLaunchKernelGGL((parallel_main<RN_BF16>), grid, dim3(kWaves * 64), 0, st, a, w, gate, out);
+  else
+    hipLaunchKernelGGL((parallel_main<RN_F32>), grid, dim3(kWaves * 64), 0, st, a, w, gate, out);
+  return hipGetLastError();
+}
+
+}  // namespace rn

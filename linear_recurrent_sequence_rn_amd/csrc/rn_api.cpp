@@ -114,14 +114,36 @@ const char* rn_status_str(rn_status s) {
   }
 }
 
+static bool use_mfma_parallel(const rn_desc* d, const rn::CallArgs& a) {
+  return !(d->flags & RN_FORCE_GENERIC) && rn::parallel_mfma_supported(a, d->in_dtype);
+}
+
+size_t rn_parallel_workspace_bytes(const rn_desc* desc) {
+  rn::CallArgs a;
+  if (check_desc(desc, Form::kParallel, &a) != RN_OK) return 0;
+  return use_mfma_parallel(desc, a) ? align256(rn::parallel_mfma_ws_bytes(a)) : 0;
+}
+
 rn_status rn_retention_parallel(const rn_desc* desc, const void* q, const void* k, const void* v,
-                                const void* gate, void* out, void* stream) {
+                                const void* gate, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   rn::CallArgs a;
   rn_status s = check_desc(desc, Form::kParallel, &a);
   if (s != RN_OK) return s;
   if ((s = check_ptrs(desc, q, k, v, gate, out)) != RN_OK) return s;
+  const bool mfma = use_mfma_parallel(desc, a);
+  if (mfma) {
+    const size_t need = align256(rn::parallel_mfma_ws_bytes(a));
+    if (!workspace || workspace_bytes < need)
+      return fail(RN_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(RN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  }
   g_err[0] = 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mfma)
+    return hip_status(rn::launch_parallel_mfma(a, desc->out_dtype, q, k, v, gate, out, workspace, st),
+                      "parallel (MFMA) launch");
   return hip_status(rn::launch_generic_parallel(a, desc->in_dtype, desc->out_dtype, q, k, v,
                                                 gate, out, st),
                     "parallel launch");

@@ -28,4 +28,11 @@ hipError_t launch_chunkwise_mfma(const CallArgs& a, int out_dt, const void* q, c
                                  float* s_out, void* out, void* ws, size_t ws_bytes,
                                  hipStream_t st);
 
+// MFMA parallel form (bf16 inputs, d_k = 256, d_v = 512).
+bool parallel_mfma_supported(const CallArgs& a, int in_dt);
+size_t parallel_mfma_ws_bytes(const CallArgs& a);
+hipError_t launch_parallel_mfma(const CallArgs& a, int out_dt, const void* q, const void* k,
+                                const void* v, const void* gate, void* out, void* ws,
+                                hipStream_t st);
+
 }  // namespace rn

@@ -49,8 +49,8 @@ def desc(**kw):
     return rn.make_desc(B, H, N, dk, dv, i, o, g, th, **p)
 
 
-def par(d, gate=FAKE):
-    return rn.lib.rn_retention_parallel(ctypes.byref(d), FAKE, FAKE, FAKE, gate, FAKE, None)
+def par(d, gate=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return rn.lib.rn_retention_parallel(ctypes.byref(d), FAKE, FAKE, FAKE, gate, FAKE, ws, ws_bytes, None)
 
 
 def chk(d, chunk=4, ws_bytes=1 << 30, ws=FAKE):
@@ -93,13 +93,15 @@ def test_invalid_descriptors_rejected_everywhere(kw, code):
     d1, keep1 = desc(**{**kw, "N": 1} if "N" not in kw else kw)
     assert step(d1) == code
     assert rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), 4) == 0
+    assert rn.lib.rn_parallel_workspace_bytes(ctypes.byref(d)) == 0
 
 
 def test_null_desc_and_pointers():
-    assert rn.lib.rn_retention_parallel(None, FAKE, FAKE, FAKE, None, FAKE, None) == rn.RN_ERR_INVALID_ARG
+    P = rn.lib.rn_retention_parallel
+    assert P(None, FAKE, FAKE, FAKE, None, FAKE, None, 0, None) == rn.RN_ERR_INVALID_ARG
     d, keep = desc()
-    assert rn.lib.rn_retention_parallel(ctypes.byref(d), None, FAKE, FAKE, None, FAKE, None) == rn.RN_ERR_INVALID_ARG
-    assert rn.lib.rn_retention_parallel(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, None) == rn.RN_ERR_INVALID_ARG
+    assert P(ctypes.byref(d), None, FAKE, FAKE, None, FAKE, None, 0, None) == rn.RN_ERR_INVALID_ARG
+    assert P(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, None, 0, None) == rn.RN_ERR_INVALID_ARG
     d, keep = desc(flags=rn.RN_EPI_GN | rn.RN_EPI_GATE)
     assert par(d, gate=None) == rn.RN_ERR_INVALID_ARG     # gate flag without a gate tensor
 
@@ -123,6 +125,18 @@ def test_workspace_independent_of_sequence_length():
         d, keep = desc(N=N, d_k=256, d_v=512, theta=np.ones(128), H=16, gamma=np.full(16, 0.9))
         sizes.add(rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), 256))
     assert len(sizes) == 1 and sizes.pop() > 0
+
+
+def test_parallel_workspace():
+    big = dict(d_k=256, d_v=512, theta=np.ones(128), H=8, gamma=np.full(8, 0.9), N=2048)
+    d, keep = desc(**big)
+    need = rn.lib.rn_parallel_workspace_bytes(ctypes.byref(d))
+    assert need == 8 * 2048 * (2 * 256 + 512) * 2          # q, k rotated + v transposed, half
+    assert par(d, ws_bytes=need - 1) == rn.RN_ERR_WORKSPACE
+    assert par(d, ws=None) == rn.RN_ERR_WORKSPACE
+    assert par(d, ws=ctypes.c_void_p(0x1010), ws_bytes=need) == rn.RN_ERR_INVALID_ARG   # misaligned
+    d, keep = desc(**big, flags=rn.RN_FORCE_GENERIC)
+    assert rn.lib.rn_parallel_workspace_bytes(ctypes.byref(d)) == 0
 
 
 def test_step_specific_errors():

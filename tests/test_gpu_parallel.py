@@ -1,0 +1,102 @@
+"""GPU parity of the MFMA parallel form (bf16 q/k/v, d_k = 256, d_v = 512).
+
+Tolerances (half-precision MFMA operands, fp32 accumulation): raw outputs per (b, h)
+||gpu - ref||_inf <= 1e-2 ||ref||_inf (Qh, Kh, V and the decayed scores are rounded to
+half, relative 2^-11 each); after GroupNorm (fp32 output) max-abs 2e-2, with the gate
+2e-2 * max(1, |swish(g)|); bf16 output adds half a bf16 ulp of the reference.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def rn():
+    import linear_recurrent_sequence_rn_amd as m
+    return m
+
+
+def rel_inf(gpu, ref):
+    g, r = O.to64(gpu), O.to64(ref)
+    err = np.abs(g - r).reshape(r.shape[0], r.shape[1], -1).max(-1)
+    nrm = np.abs(r).reshape(r.shape[0], r.shape[1], -1).max(-1)
+    return float((err / np.maximum(nrm, 1e-30)).max())
+
+
+def dev(x):
+    return None if x is None else x.to(DEV)
+
+
+def check_gated(out, ref, gate):
+    sw = np.abs(O.swish(gate)) if gate is not None else 1.0
+    bound = 2e-2 * np.maximum(1.0, sw)
+    d = np.abs(O.to64(out) - ref)
+    if out.dtype == torch.bfloat16:
+        bound = bound + np.abs(ref) * 2.0 ** -8
+    assert (d <= bound).all(), float((d / bound).max())
+
+
+def wl(**kw):
+    base = dict(name="p", form="parallel", B=1, H=2, N=200, d_k=256, d_v=512, dtype="bf16",
+                gamma_kind="small", qkv_std=1 / 16, seed=41)
+    base.update(kw)
+    return W.Workload(**base)
+
+
+@pytest.mark.parametrize("N,pos0,alpha,nd,nr", [
+    (200, 0, 1.0, False, False), (64, 7, 1 / 16, False, False), (1, 0, 1.0, False, False),
+    (130, 0, 1 / 16, True, False), (130, 3, 1 / 16, False, True), (257, 0, 1 / 16, True, True)])
+def test_raw_output(N, pos0, alpha, nd, nr):
+    x = W.make_inputs(wl(N=N))
+    out = rn().rn_retention_parallel(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"],
+                                     out_dtype=torch.float32, pos0=pos0, qk_scale=alpha,
+                                     norm_d=nd, norm_r=nr)
+    ref = O.parallel(x["q"], x["k"], x["v"], x["gamma"], x["theta"], pos0, alpha, nd, nr)
+    assert rel_inf(out.cpu(), ref) <= 1e-2
+
+
+def test_gn_gate_affine_and_bf16_out():
+    w = wl(N=190, gate=True, H=3)
+    x = W.make_inputs(w)
+    gw = torch.randn(3 * 512, generator=torch.Generator().manual_seed(8)) * 0.5 + 1
+    gb = torch.randn(3 * 512, generator=torch.Generator().manual_seed(9)) * 0.1
+    raw = O.parallel(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 0, 1 / 16, True, True)
+    ref = O.groupnorm_gate(raw, x["gate"], 1e-5, gw.reshape(3, 512), gb.reshape(3, 512))
+    for od in (torch.float32, torch.bfloat16):
+        out = rn().rn_retention_parallel(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
+                                         x["theta"], gate=dev(x["gate"]), out_dtype=od,
+                                         qk_scale=1 / 16, norm_d=True, norm_r=True, gn=True,
+                                         gn_weight=dev(gw), gn_bias=dev(gb))
+        check_gated(out.cpu(), ref, x["gate"])
+
+
+def test_matches_plain_kernel():
+    """The MFMA path and the plain float32 kernel agree on the same inputs."""
+    x = W.make_inputs(wl(N=96, H=2))
+    args = (dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"])
+    a = rn().rn_retention_parallel(*args, out_dtype=torch.float32, qk_scale=0.5, norm_r=True)
+    b = rn().rn_retention_parallel(*args, out_dtype=torch.float32, qk_scale=0.5, norm_r=True,
+                                   force_generic=True)
+    assert rel_inf(a.cpu(), b.cpu()) <= 1e-2
+
+
+def test_1p3b_shape_sampled_heads():
+    """The 1.3B-shaped workload (B=8, H=8, N=2048, alpha = 1/16, D and R normalisation,
+    GroupNorm) in the launch configuration of the full call; three (b, h) checked in full."""
+    w = W.WORKLOADS["parallel_1p3b"]
+    x = W.make_inputs(w)
+    out = rn().rn_retention_parallel(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"],
+                                     out_dtype=torch.float32, qk_scale=w.qk_scale, norm_d=True,
+                                     norm_r=True, gn=True)
+    out = out.cpu()
+    assert torch.isfinite(out).all()
+    for b, h in ((0, 0), (7, 7), (3, 5)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        raw = O.parallel(x["q"][sl], x["k"][sl], x["v"][sl], x["gamma"][h:h + 1], x["theta"], 0,
+                         w.qk_scale, True, True)
+        check_gated(out[sl], O.group_norm(raw), None)
