@@ -11,7 +11,8 @@
 //     the 64-row key blocks that have causal pairs with it. Each key block of Kh is
 //     copied once into LDS (buffer loads with the lds modifier, two buffers, two blocks
 //     ahead). Wave w computes the scores of query rows 16w..16w+15 against the 64 keys
-//     (16x16x32 f16 MFMA over all of d_k), applies gamma^(t-s) and the causal mask,
+//     (16x16x32 f16 MFMA over all of d_k, taken as K Q^T), applies gamma^(t-s) (a per-lane
+//     factor times a per-block one) and, on the two diagonal key blocks, the causal mask,
 //     accumulates the signed row sums for the R normalisation and writes the scores to
 //     LDS in half (two buffers: the scores of block kb+1 are computed while block kb is
 //     multiplied with V); every wave then multiplies all 128 score rows with its 64
@@ -74,10 +75,19 @@ __host__ __device__ inline Ws ws_layout(int N) {
   return w;
 }
 
+// Order of the 64 keys of a block inside a row of V^T (and of the score block in LDS):
+// key s = 32e + 16h + 4g + r (e, h in {0,1}, g, r in [0,4)) sits at position
+// 32e + 8g + 4h + r. Lane group g of a 16x16x32 MFMA then finds its 8 k-values (keys
+// 32e + 4g + {0..3} and 32e + 16 + 4g + {0..3}) in 16 contiguous bytes, which are also
+// the 8 scores that a lane holds after the transposed score product K Q^T.
+__host__ __device__ constexpr int vt_pos(int s) {
+  return 32 * (s >> 5) + 8 * ((s >> 2) & 3) + 4 * ((s >> 4) & 1) + (s & 3);
+}
+
 // ---- prep: one 256-thread block per (64-row block, head) ------------------------------
 // bf16 inputs only. q and k: thread = (group of 4 coordinate pairs = 16 bytes, group of
 // 8 rows); 16-byte loads, angles by recurrence along the rows. v: thread = 8 rows x 8
-// columns, transposed in registers and written as 8 rows of V^T (16 bytes each).
+// columns, transposed in registers and written as 8 rows of V^T (keys in vt_pos order).
 __global__ void __launch_bounds__(256) parallel_prep(CallArgs a, const uint16_t* q,
                                                      const uint16_t* k, const uint16_t* v,
                                                      uint16_t* ws) {
@@ -136,12 +146,13 @@ __global__ void __launch_bounds__(256) parallel_prep(CallArgs a, const uint16_t*
         f[i][2 * j + 1] = __uint_as_float(x[j] & 0xffff0000u);
       }
     }
+    // rows 8sg..8sg+3 and 8sg+4..8sg+7 land at positions p0 and p0 + 8
+    const int p0 = vt_pos(8 * sg);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      u32x4 o;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = pack_f16x2(f[2 * i][j], f[2 * i + 1][j]);
-      *reinterpret_cast<u32x4*>(vt + size_t(8 * cg + j) * kT + 8 * sg) = o;
+      uint16_t* row = vt + size_t(8 * cg + j) * kT;
+      *reinterpret_cast<u32x2*>(row + p0) = u32x2{pack_f16x2(f[0][j], f[1][j]), pack_f16x2(f[2][j], f[3][j])};
+      *reinterpret_cast<u32x2*>(row + p0 + 8) = u32x2{pack_f16x2(f[4][j], f[5][j]), pack_f16x2(f[6][j], f[7][j])};
     }
   }
 }
@@ -209,32 +220,51 @@ parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
   for (int c = 0; c < 8; ++c)
     qf[c] = as_f16x8(ld_b128(rq, static_cast<uint32_t>((t_row * kDK + 32 * c + 8 * g) * 2)));
 
-  float rsum[4] = {0.f, 0.f, 0.f, 0.f};   // partial signed sums of rows 16w + 4g + r
+  float rsum = 0.f;   // partial signed sum of the scores of row 16w + l16
 
-  // scores of key block kb (in LDS buffer kb % 2) -> sm.p[kb % 2], half
+  // Decay gamma^(t-s) with t = 128qb + 16w + l16 and s = 64kb + 16i + 4g + r, as
+  // rl * gr[r] * bi[i]: rl = gamma^(16w + l16 - 4g) per lane (exponent in [-12, 127]),
+  // gr[r] = gamma^-r (scalar registers), bi[i] = gamma^(128qb - 64kb - 16i) per wave and
+  // key block. The factors stay in float's normal range when gamma^-127 does
+  // (gamma > 0.5035); below that every element takes its own exp2.
+  const bool factored = lg * 127.f >= -126.f;
+  const float rl = exp2f(lg * float(16 * w + l16 - 4 * g));
+  float gr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    gr[r] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(exp2f(-lg * float(r)))));
+
+  // scores of key block kb (in LDS buffer kb % 2) -> sm.p[kb % 2], half. The product is
+  // taken transposed (A = Kh rows, B = Qh^T), so lane (l16, g) ends with, for query row
+  // 16w + l16, the keys 16i + 4g + r: four consecutive keys per tile i.
   auto scores = [&](int kb) {
     const int buf = kb & 1;
     f32x4 sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int s = 16 * i + l16;        // key row (B operand column)
+      const int s = 16 * i + l16;        // key row (A operand row)
       f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 8; ++c)
-        z = mfma(qf[c], as_f16x8(sm.kh[buf][kh_unit(s, 4 * c + g)]), z);
+        z = mfma(as_f16x8(sm.kh[buf][kh_unit(s, 4 * c + g)]), qf[c], z);
       sc[i] = z;
     }
-    // D layout: row t = 16w + 4g + r, column s = 16i + l16
+    const int dq = qb * kQ - kb * kT;                 // t - s without the in-block offsets
+    const bool diag = kb >= 2 * qb;                   // only these blocks hold s > t
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const float bl = rl * exp2f(lg * float(dq - 16 * i));
+      float val[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int d = (qb * kQ + 16 * w + 4 * g + r) - (kb * kT + 16 * i + l16);
-        const float val = (d >= 0) ? sc[i][r] * exp2f(lg * float(d)) : 0.f;
-        rsum[r] += val;
-        sm.p[buf][16 * w + 4 * g + r][16 * i + l16] =
-            __builtin_bit_cast(uint16_t, static_cast<_Float16>(val));
+        const int d = dq + 16 * w + l16 - 16 * i - 4 * g - r;
+        const float f = factored ? bl * gr[r] : exp2f(lg * float(d));
+        val[r] = (diag && d < 0) ? 0.f : sc[i][r] * f;
+        rsum += val[r];
       }
+      *reinterpret_cast<u32x2*>(&sm.p[buf][16 * w + l16][vt_pos(16 * i + 4 * g)]) =
+          u32x2{pack_f16x2(val[0], val[1]), pack_f16x2(val[2], val[3])};
+    }
   };
 
   // output accumulators: all 128 rows (8 t-tiles) x this wave's 64 columns (4 tiles)
@@ -266,7 +296,8 @@ parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
         vf[e][n] = as_f16x8(ld_b128(rv, (vblk + static_cast<uint32_t>(dv * kT + 32 * e + 8 * g)) * 2));
       }
     if (kb + 1 <= kb_end) scores(kb + 1);
-    // O[:, this wave's columns] += P(kb) V(kb): A = P (row t, k = s), B = V^T (col dv, k = s)
+    // O[:, this wave's columns] += P(kb) V(kb): A = P (row t, k = s), B = V^T (col dv, k = s),
+    // both with the keys in vt_pos order
     const int buf = kb & 1;
 #pragma unroll
     for (int e = 0; e < 2; ++e)
@@ -281,14 +312,11 @@ parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
   }
 
   // ---- row scalars ------------------------------------------------------------------
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float x = rsum[r];
-    x += __shfl_xor(x, 1, 64);
-    x += __shfl_xor(x, 2, 64);
-    x += __shfl_xor(x, 4, 64);
-    x += __shfl_xor(x, 8, 64);
-    if (l16 == 0) sm.rs[16 * w + 4 * g + r] = x;
+  {
+    float x = rsum;
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    if (g == 0) sm.rs[16 * w + l16] = x;
   }
   __syncthreads();
   const bool any_norm = a.flags & (RN_NORM_D_ROW | RN_NORM_R_ROW);
