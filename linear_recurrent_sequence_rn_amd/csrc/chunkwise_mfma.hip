@@ -6,42 +6,51 @@
 // slices; one 256-thread workgroup owns one slice (64 KB of state, kept in MFMA
 // accumulator registers for the whole sequence) and walks the sequence in blocks of
 // 64 tokens. Inside the workgroup the four waves split d_k into quarters: wave w
-// keeps S[64w:64w+64, slice] and computes the quarter's partial products, which are
-// summed through LDS. Per block and wave (16x16x32 f16 MFMA, fp32 accumulate):
-//   cross   acc  = xi ⊙ (Qh_w S_w)                 (Qh_w: 64 x 64 quarter of Qh)
-//   scores  P_w  = alpha (Kh_w Qh_w^T ⊙ D)^T       (partial over the quarter)
-//   intra   acc += P_w V
-//   carry   S_w  = gamma^L S_w + (zeta ⊙ Kh_w)^T V
+// keeps the quarter's rows of the state and computes the quarter's partial products,
+// which are summed through LDS.
+//
+// Decay folded into the operands. With j the row of a token inside its block, the
+// rotated rows are stored in half as
+//     Qt_j = alpha gamma^(j-31) Qh_j,      Kt_j = gamma^(31-j) Kh_j,
+// and the state is carried as Sc = gamma^32 S. Then, for a block of L rows,
+//     scores   Qt_t . Kt_s  = alpha gamma^(t-s) Qh_t . Kh_s       (causal mask only)
+//     cross    Qt_t Sc      = alpha gamma^(t+1) Qh_t S            (xi_t applied)
+//     carry    Sc <- gamma^L (Sc + Kt^T V)                        (zeta_s applied)
+// which is the chunkwise recurrence with the state update weighted per row by
+// gamma^(L-1-s), read off by unrolling the recurrent update over the block. The
+// factors gamma^(+-32) bound the operand range; the path requires gamma^32 >= 2^-6.
+// Per block and wave (16x16x32 f16 MFMA, fp32 accumulate):
+//   scores  P_w^T = Kt_w Qt_w^T                   (partial over the quarter, 20 MFMA)
+//   Kt_w^T  by MFMA against 0/1 selection matrices  (16 MFMA, exact)
+//   cross   acc  = Qt_w Sc_w                      (32 MFMA)
+//   intra   acc += P_w V                          (24 MFMA)
+//   carry   Sc_w = gamma^L (Sc_w + Kt_w^T V)      (32 MFMA)
 // The output is the sum of the four waves' acc; GroupNorm (+ gate) follows.
 //
 // Operand precision. q, k, v arrive in bf16; the rotation runs in float32 and every
-// MFMA operand (Qh, Kh, V, the decayed scores, the state copy used by the cross term)
-// is rounded to IEEE half. bf16 values are exact in half within its range, and half
-// keeps 3 more significand bits than bf16, which is what holds the error after
-// GroupNorm well inside 2e-2 (bf16 operands put it near 2.6e-2 on RetNet-shaped data).
-// Precondition of this path: operands within half's range (|x| < 65504); values
-// outside it need the plain float32 kernels (RN_FORCE_GENERIC).
+// MFMA operand is rounded to IEEE half, which keeps 3 more significand bits than bf16
+// (bf16 operands put the error after GroupNorm near 2.6e-2 on RetNet-shaped data,
+// half keeps it near 4e-3). Operands must stay within half's range (|x| < 65504).
 //
-// Sharing between the slices of one head. Every slice needs the whole rotated block
-// of q and k. Each of the nS workgroups rotates 64/nS rows of the NEXT block and
-// writes Qh, Kh and (zeta ⊙ Kh)^T in half to a ring of 4 block slots in the
-// workspace; a per-head counter says how many row groups are published. GroupNorm
-// statistics (per-row mean and centred sum of squares of each slice) go through a
-// second counter, and the normalisation of block j waits for them while block j+1
-// is computed. All slices of a head are placed on one XCD (blockIdx mod 8), so the
-// exchange runs through that XCD's L2: a writer waits for its stores to complete
-// before a relaxed agent-scope increment; readers poll with agent-scope atomic loads
-// and read shared data with L1-bypassing (sc0) buffer loads. If the slices of a
-// head turn out to sit on different XCDs, the kernel switches to release/acquire
-// fences at agent scope. Every wait has a time limit that ends the kernel normally
+// Sharing between the slices of a head. Every slice needs the whole rotated block.
+// Each of the nS workgroups rotates 64/nS rows of the block three ahead of the one
+// it computes and writes Qt, Kt to a ring of 8 block slots in the workspace; per-slot
+// counters, incremented once per wave after its stores have completed, say when a
+// block is whole. GroupNorm statistics (per-row mean and centred sum of squares of
+// each slice) go through an 8-slot ring the same way; a block is normalised and
+// stored two blocks after it is computed, once every slice has published its
+// statistics. All slices of a head are placed on one XCD (blockIdx mod 8), so the
+// exchange stays in that XCD's L2: shared data is read with L1-bypassing (sc0)
+// buffer loads. If the slices turn out to span XCDs, the kernel uses agent-scope
+// release/acquire fences. Every wait has a time limit that ends the kernel normally
 // and raises an error word in the workspace.
 //
-// Ring safety: consuming block j needs every slice to have published block j, which
-// they do at their iteration j-2; so no workgroup is more than one block ahead of
-// another. Blocks are produced two ahead, so with 8 slots the slot a workgroup
-// overwrites (block j+2) is never one a slower workgroup can still read (j-1, j). Statistics of block j are
-// read at iteration j+1 and their slot is rewritten at iteration j+4, by which time
-// every slice has passed iteration j+2.
+// Ring safety. At step j a workgroup writes block j+3 (slot (j+3) mod 8), waits for
+// block j+1 to be whole and loads it, computes block j, and reads the statistics of
+// block j-2 before publishing those of block j. Waiting for block j+1 means every
+// slice has finished step j-2, so a workgroup that writes slot (j+3) mod 8 at step j
+// knows every reader of the block held there before (j-5, read at step j-6) is done;
+// and the statistics slot written at step j (block j) was last read for block j-8.
 #include "rn_device.h"
 #include "rn_kernels.h"
 
@@ -57,18 +66,18 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kT = 64;          // tokens per block
 constexpr int kDK = 256;        // d_k of this kernel
 constexpr int kSl = 64;         // d_v columns per workgroup
-constexpr int kRing = 8;        // ring slots (blocks of Qh/Kh/Kh^T)
-constexpr int kStatRing = 4;    // statistics slots
-constexpr int kRedLd = 68;      // LDS row stride (floats) of the reduction buffer
-constexpr int kVtLd = 72;       // LDS row stride (bf16) of the transposed V slice
+constexpr int kRing = 8;        // ring slots (blocks of Qt/Kt)
+constexpr int kStatRing = 8;    // statistics slots
+constexpr int kAhead = 3;       // blocks produced ahead of the block computed
+constexpr int kLag = 2;         // blocks between computing a block and normalising it
+constexpr int kReanchor = 16;   // blocks between exact (float64-reduced) angle anchors
+constexpr int kVtLd = 72;       // LDS row stride (half) of the transposed V slice
 constexpr uint32_t kCntWords = 64;             // counter words per head
-constexpr size_t kStatsPerHead = size_t(kStatRing) * 8 * kT * 2 * sizeof(float);   // 16 KB
-constexpr size_t kSlotElems = size_t(kT) * kDK;                                  // 16384 bf16
-constexpr size_t kRingPerHead = size_t(kRing) * 3 * kSlotElems * sizeof(uint16_t);
-constexpr int kMaxWgPerLaunch = 4096;
+constexpr size_t kStatsPerHead = size_t(kStatRing) * 8 * kT * 2 * sizeof(float);   // 32 KB
+constexpr size_t kSlotElems = size_t(kT) * kDK;                                  // 16384 half
+constexpr size_t kRingPerHead = size_t(kRing) * 2 * kSlotElems * sizeof(uint16_t);  // 512 KB
 constexpr uint64_t kWaitTicks = 100000000ull;  // 1 s of the 100 MHz wall clock
 
-// counter words
 // Counter words per head. Publication counts are kept per ring slot and in waves:
 // slot s counts the waves that published blocks s, s+kRing, s+2kRing, ...; block j is
 // complete when word kReady + j%kRing reaches 4*nS*(j/kRing + 1). (A single running
@@ -92,15 +101,44 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Sum over each row of 16 lanes, every lane receiving the row's sum, with DPP moves
+// (VALU only): swap neighbours, swap pairs, mirror within 8 lanes, mirror within 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
+  x += dpp_mov<0x141>(x);   // row_half_mirror: lane i <-> 7 - i within 8
+  x += dpp_mov<0x140>(x);   // row_mirror: lane i <-> 15 - i within 16
+  return x;
+}
+
 __device__ __forceinline__ uint32_t xcc_id() {
   // HW_REG_XCC_ID (id 20), bits [3:0]
   return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xf;
 }
 
+// Order of the 64 keys of a block inside a row of V^T: key s = 32e + 16h + 4g + r
+// (e, h in {0,1}; g, r in [0,4)) sits at position 32e + 8g + 4h + r. Lane group g of
+// a 16x16x32 MFMA then finds its 8 k-values (keys 32e + 4g + {0..3} and
+// 32e + 16 + 4g + {0..3}) in 16 contiguous bytes, which are also the 8 values a lane
+// holds after a transposed product (two 16x16 tiles, four consecutive rows each).
+__device__ __forceinline__ constexpr int vt_pos(int s) {
+  return 32 * (s >> 5) + 8 * ((s >> 2) & 3) + 4 * ((s >> 4) & 1) + (s & 3);
+}
+
+// Swizzle of the reduction buffer: column c of a wave's partial output keeps its row
+// group q (rows 4q..4q+3) at q ^ red_swz(c), so that both the 16-byte writes (16
+// consecutive columns, one row group) and the 16-byte reads (columns 4b + cc for 16
+// values of b, one row group) touch 16 distinct 4-bank groups.
+__device__ __forceinline__ int red_swz(int c) { return ((c >> 2) & 15) ^ ((c & 3) << 2); }
+
 struct alignas(16) Shared {
-  float red[4][kT][kRedLd];          // partial outputs of the four waves
-  uint16_t vt[kSl][kVtLd];           // V slice of the block, transposed: [dv][s]
-  u32x4 qk[4][16][64];               // next block's Qh/Kh fragments, per wave and lane
+  float red[4][kSl][kT];             // partial outputs of the four waves: [wave][col][row]
+  uint16_t vt[2][kSl][kVtLd];        // V slice of two blocks, transposed, vt_pos order
+  u32x4 fr[4][16][64];               // next block's Qt/Kt fragments, per wave and lane
   uint32_t mode;                     // 1 = agent-scope fences
 };
 
@@ -133,9 +171,14 @@ __device__ __forceinline__ u32x2 ld_sc0_b64(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 1));
 }
 
-__device__ __forceinline__ void store_fence_release(bool agent) {
+// Makes this wave's earlier stores complete before a release count is raised. Vector
+// memory operations of a wave complete in issue order, so when the last `tail4 ? 4 : 0`
+// operations are ones that need not be waited for, vmcnt(4) covers everything before.
+__device__ __forceinline__ void store_fence_release(bool agent, bool tail4 = false) {
   if (agent) {
     __threadfence();
+  } else if (tail4) {
+    __asm__ volatile("s_waitcnt vmcnt(4)" ::: "memory");
   } else {
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
@@ -181,15 +224,23 @@ struct Params {
   uint8_t* ws;
 };
 
-template <int OUT>
+// One lane's MFMA operand fragments of a block: Qt rows 16m + l16 and Kt rows
+// 16i + l16, d_k = 64w + 32c + 8g .. +8 (w = wave, g = lane group), in half.
+struct Frags {
+  u32x4 q[4][2];
+  u32x4 k[4][2];
+};
+
+template <int OUT, int NS>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 chunkwise_fused(Params P) {
   const CallArgs& a = P.a;
   const int xcd = blockIdx.x & 7, L8 = blockIdx.x >> 3;
-  const int hg = (L8 / P.nS) * 8 + xcd;  // head within the launch group
+  const int hg = (L8 / NS) * 8 + xcd;    // head within the launch group
   if (hg >= P.heads) return;
-  const int sl = L8 % P.nS;              // d_v slice
-  const int nS = P.nS;
+  const int sl = L8 % NS;                // d_v slice
+  constexpr int nS = NS;
+  const int nb = P.nb;
   const int bh = P.head0 + hg;
   const int h = bh % a.H;
   const int N = a.N, DV = a.dv;
@@ -224,157 +275,88 @@ chunkwise_fused(Params P) {
   __syncthreads();
   const bool agent = sm.mode != 0;
 
-  // ---- per-lane constants --------------------------------------------------------
   const float lg = a.hp.log2g[h];
-  const float gam = a.hp.gamma[h];
   const float alpha = a.alpha;
-  float G16[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) G16[m] = exp2f(lg * float(16 * m));
-  // alpha * xi_t, xi_t = gamma^(t+1), for the row t = 16m + l16 this lane feeds to the
-  // cross-term MFMA, as a half splat: the cross term scales the rows of Qh.
-  f16x8 xs[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const _Float16 x = static_cast<_Float16>(alpha * exp2f(lg * float(16 * m + l16 + 1)));
-    xs[m] = f16x8{x, x, x, x, x, x, x, x};
-  }
-  // decay for P^T tile (s-tile 2e+hh, t-tile m), element r:
-  //   t - s = (l16 - 8g - 4hh - r) + 16 (m - 2e)
-  const bool factored = lg * 31.0f > -100.0f;  // gamma^-31 stays far below overflow
-  float decF[2][4];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) decF[hh][r] = alpha * exp2f(lg * float(l16 - 8 * g - 4 * hh - r));
-
-  // producer constants: this thread rotates coordinate pair pp of q (tid < 128) or k
-  const int pp = tid & 127;
-  const bool prod_k = w >= 2;        // waves 0-1 rotate q, waves 2-3 rotate k
-  const float theta_p = a.ap.theta[pp];
-  float c1, s1;
-  angle_cs(1, theta_p, &c1, &s1);
-  const int rows_per = kT / nS;
-  const int r_lo = sl * rows_per;
-
-  // ---- state: S_w tiles [a][b], a = dk tile (permuted rows), b = dv tile ------------
-  // accumulator row 4g+r of tile a = 2c+hh holds dk = 64w + 32c + 8g + 4hh + r
-  f32x4 Sacc[4][4];
-#pragma unroll
-  for (int ta = 0; ta < 4; ++ta)
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int dk = 64 * w + 32 * (ta >> 1) + 8 * g + 4 * (ta & 1) + r;
-        const int dv = sl * kSl + 16 * tb + l16;
-        Sacc[ta][tb][r] = P.s_in ? P.s_in[(size_t(bh) * kDK + dk) * DV + dv] : 0.f;
-      }
-
-  // this head's rows of q or k (producer), and its d_v slice of v, gate and out
   const bool use_gn = a.flags & RN_EPI_GN;
   const bool has_gate = P.gate != nullptr;
-  const int64_t qk_bytes = int64_t(N) * kDK * 2;
-  const __amdgpu_buffer_rsrc_t r_src = range_rsrc((prod_k ? P.k : P.q) + size_t(bh) * N * kDK, qk_bytes);
-  const int64_t slice_bytes = (int64_t(N) * DV - sl * kSl) * 2;  // to the end of this head
-  const size_t slice0 = size_t(bh) * N * DV + sl * kSl;
-  const __amdgpu_buffer_rsrc_t r_v = range_rsrc(P.v + slice0, slice_bytes);
-  const __amdgpu_buffer_rsrc_t r_g = range_rsrc(has_gate ? P.gate + slice0 : P.v + slice0, slice_bytes);
-  const int osz = (OUT == RN_BF16) ? 2 : 4;
-  const __amdgpu_buffer_rsrc_t r_o =
-      range_rsrc(static_cast<uint8_t*>(P.out) + slice0 * osz, slice_bytes / 2 * osz);
-  const int t_fin = 16 * w + (l >> 2);     // row (in block) this lane normalises and stores
-  const int c_fin = (l & 3) * 16;          // first of its 16 columns (within the slice)
-  const float inv_nS = 1.0f / float(nS);
 
-  // ---- producer ------------------------------------------------------------------
-  // Rows [rbase, rbase + 8) of block jb for this thread's coordinate pair, as packed
-  // bf16 pairs; zero past the end of the sequence.
-  auto load8 = [&](int jb, int rbase, uint32_t* xr) {
+  // ---- producer: this thread rotates rows r_lo + pr + 8u (u < U) of each block,
+  // pairs 4pq..4pq+3 (d_k 8pq..8pq+7), for q and k -----------------------------------
+  constexpr int rows_per = kT / nS, U = rows_per / 8;
+  const int r_lo = sl * rows_per;
+  const int pr = tid >> 5, pq = tid & 31;
+  float th[4], c64[4], s64[4], cc[U][4], ss[U][4], fq[U], fk[U];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      xr[u] = ld_b32(r_src, static_cast<uint32_t>(((jb * kT + rbase + u) * kDK + 2 * pp) * 2));
-  };
-  // Rotates this workgroup's rows [r_lo, r_lo + rows_per) of block jb into the block's
-  // ring slot. `first8` holds the first 8 rows, loaded one iteration earlier.
-  auto produce = [&](int jb, const uint32_t* first8) {
-    uint16_t* slot = ring + size_t(jb % kRing) * 3 * kSlotElems;
-    const int row0 = jb * kT;
-    const int Lb = min(kT, N - row0);
-    uint16_t* dst = slot + (prod_k ? kSlotElems : 0);
-    uint16_t* dstT = slot + 2 * kSlotElems;
-    float c, s;
-    angle_cs(a.pos0 + row0 + r_lo, theta_p, &c, &s);
-    for (int r8 = 0; r8 < rows_per; r8 += 8) {
-      uint32_t xr[8];
-      if (r8 == 0) {
+  for (int i = 0; i < 4; ++i) {
+    th[i] = a.ap.theta[4 * pq + i];
+    angle_cs(kT, th[i], &c64[i], &s64[i]);   // once per thread: exact
+  }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) xr[u] = first8[u];
-      } else {
-        load8(jb, r_lo + r8, xr);
-      }
-      float z0[8], z1[8];
-      // zeta_rr = gamma^(Lb-1-rr) for rr < Lb, else 0: computed at the last valid row of
-      // these 8 and multiplied by gamma going back (no overflow for gamma in (0, 1])
-      float zeta[8];
-      if (prod_k) {
-        const int rfirst = r_lo + r8;
-        const int rlast = min(rfirst + 7, Lb - 1);
-        float zcur = exp2f(lg * float(max(Lb - 1 - rlast, 0)));
+  for (int u = 0; u < U; ++u) {
+    const int row = r_lo + pr + 8 * u;
+    fq[u] = alpha * exp2f(lg * float(row - 31));
+    fk[u] = exp2f(lg * float(31 - row));
 #pragma unroll
-        for (int u = 7; u >= 0; --u) {
-          const bool ok = rfirst + u <= rlast;
-          zeta[u] = ok ? zcur : 0.f;
-          zcur = ok ? zcur * gam : zcur;
-        }
-      }
+    for (int i = 0; i < 4; ++i) {
+      cc[u][i] = 1.f;
+      ss[u][i] = 0.f;
+    }
+  }
+  const int64_t p_row0 = a.pos0 + r_lo + pr;   // position of the thread's row u = 0 in block 0
+  const size_t qk_head = size_t(bh) * N * kDK;
+  const int64_t qk_bytes = int64_t(N) * kDK * 2;
+  const __amdgpu_buffer_rsrc_t r_q = range_rsrc(P.q + qk_head, qk_bytes);
+  const __amdgpu_buffer_rsrc_t r_k = range_rsrc(P.k + qk_head, qk_bytes);
+  // raw rows of the next block to produce (past the end of the sequence: zeros)
+  u32x4 xq[U], xk[U];
+  auto load_raw = [&](int b) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int rr = r_lo + r8 + u;     // row in block
-        const float x0 = __uint_as_float(xr[u] << 16);
-        const float x1 = __uint_as_float(xr[u] & 0xffff0000u);
-        const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
-        *reinterpret_cast<uint32_t*>(dst + size_t(rr) * kDK + 2 * pp) = pack_f16x2(y0, y1);
-        if (prod_k) {
-          z0[u] = y0 * zeta[u];
-          z1[u] = y1 * zeta[u];
-        }
-        const float cn = c * c1 - s * s1;
-        s = c * s1 + s * c1;
-        c = cn;
-      }
-      if (prod_k) {
-        u32x4 t0, t1;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          t0[u] = pack_f16x2(z0[2 * u], z0[2 * u + 1]);
-          t1[u] = pack_f16x2(z1[2 * u], z1[2 * u + 1]);
-        }
-        *reinterpret_cast<u32x4*>(dstT + size_t(2 * pp) * kT + r_lo + r8) = t0;
-        *reinterpret_cast<u32x4*>(dstT + size_t(2 * pp + 1) * kT + r_lo + r8) = t1;
-      }
+    for (int u = 0; u < U; ++u) {
+      const uint32_t off = static_cast<uint32_t>(((b * kT + r_lo + pr + 8 * u) * kDK + 8 * pq) * 2);
+      xq[u] = ld_b128(r_q, off);
+      xk[u] = ld_b128(r_k, off);
     }
   };
-  // Flags are per wave: every wave publishes its own stores and every wave checks
-  // readiness for itself, so no block barrier is needed around an exchange. Counts are
-  // therefore kept in waves: block j is complete once 4*nS waves have published it.
+  // Rotates and stores this workgroup's rows of block b. Blocks are produced in order;
+  // the angles advance by 64 theta per block and are re-anchored from their
+  // float64-reduced values every kReanchor blocks.
+  auto produce = [&](int b) {
+    const bool anchor = (b % kReanchor) == 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (anchor) {
+          angle_cs_fast(p_row0 + int64_t(b) * kT + 8 * u, th[i], &cc[u][i], &ss[u][i]);
+        } else {
+          const float cn = cc[u][i] * c64[i] - ss[u][i] * s64[i];
+          ss[u][i] = cc[u][i] * s64[i] + ss[u][i] * c64[i];
+          cc[u][i] = cn;
+        }
+      }
+      u32x4 oq, ok;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float q0 = __uint_as_float(xq[u][i] << 16), q1 = __uint_as_float(xq[u][i] & 0xffff0000u);
+        const float k0 = __uint_as_float(xk[u][i] << 16), k1 = __uint_as_float(xk[u][i] & 0xffff0000u);
+        const float cq = cc[u][i] * fq[u], sq = ss[u][i] * fq[u];
+        const float ck = cc[u][i] * fk[u], sk = ss[u][i] * fk[u];
+        oq[i] = pack_f16x2(q0 * cq - q1 * sq, q0 * sq + q1 * cq);
+        ok[i] = pack_f16x2(k0 * ck - k1 * sk, k0 * sk + k1 * ck);
+      }
+      uint16_t* slot = ring + size_t(b % kRing) * 2 * kSlotElems + size_t(r_lo + pr + 8 * u) * kDK + 8 * pq;
+      *reinterpret_cast<u32x4*>(slot) = oq;
+      *reinterpret_cast<u32x4*>(slot + kSlotElems) = ok;
+    }
+  };
+
+  // ---- publication and waits --------------------------------------------------
   const uint32_t nW = 4u * uint32_t(nS);
-  // Publishes this wave's stores: block `ready_block` of the ring and/or the statistics
-  // of block `stat_block` (-1 = none).
-  auto release = [&](int ready_block, int stat_block) {
-    store_fence_release(agent);
-    if (l == 0) {
-      if (ready_block >= 0)
-        __hip_atomic_fetch_add(cnt + kReady + ready_block % kRing, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (stat_block >= 0)
-        __hip_atomic_fetch_add(cnt + kStat + stat_block % kStatRing, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  };
   // Issues a read of a count (lane 0); `settle` later waits until it reaches `target`.
+  // Issues a read of a count (every lane reads the same word, so the load is
+  // unconditional); `settle` later waits until it reaches `target`.
   auto poll = [&](int word) -> uint32_t {
-    uint32_t v = 0u;
-    if (l == 0) v = __hip_atomic_load(cnt + word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return v;
+    return __hip_atomic_load(cnt + word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   auto settle = [&](uint32_t v, int word, uint32_t target) {
     v = __builtin_amdgcn_readfirstlane(v);
@@ -399,283 +381,294 @@ chunkwise_fused(Params P) {
     if (agent) __atomic_thread_fence(__ATOMIC_ACQUIRE);
     __asm__ volatile("" ::: "memory");
   };
-  auto ready_target = [&](int jb) { return nW * uint32_t(jb / kRing + 1); };
-  auto stat_target = [&](int jb) { return nW * uint32_t(jb / kStatRing + 1); };
-
-  // ---- per-block operand loads ----------------------------------------------------
-  auto load_v = [&](int jb, u32x2* rv) {   // V rows s0..s0+3, columns d0..d0+3 (bf16)
-    const int s0 = 4 * (tid >> 4), d0 = 4 * (tid & 15);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rv[i] = ld_b64(r_v, static_cast<uint32_t>(((jb * kT + s0 + i) * DV + d0) * 2));
-  };
-  auto load_gate = [&](int jb, u32x4* gt) {
-    const uint32_t off = static_cast<uint32_t>(((jb * kT + t_fin) * DV + c_fin) * 2);
-    if (has_gate && use_gn) {
-      gt[0] = ld_b128(r_g, off);
-      gt[1] = ld_b128(r_g, off + 16);
-    } else {
-      gt[0] = gt[1] = u32x4{0u, 0u, 0u, 0u};
+  // Publishes this wave's completed stores: ring block `rb` and/or statistics of
+  // block `sb` (-1 = none).
+  auto release = [&](int rb, int sb, bool tail4) {
+    store_fence_release(agent, tail4);
+    if (l == 0) {
+      if (rb >= 0)
+        __hip_atomic_fetch_add(cnt + kReady + rb % kRing, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (sb >= 0)
+        __hip_atomic_fetch_add(cnt + kStat + sb % kStatRing, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
-  // The next block's Qh / Kh fragments of this wave are copied from the ring straight
-  // into LDS (buffer loads with the lds modifier, sc0), one iteration ahead; each lane
-  // later reads back the 16 bytes it loaded. Fragment f: Qh (m, c) -> 2m + c,
-  // Kh (i, c) -> 8 + 2i + c.
-  auto stage_qk = [&](int jb) {
-    const uint32_t slot_off = ring_off + static_cast<uint32_t>((jb % kRing) * 3 * kSlotElems * sizeof(uint16_t));
-    const uint32_t kh_off = slot_off + static_cast<uint32_t>(kSlotElems * sizeof(uint16_t));
+  auto ready_target = [&](int b) { return nW * uint32_t(b / kRing + 1); };
+  auto stat_target = [&](int b) { return nW * uint32_t(b / kStatRing + 1); };
+
+  // ---- consumer operands ---------------------------------------------------------
+  // The fragments of block b are copied from the ring straight into this wave's LDS
+  // region (buffer loads with the lds modifier, sc0): fragment f of lane l lands at
+  // fr[w][f][l], Qt (m, c) -> f = 2m + c, Kt (i, c) -> f = 8 + 2i + c.
+  auto stage_frags = [&](int b) {
+    const uint32_t so = ring_off + static_cast<uint32_t>((b % kRing) * 2 * kSlotElems * sizeof(uint16_t));
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < 2; ++c) {
+        const uint32_t o = static_cast<uint32_t>(((16 * m + l16) * kDK + 64 * w + 32 * c + 8 * g) * 2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            wsr, (__attribute__((address_space(3))) void*)(&sm.qk[w][2 * m + c][0]), 16,
-            slot_off + static_cast<uint32_t>(((16 * m + l16) * kDK + 64 * w + 32 * c + 8 * g) * 2), 0, 0, 1);
-    // K rows for tile i: A-row l16 <-> s = 32e + 8(l16>>2) + 4(i&1) + (l16&3)
+            wsr, (__attribute__((address_space(3))) void*)(&sm.fr[w][2 * m + c][0]), 16, so + o, 0, 0, 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wsr, (__attribute__((address_space(3))) void*)(&sm.fr[w][8 + 2 * m + c][0]), 16,
+            so + static_cast<uint32_t>(kSlotElems * 2) + o, 0, 0, 1);
+      }
+  };
+  auto read_frags = [&](Frags& f) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        f.q[m][c] = sm.fr[w][2 * m + c][l];
+        f.k[m][c] = sm.fr[w][8 + 2 * m + c][l];
+      }
+  };
+  // 0/1 selection matrices (B operand) for the MFMA transpose of Kt: column n of
+  // E_hh picks d_k row 8(n>>2) + 4hh + (n&3) of a 32-wide chunk.
+  f16x8 E[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+      E[hh][jj] = (g == (l16 >> 2) && jj == 4 * hh + (l16 & 3)) ? _Float16(1.0f) : _Float16(0.0f);
+
+  // V slice: thread loads rows s0..s0+3, columns d0..d0+3 (bf16) of the slice
+  const int64_t slice_bytes = (int64_t(N) * DV - sl * kSl) * 2;  // to the end of this head
+  const size_t slice0 = size_t(bh) * N * DV + sl * kSl;
+  const __amdgpu_buffer_rsrc_t r_v = range_rsrc(P.v + slice0, slice_bytes);
+  const __amdgpu_buffer_rsrc_t r_g = range_rsrc(has_gate ? P.gate + slice0 : P.v + slice0, slice_bytes);
+  const int osz = (OUT == RN_BF16) ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t r_o =
+      range_rsrc(static_cast<uint8_t*>(P.out) + slice0 * osz, slice_bytes / 2 * osz);
+  const int vs0 = 4 * (tid >> 4), vd0 = 4 * (tid & 15);
+  auto load_v = [&](int b, u32x2* rv) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      rv[i] = ld_b64(r_v, static_cast<uint32_t>(((b * kT + vs0 + i) * DV + vd0) * 2));
+  };
+  auto stage_v = [&](int buf, const u32x2* rv) {
+    float fv[4][4];   // [row i][column jj]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int s = 32 * (i >> 1) + 8 * (l16 >> 2) + 4 * (i & 1) + (l16 & 3);
+      fv[i][0] = __uint_as_float(rv[i][0] << 16);
+      fv[i][1] = __uint_as_float(rv[i][0] & 0xffff0000u);
+      fv[i][2] = __uint_as_float(rv[i][1] << 16);
+      fv[i][3] = __uint_as_float(rv[i][1] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      *reinterpret_cast<u32x2*>(&sm.vt[buf][vd0 + jj][vt_pos(vs0)]) =
+          u32x2{pack_f16x2(fv[0][jj], fv[1][jj]), pack_f16x2(fv[2][jj], fv[3][jj])};
+  };
+
+  // ---- epilogue mapping: thread (fa, fb) owns rows 4fa..4fa+3, columns 4fb..4fb+3 ----
+  const int fa = tid >> 4, fb = tid & 15;
+  float gw[4], gbias[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    const int col = h * DV + sl * kSl + 4 * fb + cc;
+    gw[cc] = a.gn_w ? a.gn_w[col] : 1.f;
+    gbias[cc] = a.gn_b ? a.gn_b[col] : 0.f;
+  }
+  auto load_gate = [&](int b, u32x2* gt) {   // (reads v when there is no gate: unused)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      gt[rr] = ld_b64(r_g, static_cast<uint32_t>(((b * kT + 4 * fa + rr) * DV + 4 * fb) * 2));
+  };
+  // Statistics (mean, M2) of rows 4fa..4fa+3 of block b from slice fb (lanes fb >= nS
+  // read slice fb mod 8 of the slot and ignore it).
+  auto load_stats = [&](int b, u32x4* sv) {
+    const uint32_t so = stats_off + static_cast<uint32_t>(
+        ((((b & (kStatRing - 1)) * 8 + (fb & 7)) * kT + 4 * fa) * 2) * sizeof(float));
+    sv[0] = ld_sc0_b128(wsr, so);
+    sv[1] = ld_sc0_b128(wsr, so + 16);
+  };
+  // Normalises (with the statistics of all slices of block b), gates and stores.
+  const float inv_dv = 1.0f / float(DV);
+  auto finalize = [&](int b, const float (*o)[4], const u32x2* gt, const u32x4* sv) {
+    float y[4][4];
+    if (use_gn) {
+      // lane fb < nS holds slice fb's (mean, M2) of rows 4fa..4fa+3
+      const bool mine = fb < nS;
+      float mu_s[4], m2_s[4];
+      mu_s[0] = mine ? __uint_as_float(sv[0][0]) : 0.f; m2_s[0] = mine ? __uint_as_float(sv[0][1]) : 0.f;
+      mu_s[1] = mine ? __uint_as_float(sv[0][2]) : 0.f; m2_s[1] = mine ? __uint_as_float(sv[0][3]) : 0.f;
+      mu_s[2] = mine ? __uint_as_float(sv[1][0]) : 0.f; m2_s[2] = mine ? __uint_as_float(sv[1][1]) : 0.f;
+      mu_s[3] = mine ? __uint_as_float(sv[1][2]) : 0.f; m2_s[3] = mine ? __uint_as_float(sv[1][3]) : 0.f;
+      // equal counts per slice: mean = average of the slice means,
+      // M2 = sum M2_s + 64 sum (mean_s - mean)^2 (Chan et al.)
+      const float inv_nS = 1.0f / float(nS);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float mu = row16_sum(mu_s[rr]) * inv_nS;
+        const float d = mu_s[rr] - mu;
+        const float m2 = row16_sum((fb < nS) ? fmaf(float(kSl) * d, d, m2_s[rr]) : 0.f);
+        const float rstd = __frsqrt_rn(fmaf(m2, inv_dv, a.eps));
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) y[rr][cc] = fmaf((o[rr][cc] - mu) * rstd, gw[cc], gbias[cc]);
+        if (has_gate) {
+          y[rr][0] *= swishf(__uint_as_float(gt[rr][0] << 16));
+          y[rr][1] *= swishf(__uint_as_float(gt[rr][0] & 0xffff0000u));
+          y[rr][2] *= swishf(__uint_as_float(gt[rr][1] << 16));
+          y[rr][3] *= swishf(__uint_as_float(gt[rr][1] & 0xffff0000u));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) y[rr][cc] = o[rr][cc];
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const uint32_t ooff = static_cast<uint32_t>(((b * kT + 4 * fa + rr) * DV + 4 * fb) * osz);
+      if constexpr (OUT == RN_BF16) {
+        const u32x2 pk = {pack_bf16x2(y[rr][0], y[rr][1]), pack_bf16x2(y[rr][2], y[rr][3])};
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, pk), r_o, ooff, 0, 0);
+      } else {
+        st_b128(r_o, ooff, __builtin_bit_cast(u32x4, f32x4{y[rr][0], y[rr][1], y[rr][2], y[rr][3]}));
+      }
+    }
+  };
+
+  // ---- state: Sc_w tiles [ta][tb], ta = d_k tile (permuted rows), tb = d_v tile ----
+  // accumulator row 4g+r of tile ta = 2c+hh holds d_k = 64w + 32c + 8g + 4hh + r
+  const float g32 = exp2f(lg * 32.f);
+  f32x4 Sacc[4][4];
+#pragma unroll
+  for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int dk = 64 * w + 32 * (ta >> 1) + 8 * g + 4 * (ta & 1) + r;
+        const int dv = sl * kSl + 16 * tb + l16;
+        Sacc[ta][tb][r] = P.s_in ? g32 * P.s_in[(size_t(bh) * kDK + dk) * DV + dv] : 0.f;
+      }
+
+  // ---- one block ---------------------------------------------------------------------
+  u32x2 rv[4];                      // V rows of the next block to stage
+  float o_m1[4][4], o_m2[4][4];     // summed outputs of blocks j-1, j-2
+  u32x2 g_m1[4], g_m2[4];           // their gate rows
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    g_m1[rr] = g_m2[rr] = u32x2{0u, 0u};
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) o_m1[rr][cc] = o_m2[rr][cc] = 0.f;
+  }
+
+  // Counts polled during the previous step (their loads drained by its release):
+  // block j+1 whole, and the statistics of block j-2.
+  uint32_t poll_r = 0u, poll_s = 0u;
+  // Memory traffic of a step is issued in the order it is needed, with no load or
+  // store under a data-dependent condition, so that each wait covers only what it
+  // needs (loads past the end of the sequence read zeros; surplus productions past
+  // the last block write zeros into slots no reader needs any more).
+  auto step = [&](int j) {
+    const int Lb = min(kT, N - j * kT);
+    const int buf = j & 1;
+    // (0) this block's fragments (copied during the previous step, whose release
+    // waited for every copy of this wave)
+    Frags cur;
+    read_frags(cur);
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // (1) operands of block j+1 (every slice published them at its step j-2) into the
+    // LDS region just read; statistics of block j-2 (published at step j-2)
+    if (j + 1 < nb) settle(poll_r, kReady + (j + 1) % kRing, ready_target(j + 1));
+    stage_frags(j + 1);
+    if (use_gn && j >= kLag) settle(poll_s, kStat + (j - kLag) % kStatRing, stat_target(j - kLag));
+    u32x4 sv[2];
+    load_stats(j - kLag, sv);
+    // (2) V of block j -> LDS (transposed); prefetch V of block j+1
+    stage_v(buf, rv);
+    load_v(j + 1, rv);
+    // (3) rotate this workgroup's rows of block j+3 into the ring; raw rows of j+4
+    const bool produced = j + kAhead < nb;
+    produce(j + kAhead);
+    load_raw(j + kAhead + 1);
+    u32x2 g_cur[4];
+    load_gate(j, g_cur);
+    __syncthreads();   // V^T of block j visible
+
+    // (4) cross term acc = Qt_w Sc_w (B operand: the state in half)
+    f32x4 acc[4][4];
+    {
+      f16x8 sf[2][4];
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            wsr, (__attribute__((address_space(3))) void*)(&sm.qk[w][8 + 2 * i + c][0]), 16,
-            kh_off + static_cast<uint32_t>((s * kDK + 64 * w + 32 * c + 8 * g) * 2), 0, 0, 1);
-    }
-  };
-  auto read_qk = [&](f16x8 (*qf)[2], f16x8 (*kf)[2]) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) qf[m][c] = as_f16x8(sm.qk[w][2 * m + c][l]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) kf[i][c] = as_f16x8(sm.qk[w][8 + 2 * i + c][l]);
-  };
-
-  // GroupNorm + gate + store of this lane's row of block `jb` (values `o`), with the
-  // slices' statistics `st` and the gate row `gt` loaded earlier.
-  auto finalize = [&](int jb, const float* o, const u32x2* st, const u32x4* gt) {
-    float y[16];
-    if (use_gn) {
-      // combine the slices' (mean, M2): equal counts, so the mean is the average of the
-      // slice means and M2 = sum M2_j + 64 sum (mean_j - mean)^2 (Chan et al.)
-      float mu = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < nS) mu += __uint_as_float(st[j][0]);
-      mu *= inv_nS;
-      float m2 = 0.f, dd = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < nS) {
-          const float d = __uint_as_float(st[j][0]) - mu;
-          m2 += __uint_as_float(st[j][1]);
-          dd = fmaf(d, d, dd);
+        for (int tb = 0; tb < 4; ++tb) {
+          u32x4 u;
+          u[0] = pack_f16x2(Sacc[2 * c][tb][0], Sacc[2 * c][tb][1]);
+          u[1] = pack_f16x2(Sacc[2 * c][tb][2], Sacc[2 * c][tb][3]);
+          u[2] = pack_f16x2(Sacc[2 * c + 1][tb][0], Sacc[2 * c + 1][tb][1]);
+          u[3] = pack_f16x2(Sacc[2 * c + 1][tb][2], Sacc[2 * c + 1][tb][3]);
+          sf[c][tb] = as_f16x8(u);
         }
-      m2 = fmaf(float(kSl), dd, m2);
-      const float rstd = 1.0f / sqrtf(m2 / float(DV) + a.eps);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) y[i] = (o[i] - mu) * rstd;
-      const int col = h * DV + sl * kSl + c_fin;
-      if (a.gn_w) {
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) y[i] *= a.gn_w[col + i];
-      }
-      if (a.gn_b) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) y[i] += a.gn_b[col + i];
-      }
-      if (has_gate) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          y[2 * i] *= swishf(__uint_as_float(gt[0][i] << 16));
-          y[2 * i + 1] *= swishf(__uint_as_float(gt[0][i] & 0xffff0000u));
-          y[8 + 2 * i] *= swishf(__uint_as_float(gt[1][i] << 16));
-          y[8 + 2 * i + 1] *= swishf(__uint_as_float(gt[1][i] & 0xffff0000u));
+        for (int tb = 0; tb < 4; ++tb) {
+          f32x4 z = mfma(as_f16x8(cur.q[m][0]), sf[0][tb], f32x4{0.f, 0.f, 0.f, 0.f});
+          acc[m][tb] = mfma(as_f16x8(cur.q[m][1]), sf[1][tb], z);
         }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) y[i] = o[i];
     }
-    const uint32_t ooff = static_cast<uint32_t>(((jb * kT + t_fin) * DV + c_fin) * osz);
-    if constexpr (OUT == RN_BF16) {
-      u32x4 p0, p1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p0[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
-        p1[i] = pack_bf16x2(y[8 + 2 * i], y[8 + 2 * i + 1]);
-      }
-      st_b128(r_o, ooff, p0);
-      st_b128(r_o, ooff + 16, p1);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        st_b128(r_o, ooff + 16 * i, __builtin_bit_cast(u32x4, f32x4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]}));
-    }
-  };
-
-  // ---- prologue: publish blocks 0 and 1, prefetch for iteration 0 -----------------
-  uint32_t xq_a[8];               // producer rows of the block produced next
-  load8(0, r_lo, xq_a);
-  produce(0, xq_a);
-  if (P.nb > 1) {
-    load8(1, r_lo, xq_a);
-    produce(1, xq_a);
-  }
-  store_fence_release(agent);
-  if (l == 0) {
-    __hip_atomic_fetch_add(cnt + kReady + 0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (P.nb > 1) __hip_atomic_fetch_add(cnt + kReady + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  load8(2, r_lo, xq_a);
-  u32x2 rv_a[4], rv_b[4];         // V rows of blocks jb and jb+1
-  load_v(0, rv_a);
-  load_v(1, rv_b);
-  u32x4 gt_a[2], gt_b[2];         // gate rows of the block normalised next
-  gt_a[0] = gt_a[1] = u32x4{0u, 0u, 0u, 0u};
-  settle(poll(kReady + 0), kReady + 0, ready_target(0));
-  stage_qk(0);
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  float o_prev[16];
-  uint32_t ps = 0u;               // pre-read count of the previous block's statistics
-
-  for (int jb = 0; jb < P.nb; ++jb) {
-    const int Lb = min(kT, N - jb * kT);
-    const bool produced = jb + 2 < P.nb;
-    // readiness of the next block, read now and checked at the end of the iteration
-    const uint32_t pr = (jb + 1 < P.nb) ? poll(kReady + (jb + 1) % kRing) : 0u;
-
-    // (a) stage the V slice of this block, transposed, in LDS (rows >= Lb are zero)
-    {
-      const int s0 = 4 * (tid >> 4), d0 = 4 * (tid & 15);
-      float fv[4][4];   // [row i][column j] as float32
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fv[i][0] = __uint_as_float(rv_a[i][0] << 16);
-        fv[i][1] = __uint_as_float(rv_a[i][0] & 0xffff0000u);
-        fv[i][2] = __uint_as_float(rv_a[i][1] << 16);
-        fv[i][3] = __uint_as_float(rv_a[i][1] & 0xffff0000u);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 o;
-        o[0] = pack_f16x2(fv[0][j], fv[1][j]);
-        o[1] = pack_f16x2(fv[2][j], fv[3][j]);
-        *reinterpret_cast<u32x2*>(&sm.vt[d0 + j][s0]) = o;
-      }
-    }
-    __syncthreads();   // (b) V visible; the previous block's LDS reads are done
-
-    // this block's Qh / Kh fragments (staged during the previous iteration), then the
-    // next block's into the same LDS region once the reads have returned
-    f16x8 qf[4][2], kf[4][2];
-    read_qk(qf, kf);
-    if (jb + 1 < P.nb) {
-      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      settle(pr, kReady + (jb + 1) % kRing, ready_target(jb + 1));
-      stage_qk(jb + 1);
-    }
-
-    // (c) statistics of the previous block, for the normalisation at the end
-    u32x2 st[8];
-    if (use_gn && jb > 0) {
-      settle(ps, kStat + (jb - 1) % kStatRing, stat_target(jb - 1));
-      const uint32_t so = stats_off + static_cast<uint32_t>((((jb - 1) % kStatRing) * 8 * kT + t_fin) * 2 * sizeof(float));
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        st[j] = (j < nS) ? ld_sc0_b64(wsr, so + static_cast<uint32_t>(j * kT * 2 * sizeof(float))) : u32x2{0u, 0u};
-    }
-
-    // transposed, zeta-weighted K of this quarter for the state carry (A operand),
-    // loaded early: it is used last
-    f16x8 ktf[4][2];
-    {
-      const uint32_t kt_off = ring_off + static_cast<uint32_t>(((jb % kRing) * 3 + 2) * kSlotElems * sizeof(uint16_t));
-#pragma unroll
-      for (int ta = 0; ta < 4; ++ta) {
-        const int dk = 64 * w + 32 * (ta >> 1) + 8 * (l16 >> 2) + 4 * (ta & 1) + (l16 & 3);
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          ktf[ta][e] = as_f16x8(ld_sc0_b128(wsr, kt_off + static_cast<uint32_t>((dk * kT + 32 * e + 8 * g) * 2)));
-      }
-    }
-
-    // (d) rotate this workgroup's rows of block jb + 2 into the ring
-    if (produced) produce(jb + 2, xq_a);
-
-    // (5) scores first (they need Qh unscaled), then the cross term
-    // scores: P^T tiles (s-tile i, t-tile m), e = i/2 <= m/2
+    __builtin_amdgcn_sched_barrier(0);
+    // (5) scores P^T tiles (i, m), i <= m, partial over this wave's quarter of d_k:
+    // D row s = 16i + 4g + r, column t = 16m + l16
     f16x8 pf[4][2];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 4; ++m) {
+      f32x4 pt[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pt[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (i > m) continue;
+        f32x4 z = mfma(as_f16x8(cur.k[i][0]), as_f16x8(cur.q[m][0]), pt[i]);
+        z = mfma(as_f16x8(cur.k[i][1]), as_f16x8(cur.q[m][1]), z);
+        if (i == m) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) z[r] = (4 * g + r <= l16) ? z[r] : 0.f;
+        }
+        pt[i] = z;
+      }
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        if (e > (m >> 1)) continue;
-        f32x4 pt[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int i = 2 * e + hh;
-          f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          z = mfma(kf[i][0], qf[m][0], z);
-          z = mfma(kf[i][1], qf[m][1], z);
-          // element r: s = 32e + 8g + 4hh + r, t = 16m + l16
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int d = (l16 - 8 * g - 4 * hh - r) + 16 * (m - 2 * e);
-            const float f = factored ? decF[hh][r] * G16[m - 2 * e] : alpha * exp2f(lg * float(d));
-            z[r] = (d >= 0) ? z[r] * f : 0.f;
-          }
-          pt[hh] = z;
-        }
         u32x4 u;
-        u[0] = pack_f16x2(pt[0][0], pt[0][1]);
-        u[1] = pack_f16x2(pt[0][2], pt[0][3]);
-        u[2] = pack_f16x2(pt[1][0], pt[1][1]);
-        u[3] = pack_f16x2(pt[1][2], pt[1][3]);
+        u[0] = pack_f16x2(pt[2 * e][0], pt[2 * e][1]);
+        u[1] = pack_f16x2(pt[2 * e][2], pt[2 * e][3]);
+        u[2] = pack_f16x2(pt[2 * e + 1][0], pt[2 * e + 1][1]);
+        u[3] = pack_f16x2(pt[2 * e + 1][2], pt[2 * e + 1][3]);
         pf[m][e] = as_f16x8(u);
       }
-
-    f16x8 sf[2][4];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // (6) Kt^T of this quarter as the carry's A operand (row d_k, k = keys in vt_pos
+    // order): tile ta = 2c + hh from Kt rows 16i.. times E_hh
+    f16x8 ktf[4][2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int ta = 0; ta < 4; ++ta) {
+      f32x4 T[4];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
+      for (int i = 0; i < 4; ++i)
+        T[i] = mfma(as_f16x8(cur.k[i][ta >> 1]), E[ta & 1], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
         u32x4 u;
-        u[0] = pack_f16x2(Sacc[2 * c][tb][0], Sacc[2 * c][tb][1]);
-        u[1] = pack_f16x2(Sacc[2 * c][tb][2], Sacc[2 * c][tb][3]);
-        u[2] = pack_f16x2(Sacc[2 * c + 1][tb][0], Sacc[2 * c + 1][tb][1]);
-        u[3] = pack_f16x2(Sacc[2 * c + 1][tb][2], Sacc[2 * c + 1][tb][3]);
-        sf[c][tb] = as_f16x8(u);
+        u[0] = pack_f16x2(T[2 * e][0], T[2 * e][1]);
+        u[1] = pack_f16x2(T[2 * e][2], T[2 * e][3]);
+        u[2] = pack_f16x2(T[2 * e + 1][0], T[2 * e + 1][1]);
+        u[3] = pack_f16x2(T[2 * e + 1][2], T[2 * e + 1][3]);
+        ktf[ta][e] = as_f16x8(u);
       }
-    // cross term: acc[m][b] = (alpha xi ⊙ Qh)[16m.., dk quarter] · S_w; the row factor
-    // alpha * xi_t is applied to the Qh fragments (after the scores used them)
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) qf[m][c] = qf[m][c] * xs[m];
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        z = mfma(qf[m][0], sf[0][tb], z);
-        z = mfma(qf[m][1], sf[1][tb], z);
-        acc[m][tb] = z;
-      }
-
-    // V fragments (B operand, k = s): vf[e][b]
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // (7) V fragments (B operand, k = keys in vt_pos order), intra term, carry
     f16x8 vf[2][4];
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
-        vf[e][tb] = as_f16x8(*reinterpret_cast<const u32x4*>(&sm.vt[16 * tb + l16][32 * e + 8 * g]));
-
-    // intra term
+        vf[e][tb] = as_f16x8(*reinterpret_cast<const u32x4*>(&sm.vt[buf][16 * tb + l16][32 * e + 8 * g]));
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -683,92 +676,125 @@ chunkwise_fused(Params P) {
         acc[m][tb] = mfma(pf[m][0], vf[0][tb], acc[m][tb]);
         if (m >= 2) acc[m][tb] = mfma(pf[m][1], vf[1][tb], acc[m][tb]);
       }
-
-    // sum the four waves' partial outputs through LDS
+    const float gL = exp2f(lg * float(Lb));
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        f32x4 z = mfma(ktf[ta][0], vf[0][tb], Sacc[ta][tb]);
+        z = mfma(ktf[ta][1], vf[1][tb], z);
+        Sacc[ta][tb] = z * gL;
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    // counts for the next step: block j+2 (published at step j-1) and statistics of
+    // block j-1 (published at the end of step j-1)
+    poll_r = poll(kReady + (j + 2) % kRing);
+    poll_s = poll(kStat + (j - 1 + kStatRing) % kStatRing);
+    // (8) partial outputs -> LDS: element (row 16m + 4g + r, column 16tb + l16)
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.red[w][16 * m + 4 * g + r][16 * tb + l16] = acc[m][tb][r];
+      for (int tb = 0; tb < 4; ++tb) {
+        const int col = 16 * tb + l16;
+        *reinterpret_cast<f32x4*>(&sm.red[w][col][4 * ((4 * m + g) ^ red_swz(col))]) = acc[m][tb];
+      }
     __syncthreads();
-    float o_cur[16];
+    float o_cur[4][4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o_cur[i] = 0.f;
+    for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww)
+      for (int cc = 0; cc < 4; ++cc) o_cur[rr][cc] = 0.f;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        f32x4 x = *reinterpret_cast<const f32x4*>(&sm.red[ww][t_fin][c_fin + 4 * i4]);
+    for (int cc = 0; cc < 4; ++cc) {
+      const int col = 4 * fb + cc;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o_cur[4 * i4 + r] += x[r];
-      }
-
-    // GroupNorm statistics of this slice: (mean, centred sum of squares) per row
-    if (use_gn) {
-      float sum = 0.f;
+      for (int ww = 0; ww < 4; ++ww) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.red[ww][col][4 * (fa ^ red_swz(col))]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sum += o_cur[i];
-      sum += __shfl_xor(sum, 1, 64);
-      sum += __shfl_xor(sum, 2, 64);
-      const float mu = sum * (1.0f / kSl);
-      float m2 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) { const float d = o_cur[i] - mu; m2 += d * d; }
-      m2 += __shfl_xor(m2, 1, 64);
-      m2 += __shfl_xor(m2, 2, 64);
-      if ((l & 3) == 0) {
-        float* sp = stats + ((jb % kStatRing) * 8 * kT + sl * kT + t_fin) * 2;
-        *reinterpret_cast<u32x2*>(sp) = u32x2{__float_as_uint(mu), __float_as_uint(m2)};
+        for (int rr = 0; rr < 4; ++rr) o_cur[rr][cc] += x[rr];
       }
     }
-
-    // state carry: S_w = gamma^Lb S_w + (zeta ⊙ Kh)^T V
-    {
-      const float gL = exp2f(lg * float(Lb));
+    // (9) this slice's statistics of block j: per row (mean, centred sum of squares)
+    if (use_gn) {
+      float st[8];
 #pragma unroll
-      for (int ta = 0; ta < 4; ++ta)
+      for (int rr = 0; rr < 4; ++rr) {
+        const float s = row16_sum((o_cur[rr][0] + o_cur[rr][1]) + (o_cur[rr][2] + o_cur[rr][3]));
+        const float mu = s * (1.0f / kSl);
+        float m2 = 0.f;
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          f32x4 z = Sacc[ta][tb] * gL;
-          z = mfma(ktf[ta][0], vf[0][tb], z);
-          z = mfma(ktf[ta][1], vf[1][tb], z);
-          Sacc[ta][tb] = z;
+        for (int cc = 0; cc < 4; ++cc) {
+          const float d = o_cur[rr][cc] - mu;
+          m2 = fmaf(d, d, m2);
         }
-    }
-
-    // (e) publish this wave's ring rows of block jb + 2 and statistics of block jb
-    release(produced ? jb + 2 : -1, use_gn ? jb : -1);
-    // (f) prefetch from HBM for later iterations
-    load8(jb + 3, r_lo, xq_a);
+        m2 = row16_sum(m2);
+        st[2 * rr] = mu;
+        st[2 * rr + 1] = m2;
+      }
+      {
+        float* sp = stats + (((j % kStatRing) * 8 + sl) * kT + 4 * fa) * 2;
+        *reinterpret_cast<f32x4*>(sp) = f32x4{st[0], st[1], st[2], st[3]};
+        *reinterpret_cast<f32x4*>(sp + 4) = f32x4{st[4], st[5], st[6], st[7]};
+      }
+      // the only memory operations between here and the release are the 4 output
+      // stores of the normalisation (release with vmcnt(4))
+      __asm__ volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      // (10) normalise block j-2
+      if (j >= kLag) finalize(j - kLag, o_m2, g_m2, sv);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rv_a[i] = rv_b[i];
-    load_v(jb + 2, rv_b);
-    load_gate(jb, gt_b);
-    // (h) normalise and store the previous block (or this one without GroupNorm)
-    if (use_gn) {
-      if (jb > 0) finalize(jb - 1, o_prev, st, gt_a);
+      for (int rr = 0; rr < 4; ++rr) {
+        g_m2[rr] = g_m1[rr];
+        g_m1[rr] = g_cur[rr];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o_prev[i] = o_cur[i];
-      gt_a[0] = gt_b[0];
-      gt_a[1] = gt_b[1];
-      ps = poll(kStat + jb % kStatRing);
+        for (int cc = 0; cc < 4; ++cc) {
+          o_m2[rr][cc] = o_m1[rr][cc];
+          o_m1[rr][cc] = o_cur[rr][cc];
+        }
+      }
     } else {
-      finalize(jb, o_cur, st, gt_a);
+      finalize(j, o_cur, g_cur, sv);
     }
+    // (11) publish this wave's ring rows of block j+3 and statistics of block j (the
+    // output stores just issued need not have completed)
+    __builtin_amdgcn_sched_barrier(0);
+    release(produced ? j + kAhead : -1, use_gn ? j : -1, !use_gn || j >= kLag);
+  };
+
+  // ---- prologue: blocks 0 .. kAhead-1 produced and published; block 0 loaded ---------
+  for (int b = 0; b < kAhead; ++b) {
+    load_raw(b);
+    produce(b);
   }
+  load_raw(kAhead);
+  load_v(0, rv);
+  store_fence_release(agent);
+  if (l == 0) {
+    for (int b = 0; b < kAhead && b < nb; ++b)
+      __hip_atomic_fetch_add(cnt + kReady + b % kRing, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  settle(poll(kReady + 0), kReady + 0, ready_target(0));
+  stage_frags(0);
+  poll_r = poll(kReady + 1);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  for (int j = 0; j < nb; ++j) step(j);
+
+  // ---- the last kLag blocks ---------------------------------------------------------
   if (use_gn) {
-    const int jl = P.nb - 1;
-    settle(ps, kStat + jl % kStatRing, stat_target(jl));
-    u32x2 st[8];
-    const uint32_t so = stats_off + static_cast<uint32_t>(((jl % kStatRing) * 8 * kT + t_fin) * 2 * sizeof(float));
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      st[j] = (j < nS) ? ld_sc0_b64(wsr, so + static_cast<uint32_t>(j * kT * 2 * sizeof(float))) : u32x2{0u, 0u};
-    finalize(jl, o_prev, st, gt_a);
+    u32x4 sv[2];
+    if (nb >= 2) {
+      settle(poll(kStat + (nb - 2) % kStatRing), kStat + (nb - 2) % kStatRing, stat_target(nb - 2));
+      load_stats(nb - 2, sv);
+      finalize(nb - 2, o_m2, g_m2, sv);
+    }
+    settle(poll(kStat + (nb - 1) % kStatRing), kStat + (nb - 1) % kStatRing, stat_target(nb - 1));
+    load_stats(nb - 1, sv);
+    finalize(nb - 1, o_m1, g_m1, sv);
   }
 
   if (P.s_out) {
+    const float gi32 = exp2f(-lg * 32.f);
 #pragma unroll
     for (int ta = 0; ta < 4; ++ta)
 #pragma unroll
@@ -777,13 +803,28 @@ chunkwise_fused(Params P) {
         for (int r = 0; r < 4; ++r) {
           const int dk = 64 * w + 32 * (ta >> 1) + 8 * g + 4 * (ta & 1) + r;
           const int dv = sl * kSl + 16 * tb + l16;
-          P.s_out[(size_t(bh) * kDK + dk) * DV + dv] = Sacc[ta][tb][r];
+          P.s_out[(size_t(bh) * kDK + dk) * DV + dv] = Sacc[ta][tb][r] * gi32;
         }
   }
 }
 
 __global__ void zero_words(uint32_t* p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+const void* kernel_for(int out_dt, int nS) {
+#define RN_CW_CASE(NS_)                                                                  \
+  case NS_:                                                                              \
+    return out_dt == RN_BF16 ? reinterpret_cast<const void*>(&chunkwise_fused<RN_BF16, NS_>) \
+                             : reinterpret_cast<const void*>(&chunkwise_fused<RN_F32, NS_>);
+  switch (nS) {
+    RN_CW_CASE(1)
+    RN_CW_CASE(2)
+    RN_CW_CASE(4)
+    RN_CW_CASE(8)
+  }
+#undef RN_CW_CASE
+  return nullptr;
 }
 
 int cu_count() {
@@ -807,9 +848,14 @@ int heads_per_group(int nS) {
 
 }  // namespace
 
+// The decay factors gamma^(+-32) folded into the half operands need gamma^32 >= 2^-6.
 bool chunkwise_mfma_supported(const CallArgs& a, int in_dt) {
-  return in_dt == RN_BF16 && a.dk == kDK &&
-         (a.dv == 64 || a.dv == 128 || a.dv == 256 || a.dv == 512);
+  if (in_dt != RN_BF16 || a.dk != kDK ||
+      !(a.dv == 64 || a.dv == 128 || a.dv == 256 || a.dv == 512))
+    return false;
+  for (int h = 0; h < a.H; ++h)
+    if (!(a.hp.log2g[h] * 32.0f >= -6.0f)) return false;
+  return true;
 }
 
 size_t chunkwise_mfma_ws_bytes(const CallArgs& a) {
@@ -853,12 +899,7 @@ hipError_t launch_chunkwise_mfma(const CallArgs& a, int out_dt, const void* q, c
     if (e != hipSuccess) return e;
     const int grid = 8 * nS * ((heads + 7) / 8);
     void* args[] = {&p};
-    if (out_dt == RN_BF16)
-      e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&chunkwise_fused<RN_BF16>),
-                                     dim3(grid), dim3(256), args, 0, st);
-    else
-      e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&chunkwise_fused<RN_F32>),
-                                     dim3(grid), dim3(256), args, 0, st);
+    e = hipLaunchCooperativeKernel(kernel_for(out_dt, nS), dim3(grid), dim3(256), args, 0, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

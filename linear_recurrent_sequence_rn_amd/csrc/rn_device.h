@@ -72,6 +72,21 @@ __device__ __forceinline__ void angle_cs(int64_t p, float theta, float* c, float
   sincosf(static_cast<float>(r), s, c);
 }
 
+// Same reduction, then the hardware sine/cosine (absolute error near 1e-6 on the
+// reduced range [-pi, pi]): for paths whose operands are rounded to half anyway.
+__device__ __forceinline__ void angle_cs_fast(int64_t p, float theta, float* c, float* s) {
+  const double kTwoPiHi = 6.283185307179586232;
+  const double kTwoPiLo = 2.4492935982947064e-16;
+  const double kInvTwoPi = 0.15915494309189535;
+  double a = static_cast<double>(p) * static_cast<double>(theta);
+  double k = rint(a * kInvTwoPi);
+  double r = fma(-k, kTwoPiHi, a);
+  r = fma(-k, kTwoPiLo, r);
+  const float rf = static_cast<float>(r);
+  *s = __sinf(rf);
+  *c = __cosf(rf);
+}
+
 // gamma^n for a non-negative (possibly fractional) exponent, exact 1 at n = 0 and for
 // gamma = 1 (log2g = 0).
 __device__ __forceinline__ float gpow(float log2g, float n) {
