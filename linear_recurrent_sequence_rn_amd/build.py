@@ -28,6 +28,9 @@ COMMON = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
     # packed fp32 instructions stay off in every HIP object
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in arch VGPRs: the kernels scale, convert and store most of them
+    # with VALU instructions, which would otherwise copy them out of AGPRs first
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
     f"-I{ROOT / 'include'}", f"-I{CSRC}",
 ]

@@ -547,13 +547,16 @@ chunkwise_fused(Params P) {
 
   // ---- one block ---------------------------------------------------------------------
   u32x2 rv[4];                      // V rows of the next block to stage
-  float o_m1[4][4], o_m2[4][4];     // summed outputs of blocks j-1, j-2
-  u32x2 g_m1[4], g_m2[4];           // their gate rows
+  // Summed outputs and gate rows waiting for their normalisation, kLag = 2 blocks
+  // later: even blocks in (o_e, g_e), odd blocks in (o_o, g_o). The loop runs two
+  // blocks per iteration so that each buffer keeps its registers.
+  float o_e[4][4], o_o[4][4];
+  u32x2 g_e[4], g_o[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
-    g_m1[rr] = g_m2[rr] = u32x2{0u, 0u};
+    g_e[rr] = g_o[rr] = u32x2{0u, 0u};
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) o_m1[rr][cc] = o_m2[rr][cc] = 0.f;
+    for (int cc = 0; cc < 4; ++cc) o_e[rr][cc] = o_o[rr][cc] = 0.f;
   }
 
   // Counts polled during the previous step (their loads drained by its release):
@@ -563,7 +566,7 @@ chunkwise_fused(Params P) {
   // store under a data-dependent condition, so that each wait covers only what it
   // needs (loads past the end of the sequence read zeros; surplus productions past
   // the last block write zeros into slots no reader needs any more).
-  auto step = [&](int j) {
+  auto step = [&](int j, float (*o_buf)[4], u32x2* g_buf) {
     const int Lb = min(kT, N - j * kT);
     const int buf = j & 1;
     // (0) this block's fragments (copied during the previous step, whose release
@@ -741,16 +744,12 @@ chunkwise_fused(Params P) {
       __asm__ volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       // (10) normalise block j-2
-      if (j >= kLag) finalize(j - kLag, o_m2, g_m2, sv);
+      if (j >= kLag) finalize(j - kLag, o_buf, g_buf, sv);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        g_m2[rr] = g_m1[rr];
-        g_m1[rr] = g_cur[rr];
+        g_buf[rr] = g_cur[rr];
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          o_m2[rr][cc] = o_m1[rr][cc];
-          o_m1[rr][cc] = o_cur[rr][cc];
-        }
+        for (int cc = 0; cc < 4; ++cc) o_buf[rr][cc] = o_cur[rr][cc];
       }
     } else {
       finalize(j, o_cur, g_cur, sv);
@@ -778,19 +777,24 @@ chunkwise_fused(Params P) {
   poll_r = poll(kReady + 1);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  for (int j = 0; j < nb; ++j) step(j);
+  int j = 0;
+  for (; j + 1 < nb; j += 2) {
+    step(j, o_e, g_e);
+    step(j + 1, o_o, g_o);
+  }
+  if (j < nb) step(j, o_e, g_e);
 
   // ---- the last kLag blocks ---------------------------------------------------------
   if (use_gn) {
     u32x4 sv[2];
-    if (nb >= 2) {
-      settle(poll(kStat + (nb - 2) % kStatRing), kStat + (nb - 2) % kStatRing, stat_target(nb - 2));
-      load_stats(nb - 2, sv);
-      finalize(nb - 2, o_m2, g_m2, sv);
+    for (int b = max(nb - kLag, 0); b < nb; ++b) {
+      settle(poll(kStat + b % kStatRing), kStat + b % kStatRing, stat_target(b));
+      load_stats(b, sv);
+      if (b & 1)
+        finalize(b, o_o, g_o, sv);
+      else
+        finalize(b, o_e, g_e, sv);
     }
-    settle(poll(kStat + (nb - 1) % kStatRing), kStat + (nb - 1) % kStatRing, stat_target(nb - 1));
-    load_stats(nb - 1, sv);
-    finalize(nb - 1, o_m1, g_m1, sv);
   }
 
   if (P.s_out) {
