@@ -123,38 +123,42 @@ struct CallArgs {
   AngleParams ap;
 };
 
-// Sum over a 256-thread block (4 waves). `red` is 4 floats of LDS; every thread
-// receives the total. Ends with the LDS slots free for reuse after a barrier.
-__device__ __forceinline__ float block_sum256(float x, float* red) {
+// Sum over a block of NT threads (NT/64 waves). `red` is NT/64 floats of LDS; every
+// thread receives the total. Ends with the LDS slots free for reuse after a barrier.
+template <int NT>
+__device__ __forceinline__ float block_sum(float x, float* red) {
   x = wave_sum(x);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[w] = x;
   __syncthreads();
-  float t = red[0] + red[1] + red[2] + red[3];
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) t += red[i];
   __syncthreads();
   return t;
 }
+__device__ __forceinline__ float block_sum256(float x, float* red) { return block_sum<256>(x, red); }
 
 // GroupNorm (+ swish gate) epilogue of one row of d_v values held in LDS `o`
-// (float32), computed by a 256-thread block and stored at out[row_off + c].
+// (float32), computed by a block of NT threads and stored at out[row_off + c].
 // Statistics: mean, then the biased variance of (o - mean), eps inside the root.
-template <int IN, int OUT>
-__device__ __forceinline__ void row_epilogue256(const float* o, int dv, const CallArgs& a,
-                                                int head, const void* gate, int64_t row_off,
-                                                void* out, float* red) {
+template <int IN, int OUT, int NT = 256>
+__device__ __forceinline__ void row_epilogue(const float* o, int dv, const CallArgs& a,
+                                             int head, const void* gate, int64_t row_off,
+                                             void* out, float* red) {
   const bool gn = a.flags & RN_EPI_GN;
   const bool gt = a.flags & RN_EPI_GATE;
   float mean = 0.f, rstd = 1.f;
   if (gn) {
     float s = 0.f;
-    for (int c = threadIdx.x; c < dv; c += 256) s += o[c];
-    mean = block_sum256(s, red) / dv;
+    for (int c = threadIdx.x; c < dv; c += NT) s += o[c];
+    mean = block_sum<NT>(s, red) / dv;
     float s2 = 0.f;
-    for (int c = threadIdx.x; c < dv; c += 256) { float d = o[c] - mean; s2 += d * d; }
-    float var = block_sum256(s2, red) / dv;
+    for (int c = threadIdx.x; c < dv; c += NT) { float d = o[c] - mean; s2 += d * d; }
+    float var = block_sum<NT>(s2, red) / dv;
     rstd = 1.0f / sqrtf(var + a.eps);
   }
-  for (int c = threadIdx.x; c < dv; c += 256) {
+  for (int c = threadIdx.x; c < dv; c += NT) {
     float y = o[c];
     if (gn) {
       y = (y - mean) * rstd;
@@ -164,6 +168,12 @@ __device__ __forceinline__ void row_epilogue256(const float* o, int dv, const Ca
     }
     Elem<OUT>::store(out, row_off + c, y);
   }
+}
+template <int IN, int OUT>
+__device__ __forceinline__ void row_epilogue256(const float* o, int dv, const CallArgs& a,
+                                                int head, const void* gate, int64_t row_off,
+                                                void* out, float* red) {
+  row_epilogue<IN, OUT, 256>(o, dv, a, head, gate, row_off, out, red);
 }
 
 }  // namespace rn

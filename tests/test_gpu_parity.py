@@ -163,6 +163,24 @@ def test_decode_full_batch_sampled():
         assert rel_inf(Sg[sl], s_ref) <= 1e-4
 
 
+@pytest.mark.parametrize("dk,dv", [(256, 256), (128, 128), (64, 256), (48, 512), (256, 384)])
+def test_decode_other_shapes(dk, dv):
+    """Decode at other head shapes: the pipelined kernel's d_v = 256 and 128 layouts
+    (G = 8 and 16 row groups), and shapes it does not take (d_k not a multiple of 8G,
+    d_v outside {128, 256, 512}), which run the one-batch kernel; 3 chained steps."""
+    w = W.Workload(**{**W.WORKLOADS["decode_6p7b"].__dict__, "B": 2, "H": 3, "d_k": dk, "d_v": dv})
+    S0 = W.initial_state(w)
+    S = dev(S0.clone())
+    Sref = S0
+    for i in range(3):
+        x = W.make_decode_step_inputs(w, i)
+        out = rn().rn_retention_recurrent_step(dev(x["q"]), dev(x["k"]), dev(x["v"]), w.gamma(),
+                                               w.theta(), S, 100 + i, out_dtype=torch.float32)
+        o_ref, Sref = O.recurrent_step(x["q"], x["k"], x["v"], w.gamma(), w.theta(), 100 + i, 1.0, Sref)
+        assert rel_inf(out.cpu()[:, :, 0], o_ref) <= 1e-4
+    assert rel_inf(S.cpu(), Sref) <= 1e-4
+
+
 def test_decode_gn_gate_bf16_out():
     w = W.Workload(**{**W.WORKLOADS["decode_6p7b"].__dict__, "B": 2})
     S0 = W.initial_state(w)
