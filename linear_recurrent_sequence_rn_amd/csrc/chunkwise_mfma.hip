@@ -3,11 +3,21 @@
 // "Chunkwise representation"; GroupNorm + swish gate of the multi-scale layer).
 //
 // Work split. A head's float32 state S (d_k x d_v) is cut into nS = d_v/64 column
-// slices; one 256-thread workgroup owns one slice (64 KB of state, kept in MFMA
-// accumulator registers for the whole sequence) and walks the sequence in blocks of
-// 64 tokens. Inside the workgroup the four waves split d_k into quarters: wave w
-// keeps the quarter's rows of the state and computes the quarter's partial products,
-// which are summed through LDS.
+// slices; one 512-thread workgroup owns one slice and walks the sequence in blocks of
+// 64 tokens. Its eight waves take two roles, one wave of each per SIMD, so that the
+// matrix work of one role runs while the other role's vector work issues:
+//   M waves (0-3): wave w keeps rows [64w, 64w+64) of the slice's state (64 KB in all,
+//     in MFMA accumulator registers for the whole sequence) and does every MFMA of a
+//     block over its quarter of d_k. Its partial outputs go to LDS. The M waves also do
+//     every wait on other workgroups, because their only memory traffic is the L2 ->
+//     LDS copies they issue themselves, so a wait there never drains an HBM prefetch.
+//   E waves (4-7): everything else. They rotate this slice's share of a future block
+//     into the shared ring, stage V^T for the next block, sum the four partial outputs
+//     of the previous block, publish its GroupNorm statistics, normalise + gate + store
+//     the block computed four iterations earlier, and keep the HBM streams (q, k, v,
+//     gate) two iterations ahead in registers.
+// Two LDS-only barriers per block separate the phases (B1 at the top of an iteration,
+// B2 once the E waves have read the partial outputs).
 //
 // Decay folded into the operands. With j the row of a token inside its block, the
 // rotated rows are stored in half as
@@ -19,12 +29,14 @@
 // which is the chunkwise recurrence with the state update weighted per row by
 // gamma^(L-1-s), read off by unrolling the recurrent update over the block. The
 // factors gamma^(+-32) bound the operand range; the path requires gamma^32 >= 2^-6.
-// Per block and wave (16x16x32 f16 MFMA, fp32 accumulate):
+// Per block and M wave (16x16x32 f16 MFMA, fp32 accumulate):
 //   scores  P_w^T = Kt_w Qt_w^T                   (partial over the quarter, 20 MFMA)
 //   Kt_w^T  by MFMA against 0/1 selection matrices  (16 MFMA, exact)
-//   cross   acc  = Qt_w Sc_w                      (32 MFMA)
-//   intra   acc += P_w V                          (24 MFMA)
-//   carry   Sc_w = gamma^L (Sc_w + Kt_w^T V)      (32 MFMA)
+//   then per 16-column tile of the slice:
+//     cross  acc  = Qt_w Sc_w                     (8 MFMA)
+//     intra  acc += P_w V                         (6 MFMA)
+//     carry  Sc_w = gamma^L (Sc_w + Kt_w^T V)     (8 MFMA)
+// (a column tile's cross term reads its state columns before the carry updates them).
 // The output is the sum of the four waves' acc; GroupNorm (+ gate) follows.
 //
 // Operand precision. q, k, v arrive in bf16; the rotation runs in float32 and every
@@ -34,23 +46,29 @@
 //
 // Sharing between the slices of a head. Every slice needs the whole rotated block.
 // Each of the nS workgroups rotates 64/nS rows of the block three ahead of the one
-// it computes and writes Qt, Kt to a ring of 8 block slots in the workspace; per-slot
-// counters, incremented once per wave after its stores have completed, say when a
-// block is whole. GroupNorm statistics (per-row mean and centred sum of squares of
-// each slice) go through an 8-slot ring the same way; a block is normalised and
-// stored two blocks after it is computed, once every slice has published its
-// statistics. All slices of a head are placed on one XCD (blockIdx mod 8), so the
-// exchange stays in that XCD's L2: shared data is read with L1-bypassing (sc0)
-// buffer loads. If the slices turn out to span XCDs, the kernel uses agent-scope
-// release/acquire fences. Every wait has a time limit that ends the kernel normally
-// and raises an error word in the workspace.
+// its M waves compute and writes Qt, Kt to a ring of 8 block slots in the workspace;
+// per-slot counters, incremented once per E wave after its stores have completed, say
+// when a block is whole. GroupNorm statistics (per-row mean and centred sum of squares
+// of each slice) go through an 8-slot ring the same way. All slices of a head are
+// placed on one XCD (blockIdx mod 8), so the exchange stays in that XCD's L2: shared
+// data is read with L1-bypassing (sc0) buffer loads. If the slices turn out to span
+// XCDs, the kernel uses agent-scope release/acquire fences. Every wait has a time
+// limit that ends the kernel normally and raises an error word in the workspace.
 //
-// Ring safety. At step j a workgroup writes block j+3 (slot (j+3) mod 8), waits for
-// block j+1 to be whole and loads it, computes block j, and reads the statistics of
-// block j-2 before publishing those of block j. Waiting for block j+1 means every
-// slice has finished step j-2, so a workgroup that writes slot (j+3) mod 8 at step j
-// knows every reader of the block held there before (j-5, read at step j-6) is done;
-// and the statistics slot written at step j (block j) was last read for block j-8.
+// Schedule of iteration i (both roles run iterations 0 .. nb+3, rounded up to a
+// multiple of 4; iterations past the end do only what is left of the last blocks):
+//   M: wait for its copies; read the fragments of block i; wait for block i+1 to be
+//      whole and copy it into its LDS region; wait for the statistics of block i-3 and
+//      copy them to LDS | B2 | poll the counts for the next iteration; compute block i.
+//   E: read the partial outputs of block i-1 | B2 | publish its statistics; rotate
+//      block i+3 into the ring; normalise, gate and store block i-4; stage V^T of
+//      block i+1; issue the loads of blocks i+5 (q, k), i+3 (v) and i-2 (gate); raise
+//      the counts once the ring and statistics stores have completed.
+// Ring safety. At iteration i an E wave writes slot (i+3) mod 8 after its M waves saw
+// block i+1 whole, which means every slice has finished iteration i-2, so every copy
+// of the block previously held in that slot (block i-5, copied at iteration i-6) is
+// done. The statistics slot written at iteration i (block i-1) last held block i-9,
+// copied at iteration i-6.
 #include "rn_device.h"
 #include "rn_kernels.h"
 
@@ -63,13 +81,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+constexpr int kThreads = 512;   // 4 M waves + 4 E waves
 constexpr int kT = 64;          // tokens per block
 constexpr int kDK = 256;        // d_k of this kernel
 constexpr int kSl = 64;         // d_v columns per workgroup
 constexpr int kRing = 8;        // ring slots (blocks of Qt/Kt)
 constexpr int kStatRing = 8;    // statistics slots
 constexpr int kAhead = 3;       // blocks produced ahead of the block computed
-constexpr int kLag = 2;         // blocks between computing a block and normalising it
+constexpr int kLag = 4;         // iterations between computing a block and storing it
 constexpr int kReanchor = 16;   // blocks between exact (float64-reduced) angle anchors
 constexpr int kVtLd = 72;       // LDS row stride (half) of the transposed V slice
 constexpr uint32_t kCntWords = 64;             // counter words per head
@@ -77,6 +96,9 @@ constexpr size_t kStatsPerHead = size_t(kStatRing) * 8 * kT * 2 * sizeof(float);
 constexpr size_t kSlotElems = size_t(kT) * kDK;                                  // 16384 half
 constexpr size_t kRingPerHead = size_t(kRing) * 2 * kSlotElems * sizeof(uint16_t);  // 512 KB
 constexpr uint64_t kWaitTicks = 100000000ull;  // 1 s of the 100 MHz wall clock
+// Buffer offset past the end of every range used for stores: the store is dropped
+// (it still counts as an issued memory operation, which keeps the waits' counts fixed).
+constexpr uint32_t kSink = 0x80000000u;
 
 // Counter words per head. Publication counts are kept per ring slot and in waves:
 // slot s counts the waves that published blocks s, s+kRing, s+2kRing, ...; block j is
@@ -136,9 +158,10 @@ __device__ __forceinline__ constexpr int vt_pos(int s) {
 __device__ __forceinline__ int red_swz(int c) { return ((c >> 2) & 15) ^ ((c & 3) << 2); }
 
 struct alignas(16) Shared {
-  float red[4][kSl][kT];             // partial outputs of the four waves: [wave][col][row]
+  float red[4][kSl][kT];             // partial outputs of the M waves: [wave][col][row]
+  u32x4 fr[4][16][64];               // the current block's Qt/Kt fragments, per M wave and lane
   uint16_t vt[2][kSl][kVtLd];        // V slice of two blocks, transposed, vt_pos order
-  u32x4 fr[4][16][64];               // next block's Qt/Kt fragments, per wave and lane
+  float stat[2][8][kT][2];           // statistics of the block to normalise: [slice][row][mean, M2]
   uint32_t mode;                     // 1 = agent-scope fences
 };
 
@@ -147,13 +170,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
 }
 // Buffer resource over [base, base + bytes): loads past the end return 0 and stores
-// past the end are dropped, which is how ragged tails and rows beyond N are handled.
+// past the end are dropped, which is how ragged tails, rows beyond N and the blocks
+// before the first and after the last one are handled.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
                                            static_cast<int>(bytes > 0 ? bytes : 0), 0x00020000);
-}
-__device__ __forceinline__ uint32_t ld_b32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 __device__ __forceinline__ u32x2 ld_b64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
@@ -164,30 +185,40 @@ __device__ __forceinline__ u32x4 ld_b128(__amdgpu_buffer_rsrc_t r, uint32_t off)
 __device__ __forceinline__ void st_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, 0);
 }
-__device__ __forceinline__ u32x4 ld_sc0_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 1));
+__device__ __forceinline__ void st_b64(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v), r, off, 0, 0);
 }
-__device__ __forceinline__ u32x2 ld_sc0_b64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 1));
+// 16 bytes per lane from the workspace into LDS at dst + 16 * lane (sc0: bypass L1).
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 1);
 }
 
-// Makes this wave's earlier stores complete before a release count is raised. Vector
-// memory operations of a wave complete in issue order, so when the last `tail4 ? 4 : 0`
-// operations are ones that need not be waited for, vmcnt(4) covers everything before.
-__device__ __forceinline__ void store_fence_release(bool agent, bool tail4 = false) {
-  if (agent) {
-    __threadfence();
-  } else if (tail4) {
-    __asm__ volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  } else {
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8). Issued through the builtin rather than inline assembly so that the
+// compiler's own wait insertion sees them and does not wait again for what they cover.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | (((vm >> 4) & 3) << 14);
+}
+template <int VM>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(VM >= 0 && VM <= 63, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, 15));
+  __asm__ volatile("" ::: "memory");
+}
+
+// Barrier over the workgroup for LDS traffic only: this wave's LDS operations are
+// complete, global memory operations may still be in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
 }
 
 // Thread 0 waits until cnt[word] >= target, then the block synchronises. A wait that
 // exceeds kWaitTicks raises cnt[kError]; once raised, every later wait of every
 // workgroup of the head returns at once, so a broken exchange costs one time limit.
-__device__ __forceinline__ void wait_count(uint32_t* cnt, int word, uint32_t target, bool agent) {
+__device__ __forceinline__ void wait_count(uint32_t* cnt, int word, uint32_t target) {
   if (threadIdx.x == 0) {
     uint32_t* p = cnt + word;
     if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
@@ -203,10 +234,8 @@ __device__ __forceinline__ void wait_count(uint32_t* cnt, int word, uint32_t tar
     }
   }
   __syncthreads();
-  if (agent) __atomic_thread_fence(__ATOMIC_ACQUIRE);
-  __asm__ volatile("" ::: "memory");
+  __atomic_thread_fence(__ATOMIC_ACQUIRE);
 }
-
 
 struct Params {
   CallArgs a;
@@ -224,15 +253,10 @@ struct Params {
   uint8_t* ws;
 };
 
-// One lane's MFMA operand fragments of a block: Qt rows 16m + l16 and Kt rows
-// 16i + l16, d_k = 64w + 32c + 8g .. +8 (w = wave, g = lane group), in half.
-struct Frags {
-  u32x4 q[4][2];
-  u32x4 k[4][2];
-};
+template <int C> struct Ic { static constexpr int value = C; };
 
 template <int OUT, int NS>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 chunkwise_fused(Params P) {
   const CallArgs& a = P.a;
   const int xcd = blockIdx.x & 7, L8 = blockIdx.x >> 3;
@@ -241,20 +265,21 @@ chunkwise_fused(Params P) {
   const int sl = L8 % NS;                // d_v slice
   constexpr int nS = NS;
   const int nb = P.nb;
+  // iterations: the E waves store block nb-1 at iteration nb-1+kLag; the count is
+  // rounded up to a multiple of 4 (the E waves' loop body holds four iterations)
+  const int n_iter = (nb + kLag + 3) & ~3;
   const int bh = P.head0 + hg;
   const int h = bh % a.H;
   const int N = a.N, DV = a.dv;
   const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, g = l >> 4;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
 
   __shared__ Shared sm;
 
   // workspace views
   uint32_t* cnt = reinterpret_cast<uint32_t*>(P.ws) + size_t(hg) * kCntWords;
   uint8_t* stats_base = P.ws + size_t(P.heads) * kCntWords * 4;
-  float* stats = reinterpret_cast<float*>(stats_base + size_t(hg) * kStatsPerHead);
   uint8_t* ring_base = stats_base + size_t(P.heads) * kStatsPerHead;
-  uint16_t* ring = reinterpret_cast<uint16_t*>(ring_base + size_t(hg) * kRingPerHead);
   const __amdgpu_buffer_rsrc_t wsr = ws_rsrc(P.ws);
   const uint32_t ring_off = static_cast<uint32_t>((ring_base - P.ws) + size_t(hg) * kRingPerHead);
   const uint32_t stats_off = static_cast<uint32_t>((stats_base - P.ws) + size_t(hg) * kStatsPerHead);
@@ -267,7 +292,7 @@ chunkwise_fused(Params P) {
     __threadfence();
     __hip_atomic_fetch_add(cnt + kArrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  wait_count(cnt, kArrive, nS, true);
+  wait_count(cnt, kArrive, nS);
   if (tid == 0) {
     uint32_t m = __hip_atomic_load(cnt + kXccMask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm.mode = (__builtin_popcount(m) == 1) ? 0u : 1u;
@@ -276,529 +301,78 @@ chunkwise_fused(Params P) {
   const bool agent = sm.mode != 0;
 
   const float lg = a.hp.log2g[h];
-  const float alpha = a.alpha;
   const bool use_gn = a.flags & RN_EPI_GN;
-  const bool has_gate = P.gate != nullptr;
-
-  // ---- producer: this thread rotates rows r_lo + pr + 8u (u < U) of each block,
-  // pairs 4pq..4pq+3 (d_k 8pq..8pq+7), for q and k -----------------------------------
-  constexpr int rows_per = kT / nS, U = rows_per / 8;
-  const int r_lo = sl * rows_per;
-  const int pr = tid >> 5, pq = tid & 31;
-  float th[4], c64[4], s64[4], cc[U][4], ss[U][4], fq[U], fk[U];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    th[i] = a.ap.theta[4 * pq + i];
-    angle_cs(kT, th[i], &c64[i], &s64[i]);   // once per thread: exact
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int row = r_lo + pr + 8 * u;
-    fq[u] = alpha * exp2f(lg * float(row - 31));
-    fk[u] = exp2f(lg * float(31 - row));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      cc[u][i] = 1.f;
-      ss[u][i] = 0.f;
-    }
-  }
-  const int64_t p_row0 = a.pos0 + r_lo + pr;   // position of the thread's row u = 0 in block 0
-  const size_t qk_head = size_t(bh) * N * kDK;
-  const int64_t qk_bytes = int64_t(N) * kDK * 2;
-  const __amdgpu_buffer_rsrc_t r_q = range_rsrc(P.q + qk_head, qk_bytes);
-  const __amdgpu_buffer_rsrc_t r_k = range_rsrc(P.k + qk_head, qk_bytes);
-  // raw rows of the next block to produce (past the end of the sequence: zeros)
-  u32x4 xq[U], xk[U];
-  auto load_raw = [&](int b) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t off = static_cast<uint32_t>(((b * kT + r_lo + pr + 8 * u) * kDK + 8 * pq) * 2);
-      xq[u] = ld_b128(r_q, off);
-      xk[u] = ld_b128(r_k, off);
-    }
-  };
-  // Rotates and stores this workgroup's rows of block b. Blocks are produced in order;
-  // the angles advance by 64 theta per block and are re-anchored from their
-  // float64-reduced values every kReanchor blocks.
-  auto produce = [&](int b) {
-    const bool anchor = (b % kReanchor) == 0;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (anchor) {
-          angle_cs_fast(p_row0 + int64_t(b) * kT + 8 * u, th[i], &cc[u][i], &ss[u][i]);
-        } else {
-          const float cn = cc[u][i] * c64[i] - ss[u][i] * s64[i];
-          ss[u][i] = cc[u][i] * s64[i] + ss[u][i] * c64[i];
-          cc[u][i] = cn;
-        }
-      }
-      u32x4 oq, ok;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float q0 = __uint_as_float(xq[u][i] << 16), q1 = __uint_as_float(xq[u][i] & 0xffff0000u);
-        const float k0 = __uint_as_float(xk[u][i] << 16), k1 = __uint_as_float(xk[u][i] & 0xffff0000u);
-        const float cq = cc[u][i] * fq[u], sq = ss[u][i] * fq[u];
-        const float ck = cc[u][i] * fk[u], sk = ss[u][i] * fk[u];
-        oq[i] = pack_f16x2(q0 * cq - q1 * sq, q0 * sq + q1 * cq);
-        ok[i] = pack_f16x2(k0 * ck - k1 * sk, k0 * sk + k1 * ck);
-      }
-      uint16_t* slot = ring + size_t(b % kRing) * 2 * kSlotElems + size_t(r_lo + pr + 8 * u) * kDK + 8 * pq;
-      *reinterpret_cast<u32x4*>(slot) = oq;
-      *reinterpret_cast<u32x4*>(slot + kSlotElems) = ok;
-    }
-  };
-
-  // ---- publication and waits --------------------------------------------------
-  const uint32_t nW = 4u * uint32_t(nS);
-  // Issues a read of a count (lane 0); `settle` later waits until it reaches `target`.
-  // Issues a read of a count (every lane reads the same word, so the load is
-  // unconditional); `settle` later waits until it reaches `target`.
-  auto poll = [&](int word) -> uint32_t {
-    return __hip_atomic_load(cnt + word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  auto settle = [&](uint32_t v, int word, uint32_t target) {
-    v = __builtin_amdgcn_readfirstlane(v);
-    if (v < target) {
-      const uint64_t t0 = wall_clock64();
-      while (true) {
-        uint32_t x = 0u, err = 0u;
-        if (l == 0) {
-          x = __hip_atomic_load(cnt + word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          err = __hip_atomic_load(cnt + kError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        x = __builtin_amdgcn_readfirstlane(x);
-        err = __builtin_amdgcn_readfirstlane(err);
-        if (x >= target || err) break;
-        __builtin_amdgcn_s_sleep(1);
-        if (wall_clock64() - t0 > kWaitTicks) {
-          if (l == 0) __hip_atomic_fetch_or(cnt + kError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-      }
-    }
-    if (agent) __atomic_thread_fence(__ATOMIC_ACQUIRE);
-    __asm__ volatile("" ::: "memory");
-  };
-  // Publishes this wave's completed stores: ring block `rb` and/or statistics of
-  // block `sb` (-1 = none).
-  auto release = [&](int rb, int sb, bool tail4) {
-    store_fence_release(agent, tail4);
-    if (l == 0) {
-      if (rb >= 0)
-        __hip_atomic_fetch_add(cnt + kReady + rb % kRing, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (sb >= 0)
-        __hip_atomic_fetch_add(cnt + kStat + sb % kStatRing, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  };
+  const uint32_t nW = 4u * uint32_t(nS);   // publishing (E) waves per head
   auto ready_target = [&](int b) { return nW * uint32_t(b / kRing + 1); };
   auto stat_target = [&](int b) { return nW * uint32_t(b / kStatRing + 1); };
 
-  // ---- consumer operands ---------------------------------------------------------
-  // The fragments of block b are copied from the ring straight into this wave's LDS
-  // region (buffer loads with the lds modifier, sc0): fragment f of lane l lands at
-  // fr[w][f][l], Qt (m, c) -> f = 2m + c, Kt (i, c) -> f = 8 + 2i + c.
-  auto stage_frags = [&](int b) {
-    const uint32_t so = ring_off + static_cast<uint32_t>((b % kRing) * 2 * kSlotElems * sizeof(uint16_t));
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint32_t o = static_cast<uint32_t>(((16 * m + l16) * kDK + 64 * w + 32 * c + 8 * g) * 2);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            wsr, (__attribute__((address_space(3))) void*)(&sm.fr[w][2 * m + c][0]), 16, so + o, 0, 0, 1);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            wsr, (__attribute__((address_space(3))) void*)(&sm.fr[w][8 + 2 * m + c][0]), 16,
-            so + static_cast<uint32_t>(kSlotElems * 2) + o, 0, 0, 1);
-      }
-  };
-  auto read_frags = [&](Frags& f) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        f.q[m][c] = sm.fr[w][2 * m + c][l];
-        f.k[m][c] = sm.fr[w][8 + 2 * m + c][l];
-      }
-  };
-  // 0/1 selection matrices (B operand) for the MFMA transpose of Kt: column n of
-  // E_hh picks d_k row 8(n>>2) + 4hh + (n&3) of a 32-wide chunk.
-  f16x8 E[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-      E[hh][jj] = (g == (l16 >> 2) && jj == 4 * hh + (l16 & 3)) ? _Float16(1.0f) : _Float16(0.0f);
-
-  // V slice: thread loads rows s0..s0+3, columns d0..d0+3 (bf16) of the slice
-  const int64_t slice_bytes = (int64_t(N) * DV - sl * kSl) * 2;  // to the end of this head
-  const size_t slice0 = size_t(bh) * N * DV + sl * kSl;
-  const __amdgpu_buffer_rsrc_t r_v = range_rsrc(P.v + slice0, slice_bytes);
-  const __amdgpu_buffer_rsrc_t r_g = range_rsrc(has_gate ? P.gate + slice0 : P.v + slice0, slice_bytes);
-  const int osz = (OUT == RN_BF16) ? 2 : 4;
-  const __amdgpu_buffer_rsrc_t r_o =
-      range_rsrc(static_cast<uint8_t*>(P.out) + slice0 * osz, slice_bytes / 2 * osz);
-  const int vs0 = 4 * (tid >> 4), vd0 = 4 * (tid & 15);
-  auto load_v = [&](int b, u32x2* rv) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rv[i] = ld_b64(r_v, static_cast<uint32_t>(((b * kT + vs0 + i) * DV + vd0) * 2));
-  };
-  auto stage_v = [&](int buf, const u32x2* rv) {
-    float fv[4][4];   // [row i][column jj]
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fv[i][0] = __uint_as_float(rv[i][0] << 16);
-      fv[i][1] = __uint_as_float(rv[i][0] & 0xffff0000u);
-      fv[i][2] = __uint_as_float(rv[i][1] << 16);
-      fv[i][3] = __uint_as_float(rv[i][1] & 0xffff0000u);
-    }
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      *reinterpret_cast<u32x2*>(&sm.vt[buf][vd0 + jj][vt_pos(vs0)]) =
-          u32x2{pack_f16x2(fv[0][jj], fv[1][jj]), pack_f16x2(fv[2][jj], fv[3][jj])};
-  };
-
-  // ---- epilogue mapping: thread (fa, fb) owns rows 4fa..4fa+3, columns 4fb..4fb+3 ----
-  const int fa = tid >> 4, fb = tid & 15;
-  float gw[4], gbias[4];
-#pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
-    const int col = h * DV + sl * kSl + 4 * fb + cc;
-    gw[cc] = a.gn_w ? a.gn_w[col] : 1.f;
-    gbias[cc] = a.gn_b ? a.gn_b[col] : 0.f;
-  }
-  auto load_gate = [&](int b, u32x2* gt) {   // (reads v when there is no gate: unused)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      gt[rr] = ld_b64(r_g, static_cast<uint32_t>(((b * kT + 4 * fa + rr) * DV + 4 * fb) * 2));
-  };
-  // Statistics (mean, M2) of rows 4fa..4fa+3 of block b from slice fb (lanes fb >= nS
-  // read slice fb mod 8 of the slot and ignore it).
-  auto load_stats = [&](int b, u32x4* sv) {
-    const uint32_t so = stats_off + static_cast<uint32_t>(
-        ((((b & (kStatRing - 1)) * 8 + (fb & 7)) * kT + 4 * fa) * 2) * sizeof(float));
-    sv[0] = ld_sc0_b128(wsr, so);
-    sv[1] = ld_sc0_b128(wsr, so + 16);
-  };
-  // Normalises (with the statistics of all slices of block b), gates and stores.
-  const float inv_dv = 1.0f / float(DV);
-  auto finalize = [&](int b, const float (*o)[4], const u32x2* gt, const u32x4* sv) {
-    float y[4][4];
-    if (use_gn) {
-      // lane fb < nS holds slice fb's (mean, M2) of rows 4fa..4fa+3
-      const bool mine = fb < nS;
-      float mu_s[4], m2_s[4];
-      mu_s[0] = mine ? __uint_as_float(sv[0][0]) : 0.f; m2_s[0] = mine ? __uint_as_float(sv[0][1]) : 0.f;
-      mu_s[1] = mine ? __uint_as_float(sv[0][2]) : 0.f; m2_s[1] = mine ? __uint_as_float(sv[0][3]) : 0.f;
-      mu_s[2] = mine ? __uint_as_float(sv[1][0]) : 0.f; m2_s[2] = mine ? __uint_as_float(sv[1][1]) : 0.f;
-      mu_s[3] = mine ? __uint_as_float(sv[1][2]) : 0.f; m2_s[3] = mine ? __uint_as_float(sv[1][3]) : 0.f;
-      // equal counts per slice: mean = average of the slice means,
-      // M2 = sum M2_s + 64 sum (mean_s - mean)^2 (Chan et al.)
-      const float inv_nS = 1.0f / float(nS);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float mu = row16_sum(mu_s[rr]) * inv_nS;
-        const float d = mu_s[rr] - mu;
-        const float m2 = row16_sum((fb < nS) ? fmaf(float(kSl) * d, d, m2_s[rr]) : 0.f);
-        const float rstd = __frsqrt_rn(fmaf(m2, inv_dv, a.eps));
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) y[rr][cc] = fmaf((o[rr][cc] - mu) * rstd, gw[cc], gbias[cc]);
-        if (has_gate) {
-          y[rr][0] *= swishf(__uint_as_float(gt[rr][0] << 16));
-          y[rr][1] *= swishf(__uint_as_float(gt[rr][0] & 0xffff0000u));
-          y[rr][2] *= swishf(__uint_as_float(gt[rr][1] << 16));
-          y[rr][3] *= swishf(__uint_as_float(gt[rr][1] & 0xffff0000u));
+  if (wv < 4) {
+    // =============================== M waves ===========================================
+    const int w = wv;
+    // Issues a read of a count (every lane reads the same word, so the load is
+    // unconditional); `settle` later waits until it reaches `target`.
+    auto poll = [&](int word) -> uint32_t {
+      return __hip_atomic_load(cnt + word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto settle = [&](uint32_t v, int word, uint32_t target) {
+      v = __builtin_amdgcn_readfirstlane(v);
+      if (v < target) {
+        const uint64_t t0 = wall_clock64();
+        while (true) {
+          uint32_t x = 0u, err = 0u;
+          if (l == 0) {
+            x = __hip_atomic_load(cnt + word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            err = __hip_atomic_load(cnt + kError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          x = __builtin_amdgcn_readfirstlane(x);
+          err = __builtin_amdgcn_readfirstlane(err);
+          if (x >= target || err) break;
+          __builtin_amdgcn_s_sleep(1);
+          if (wall_clock64() - t0 > kWaitTicks) {
+            if (l == 0) __hip_atomic_fetch_or(cnt + kError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
         }
       }
-    } else {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) y[rr][cc] = o[rr][cc];
-    }
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const uint32_t ooff = static_cast<uint32_t>(((b * kT + 4 * fa + rr) * DV + 4 * fb) * osz);
-      if constexpr (OUT == RN_BF16) {
-        const u32x2 pk = {pack_bf16x2(y[rr][0], y[rr][1]), pack_bf16x2(y[rr][2], y[rr][3])};
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, pk), r_o, ooff, 0, 0);
-      } else {
-        st_b128(r_o, ooff, __builtin_bit_cast(u32x4, f32x4{y[rr][0], y[rr][1], y[rr][2], y[rr][3]}));
-      }
-    }
-  };
-
-  // ---- state: Sc_w tiles [ta][tb], ta = d_k tile (permuted rows), tb = d_v tile ----
-  // accumulator row 4g+r of tile ta = 2c+hh holds d_k = 64w + 32c + 8g + 4hh + r
-  const float g32 = exp2f(lg * 32.f);
-  f32x4 Sacc[4][4];
-#pragma unroll
-  for (int ta = 0; ta < 4; ++ta)
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int dk = 64 * w + 32 * (ta >> 1) + 8 * g + 4 * (ta & 1) + r;
-        const int dv = sl * kSl + 16 * tb + l16;
-        Sacc[ta][tb][r] = P.s_in ? g32 * P.s_in[(size_t(bh) * kDK + dk) * DV + dv] : 0.f;
-      }
-
-  // ---- one block ---------------------------------------------------------------------
-  u32x2 rv[4];                      // V rows of the next block to stage
-  // Summed outputs and gate rows waiting for their normalisation, kLag = 2 blocks
-  // later: even blocks in (o_e, g_e), odd blocks in (o_o, g_o). The loop runs two
-  // blocks per iteration so that each buffer keeps its registers.
-  float o_e[4][4], o_o[4][4];
-  u32x2 g_e[4], g_o[4];
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    g_e[rr] = g_o[rr] = u32x2{0u, 0u};
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) o_e[rr][cc] = o_o[rr][cc] = 0.f;
-  }
-
-  // Counts polled during the previous step (their loads drained by its release):
-  // block j+1 whole, and the statistics of block j-2.
-  uint32_t poll_r = 0u, poll_s = 0u;
-  // Memory traffic of a step is issued in the order it is needed, with no load or
-  // store under a data-dependent condition, so that each wait covers only what it
-  // needs (loads past the end of the sequence read zeros; surplus productions past
-  // the last block write zeros into slots no reader needs any more).
-  auto step = [&](int j, float (*o_buf)[4], u32x2* g_buf) {
-    const int Lb = min(kT, N - j * kT);
-    const int buf = j & 1;
-    // (0) this block's fragments (copied during the previous step, whose release
-    // waited for every copy of this wave)
-    Frags cur;
-    read_frags(cur);
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // (1) operands of block j+1 (every slice published them at its step j-2) into the
-    // LDS region just read; statistics of block j-2 (published at step j-2)
-    if (j + 1 < nb) settle(poll_r, kReady + (j + 1) % kRing, ready_target(j + 1));
-    stage_frags(j + 1);
-    if (use_gn && j >= kLag) settle(poll_s, kStat + (j - kLag) % kStatRing, stat_target(j - kLag));
-    u32x4 sv[2];
-    load_stats(j - kLag, sv);
-    // (2) V of block j -> LDS (transposed); prefetch V of block j+1
-    stage_v(buf, rv);
-    load_v(j + 1, rv);
-    // (3) rotate this workgroup's rows of block j+3 into the ring; raw rows of j+4
-    const bool produced = j + kAhead < nb;
-    produce(j + kAhead);
-    load_raw(j + kAhead + 1);
-    u32x2 g_cur[4];
-    load_gate(j, g_cur);
-    __syncthreads();   // V^T of block j visible
-
-    // (4) cross term acc = Qt_w Sc_w (B operand: the state in half)
-    f32x4 acc[4][4];
-    {
-      f16x8 sf[2][4];
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          u32x4 u;
-          u[0] = pack_f16x2(Sacc[2 * c][tb][0], Sacc[2 * c][tb][1]);
-          u[1] = pack_f16x2(Sacc[2 * c][tb][2], Sacc[2 * c][tb][3]);
-          u[2] = pack_f16x2(Sacc[2 * c + 1][tb][0], Sacc[2 * c + 1][tb][1]);
-          u[3] = pack_f16x2(Sacc[2 * c + 1][tb][2], Sacc[2 * c + 1][tb][3]);
-          sf[c][tb] = as_f16x8(u);
-        }
+      if (agent) __atomic_thread_fence(__ATOMIC_ACQUIRE);
+      __asm__ volatile("" ::: "memory");
+    };
+    // The fragments of block b are copied from the ring straight into this wave's LDS
+    // region: fragment f of lane l lands at fr[w][f][l], Qt (m, c) -> f = 2m + c,
+    // Kt (i, c) -> f = 8 + 2i + c; lane l holds row 16m + l16 (16i + l16), d_k
+    // 64w + 32c + 8g .. +8.
+    auto stage_frags = [&](int b) {
+      const uint32_t so = ring_off + static_cast<uint32_t>((b & (kRing - 1)) * 2 * kSlotElems * sizeof(uint16_t));
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          f32x4 z = mfma(as_f16x8(cur.q[m][0]), sf[0][tb], f32x4{0.f, 0.f, 0.f, 0.f});
-          acc[m][tb] = mfma(as_f16x8(cur.q[m][1]), sf[1][tb], z);
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t o = static_cast<uint32_t>(((16 * m + l16) * kDK + 64 * w + 32 * c + 8 * g) * 2);
+          copy_to_lds(wsr, &sm.fr[w][2 * m + c][0], so + o);
+          copy_to_lds(wsr, &sm.fr[w][8 + 2 * m + c][0], so + static_cast<uint32_t>(kSlotElems * 2) + o);
         }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // (5) scores P^T tiles (i, m), i <= m, partial over this wave's quarter of d_k:
-    // D row s = 16i + 4g + r, column t = 16m + l16
-    f16x8 pf[4][2];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      f32x4 pt[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pt[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (i > m) continue;
-        f32x4 z = mfma(as_f16x8(cur.k[i][0]), as_f16x8(cur.q[m][0]), pt[i]);
-        z = mfma(as_f16x8(cur.k[i][1]), as_f16x8(cur.q[m][1]), z);
-        if (i == m) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) z[r] = (4 * g + r <= l16) ? z[r] : 0.f;
-        }
-        pt[i] = z;
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        u32x4 u;
-        u[0] = pack_f16x2(pt[2 * e][0], pt[2 * e][1]);
-        u[1] = pack_f16x2(pt[2 * e][2], pt[2 * e][3]);
-        u[2] = pack_f16x2(pt[2 * e + 1][0], pt[2 * e + 1][1]);
-        u[3] = pack_f16x2(pt[2 * e + 1][2], pt[2 * e + 1][3]);
-        pf[m][e] = as_f16x8(u);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // (6) Kt^T of this quarter as the carry's A operand (row d_k, k = keys in vt_pos
-    // order): tile ta = 2c + hh from Kt rows 16i.. times E_hh
-    f16x8 ktf[4][2];
-#pragma unroll
-    for (int ta = 0; ta < 4; ++ta) {
-      f32x4 T[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        T[i] = mfma(as_f16x8(cur.k[i][ta >> 1]), E[ta & 1], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        u32x4 u;
-        u[0] = pack_f16x2(T[2 * e][0], T[2 * e][1]);
-        u[1] = pack_f16x2(T[2 * e][2], T[2 * e][3]);
-        u[2] = pack_f16x2(T[2 * e + 1][0], T[2 * e + 1][1]);
-        u[3] = pack_f16x2(T[2 * e + 1][2], T[2 * e + 1][3]);
-        ktf[ta][e] = as_f16x8(u);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // (7) V fragments (B operand, k = keys in vt_pos order), intra term, carry
-    f16x8 vf[2][4];
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-        vf[e][tb] = as_f16x8(*reinterpret_cast<const u32x4*>(&sm.vt[buf][16 * tb + l16][32 * e + 8 * g]));
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        acc[m][tb] = mfma(pf[m][0], vf[0][tb], acc[m][tb]);
-        if (m >= 2) acc[m][tb] = mfma(pf[m][1], vf[1][tb], acc[m][tb]);
-      }
-    const float gL = exp2f(lg * float(Lb));
-#pragma unroll
-    for (int ta = 0; ta < 4; ++ta)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        f32x4 z = mfma(ktf[ta][0], vf[0][tb], Sacc[ta][tb]);
-        z = mfma(ktf[ta][1], vf[1][tb], z);
-        Sacc[ta][tb] = z * gL;
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    // counts for the next step: block j+2 (published at step j-1) and statistics of
-    // block j-1 (published at the end of step j-1)
-    poll_r = poll(kReady + (j + 2) % kRing);
-    poll_s = poll(kStat + (j - 1 + kStatRing) % kStatRing);
-    // (8) partial outputs -> LDS: element (row 16m + 4g + r, column 16tb + l16)
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const int col = 16 * tb + l16;
-        *reinterpret_cast<f32x4*>(&sm.red[w][col][4 * ((4 * m + g) ^ red_swz(col))]) = acc[m][tb];
-      }
-    __syncthreads();
-    float o_cur[4][4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) o_cur[rr][cc] = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const int col = 4 * fb + cc;
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.red[ww][col][4 * (fa ^ red_swz(col))]);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) o_cur[rr][cc] += x[rr];
-      }
-    }
-    // (9) this slice's statistics of block j: per row (mean, centred sum of squares)
-    if (use_gn) {
-      float st[8];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float s = row16_sum((o_cur[rr][0] + o_cur[rr][1]) + (o_cur[rr][2] + o_cur[rr][3]));
-        const float mu = s * (1.0f / kSl);
-        float m2 = 0.f;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const float d = o_cur[rr][cc] - mu;
-          m2 = fmaf(d, d, m2);
-        }
-        m2 = row16_sum(m2);
-        st[2 * rr] = mu;
-        st[2 * rr + 1] = m2;
-      }
-      {
-        float* sp = stats + (((j % kStatRing) * 8 + sl) * kT + 4 * fa) * 2;
-        *reinterpret_cast<f32x4*>(sp) = f32x4{st[0], st[1], st[2], st[3]};
-        *reinterpret_cast<f32x4*>(sp + 4) = f32x4{st[4], st[5], st[6], st[7]};
-      }
-      // the only memory operations between here and the release are the 4 output
-      // stores of the normalisation (release with vmcnt(4))
-      __asm__ volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-      // (10) normalise block j-2
-      if (j >= kLag) finalize(j - kLag, o_buf, g_buf, sv);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        g_buf[rr] = g_cur[rr];
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) o_buf[rr][cc] = o_cur[rr][cc];
-      }
-    } else {
-      finalize(j, o_cur, g_cur, sv);
-    }
-    // (11) publish this wave's ring rows of block j+3 and statistics of block j (the
-    // output stores just issued need not have completed)
-    __builtin_amdgcn_sched_barrier(0);
-    release(produced ? j + kAhead : -1, use_gn ? j : -1, !use_gn || j >= kLag);
-  };
+    };
+    // Statistics slot of block b (every slice's 64 rows) -> sm.stat[buf]: 4 KB, one
+    // 16-byte piece per lane of the four M waves.
+    auto stage_stats = [&](int b, int buf) {
+      const uint32_t so = stats_off + static_cast<uint32_t>(((b & (kStatRing - 1)) * 8 * kT * 2) * sizeof(float));
+      copy_to_lds(wsr, reinterpret_cast<uint8_t*>(&sm.stat[buf][0][0][0]) + 1024 * w,
+                  so + static_cast<uint32_t>(1024 * w + 16 * l));
+    };
 
-  // ---- prologue: blocks 0 .. kAhead-1 produced and published; block 0 loaded ---------
-  for (int b = 0; b < kAhead; ++b) {
-    load_raw(b);
-    produce(b);
-  }
-  load_raw(kAhead);
-  load_v(0, rv);
-  store_fence_release(agent);
-  if (l == 0) {
-    for (int b = 0; b < kAhead && b < nb; ++b)
-      __hip_atomic_fetch_add(cnt + kReady + b % kRing, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  settle(poll(kReady + 0), kReady + 0, ready_target(0));
-  stage_frags(0);
-  poll_r = poll(kReady + 1);
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // 0/1 selection matrices (B operand) for the MFMA transpose of Kt: column n of
+    // E_hh picks d_k row 8(n>>2) + 4hh + (n&3) of a 32-wide chunk.
+    f16x8 E[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        E[hh][jj] = (g == (l16 >> 2) && jj == 4 * hh + (l16 & 3)) ? _Float16(1.0f) : _Float16(0.0f);
 
-  int j = 0;
-  for (; j + 1 < nb; j += 2) {
-    step(j, o_e, g_e);
-    step(j + 1, o_o, g_o);
-  }
-  if (j < nb) step(j, o_e, g_e);
-
-  // ---- the last kLag blocks ---------------------------------------------------------
-  if (use_gn) {
-    u32x4 sv[2];
-    for (int b = max(nb - kLag, 0); b < nb; ++b) {
-      settle(poll(kStat + b % kStatRing), kStat + b % kStatRing, stat_target(b));
-      load_stats(b, sv);
-      if (b & 1)
-        finalize(b, o_o, g_o, sv);
-      else
-        finalize(b, o_e, g_e, sv);
-    }
-  }
-
-  if (P.s_out) {
-    const float gi32 = exp2f(-lg * 32.f);
+    // state: Sc_w tiles [ta][tb], ta = d_k tile (permuted rows), tb = d_v tile;
+    // accumulator row 4g+r of tile ta = 2c+hh holds d_k = 64w + 32c + 8g + 4hh + r
+    const float g32 = exp2f(lg * 32.f);
+    f32x4 Sacc[4][4];
 #pragma unroll
     for (int ta = 0; ta < 4; ++ta)
 #pragma unroll
@@ -807,8 +381,442 @@ chunkwise_fused(Params P) {
         for (int r = 0; r < 4; ++r) {
           const int dk = 64 * w + 32 * (ta >> 1) + 8 * g + 4 * (ta & 1) + r;
           const int dv = sl * kSl + 16 * tb + l16;
-          P.s_out[(size_t(bh) * kDK + dk) * DV + dv] = Sacc[ta][tb][r] * gi32;
+          Sacc[ta][tb][r] = P.s_in ? g32 * P.s_in[(size_t(bh) * kDK + dk) * DV + dv] : 0.f;
         }
+
+    // prologue: block 0 (published by the E waves' prologue) copied in
+    uint32_t poll_r = 0u, poll_s = 0u;
+    if (nb > 0) settle(poll(kReady + 0), kReady + 0, ready_target(0));
+    stage_frags(0);
+    poll_r = poll(kReady + 1);
+
+    for (int i = 0; i < n_iter; ++i) {
+      lds_barrier();   // B1
+      // copies of the previous iteration (fragments of block i, statistics of block
+      // i-4) and the polled counts are complete
+      wait_vm<0>();
+      u32x4 q[4][2], k[4][2];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          q[m][c] = sm.fr[w][2 * m + c][l];
+          k[m][c] = sm.fr[w][8 + 2 * m + c][l];
+        }
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+      __asm__ volatile("" ::: "memory");
+      // block i+1 into the fragment region just read; statistics of block i-3
+      if (i + 1 < nb) settle(poll_r, kReady + (i + 1) % kRing, ready_target(i + 1));
+      stage_frags(i + 1);
+      if (use_gn && i >= 3 && i - 3 < nb) settle(poll_s, kStat + (i - 3) % kStatRing, stat_target(i - 3));
+      stage_stats(i - 3, i & 1);
+      lds_barrier();   // B2: the E waves have read the partial outputs of block i-1
+      // counts for the next iteration: block i+2 whole, statistics of block i-2
+      poll_r = poll(kReady + (i + 2) % kRing);
+      poll_s = poll(kStat + ((i - 2) & (kStatRing - 1)));
+      if (i >= nb) continue;
+
+      const int vb = i & 1;
+      // scores P^T tiles (i, m), i <= m, partial over this wave's quarter of d_k:
+      // D row s = 16i + 4g + r, column t = 16m + l16
+      f16x8 pf[4][2];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f32x4 pt[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          pt[ii] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (ii > m) continue;
+          f32x4 z = mfma(as_f16x8(k[ii][0]), as_f16x8(q[m][0]), pt[ii]);
+          z = mfma(as_f16x8(k[ii][1]), as_f16x8(q[m][1]), z);
+          if (ii == m) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) z[r] = (4 * g + r <= l16) ? z[r] : 0.f;
+          }
+          pt[ii] = z;
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          u32x4 u;
+          u[0] = pack_f16x2(pt[2 * e][0], pt[2 * e][1]);
+          u[1] = pack_f16x2(pt[2 * e][2], pt[2 * e][3]);
+          u[2] = pack_f16x2(pt[2 * e + 1][0], pt[2 * e + 1][1]);
+          u[3] = pack_f16x2(pt[2 * e + 1][2], pt[2 * e + 1][3]);
+          pf[m][e] = as_f16x8(u);
+        }
+      }
+      // Kt^T of this quarter as the carry's A operand (row d_k, k = keys in vt_pos
+      // order): tile ta = 2c + hh from Kt rows 16i.. times E_hh
+      f16x8 ktf[4][2];
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta) {
+        f32x4 T[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          T[ii] = mfma(as_f16x8(k[ii][ta >> 1]), E[ta & 1], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          u32x4 u;
+          u[0] = pack_f16x2(T[2 * e][0], T[2 * e][1]);
+          u[1] = pack_f16x2(T[2 * e][2], T[2 * e][3]);
+          u[2] = pack_f16x2(T[2 * e + 1][0], T[2 * e + 1][1]);
+          u[3] = pack_f16x2(T[2 * e + 1][2], T[2 * e + 1][3]);
+          ktf[ta][e] = as_f16x8(u);
+        }
+      }
+      const float gL = exp2f(lg * float(min(kT, N - i * kT)));
+      // per 16-column tile: cross term from the old state, intra term, partial output
+      // to LDS, then the carry of that tile's state columns
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        f16x8 sf[2], vf[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          u32x4 u;
+          u[0] = pack_f16x2(Sacc[2 * c][tb][0], Sacc[2 * c][tb][1]);
+          u[1] = pack_f16x2(Sacc[2 * c][tb][2], Sacc[2 * c][tb][3]);
+          u[2] = pack_f16x2(Sacc[2 * c + 1][tb][0], Sacc[2 * c + 1][tb][1]);
+          u[3] = pack_f16x2(Sacc[2 * c + 1][tb][2], Sacc[2 * c + 1][tb][3]);
+          sf[c] = as_f16x8(u);
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          vf[e] = as_f16x8(*reinterpret_cast<const u32x4*>(&sm.vt[vb][16 * tb + l16][32 * e + 8 * g]));
+        const int col = 16 * tb + l16;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          f32x4 acc = mfma(as_f16x8(q[m][0]), sf[0], f32x4{0.f, 0.f, 0.f, 0.f});
+          acc = mfma(as_f16x8(q[m][1]), sf[1], acc);
+          acc = mfma(pf[m][0], vf[0], acc);
+          if (m >= 2) acc = mfma(pf[m][1], vf[1], acc);
+          *reinterpret_cast<f32x4*>(&sm.red[w][col][4 * ((4 * m + g) ^ red_swz(col))]) = acc;
+        }
+#pragma unroll
+        for (int ta = 0; ta < 4; ++ta) {
+          f32x4 z = mfma(ktf[ta][0], vf[0], Sacc[ta][tb]);
+          z = mfma(ktf[ta][1], vf[1], z);
+          Sacc[ta][tb] = z * gL;
+        }
+      }
+    }
+
+    if (P.s_out) {
+      const float gi32 = exp2f(-lg * 32.f);
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int dk = 64 * w + 32 * (ta >> 1) + 8 * g + 4 * (ta & 1) + r;
+            const int dv = sl * kSl + 16 * tb + l16;
+            P.s_out[(size_t(bh) * kDK + dk) * DV + dv] = Sacc[ta][tb][r] * gi32;
+          }
+    }
+  } else {
+    // =============================== E waves ===========================================
+    const int te = tid - 256;   // 0..255
+    const float alpha = a.alpha;
+    const bool has_gate = P.gate != nullptr;
+    uint16_t* ring = reinterpret_cast<uint16_t*>(ring_base + size_t(hg) * kRingPerHead);
+    float* stats = reinterpret_cast<float*>(stats_base + size_t(hg) * kStatsPerHead);
+
+    // ---- producer: this thread rotates rows r_lo + pr + 8u (u < U) of each block,
+    // pairs 4pq..4pq+3 (d_k 8pq..8pq+7), for q and k -------------------------------
+    constexpr int rows_per = kT / nS, U = rows_per / 8;
+    const int r_lo = sl * rows_per;
+    const int pr = te >> 5, pq = te & 31;
+    float th[4], c64[4], s64[4], cc[U][4], ss[U][4], fq[U], fk[U];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      th[i] = a.ap.theta[4 * pq + i];
+      angle_cs(kT, th[i], &c64[i], &s64[i]);   // once per thread: exact
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = r_lo + pr + 8 * u;
+      fq[u] = alpha * exp2f(lg * float(row - 31));
+      fk[u] = exp2f(lg * float(31 - row));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        cc[u][i] = 1.f;
+        ss[u][i] = 0.f;
+      }
+    }
+    const int64_t p_row0 = a.pos0 + r_lo + pr;   // position of the thread's row u = 0 in block 0
+    const size_t qk_head = size_t(bh) * N * kDK;
+    const int64_t qk_bytes = int64_t(N) * kDK * 2;
+    const __amdgpu_buffer_rsrc_t r_q = range_rsrc(P.q + qk_head, qk_bytes);
+    const __amdgpu_buffer_rsrc_t r_k = range_rsrc(P.k + qk_head, qk_bytes);
+    const __amdgpu_buffer_rsrc_t r_ring = range_rsrc(ring, int64_t(kRingPerHead));
+    const __amdgpu_buffer_rsrc_t r_stats = range_rsrc(stats, int64_t(kStatsPerHead));
+    // raw rows of blocks to produce, two blocks in flight (past the sequence: zeros)
+    u32x4 xq[2][U], xk[2][U];
+    auto load_raw = [&](int b, u32x4* dq, u32x4* dk) {
+      const int bb = b < 0 ? 0 : b;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t off = static_cast<uint32_t>(((bb * kT + r_lo + pr + 8 * u) * kDK + 8 * pq) * 2);
+        dq[u] = ld_b128(r_q, off);
+        dk[u] = ld_b128(r_k, off);
+      }
+    };
+    // Rotates and stores this workgroup's rows of block b. Blocks are produced in
+    // order; the angles advance by 64 theta per block and are re-anchored from their
+    // float64-reduced values every kReanchor blocks.
+    auto produce = [&](int b, const u32x4* sq, const u32x4* sk) {
+      const bool anchor = (b % kReanchor) == 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (anchor) {
+            angle_cs_fast(p_row0 + int64_t(b) * kT + 8 * u, th[i], &cc[u][i], &ss[u][i]);
+          } else {
+            const float cn = cc[u][i] * c64[i] - ss[u][i] * s64[i];
+            ss[u][i] = cc[u][i] * s64[i] + ss[u][i] * c64[i];
+            cc[u][i] = cn;
+          }
+        }
+        u32x4 oq, ok;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float q0 = __uint_as_float(sq[u][i] << 16), q1 = __uint_as_float(sq[u][i] & 0xffff0000u);
+          const float k0 = __uint_as_float(sk[u][i] << 16), k1 = __uint_as_float(sk[u][i] & 0xffff0000u);
+          const float cq = cc[u][i] * fq[u], sq_ = ss[u][i] * fq[u];
+          const float ck = cc[u][i] * fk[u], sk_ = ss[u][i] * fk[u];
+          oq[i] = pack_f16x2(q0 * cq - q1 * sq_, q0 * sq_ + q1 * cq);
+          ok[i] = pack_f16x2(k0 * ck - k1 * sk_, k0 * sk_ + k1 * ck);
+        }
+        // (blocks past the last: an offset past the end of the ring, store dropped)
+        const uint32_t so = b < nb ? static_cast<uint32_t>(
+            ((size_t(b & (kRing - 1)) * 2 * kSlotElems + size_t(r_lo + pr + 8 * u) * kDK + 8 * pq) * 2))
+                                   : kSink;
+        st_b128(r_ring, so, oq);
+        st_b128(r_ring, so + static_cast<uint32_t>(kSlotElems * 2), ok);
+      }
+    };
+
+    // V slice: thread loads rows vs0..vs0+3, columns vd0..vd0+3 (bf16) of the slice
+    const int64_t slice_bytes = (int64_t(N) * DV - sl * kSl) * 2;  // to the end of this head
+    const size_t slice0 = size_t(bh) * N * DV + sl * kSl;
+    const __amdgpu_buffer_rsrc_t r_v = range_rsrc(P.v + slice0, slice_bytes);
+    const __amdgpu_buffer_rsrc_t r_g = range_rsrc(has_gate ? P.gate + slice0 : P.v + slice0, slice_bytes);
+    const int osz = (OUT == RN_BF16) ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t r_o =
+        range_rsrc(static_cast<uint8_t*>(P.out) + slice0 * osz, slice_bytes / 2 * osz);
+    const int vs0 = 4 * (te >> 4), vd0 = 4 * (te & 15);
+    auto load_v = [&](int b, u32x2* rv) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        rv[i] = ld_b64(r_v, static_cast<uint32_t>(((b * kT + vs0 + i) * DV + vd0) * 2));
+    };
+    auto stage_v = [&](int buf, const u32x2* rv) {
+      float fv[4][4];   // [row i][column jj]
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fv[i][0] = __uint_as_float(rv[i][0] << 16);
+        fv[i][1] = __uint_as_float(rv[i][0] & 0xffff0000u);
+        fv[i][2] = __uint_as_float(rv[i][1] << 16);
+        fv[i][3] = __uint_as_float(rv[i][1] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<u32x2*>(&sm.vt[buf][vd0 + jj][vt_pos(vs0)]) =
+            u32x2{pack_f16x2(fv[0][jj], fv[1][jj]), pack_f16x2(fv[2][jj], fv[3][jj])};
+    };
+
+    // ---- epilogue mapping: thread (fa, fb) owns rows 4fa..4fa+3, columns 4fb..4fb+3 ----
+    const int fa = te >> 4, fb = te & 15;
+    float gw[4], gbias[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int col = h * DV + sl * kSl + 4 * fb + c;
+      gw[c] = a.gn_w ? a.gn_w[col] : 1.f;
+      gbias[c] = a.gn_b ? a.gn_b[col] : 0.f;
+    }
+    // gate rows of block b (reads v when there is no gate: unused; before the first
+    // block: an offset past the end, so zeros)
+    auto load_gate = [&](int b, u32x2* gt) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        gt[rr] = ld_b64(r_g, static_cast<uint32_t>(((b * kT + 4 * fa + rr) * DV + 4 * fb) * 2));
+    };
+    // Normalises block b with the statistics of all slices in sm.stat[sbuf] (lane
+    // fb < nS reads slice fb's mean and M2 of rows 4fa..4fa+3), gates and stores
+    // (blocks outside the sequence: offsets past the end, stores dropped).
+    const float inv_dv = 1.0f / float(DV);
+    auto finalize = [&](int b, const float (*o)[4], const u32x2* gt, int sbuf) {
+      float y[4][4];
+      if (use_gn) {
+        const u32x4 s0 = *reinterpret_cast<const u32x4*>(&sm.stat[sbuf][fb & 7][4 * fa][0]);
+        const u32x4 s1 = *reinterpret_cast<const u32x4*>(&sm.stat[sbuf][fb & 7][4 * fa + 2][0]);
+        const bool mine = fb < nS;
+        float mu_s[4], m2_s[4];
+        mu_s[0] = mine ? __uint_as_float(s0[0]) : 0.f; m2_s[0] = mine ? __uint_as_float(s0[1]) : 0.f;
+        mu_s[1] = mine ? __uint_as_float(s0[2]) : 0.f; m2_s[1] = mine ? __uint_as_float(s0[3]) : 0.f;
+        mu_s[2] = mine ? __uint_as_float(s1[0]) : 0.f; m2_s[2] = mine ? __uint_as_float(s1[1]) : 0.f;
+        mu_s[3] = mine ? __uint_as_float(s1[2]) : 0.f; m2_s[3] = mine ? __uint_as_float(s1[3]) : 0.f;
+        // equal counts per slice: mean = average of the slice means,
+        // M2 = sum M2_s + 64 sum (mean_s - mean)^2 (Chan et al.)
+        const float inv_nS = 1.0f / float(nS);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float mu = row16_sum(mu_s[rr]) * inv_nS;
+          const float d = mu_s[rr] - mu;
+          const float m2 = row16_sum(mine ? fmaf(float(kSl) * d, d, m2_s[rr]) : 0.f);
+          const float rstd = __frsqrt_rn(fmaf(m2, inv_dv, a.eps));
+#pragma unroll
+          for (int c = 0; c < 4; ++c) y[rr][c] = fmaf((o[rr][c] - mu) * rstd, gw[c], gbias[c]);
+          if (has_gate) {
+            y[rr][0] *= swishf(__uint_as_float(gt[rr][0] << 16));
+            y[rr][1] *= swishf(__uint_as_float(gt[rr][0] & 0xffff0000u));
+            y[rr][2] *= swishf(__uint_as_float(gt[rr][1] << 16));
+            y[rr][3] *= swishf(__uint_as_float(gt[rr][1] & 0xffff0000u));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) y[rr][c] = o[rr][c];
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const uint32_t ooff = static_cast<uint32_t>(((b * kT + 4 * fa + rr) * DV + 4 * fb) * osz);
+        if constexpr (OUT == RN_BF16) {
+          st_b64(r_o, ooff, u32x2{pack_bf16x2(y[rr][0], y[rr][1]), pack_bf16x2(y[rr][2], y[rr][3])});
+        } else {
+          st_b128(r_o, ooff, __builtin_bit_cast(u32x4, f32x4{y[rr][0], y[rr][1], y[rr][2], y[rr][3]}));
+        }
+      }
+    };
+
+    // Makes this wave's ring and statistics stores complete, then raises the counts.
+    // Vector memory operations of a wave complete in issue order; the last 12 + 2U
+    // operations issued (4 output stores, 2U raw loads, 4 v loads, 4 gate loads)
+    // need not be waited for. Every iteration issues the same operations (stores
+    // that fall outside the sequence go to a dropped offset), so the count is fixed.
+    auto release = [&](bool ring_pub, int rb, bool stat_pub, int sb) {
+      if (agent) {
+        __threadfence();
+      } else {
+        wait_vm<12 + 2 * U>();
+      }
+      if (l == 0) {
+        if (ring_pub)
+          __hip_atomic_fetch_add(cnt + kReady + rb % kRing, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (stat_pub)
+          __hip_atomic_fetch_add(cnt + kStat + sb % kStatRing, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    };
+
+    // deferred outputs and gate rows of the blocks awaiting normalisation, by block mod
+    // 4; V rows two iterations ahead, by block mod 2
+    float ob[4][4][4];
+    u32x2 gb[4][4];
+    u32x2 vb[2][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        gb[s][rr] = u32x2{0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ob[s][rr][c] = 0.f;
+      }
+
+    // ---- prologue: blocks 0 .. kAhead-1 produced and published, V^T of block 0
+    // staged; then the loads the first two iterations consume: q/k rows of blocks 3
+    // and 4, V of blocks 1 and 2 (the gate rows they would use belong to blocks before
+    // the first, whose outputs are dropped) ---------------------------------------------
+    for (int b = 0; b < kAhead; ++b) {
+      load_raw(b, xq[0], xk[0]);
+      produce(b, xq[0], xk[0]);
+    }
+    load_v(0, vb[0]);
+    stage_v(0, vb[0]);
+    if (agent) __threadfence();
+    else wait_vm<0>();
+    if (l == 0) {
+      for (int b = 0; b < kAhead && b < nb; ++b)
+        __hip_atomic_fetch_add(cnt + kReady + b % kRing, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    load_raw(kAhead, xq[kAhead & 1], xk[kAhead & 1]);
+    load_raw(kAhead + 1, xq[(kAhead + 1) & 1], xk[(kAhead + 1) & 1]);
+    load_v(1, vb[1]);
+    load_v(2, vb[0]);
+    // nothing in flight on entry to the loop: its first iteration then waits for
+    // exactly what it consumes, as later ones do
+    wait_vm<0>();
+
+    // one iteration; C = i mod 4 (compile time)
+    auto iter = [&](auto cst, int i) {
+      constexpr int C = decltype(cst)::value;
+      float o_cur[4][4];
+      lds_barrier();   // B1
+      // (1) partial outputs of block i-1 summed
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o_cur[rr][c] = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int col = 4 * fb + c;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.red[ww][col][4 * (fa ^ red_swz(col))]);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) o_cur[rr][c] += x[rr];
+        }
+      }
+      lds_barrier();   // B2
+      // (2) statistics of block i-1 (per row: mean, centred sum of squares) -> ring
+      {
+        float st[8];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float s = row16_sum((o_cur[rr][0] + o_cur[rr][1]) + (o_cur[rr][2] + o_cur[rr][3]));
+          const float mu = s * (1.0f / kSl);
+          float m2 = 0.f;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float d = o_cur[rr][c] - mu;
+            m2 = fmaf(d, d, m2);
+          }
+          m2 = row16_sum(m2);
+          st[2 * rr] = mu;
+          st[2 * rr + 1] = m2;
+        }
+        const uint32_t so = (i >= 1 && i <= nb) ? static_cast<uint32_t>(
+            (((((i - 1) & (kStatRing - 1)) * 8 + sl) * kT + 4 * fa) * 2) * sizeof(float)) : kSink;
+        st_b128(r_stats, so, __builtin_bit_cast(u32x4, f32x4{st[0], st[1], st[2], st[3]}));
+        st_b128(r_stats, so + 16, __builtin_bit_cast(u32x4, f32x4{st[4], st[5], st[6], st[7]}));
+      }
+      // (3) this workgroup's rows of block i+3 into the ring (raw rows loaded at i-2)
+      produce(i + kAhead, xq[(C + kAhead) & 1], xk[(C + kAhead) & 1]);
+      __asm__ volatile("" ::: "memory");
+      // (4) block i-4: normalise, gate, store (statistics copied by the M waves at i-1)
+      finalize(i - kLag, ob[C], gb[C], (i - 1) & 1);
+      // (5) V^T of block i+1 (loaded at i-2)
+      stage_v((C + 1) & 1, vb[(C + 1) & 1]);
+      // (6) prefetches: q/k rows of block i+5, V of block i+3, gate of block i-2
+      load_raw(i + kAhead + 2, xq[(C + kAhead) & 1], xk[(C + kAhead) & 1]);
+      load_v(i + 3, vb[(C + 3) & 1]);
+      load_gate(i - 2, gb[(C + 2) & 3]);
+      // (7) keep block i-1's outputs for its normalisation at i+3
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ob[(C + 3) & 3][rr][c] = o_cur[rr][c];
+      // (8) publish the ring rows of block i+3 and the statistics of block i-1
+      release(i + kAhead < nb, i + kAhead, use_gn && i >= 1 && i <= nb, i - 1);
+    };
+    for (int i0 = 0; i0 < n_iter; i0 += 4) {
+      iter(Ic<0>{}, i0);
+      iter(Ic<1>{}, i0 + 1);
+      iter(Ic<2>{}, i0 + 2);
+      iter(Ic<3>{}, i0 + 3);
+    }
   }
 }
 
@@ -903,7 +911,7 @@ hipError_t launch_chunkwise_mfma(const CallArgs& a, int out_dt, const void* q, c
     if (e != hipSuccess) return e;
     const int grid = 8 * nS * ((heads + 7) / 8);
     void* args[] = {&p};
-    e = hipLaunchCooperativeKernel(kernel_for(out_dt, nS), dim3(grid), dim3(256), args, 0, st);
+    e = hipLaunchCooperativeKernel(kernel_for(out_dt, nS), dim3(grid), dim3(kThreads), args, 0, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
