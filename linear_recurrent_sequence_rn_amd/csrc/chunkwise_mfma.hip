@@ -51,7 +51,7 @@
 // when a block is whole. GroupNorm statistics (per-row mean and centred sum of squares
 // of each slice) go through an 8-slot ring the same way. All slices of a head are
 // placed on one XCD (blockIdx mod 8), so the exchange stays in that XCD's L2: shared
-// data is read with L1-bypassing (sc0) buffer loads. If the slices turn out to span
+// data is read with L1-bypassing (sc1) buffer loads. If the slices turn out to span
 // XCDs, the kernel uses agent-scope release/acquire fences. Every wait has a time
 // limit that ends the kernel normally and raises an error word in the workspace.
 //
@@ -165,7 +165,7 @@ struct alignas(16) Shared {
   uint32_t mode;                     // 1 = agent-scope fences
 };
 
-// Buffer resource over the whole workspace; loads through it use sc0 (bypass L1).
+// Buffer resource over the whole workspace (the exchange copies read it with sc1).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
 }
@@ -188,9 +188,11 @@ __device__ __forceinline__ void st_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, 
 __device__ __forceinline__ void st_b64(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v), r, off, 0, 0);
 }
-// 16 bytes per lane from the workspace into LDS at dst + 16 * lane (sc0: bypass L1).
+// 16 bytes per lane from the workspace into LDS at dst + 16 * lane, with device scope
+// (sc1): the CU's L1 is bypassed, so data another CU has just written to the XCD's L2 is
+// seen. (A load with sc0 alone may be served from a stale L1 line on this chip.)
 __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 1);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 16);
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
