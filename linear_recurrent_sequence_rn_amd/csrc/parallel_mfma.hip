@@ -167,6 +167,7 @@ struct alignas(16) PShared {
   float red[kWaves][kQ];         // per-wave row partials for the GroupNorm statistics
   float rs[kQ];                  // signed row sums of the scores
   float mean[kQ], rstd[kQ];      // GroupNorm statistics per row
+  float scale[kQ];               // D and R rescaling factor per row
 };
 
 // Unit u (16 bytes = 8 halves, u in [0, 32)) of key row s sits at LDS unit
@@ -321,21 +322,26 @@ parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
   __syncthreads();
   const bool any_norm = a.flags & (RN_NORM_D_ROW | RN_NORM_R_ROW);
   if (any_norm) {
+    // One factor per row, computed once (in float64) by the first 128 threads:
+    // c_t = 1/sqrt(sum_{m<=t} gamma^m) (D rescaling), then 1/max(c_t |rowsum|, 1) (R).
+    if (tid < kQ) {
+      const int t = qb * kQ + tid;
+      double ct = 1.0;
+      if (a.flags & RN_NORM_D_ROW) {
+        const double gm = a.hp.gamma[h];
+        const double G = (gm == 1.0) ? double(t + 1) : -expm1(double(t + 1) * log(gm)) / (1.0 - gm);
+        ct = 1.0 / sqrt(G);
+      }
+      double sc = ct;
+      if (a.flags & RN_NORM_R_ROW) sc = ct / fmax(fabs(ct * double(sm.rs[tid])), 1.0);
+      sm.scale[tid] = static_cast<float>(sc);
+    }
+    __syncthreads();
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int tl = 16 * m + 4 * g + r;
-        const int t = qb * kQ + tl;
-        double ct = 1.0;
-        if (a.flags & RN_NORM_D_ROW) {
-          const double gm = a.hp.gamma[h];
-          const double G = (gm == 1.0) ? double(t + 1) : -expm1(double(t + 1) * log(gm)) / (1.0 - gm);
-          ct = 1.0 / sqrt(G);
-        }
-        double sc = ct;
-        if (a.flags & RN_NORM_R_ROW) sc = ct / fmax(fabs(ct * double(sm.rs[tl])), 1.0);
-        const float f = static_cast<float>(sc);
+        const float f = sm.scale[16 * m + 4 * g + r];
 #pragma unroll
         for (int n = 0; n < 4; ++n) acc[m][n][r] *= f;
       }
