@@ -100,8 +100,28 @@ __global__ void __launch_bounds__(256) parallel_prep(CallArgs a, const uint16_t*
   const __amdgpu_buffer_rsrc_t rq = range_rsrc(q + size_t(bh) * N * kDK, bytes_qk);
   const __amdgpu_buffer_rsrc_t rk = range_rsrc(k + size_t(bh) * N * kDK, bytes_qk);
   const __amdgpu_buffer_rsrc_t rv = range_rsrc(v + size_t(bh) * N * kDV, bytes_v);
+  // Every load of the thread is issued before any store (the compiler cannot reorder a
+  // load past a store to memory it cannot prove distinct), so the 32 loads are in
+  // flight together.
+  const int pg = tid & 31, rg = tid >> 5;     // q/k: pairs 4pg..4pg+3, rows 8rg..8rg+7
+  u32x4 xq[8], xk[8], xv[2][8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t off = static_cast<uint32_t>(((row0 + 8 * rg + u) * kDK + 8 * pg) * 2);
+    xq[u] = ld_b128(rq, off);   // zero past N
+    xk[u] = ld_b128(rk, off);
+  }
+  // v: 8x8 tiles; 64 x 512 block = 512 tiles, 2 per thread: columns 8cg..8cg+7, rows
+  // 8sg..8sg+7 of tile tid + 256 rep
+#pragma unroll
+  for (int rep = 0; rep < 2; ++rep) {
+    const int tile = tid + 256 * rep;
+    const int cg = tile & 63, sg = tile >> 6;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      xv[rep][i] = ld_b128(rv, static_cast<uint32_t>(((row0 + 8 * sg + i) * kDV + 8 * cg) * 2));
+  }
   {
-    const int pg = tid & 31, rg = tid >> 5;     // pairs 4pg..4pg+3, rows 8rg..8rg+7
     float cs[4], sn[4], c1[4], s1[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -113,13 +133,11 @@ __global__ void __launch_bounds__(256) parallel_prep(CallArgs a, const uint16_t*
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int t = row0 + 8 * rg + u;
-      const uint32_t off = static_cast<uint32_t>((t * kDK + 8 * pg) * 2);
-      const u32x4 xq = ld_b128(rq, off), xk = ld_b128(rk, off);   // zero past N
       u32x4 oq, ok;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float q0 = __uint_as_float(xq[i] << 16), q1 = __uint_as_float(xq[i] & 0xffff0000u);
-        const float k0 = __uint_as_float(xk[i] << 16), k1 = __uint_as_float(xk[i] & 0xffff0000u);
+        const float q0 = __uint_as_float(xq[u][i] << 16), q1 = __uint_as_float(xq[u][i] & 0xffff0000u);
+        const float k0 = __uint_as_float(xk[u][i] << 16), k1 = __uint_as_float(xk[u][i] & 0xffff0000u);
         oq[i] = pack_f16x2(al * (q0 * cs[i] - q1 * sn[i]), al * (q0 * sn[i] + q1 * cs[i]));
         ok[i] = pack_f16x2(k0 * cs[i] - k1 * sn[i], k0 * sn[i] + k1 * cs[i]);
         const float cn = cs[i] * c1[i] - sn[i] * s1[i];
@@ -130,22 +148,19 @@ __global__ void __launch_bounds__(256) parallel_prep(CallArgs a, const uint16_t*
       *reinterpret_cast<u32x4*>(base + L.k + size_t(t) * kDK + 8 * pg) = ok;
     }
   }
-  // v: 8x8 tiles; 64 x 512 block = 512 tiles, 2 per thread
   uint16_t* vt = base + L.v + size_t(jb) * kDV * kT;
 #pragma unroll
   for (int rep = 0; rep < 2; ++rep) {
     const int tile = tid + 256 * rep;
-    const int cg = tile & 63, sg = tile >> 6;     // columns 8cg..8cg+7, rows 8sg..8sg+7
+    const int cg = tile & 63, sg = tile >> 6;
     float f[8][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32x4 x = ld_b128(rv, static_cast<uint32_t>(((row0 + 8 * sg + i) * kDV + 8 * cg) * 2));
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        f[i][2 * j] = __uint_as_float(x[j] << 16);
-        f[i][2 * j + 1] = __uint_as_float(x[j] & 0xffff0000u);
+        f[i][2 * j] = __uint_as_float(xv[rep][i][j] << 16);
+        f[i][2 * j + 1] = __uint_as_float(xv[rep][i][j] & 0xffff0000u);
       }
-    }
     // rows 8sg..8sg+3 and 8sg+4..8sg+7 land at positions p0 and p0 + 8
     const int p0 = vt_pos(8 * sg);
 #pragma unroll
