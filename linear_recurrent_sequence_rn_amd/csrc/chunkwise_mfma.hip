@@ -123,17 +123,16 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Sum over each row of 16 lanes, every lane receiving the row's sum, with DPP moves
-// (VALU only): swap neighbours, swap pairs, mirror within 8 lanes, mirror within 16.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
-  x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
-  x += dpp_mov<0x141>(x);   // row_half_mirror: lane i <-> 7 - i within 8
-  x += dpp_mov<0x140>(x);   // row_mirror: lane i <-> 15 - i within 16
+// Sum over each group of 8 lanes, every lane receiving the group's sum, with DPP moves
+// (VALU only): swap neighbours, swap pairs, mirror within 8 lanes.
+__device__ __forceinline__ float row8_sum(float x) {
+  x += dpp_mov<0xB1>(x);    // lane ^ 1
+  x += dpp_mov<0x4E>(x);    // lane ^ 2
+  x += dpp_mov<0x141>(x);   // lane i <-> 7 - i within 8
   return x;
 }
 
@@ -628,82 +627,83 @@ chunkwise_fused(Params P) {
             u32x2{pack_f16x2(fv[0][jj], fv[1][jj]), pack_f16x2(fv[2][jj], fv[3][jj])};
     };
 
-    // ---- epilogue mapping: thread (fa, fb) owns rows 4fa..4fa+3, columns 4fb..4fb+3 ----
-    const int fa = te >> 4, fb = te & 15;
-    float gw[4], gbias[4];
+    // ---- epilogue mapping: thread (ea, eb) owns rows 2ea, 2ea+1 and columns
+    // 8eb..8eb+7, so that gate rows and bf16 output rows move in 16-byte pieces ----
+    const int ea = te >> 3, eb = te & 7;
+    float gw[8], gbias[8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int col = h * DV + sl * kSl + 4 * fb + c;
+    for (int c = 0; c < 8; ++c) {
+      const int col = h * DV + sl * kSl + 8 * eb + c;
       gw[c] = a.gn_w ? a.gn_w[col] : 1.f;
       gbias[c] = a.gn_b ? a.gn_b[col] : 0.f;
     }
     // gate rows of block b (reads v when there is no gate: unused; before the first
     // block: an offset past the end, so zeros)
-    auto load_gate = [&](int b, u32x2* gt) {
+    auto load_gate = [&](int b, u32x4* gt) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        gt[rr] = ld_b64(r_g, static_cast<uint32_t>(((b * kT + 4 * fa + rr) * DV + 4 * fb) * 2));
+      for (int rr = 0; rr < 2; ++rr)
+        gt[rr] = ld_b128(r_g, static_cast<uint32_t>(((b * kT + 2 * ea + rr) * DV + 8 * eb) * 2));
     };
     // Normalises block b with the statistics of all slices in sm.stat[sbuf] (lane
-    // fb < nS reads slice fb's mean and M2 of rows 4fa..4fa+3), gates and stores
+    // eb < nS reads slice eb's mean and M2 of rows 2ea, 2ea+1), gates and stores
     // (blocks outside the sequence: offsets past the end, stores dropped).
     const float inv_dv = 1.0f / float(DV);
-    auto finalize = [&](int b, const float (*o)[4], const u32x2* gt, int sbuf) {
-      float y[4][4];
+    auto finalize = [&](int b, const float (*o)[8], const u32x4* gt, int sbuf) {
+      float y[2][8];
       if (use_gn) {
-        const u32x4 s0 = *reinterpret_cast<const u32x4*>(&sm.stat[sbuf][fb & 7][4 * fa][0]);
-        const u32x4 s1 = *reinterpret_cast<const u32x4*>(&sm.stat[sbuf][fb & 7][4 * fa + 2][0]);
-        const bool mine = fb < nS;
-        float mu_s[4], m2_s[4];
-        mu_s[0] = mine ? __uint_as_float(s0[0]) : 0.f; m2_s[0] = mine ? __uint_as_float(s0[1]) : 0.f;
-        mu_s[1] = mine ? __uint_as_float(s0[2]) : 0.f; m2_s[1] = mine ? __uint_as_float(s0[3]) : 0.f;
-        mu_s[2] = mine ? __uint_as_float(s1[0]) : 0.f; m2_s[2] = mine ? __uint_as_float(s1[1]) : 0.f;
-        mu_s[3] = mine ? __uint_as_float(s1[2]) : 0.f; m2_s[3] = mine ? __uint_as_float(s1[3]) : 0.f;
+        const u32x4 st = *reinterpret_cast<const u32x4*>(&sm.stat[sbuf][eb][2 * ea][0]);
+        const bool mine = eb < nS;
         // equal counts per slice: mean = average of the slice means,
         // M2 = sum M2_s + 64 sum (mean_s - mean)^2 (Chan et al.)
         const float inv_nS = 1.0f / float(nS);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float mu = row16_sum(mu_s[rr]) * inv_nS;
-          const float d = mu_s[rr] - mu;
-          const float m2 = row16_sum(mine ? fmaf(float(kSl) * d, d, m2_s[rr]) : 0.f);
+        for (int rr = 0; rr < 2; ++rr) {
+          const float mu_s = mine ? __uint_as_float(st[2 * rr]) : 0.f;
+          const float m2_s = mine ? __uint_as_float(st[2 * rr + 1]) : 0.f;
+          const float mu = row8_sum(mu_s) * inv_nS;
+          const float d = mu_s - mu;
+          const float m2 = row8_sum(mine ? fmaf(float(kSl) * d, d, m2_s) : 0.f);
           const float rstd = __frsqrt_rn(fmaf(m2, inv_dv, a.eps));
 #pragma unroll
-          for (int c = 0; c < 4; ++c) y[rr][c] = fmaf((o[rr][c] - mu) * rstd, gw[c], gbias[c]);
+          for (int c = 0; c < 8; ++c) y[rr][c] = fmaf((o[rr][c] - mu) * rstd, gw[c], gbias[c]);
           if (has_gate) {
-            y[rr][0] *= swishf(__uint_as_float(gt[rr][0] << 16));
-            y[rr][1] *= swishf(__uint_as_float(gt[rr][0] & 0xffff0000u));
-            y[rr][2] *= swishf(__uint_as_float(gt[rr][1] << 16));
-            y[rr][3] *= swishf(__uint_as_float(gt[rr][1] & 0xffff0000u));
+#pragma unroll
+            for (int c2 = 0; c2 < 4; ++c2) {
+              y[rr][2 * c2] *= swishf(__uint_as_float(gt[rr][c2] << 16));
+              y[rr][2 * c2 + 1] *= swishf(__uint_as_float(gt[rr][c2] & 0xffff0000u));
+            }
           }
         }
       } else {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
+        for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) y[rr][c] = o[rr][c];
+          for (int c = 0; c < 8; ++c) y[rr][c] = o[rr][c];
       }
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const uint32_t ooff = static_cast<uint32_t>(((b * kT + 4 * fa + rr) * DV + 4 * fb) * osz);
+      for (int rr = 0; rr < 2; ++rr) {
+        const uint32_t ooff = static_cast<uint32_t>(((b * kT + 2 * ea + rr) * DV + 8 * eb) * osz);
         if constexpr (OUT == RN_BF16) {
-          st_b64(r_o, ooff, u32x2{pack_bf16x2(y[rr][0], y[rr][1]), pack_bf16x2(y[rr][2], y[rr][3])});
+          st_b128(r_o, ooff, u32x4{pack_bf16x2(y[rr][0], y[rr][1]), pack_bf16x2(y[rr][2], y[rr][3]),
+                                   pack_bf16x2(y[rr][4], y[rr][5]), pack_bf16x2(y[rr][6], y[rr][7])});
         } else {
           st_b128(r_o, ooff, __builtin_bit_cast(u32x4, f32x4{y[rr][0], y[rr][1], y[rr][2], y[rr][3]}));
+          st_b128(r_o, ooff + 16, __builtin_bit_cast(u32x4, f32x4{y[rr][4], y[rr][5], y[rr][6], y[rr][7]}));
         }
       }
     };
 
     // Makes this wave's ring and statistics stores complete, then raises the counts.
-    // Vector memory operations of a wave complete in issue order; the last 12 + 2U
-    // operations issued (4 output stores, 2U raw loads, 4 v loads, 4 gate loads)
-    // need not be waited for. Every iteration issues the same operations (stores
+    // Vector memory operations of a wave complete in issue order; the last kTail
+    // operations issued (2 output stores, 4 for float32 output; 2U raw loads, 4 v loads,
+    // 2 gate loads) need not be waited for. Every iteration issues the same operations (stores
     // that fall outside the sequence go to a dropped offset), so the count is fixed.
+    constexpr int kTail = (OUT == RN_BF16 ? 2 : 4) + 2 * U + 4 + 2;
     auto release = [&](bool ring_pub, int rb, bool stat_pub, int sb) {
       if (agent) {
         __threadfence();
       } else {
-        wait_vm<12 + 2 * U>();
+        wait_vm<kTail>();
       }
       if (l == 0) {
         if (ring_pub)
@@ -715,16 +715,16 @@ chunkwise_fused(Params P) {
 
     // deferred outputs and gate rows of the blocks awaiting normalisation, by block mod
     // 4; V rows two iterations ahead, by block mod 2
-    float ob[4][4][4];
-    u32x2 gb[4][4];
+    float ob[4][2][8];
+    u32x4 gb[4][2];
     u32x2 vb[2][4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        gb[s][rr] = u32x2{0u, 0u};
+      for (int rr = 0; rr < 2; ++rr) {
+        gb[s][rr] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) ob[s][rr][c] = 0.f;
+        for (int c = 0; c < 8; ++c) ob[s][rr][c] = 0.f;
       }
 
     // ---- prologue: blocks 0 .. kAhead-1 produced and published, V^T of block 0
@@ -754,45 +754,47 @@ chunkwise_fused(Params P) {
     // one iteration; C = i mod 4 (compile time)
     auto iter = [&](auto cst, int i) {
       constexpr int C = decltype(cst)::value;
-      float o_cur[4][4];
+      float o_cur[2][8];
       lds_barrier();   // B1
-      // (1) partial outputs of block i-1 summed
+      // (1) partial outputs of block i-1 summed: rows 2ea, 2ea+1 sit in row group ea/2
+      // of each column, at offset 2 (ea % 2)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
+      for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) o_cur[rr][c] = 0.f;
+        for (int c = 0; c < 8; ++c) o_cur[rr][c] = 0.f;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int col = 4 * fb + c;
+      for (int c = 0; c < 8; ++c) {
+        const int col = 8 * eb + c;
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.red[ww][col][4 * (fa ^ red_swz(col))]);
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) o_cur[rr][c] += x[rr];
+          const u32x2 x = *reinterpret_cast<const u32x2*>(
+              &sm.red[ww][col][4 * ((ea >> 1) ^ red_swz(col)) + 2 * (ea & 1)]);
+          o_cur[0][c] += __uint_as_float(x[0]);
+          o_cur[1][c] += __uint_as_float(x[1]);
         }
       }
       lds_barrier();   // B2
       // (2) statistics of block i-1 (per row: mean, centred sum of squares) -> ring
       {
-        float st[8];
+        float st[4];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float s = row16_sum((o_cur[rr][0] + o_cur[rr][1]) + (o_cur[rr][2] + o_cur[rr][3]));
-          const float mu = s * (1.0f / kSl);
+        for (int rr = 0; rr < 2; ++rr) {
+          float sum = 0.f;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) sum += o_cur[rr][c];
+          const float mu = row8_sum(sum) * (1.0f / kSl);
           float m2 = 0.f;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
+          for (int c = 0; c < 8; ++c) {
             const float d = o_cur[rr][c] - mu;
             m2 = fmaf(d, d, m2);
           }
-          m2 = row16_sum(m2);
           st[2 * rr] = mu;
-          st[2 * rr + 1] = m2;
+          st[2 * rr + 1] = row8_sum(m2);
         }
         const uint32_t so = (i >= 1 && i <= nb) ? static_cast<uint32_t>(
-            (((((i - 1) & (kStatRing - 1)) * 8 + sl) * kT + 4 * fa) * 2) * sizeof(float)) : kSink;
+            (((((i - 1) & (kStatRing - 1)) * 8 + sl) * kT + 2 * ea) * 2) * sizeof(float)) : kSink;
         st_b128(r_stats, so, __builtin_bit_cast(u32x4, f32x4{st[0], st[1], st[2], st[3]}));
-        st_b128(r_stats, so + 16, __builtin_bit_cast(u32x4, f32x4{st[4], st[5], st[6], st[7]}));
       }
       // (3) this workgroup's rows of block i+3 into the ring (raw rows loaded at i-2)
       produce(i + kAhead, xq[(C + kAhead) & 1], xk[(C + kAhead) & 1]);
@@ -807,9 +809,9 @@ chunkwise_fused(Params P) {
       load_gate(i - 2, gb[(C + 2) & 3]);
       // (7) keep block i-1's outputs for its normalisation at i+3
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
+      for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) ob[(C + 3) & 3][rr][c] = o_cur[rr][c];
+        for (int c = 0; c < 8; ++c) ob[(C + 3) & 3][rr][c] = o_cur[rr][c];
       // (8) publish the ring rows of block i+3 and the statistics of block i-1
       release(i + kAhead < nb, i + kAhead, use_gn && i >= 1 && i <= nb, i - 1);
     };
