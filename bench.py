@@ -253,13 +253,15 @@ def main():
         g_d, th_d = wd.gamma(), wd.theta()
         for i in range(3):
             d = ins[i % n_in]
-            rn.rn_retention_recurrent_step(d["q"], d["k"], d["v"], g_d, th_d, state, i, out=dout)
+            rn.rn_retention_recurrent_step(d["q"], d["k"], d["v"], g_d, th_d, state, i, out=dout,
+                                           out_dtype=torch.float32)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(args.decode_steps):
             d = ins[i % n_in]
-            rn.rn_retention_recurrent_step(d["q"], d["k"], d["v"], g_d, th_d, state, i, out=dout)
+            rn.rn_retention_recurrent_step(d["q"], d["k"], d["v"], g_d, th_d, state, i, out=dout,
+                                           out_dtype=torch.float32)
         e1.record(stream)
         torch.cuda.synchronize()
         step_us = e0.elapsed_time(e1) * 1e3 / args.decode_steps

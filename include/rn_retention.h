@@ -134,6 +134,35 @@ rn_status rn_retention_chunkwise(const rn_desc* desc, int32_t chunk, const void*
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Chunkwise form over a padded batch of sequences that start at positions of their own
+ * and hold numbers of tokens of their own: the prompt (prefill) half of serving, whose
+ * state_out the decode steps below continue from. (eepw translation, "inference cost"
+ * section with Fig. 6: decoding runs on the recurrent representation, so its cost per
+ * token does not grow with the length already processed; hwhale notes, chunkwise and
+ * recurrent equations: the state after a prefix is all the recurrence needs.)
+ * Sequence b takes rows [0, lengths[b]) of its [N, .] slices of q, k, v, gate and
+ * out; token t of it sits at absolute position pos[b] + t. Everything else is as in
+ * rn_retention_chunkwise, with N replaced by lengths[b] per sequence:
+ *   out rows t >= lengths[b] are not written;
+ *   state_out[b] is the state after lengths[b] tokens (state_in[b], or zeros, when
+ *   lengths[b] == 0).
+ * pos:     DEVICE int64 [B], 8-byte aligned, or NULL for desc->pos0 everywhere. The
+ *          values are not checked (they move no memory access); angles are formed
+ *          and reduced in float64 as for pos0, so |p| <= 2^40 keeps them accurate.
+ * lengths: DEVICE int32 [B], 4-byte aligned, or NULL for N everywhere. Each value is
+ *          clamped to [0, N] on the device, so no value can reach outside the padded
+ *          buffers.
+ * The same workspace size as rn_retention_chunkwise applies
+ * (rn_chunkwise_workspace_bytes).
+ */
+rn_status rn_retention_chunkwise_varlen(const rn_desc* desc, int32_t chunk,
+                                        const int64_t* pos, const int32_t* lengths,
+                                        const void* q, const void* k, const void* v,
+                                        const void* gate, const float* state_in,
+                                        float* state_out, void* out, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
  * One recurrent (decode) step at absolute position desc->pos0 (desc->N must be 1):
  *   S <- gamma S + Kh^T v   (in place),   o = alpha Qh S,   optional GN / gate.
  * (hwhale notes: recurrent equations and the RecurrentRetention listing, which
@@ -143,6 +172,23 @@ rn_status rn_retention_chunkwise(const rn_desc* desc, int32_t chunk, const void*
 rn_status rn_retention_recurrent_step(const rn_desc* desc, const void* q, const void* k,
                                       const void* v, const void* gate, float* state,
                                       void* out, void* stream);
+
+/*
+ * One recurrent (decode) step with a position per sequence: the token of sequence b
+ * sits at pos[b] (batched decode of sequences of different lengths, e.g. continuing
+ * from rn_retention_chunkwise_varlen with pos[b] = its pos[b] + lengths[b]).
+ * Otherwise identical to rn_retention_recurrent_step; desc->pos0 is not used.
+ * (eepw translation, "inference cost" section: batched decode on the recurrent
+ * representation; hwhale notes, recurrent equations.)
+ * pos: DEVICE int64 [B], 8-byte aligned, required; the values are not checked (they
+ *      move no memory access); |p| <= 2^40 keeps the float64-reduced angles accurate.
+ *      Keeping the positions on the device lets a decode loop advance them without
+ *      host work.
+ */
+rn_status rn_retention_recurrent_step_at(const rn_desc* desc, const int64_t* pos,
+                                         const void* q, const void* k, const void* v,
+                                         const void* gate, float* state, void* out,
+                                         void* stream);
 
 /*
  * Standalone per-head GroupNorm (+ swish gate):

@@ -23,7 +23,7 @@ __all__ = [
     "RN_F32", "RN_BF16", "RN_NORM_D_ROW", "RN_NORM_R_ROW", "RN_EPI_GN", "RN_EPI_GATE",
     "RN_FORCE_GENERIC", "RnError", "RnDesc", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
     "rn_retention_parallel", "rn_retention_chunkwise", "rn_retention_recurrent_step",
-    "rn_groupnorm_gate", "rn_chunkwise_workspace_bytes", "rn_parallel_workspace_bytes",
+    "rn_retention_chunkwise_varlen", "rn_retention_recurrent_step_at", "rn_groupnorm_gate", "rn_chunkwise_workspace_bytes", "rn_parallel_workspace_bytes",
     "rn_version", "make_desc",
 ]
 
@@ -36,7 +36,8 @@ RN_FORCE_GENERIC = 1 << 8
 
 EXPORTED_SYMBOLS = (
     "rn_parallel_workspace_bytes", "rn_retention_parallel", "rn_chunkwise_workspace_bytes", "rn_retention_chunkwise",
-    "rn_retention_recurrent_step", "rn_groupnorm_gate", "rn_status_str", "rn_last_error",
+    "rn_retention_recurrent_step", "rn_retention_chunkwise_varlen",
+    "rn_retention_recurrent_step_at", "rn_groupnorm_gate", "rn_status_str", "rn_last_error",
     "rn_version",
 )
 
@@ -76,6 +77,10 @@ def _load():
     L.rn_retention_chunkwise.restype = i32
     L.rn_retention_recurrent_step.argtypes = [D, vp, vp, vp, vp, vp, vp, vp]
     L.rn_retention_recurrent_step.restype = i32
+    L.rn_retention_chunkwise_varlen.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.rn_retention_chunkwise_varlen.restype = i32
+    L.rn_retention_recurrent_step_at.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.rn_retention_recurrent_step_at.restype = i32
     L.rn_groupnorm_gate.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                     ctypes.c_float, vp, vp]
     L.rn_groupnorm_gate.restype = i32
@@ -121,6 +126,17 @@ def _ptr(t: Optional[torch.Tensor]):
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _out(out, shape, dtype, device, fill=None):
+    """A new output tensor, or the caller's after checking it matches the call."""
+    if out is None:
+        if fill is None:
+            return torch.empty(shape, dtype=dtype, device=device)
+        return torch.full(shape, fill, dtype=dtype, device=device)
+    if tuple(out.shape) != tuple(shape) or out.dtype != dtype:
+        raise ValueError(f"out must be {dtype} {tuple(shape)}; got {out.dtype} {tuple(out.shape)}")
+    return out
 
 
 def _stream(t: torch.Tensor):
@@ -184,8 +200,7 @@ def rn_retention_parallel(q, k, v, gamma, theta, *, gate=None, out=None, out_dty
     flags = _flags(norm_d, norm_r, gn, gate, force_generic)
     d, keep, od = _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos0, qk_scale, gn_eps,
                             gn_weight, gn_bias)
-    if out is None:
-        out = torch.empty(v.shape, dtype=od, device=v.device)
+    out = _out(out, v.shape, od, v.device)
     need = int(lib.rn_parallel_workspace_bytes(ctypes.byref(d)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -215,19 +230,50 @@ def rn_chunkwise_workspace_bytes(q, v, gamma, theta, chunk, *, gn=False, gate=No
     return int(lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), chunk))
 
 
+def _seq_array(t, B, dtype, name):
+    if t is None:
+        return None
+    if t.dtype != dtype or tuple(t.shape) != (B,):
+        raise ValueError(f"{name} must be a {dtype} tensor of shape [{B}]")
+    return _ptr(t)
+
+
 def rn_retention_chunkwise(q, k, v, gamma, theta, chunk, *, gate=None, state_in=None,
                            state_out=None, out=None, out_dtype=None, workspace=None, pos0=0,
                            qk_scale=1.0, gn=False, gn_eps=1e-5, gn_weight=None, gn_bias=None,
                            force_generic=False):
     """Chunkwise form; returns (out, state_out). ``state_out`` may be a tensor (written),
     True (allocated), or None/False (discarded)."""
+    return _chunkwise(q, k, v, gamma, theta, chunk, None, None, gate, state_in, state_out, out,
+                      out_dtype, workspace, pos0, qk_scale, gn, gn_eps, gn_weight, gn_bias,
+                      force_generic)
+
+
+def rn_retention_chunkwise_varlen(q, k, v, gamma, theta, chunk, *, pos=None, lengths=None,
+                                  gate=None, state_in=None, state_out=None, out=None,
+                                  out_dtype=None, workspace=None, pos0=0, qk_scale=1.0, gn=False,
+                                  gn_eps=1e-5, gn_weight=None, gn_bias=None, force_generic=False):
+    """Chunkwise form over a padded batch: sequence b holds ``lengths[b]`` tokens
+    (device int32 [B]) starting at position ``pos[b]`` (device int64 [B]); either may be
+    None (N tokens / ``pos0``). Rows past a sequence's length are not written (a new
+    ``out`` is zero-filled there). Returns (out, state_out)."""
+    if out is None and lengths is not None:
+        od = q.dtype if out_dtype is None else out_dtype
+        out = _out(None, v.shape, od, v.device, fill=0)
+    return _chunkwise(q, k, v, gamma, theta, chunk, pos, lengths, gate, state_in, state_out, out,
+                      out_dtype, workspace, pos0, qk_scale, gn, gn_eps, gn_weight, gn_bias,
+                      force_generic)
+
+
+def _chunkwise(q, k, v, gamma, theta, chunk, pos, lengths, gate, state_in, state_out, out,
+               out_dtype, workspace, pos0, qk_scale, gn, gn_eps, gn_weight, gn_bias,
+               force_generic):
     flags = _flags(False, False, gn, gate, force_generic)
     d, keep, od = _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos0, qk_scale, gn_eps,
                             gn_weight, gn_bias)
     B, H, N, dk = q.shape
     dv = v.shape[-1]
-    if out is None:
-        out = torch.empty(v.shape, dtype=od, device=v.device)
+    out = _out(out, v.shape, od, v.device)
     if state_out is True:
         state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
     elif state_out is False:
@@ -238,9 +284,14 @@ def rn_retention_chunkwise(q, k, v, gamma, theta, chunk, *, gate=None, state_in=
     need = int(lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), chunk))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    _check(lib.rn_retention_chunkwise(ctypes.byref(d), chunk, _ptr(q), _ptr(k), _ptr(v),
-                                      _ptr(gate), _ptr(state_in), _ptr(state_out), _ptr(out),
-                                      _ptr(workspace), workspace.numel(), _stream(q)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(state_in), _ptr(state_out), _ptr(out),
+            _ptr(workspace), workspace.numel(), _stream(q))
+    if pos is None and lengths is None:
+        _check(lib.rn_retention_chunkwise(ctypes.byref(d), chunk, *args))
+    else:
+        _check(lib.rn_retention_chunkwise_varlen(
+            ctypes.byref(d), chunk, _seq_array(pos, B, torch.int64, "pos"),
+            _seq_array(lengths, B, torch.int32, "lengths"), *args))
     return out, state_out
 
 
@@ -254,10 +305,28 @@ def rn_retention_recurrent_step(q, k, v, gamma, theta, state, pos, *, gate=None,
                             gn_weight, gn_bias)
     if state.dtype != torch.float32 or tuple(state.shape) != (q.shape[0], q.shape[1], q.shape[3], v.shape[3]):
         raise ValueError("state must be float32 [B,H,d_k,d_v]")
-    if out is None:
-        out = torch.empty(v.shape, dtype=od, device=v.device)
+    out = _out(out, v.shape, od, v.device)
     _check(lib.rn_retention_recurrent_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
                                            _ptr(state), _ptr(out), _stream(q)))
+    return out
+
+
+def rn_retention_recurrent_step_at(q, k, v, gamma, theta, state, pos, *, gate=None, out=None,
+                                   out_dtype=None, qk_scale=1.0, gn=False, gn_eps=1e-5,
+                                   gn_weight=None, gn_bias=None):
+    """One decode step with the token of sequence b at position ``pos[b]`` (device int64
+    [B]); otherwise as rn_retention_recurrent_step. Returns out [B,H,1,d_v]."""
+    flags = _flags(False, False, gn, gate, False)
+    d, keep, od = _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, 0, qk_scale, gn_eps,
+                            gn_weight, gn_bias)
+    if state.dtype != torch.float32 or tuple(state.shape) != (q.shape[0], q.shape[1], q.shape[3], v.shape[3]):
+        raise ValueError("state must be float32 [B,H,d_k,d_v]")
+    pp = _seq_array(pos, q.shape[0], torch.int64, "pos")
+    if pp is None:
+        raise ValueError("pos is required")
+    out = _out(out, v.shape, od, v.device)
+    _check(lib.rn_retention_recurrent_step_at(ctypes.byref(d), pp, _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(gate), _ptr(state), _ptr(out), _stream(q)))
     return out
 
 
@@ -265,8 +334,7 @@ def rn_groupnorm_gate(x, gate=None, weight=None, bias=None, eps=1e-5, *, out=Non
     """Per-head GroupNorm over the last axis of x [B,H,N,d_v] (+ swish gate)."""
     B, H, N, dv = x.shape
     od = x.dtype if out_dtype is None else out_dtype
-    if out is None:
-        out = torch.empty(x.shape, dtype=od, device=x.device)
+    out = _out(out, x.shape, od, x.device)
     if gate is not None and (gate.shape != x.shape or gate.dtype != x.dtype):
         raise ValueError("gate must match x in shape and dtype")
     _check(lib.rn_groupnorm_gate(B, H, N, dv, _dtype_code(x.dtype), _dtype_code(od), _ptr(x),

@@ -169,8 +169,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
 }
 // Buffer resource over [base, base + bytes): loads past the end return 0 and stores
-// past the end are dropped, which is how ragged tails, rows beyond N and the blocks
-// before the first and after the last one are handled.
+// past the end are dropped, which is how ragged tails, rows past a sequence's length
+// and the blocks before the first and after the last one are handled.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
                                            static_cast<int>(bytes > 0 ? bytes : 0), 0x00020000);
@@ -243,7 +243,6 @@ struct Params {
   int head0;       // first (b*H + h) of this launch group
   int heads;       // heads in this group
   int nS;          // slices per head
-  int nb;          // blocks of 64 tokens
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
@@ -265,13 +264,14 @@ chunkwise_fused(Params P) {
   if (hg >= P.heads) return;
   const int sl = L8 % NS;                // d_v slice
   constexpr int nS = NS;
-  const int nb = P.nb;
+  const int bh = P.head0 + hg;
+  const int h = bh % a.H;
+  const int N = a.N, DV = a.dv;          // N: row stride of the padded layout
+  const int len = seq_len(a, bh / a.H);  // tokens of this sequence
+  const int nb = (len + kT - 1) / kT;    // blocks of 64 tokens
   // iterations: the E waves store block nb-1 at iteration nb-1+kLag; the count is
   // rounded up to a multiple of 4 (the E waves' loop body holds four iterations)
   const int n_iter = (nb + kLag + 3) & ~3;
-  const int bh = P.head0 + hg;
-  const int h = bh % a.H;
-  const int N = a.N, DV = a.dv;
   const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, g = l >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
 
@@ -465,7 +465,7 @@ chunkwise_fused(Params P) {
           ktf[ta][e] = as_f16x8(u);
         }
       }
-      const float gL = exp2f(lg * float(min(kT, N - i * kT)));
+      const float gL = exp2f(lg * float(min(kT, len - i * kT)));
       // per 16-column tile: cross term from the old state, intra term, partial output
       // to LDS, then the carry of that tile's state columns
 #pragma unroll
@@ -544,9 +544,9 @@ chunkwise_fused(Params P) {
         ss[u][i] = 0.f;
       }
     }
-    const int64_t p_row0 = a.pos0 + r_lo + pr;   // position of the thread's row u = 0 in block 0
+    const int64_t p_row0 = seq_pos0(a, bh / a.H) + r_lo + pr;   // position of row u = 0 in block 0
     const size_t qk_head = size_t(bh) * N * kDK;
-    const int64_t qk_bytes = int64_t(N) * kDK * 2;
+    const int64_t qk_bytes = int64_t(len) * kDK * 2;
     const __amdgpu_buffer_rsrc_t r_q = range_rsrc(P.q + qk_head, qk_bytes);
     const __amdgpu_buffer_rsrc_t r_k = range_rsrc(P.k + qk_head, qk_bytes);
     const __amdgpu_buffer_rsrc_t r_ring = range_rsrc(ring, int64_t(kRingPerHead));
@@ -599,7 +599,8 @@ chunkwise_fused(Params P) {
     };
 
     // V slice: thread loads rows vs0..vs0+3, columns vd0..vd0+3 (bf16) of the slice
-    const int64_t slice_bytes = (int64_t(N) * DV - sl * kSl) * 2;  // to the end of this head
+    // to the end of the sequence's last row (rows past it read as zeros, stores dropped)
+    const int64_t slice_bytes = max(int64_t(len) * DV - sl * kSl, int64_t(0)) * 2;
     const size_t slice0 = size_t(bh) * N * DV + sl * kSl;
     const __amdgpu_buffer_rsrc_t r_v = range_rsrc(P.v + slice0, slice_bytes);
     const __amdgpu_buffer_rsrc_t r_g = range_rsrc(has_gate ? P.gate + slice0 : P.v + slice0, slice_bytes);
@@ -865,9 +866,13 @@ int heads_per_group(int nS) {
 }  // namespace
 
 // The decay factors gamma^(+-32) folded into the half operands need gamma^32 >= 2^-6.
+// Buffer offsets within one head's rows are 32-bit: N d_v (4-byte output) and N d_k
+// (2-byte input) must stay below 2^31 bytes.
 bool chunkwise_mfma_supported(const CallArgs& a, int in_dt) {
   if (in_dt != RN_BF16 || a.dk != kDK ||
       !(a.dv == 64 || a.dv == 128 || a.dv == 256 || a.dv == 512))
+    return false;
+  if (int64_t(a.N) * a.dv * 4 >= (int64_t(1) << 31) || int64_t(a.N) * kDK * 2 >= (int64_t(1) << 31))
     return false;
   for (int h = 0; h < a.H; ++h)
     if (!(a.hp.log2g[h] * 32.0f >= -6.0f)) return false;
@@ -893,7 +898,6 @@ hipError_t launch_chunkwise_mfma(const CallArgs& a, int out_dt, const void* q, c
   Params p;
   p.a = a;
   p.nS = nS;
-  p.nb = (a.N + kT - 1) / kT;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);

@@ -1,5 +1,7 @@
 // One recurrent retention step (decode): S <- gamma S + Kh^T v in place, o = alpha Qh S
-// (hwhale notes: recurrent equations and the RecurrentRetention listing).
+// (hwhale notes: recurrent equations and the RecurrentRetention listing). The token of
+// sequence b sits at the descriptor's position, or at pos[b] when the call passes one
+// position per sequence (batched decode of sequences of different lengths).
 //
 // HBM-bound: the float32 state is read and written once per step; everything else is
 // a few KB. One block owns one (b, h) state of d_k x d_v floats. Thread (group g,
@@ -36,9 +38,10 @@ __global__ void __launch_bounds__(256) decode_step(CallArgs a, const void* q, co
   const int bh = blockIdx.x;
   const int h = bh % a.H;
   const int dk = a.dk, dv = a.dv;
+  const int64_t pos = seq_pos0(a, bh / a.H);
   for (int j = threadIdx.x; j < dk / 2; j += 256) {
     float c, s;
-    angle_cs(a.pos0, a.ap.theta[j], &c, &s);
+    angle_cs(pos, a.ap.theta[j], &c, &s);
     const int64_t o = static_cast<int64_t>(bh) * dk + 2 * j;
     float q0 = Elem<IN>::load(q, o), q1 = Elem<IN>::load(q, o + 1);
     float k0 = Elem<IN>::load(k, o), k1 = Elem<IN>::load(k, o + 1);
@@ -133,9 +136,10 @@ __global__ void __launch_bounds__(kFastThreads) decode_step_pipelined(CallArgs a
   const int h = bh % a.H;
   const int dk = a.dk;
   const int tid = threadIdx.x, cq = tid % NQ, grp = tid / NQ;
+  const int64_t pos = seq_pos0(a, bh / a.H);
   for (int j = tid; j < dk / 2; j += kFastThreads) {
     float c, s;
-    angle_cs(a.pos0, a.ap.theta[j], &c, &s);
+    angle_cs(pos, a.ap.theta[j], &c, &s);
     const int64_t o = static_cast<int64_t>(bh) * dk + 2 * j;
     float q0 = Elem<IN>::load(q, o), q1 = Elem<IN>::load(q, o + 1);
     float k0 = Elem<IN>::load(k, o), k1 = Elem<IN>::load(k, o + 1);

@@ -92,7 +92,9 @@ __global__ void __launch_bounds__(256) generic_parallel(CallArgs a, const void* 
 //   rows t:  O_t = alpha [ sum_{c0<=s<=t} gamma^(t-s) (Qh_t.Kh_s) V_s
 //                         + gamma^(t-c0+1) Qh_t S ]
 //   then     S <- gamma^L S + sum_j gamma^(L-1-j) Kh_j^T V_j
-// (hwhale notes: chunkwise equation and ChunkwiseRetention listing).
+// (hwhale notes: chunkwise equation and ChunkwiseRetention listing). Sequence b runs
+// over its own number of tokens and from its own starting position when the call
+// gives them; rows past its length are left untouched.
 template <int IN, int OUT>
 __global__ void __launch_bounds__(256) generic_chunkwise(CallArgs a, const void* q, const void* k,
                                                          const void* v, const void* gate,
@@ -107,6 +109,8 @@ __global__ void __launch_bounds__(256) generic_chunkwise(CallArgs a, const void*
   __shared__ float red[4];
   const int h = blockIdx.x, b = blockIdx.y;
   const int dk = a.dk, dv = a.dv, N = a.N, C = a.chunk;
+  const int len = seq_len(a, b);          // tokens of this sequence (rows of stride N)
+  const int64_t p0 = seq_pos0(a, b);
   const int64_t bh = static_cast<int64_t>(b) * a.H + h;
   const int64_t nS = static_cast<int64_t>(dk) * dv;
   float* S = ws + bh * nS;
@@ -114,10 +118,10 @@ __global__ void __launch_bounds__(256) generic_chunkwise(CallArgs a, const void*
   __syncthreads();
   const float lg = a.hp.log2g[h];
   const int c0 = threadIdx.x, c1 = threadIdx.x + 256;
-  for (int cs = 0; cs < N; cs += C) {
-    const int L = min(C, N - cs);
+  for (int cs = 0; cs < len; cs += C) {
+    const int L = min(C, len - cs);
     for (int t = cs; t < cs + L; ++t) {
-      const int64_t pt = a.pos0 + t;
+      const int64_t pt = p0 + t;
       for (int j = threadIdx.x; j < dk / 2; j += 256)
         rot_pair<IN>(q, (bh * N + t) * dk, j, pt, a.ap.theta[j], &qh[2 * j], &qh[2 * j + 1]);
       __syncthreads();
@@ -130,7 +134,7 @@ __global__ void __launch_bounds__(256) generic_chunkwise(CallArgs a, const void*
           float dot = 0.f;
           for (int j = 0; j < dk / 2; ++j) {
             float k0, k1;
-            rot_pair<IN>(k, koff, j, a.pos0 + s, a.ap.theta[j], &k0, &k1);
+            rot_pair<IN>(k, koff, j, p0 + s, a.ap.theta[j], &k0, &k1);
             dot += qh[2 * j] * k0 + qh[2 * j + 1] * k1;
           }
           val = dot * gpow(lg, static_cast<float>(t - s));
@@ -167,7 +171,7 @@ __global__ void __launch_bounds__(256) generic_chunkwise(CallArgs a, const void*
         const int s = cs + j0 + jj;
         const float zeta = gpow(lg, static_cast<float>(L - 1 - (j0 + jj)));
         float k0, k1;
-        rot_pair<IN>(k, (bh * N + s) * dk, p, a.pos0 + s, a.ap.theta[p], &k0, &k1);
+        rot_pair<IN>(k, (bh * N + s) * dk, p, p0 + s, a.ap.theta[p], &k0, &k1);
         kt[jj][2 * p] = zeta * k0;
         kt[jj][2 * p + 1] = zeta * k1;
       }

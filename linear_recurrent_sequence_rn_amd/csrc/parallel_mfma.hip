@@ -430,8 +430,10 @@ parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
 
 }  // namespace
 
+// Buffer offsets within one head's rows are 32-bit: N d_v 2-byte elements must stay
+// below 2^31 bytes.
 bool parallel_mfma_supported(const CallArgs& a, int in_dt) {
-  return in_dt == RN_BF16 && a.dk == kDK && a.dv == kDV;
+  return in_dt == RN_BF16 && a.dk == kDK && a.dv == kDV && int64_t(a.N) * kDV * 2 < (int64_t(1) << 31);
 }
 
 size_t parallel_mfma_ws_bytes(const CallArgs& a) {

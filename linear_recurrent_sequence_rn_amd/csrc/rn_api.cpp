@@ -91,6 +91,18 @@ rn_status check_ptrs(const rn_desc* d, const void* q, const void* k, const void*
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Device arrays of the serving entry points: only their alignment can be checked on
+// the host; their values are read by the kernels.
+rn_status check_seq_arrays(const int64_t* pos, const int32_t* lengths, rn::CallArgs* a) {
+  if (reinterpret_cast<uintptr_t>(pos) % alignof(int64_t))
+    return fail(RN_ERR_INVALID_ARG, "pos must be 8-byte aligned");
+  if (reinterpret_cast<uintptr_t>(lengths) % alignof(int32_t))
+    return fail(RN_ERR_INVALID_ARG, "lengths must be 4-byte aligned");
+  a->pos = pos;
+  a->lens = lengths;
+  return RN_OK;
+}
+
 size_t generic_ws_bytes(const rn_desc* d) {
   return align256(size_t(d->B) * d->H * d->d_k * d->d_v * sizeof(float));
 }
@@ -160,13 +172,15 @@ size_t rn_chunkwise_workspace_bytes(const rn_desc* desc, int32_t chunk) {
   return generic_ws_bytes(desc);
 }
 
-rn_status rn_retention_chunkwise(const rn_desc* desc, int32_t chunk, const void* q, const void* k,
-                                 const void* v, const void* gate, const float* state_in,
-                                 float* state_out, void* out, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+static rn_status chunkwise_call(const rn_desc* desc, int32_t chunk, const int64_t* pos,
+                                const int32_t* lengths, const void* q, const void* k,
+                                const void* v, const void* gate, const float* state_in,
+                                float* state_out, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   rn::CallArgs a;
   rn_status s = check_desc(desc, Form::kChunkwise, &a);
   if (s != RN_OK) return s;
+  if ((s = check_seq_arrays(pos, lengths, &a)) != RN_OK) return s;
   if (chunk < 1) return fail(RN_ERR_INVALID_ARG, "chunk=%d must be >= 1", chunk);
   if ((s = check_ptrs(desc, q, k, v, gate, out)) != RN_OK) return s;
   const size_t need = rn_chunkwise_workspace_bytes(desc, chunk);
@@ -187,12 +201,30 @@ rn_status rn_retention_chunkwise(const rn_desc* desc, int32_t chunk, const void*
                     "chunkwise launch");
 }
 
-rn_status rn_retention_recurrent_step(const rn_desc* desc, const void* q, const void* k,
-                                      const void* v, const void* gate, float* state, void* out,
-                                      void* stream) {
+rn_status rn_retention_chunkwise(const rn_desc* desc, int32_t chunk, const void* q, const void* k,
+                                 const void* v, const void* gate, const float* state_in,
+                                 float* state_out, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return chunkwise_call(desc, chunk, nullptr, nullptr, q, k, v, gate, state_in, state_out, out,
+                        workspace, workspace_bytes, stream);
+}
+
+rn_status rn_retention_chunkwise_varlen(const rn_desc* desc, int32_t chunk, const int64_t* pos,
+                                        const int32_t* lengths, const void* q, const void* k,
+                                        const void* v, const void* gate, const float* state_in,
+                                        float* state_out, void* out, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return chunkwise_call(desc, chunk, pos, lengths, q, k, v, gate, state_in, state_out, out,
+                        workspace, workspace_bytes, stream);
+}
+
+static rn_status step_call(const rn_desc* desc, const int64_t* pos, const void* q, const void* k,
+                           const void* v, const void* gate, float* state, void* out,
+                           void* stream) {
   rn::CallArgs a;
   rn_status s = check_desc(desc, Form::kStep, &a);
   if (s != RN_OK) return s;
+  if ((s = check_seq_arrays(pos, nullptr, &a)) != RN_OK) return s;
   if ((s = check_ptrs(desc, q, k, v, gate, out)) != RN_OK) return s;
   if (!state) return fail(RN_ERR_INVALID_ARG, "state pointer is NULL");
   if (reinterpret_cast<uintptr_t>(state) % 16)
@@ -202,6 +234,19 @@ rn_status rn_retention_recurrent_step(const rn_desc* desc, const void* q, const 
   return hip_status(rn::launch_decode_step(a, desc->in_dtype, desc->out_dtype, q, k, v, gate,
                                            state, out, st),
                     "recurrent step launch");
+}
+
+rn_status rn_retention_recurrent_step(const rn_desc* desc, const void* q, const void* k,
+                                      const void* v, const void* gate, float* state, void* out,
+                                      void* stream) {
+  return step_call(desc, nullptr, q, k, v, gate, state, out, stream);
+}
+
+rn_status rn_retention_recurrent_step_at(const rn_desc* desc, const int64_t* pos, const void* q,
+                                         const void* k, const void* v, const void* gate,
+                                         float* state, void* out, void* stream) {
+  if (!pos) return fail(RN_ERR_INVALID_ARG, "pos is NULL");
+  return step_call(desc, pos, q, k, v, gate, state, out, stream);
 }
 
 rn_status rn_groupnorm_gate(int32_t B, int32_t H, int32_t N, int32_t d_v, rn_dtype in_dtype,

@@ -119,9 +119,21 @@ struct CallArgs {
   uint32_t flags;
   const float* gn_w;   // device [H*dv] or null
   const float* gn_b;   // device [H*dv] or null
+  const int64_t* pos;  // device [B]: position of each sequence's token 0, or null (pos0)
+  const int32_t* lens; // device [B]: tokens of each sequence, or null (N)
   HeadParams hp;
   AngleParams ap;
 };
+
+// Absolute position of token 0 of sequence b.
+__device__ __forceinline__ int64_t seq_pos0(const CallArgs& a, int b) {
+  return a.pos ? a.pos[b] : a.pos0;
+}
+// Tokens of sequence b, clamped to [0, N] (the rows of the padded layout), so that a
+// length out of range can never move an access outside the caller's buffers.
+__device__ __forceinline__ int seq_len(const CallArgs& a, int b) {
+  return a.lens ? min(max(a.lens[b], 0), a.N) : a.N;
+}
 
 // Sum over a block of NT threads (NT/64 waves). `red` is NT/64 floats of LDS; every
 // thread receives the total. Ends with the LDS slots free for reuse after a barrier.

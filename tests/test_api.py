@@ -63,6 +63,16 @@ def step(d, state=FAKE):
                                               FAKE, None)
 
 
+def chk_varlen(d, pos=FAKE, lengths=FAKE, chunk=4, ws_bytes=1 << 30):
+    return rn.lib.rn_retention_chunkwise_varlen(ctypes.byref(d), chunk, pos, lengths, FAKE, FAKE,
+                                                FAKE, FAKE, None, None, FAKE, FAKE, ws_bytes, None)
+
+
+def step_at(d, pos=FAKE, state=FAKE):
+    return rn.lib.rn_retention_recurrent_step_at(ctypes.byref(d), pos, FAKE, FAKE, FAKE, FAKE,
+                                                 state, FAKE, None)
+
+
 BAD_DESCS = [
     (dict(B=0), rn.RN_ERR_INVALID_ARG),
     (dict(N=0), rn.RN_ERR_INVALID_ARG),
@@ -90,8 +100,11 @@ def test_invalid_descriptors_rejected_everywhere(kw, code):
     assert par(d) == code, rn.lib.rn_last_error()
     assert rn.lib.rn_last_error() != b""
     assert chk(d) == code
+    assert chk_varlen(d) == code
+    assert chk_varlen(d, pos=None, lengths=None) == code
     d1, keep1 = desc(**{**kw, "N": 1} if "N" not in kw else kw)
     assert step(d1) == code
+    assert step_at(d1) == code
     assert rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), 4) == 0
     assert rn.lib.rn_parallel_workspace_bytes(ctypes.byref(d)) == 0
 
@@ -155,3 +168,39 @@ def test_groupnorm_errors():
     assert f(1, 1, 1, 8, rn.RN_F32, rn.RN_F32, None, None, None, None, 1e-5, FAKE, None) == rn.RN_ERR_INVALID_ARG
     assert f(1, 1, 1, 8, rn.RN_F32, rn.RN_F32, FAKE, None, None, None, -1.0, FAKE, None) == rn.RN_ERR_INVALID_ARG
     assert f(1, 1, 1, 8, rn.RN_F32, rn.RN_BF16, FAKE, None, None, None, 1e-5, FAKE, None) == rn.RN_ERR_INVALID_ARG  # in place, dtype change
+
+
+def test_serving_entry_point_errors():
+    """Per-sequence arrays are device pointers: their alignment is checked on the host,
+    the decode variant requires its positions, and the common checks still apply."""
+    d, keep = desc()
+    assert chk_varlen(d, pos=ctypes.c_void_p(0x1004)) == rn.RN_ERR_INVALID_ARG    # int64 misaligned
+    assert b"pos" in rn.lib.rn_last_error()
+    assert chk_varlen(d, lengths=ctypes.c_void_p(0x1002)) == rn.RN_ERR_INVALID_ARG
+    assert b"lengths" in rn.lib.rn_last_error()
+    assert chk_varlen(d, chunk=0) == rn.RN_ERR_INVALID_ARG
+    need = rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), 4)
+    assert chk_varlen(d, ws_bytes=need - 1) == rn.RN_ERR_WORKSPACE
+    d1, keep1 = desc(N=1)
+    assert step_at(d1, pos=None) == rn.RN_ERR_INVALID_ARG
+    assert step_at(d1, pos=ctypes.c_void_p(0x1004)) == rn.RN_ERR_INVALID_ARG
+    assert step_at(d1, state=None) == rn.RN_ERR_INVALID_ARG
+    d2, keep2 = desc(N=2)
+    assert step_at(d2) == rn.RN_ERR_INVALID_ARG                          # one token per call
+
+
+def test_binding_checks_sequence_arrays():
+    """The Python layer rejects per-sequence arrays of the wrong dtype or shape before
+    any call (CPU tensors never reach the library)."""
+    import torch
+    q = torch.zeros(2, 1, 4, 16, dtype=torch.bfloat16)
+    v = torch.zeros(2, 1, 4, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        rn._seq_array(torch.zeros(3, dtype=torch.int64), 2, torch.int64, "pos")
+    with pytest.raises(ValueError):
+        rn._seq_array(torch.zeros(2, dtype=torch.int32), 2, torch.int64, "pos")
+    with pytest.raises(ValueError):   # tensors must be on the GPU
+        rn._seq_array(torch.zeros(2, dtype=torch.int32), 2, torch.int32, "lengths")
+    with pytest.raises(ValueError):
+        rn.rn_retention_recurrent_step_at(q[:, :, :1], q[:, :, :1], v[:, :, :1], [0.9], np.ones(8),
+                                          torch.zeros(2, 1, 16, 16), None)
