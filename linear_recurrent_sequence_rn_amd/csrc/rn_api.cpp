@@ -30,8 +30,8 @@ rn_status hip_status(hipError_t e, const char* what) {
 
 enum class Form { kParallel, kChunkwise, kStep };
 
-constexpr uint32_t kKnownFlags =
-    RN_NORM_D_ROW | RN_NORM_R_ROW | RN_EPI_GN | RN_EPI_GATE | RN_FORCE_GENERIC;
+constexpr uint32_t kKnownFlags = RN_NORM_D_ROW | RN_NORM_R_ROW | RN_EPI_GN | RN_EPI_GATE |
+                                 RN_FORCE_GENERIC | RN_CHUNK_PARALLEL;
 
 bool dtype_ok(rn_dtype d) { return d == RN_F32 || d == RN_BF16; }
 
@@ -161,15 +161,28 @@ rn_status rn_retention_parallel(const rn_desc* desc, const void* q, const void* 
                     "parallel launch");
 }
 
-static bool use_mfma_chunkwise(const rn_desc* d, const rn::CallArgs& a) {
-  return !(d->flags & RN_FORCE_GENERIC) && rn::chunkwise_mfma_supported(a, d->in_dtype);
+// Chunkwise schedules: the sequential fused kernel (default where it applies), the
+// chunk-parallel pair (on request, or where the sequential kernel's decay range does not
+// hold), the generic float32 kernel (everything else).
+enum class ChunkPath { kParallelPair, kSequential, kGeneric };
+
+static ChunkPath chunk_path(const rn_desc* d, const rn::CallArgs& a) {
+  if (d->flags & RN_FORCE_GENERIC) return ChunkPath::kGeneric;
+  const bool pair = rn::chunkwise_cp_supported(a, d->in_dtype);
+  if ((d->flags & RN_CHUNK_PARALLEL) && pair) return ChunkPath::kParallelPair;
+  if (rn::chunkwise_mfma_supported(a, d->in_dtype)) return ChunkPath::kSequential;
+  if (pair) return ChunkPath::kParallelPair;
+  return ChunkPath::kGeneric;
 }
 
 size_t rn_chunkwise_workspace_bytes(const rn_desc* desc, int32_t chunk) {
   rn::CallArgs a;
   if (chunk < 1 || check_desc(desc, Form::kChunkwise, &a) != RN_OK) return 0;
-  if (use_mfma_chunkwise(desc, a)) return align256(rn::chunkwise_mfma_ws_bytes(a));
-  return generic_ws_bytes(desc);
+  switch (chunk_path(desc, a)) {
+    case ChunkPath::kParallelPair: return align256(rn::chunkwise_cp_ws_bytes(a));
+    case ChunkPath::kSequential: return align256(rn::chunkwise_mfma_ws_bytes(a));
+    default: return generic_ws_bytes(desc);
+  }
 }
 
 static rn_status chunkwise_call(const rn_desc* desc, int32_t chunk, const int64_t* pos,
@@ -191,10 +204,15 @@ static rn_status chunkwise_call(const rn_desc* desc, int32_t chunk, const int64_
   a.chunk = chunk;
   g_err[0] = 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (use_mfma_chunkwise(desc, a))
+  const ChunkPath path = chunk_path(desc, a);
+  if (path == ChunkPath::kParallelPair)
+    return hip_status(rn::launch_chunkwise_cp(a, desc->out_dtype, q, k, v, gate, state_in,
+                                              state_out, out, workspace, workspace_bytes, st),
+                      "chunkwise (chunk-parallel) launch");
+  if (path == ChunkPath::kSequential)
     return hip_status(rn::launch_chunkwise_mfma(a, desc->out_dtype, q, k, v, gate, state_in,
                                                 state_out, out, workspace, workspace_bytes, st),
-                      "chunkwise (MFMA) launch");
+                      "chunkwise (sequential MFMA) launch");
   return hip_status(rn::launch_generic_chunkwise(a, desc->in_dtype, desc->out_dtype, q, k, v,
                                                  gate, state_in, state_out, out,
                                                  static_cast<float*>(workspace), st),

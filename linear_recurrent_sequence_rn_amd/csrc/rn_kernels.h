@@ -28,6 +28,13 @@ hipError_t launch_chunkwise_mfma(const CallArgs& a, int out_dt, const void* q, c
                                  float* s_out, void* out, void* ws, size_t ws_bytes,
                                  hipStream_t st);
 
+// Chunk-parallel chunkwise pair: state snapshots, then outputs (bf16, d_k 256, d_v 512).
+bool chunkwise_cp_supported(const CallArgs& a, int in_dt);
+size_t chunkwise_cp_ws_bytes(const CallArgs& a);
+hipError_t launch_chunkwise_cp(const CallArgs& a, int out_dt, const void* q, const void* k,
+                               const void* v, const void* gate, const float* s_in, float* s_out,
+                               void* out, void* ws, size_t ws_bytes, hipStream_t st);
+
 // MFMA parallel form (bf16 inputs, d_k = 256, d_v = 512).
 bool parallel_mfma_supported(const CallArgs& a, int in_dt);
 size_t parallel_mfma_ws_bytes(const CallArgs& a);

@@ -1,4 +1,6 @@
-"""GPU parity of the fused MFMA chunkwise kernel (bf16 q/k/v, d_k = 256).
+"""GPU parity of the MFMA chunkwise schedules (bf16 q/k/v, d_k = 256): the sequential
+single kernel (the default) and the chunk-parallel pair (RN_CHUNK_PARALLEL: state
+snapshots, then outputs; d_v = 512).
 
 Tolerances (half-precision MFMA operands, fp32 accumulation):
   * raw outputs and final states: per (b, h), ||gpu - ref||_inf <= 1e-2 ||ref||_inf.
@@ -63,19 +65,24 @@ def counters(ws, heads):
     return c
 
 
-@pytest.mark.parametrize("N,pos0", [(200, 0), (64, 5), (1, 70000), (129, 3)])
-def test_raw_output_and_state(N, pos0):
+SCHEDULES = [False, True]   # chunk-parallel pair?
+
+
+@pytest.mark.parametrize("cp", SCHEDULES)
+@pytest.mark.parametrize("N,pos0", [(200, 0), (64, 5), (1, 70000), (129, 3), (700, 11)])
+def test_raw_output_and_state(N, pos0, cp):
     w = wl(N=N, state_std=0.05)
     x = W.make_inputs(w)
     out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
                                          x["theta"], 64, state_in=dev(x["state"]), state_out=True,
-                                         out_dtype=torch.float32, pos0=pos0)
+                                         out_dtype=torch.float32, pos0=pos0, chunk_parallel=cp)
     ref, Sref = O.chunkwise(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 64, pos0, 1.0, x["state"])
     assert rel_inf(out.cpu(), ref) <= 1e-2
     assert rel_inf(S.cpu(), Sref) <= 1e-2
 
 
-def test_gn_gate_affine_fp32_and_bf16_out():
+@pytest.mark.parametrize("cp", SCHEDULES)
+def test_gn_gate_affine_fp32_and_bf16_out(cp):
     w = wl(N=333, gate=True)
     x = W.make_inputs(w)
     H, dv = 2, 512
@@ -86,7 +93,8 @@ def test_gn_gate_affine_fp32_and_bf16_out():
     for od in (torch.float32, torch.bfloat16):
         out, _ = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
                                              x["theta"], 256, gate=dev(x["gate"]), gn=True,
-                                             gn_weight=dev(gw), gn_bias=dev(gb), out_dtype=od)
+                                             gn_weight=dev(gw), gn_bias=dev(gb), out_dtype=od,
+                                             chunk_parallel=cp)
         check_gated(out.cpu(), ref, x["gate"])
 
 
@@ -128,18 +136,22 @@ def test_exchange_diagnostics_and_determinism():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
-def test_more_heads_than_one_launch():
-    """48 heads x 8 slices exceed one co-resident launch: the heads run in groups."""
-    w = wl(B=3, H=16, N=70)
+@pytest.mark.parametrize("cp", SCHEDULES)
+def test_more_heads_than_one_launch(cp):
+    """80 heads: more than one co-resident launch of the sequential kernel (48 heads x 8
+    slices fill 256 CUs) and more than one 64-head group of the chunk-parallel pair."""
+    w = wl(B=5, H=16, N=70)
     x = W.make_inputs(w)
     out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
-                                         x["theta"], 64, state_out=True, out_dtype=torch.float32)
+                                         x["theta"], 64, state_out=True, out_dtype=torch.float32,
+                                         chunk_parallel=cp)
     ref, Sref = O.chunkwise(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 64)
     assert rel_inf(out.cpu(), ref) <= 1e-2
     assert rel_inf(S.cpu(), Sref) <= 1e-2
 
 
-def test_6p7b_training_shape_sampled_heads():
+@pytest.mark.parametrize("cp", SCHEDULES)
+def test_6p7b_training_shape_sampled_heads(cp):
     """The 6.7B-shaped training workload (B=2, H=16, N=8192, chunk 256, GroupNorm + gate)
     in the launch configuration the benchmark times; three sampled heads checked in full
     against the oracle (outputs and final states)."""
@@ -147,7 +159,7 @@ def test_6p7b_training_shape_sampled_heads():
     x = W.make_inputs(w)
     out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
                                          x["theta"], w.chunk, gate=dev(x["gate"]), gn=True,
-                                         state_out=True, out_dtype=torch.float32)
+                                         state_out=True, out_dtype=torch.float32, chunk_parallel=cp)
     out, S = out.cpu(), S.cpu()
     assert torch.isfinite(out).all()
     for b, h in ((0, 0), (1, 15), (0, 9)):
@@ -158,17 +170,21 @@ def test_6p7b_training_shape_sampled_heads():
         assert rel_inf(S[sl], Sref) <= 1e-2
 
 
-def test_long_sequence_sampled_head():
+@pytest.mark.parametrize("cp", SCHEDULES)
+def test_long_sequence_sampled_head(cp):
     """Long-sequence workload (B=1, H=16, N=65536, chunk 512, GroupNorm): head 11 checked
-    in full; workspace stays the N-independent size."""
+    in full; the workspace does not grow with N (the chunk-parallel pair runs 8 windows of
+    32 chunks and carries the state between them)."""
     w = W.WORKLOADS["chunkwise_long"]
     x = W.make_inputs(w)
-    n64 = rn().rn_chunkwise_workspace_bytes(x["q"][:, :, :64], x["v"][:, :, :64], x["gamma"], x["theta"], 512, gn=True)
-    nfull = rn().rn_chunkwise_workspace_bytes(x["q"], x["v"], x["gamma"], x["theta"], 512, gn=True)
-    assert n64 == nfull
+    sizes = [rn().rn_chunkwise_workspace_bytes(x["q"][:, :, :n], x["v"][:, :, :n], x["gamma"],
+                                               x["theta"], 512, gn=True, chunk_parallel=cp)
+             for n in (8192 + 256, 65536)]
+    assert sizes[0] == sizes[1]
     args = (dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"], w.chunk)
-    out, S = rn().rn_retention_chunkwise(*args, gn=True, state_out=True, out_dtype=torch.float32)
-    out2, S2 = rn().rn_retention_chunkwise(*args, gn=True, state_out=True, out_dtype=torch.float32)
+    kw = dict(gn=True, state_out=True, out_dtype=torch.float32, chunk_parallel=cp)
+    out, S = rn().rn_retention_chunkwise(*args, **kw)
+    out2, S2 = rn().rn_retention_chunkwise(*args, **kw)
     assert torch.equal(out, out2) and torch.equal(S, S2), "runs differ: exchange race"
     del out2, S2
     out, S = out.cpu(), S.cpu()
@@ -177,3 +193,46 @@ def test_long_sequence_sampled_head():
     raw, Sref = O.chunkwise(x["q"][sl], x["k"][sl], x["v"][sl], x["gamma"][h:h + 1], x["theta"], 2048)
     check_gated(out[sl], O.group_norm(raw), None)
     assert rel_inf(S[sl], Sref) <= 1e-2
+
+
+def test_chunk_parallel_snapshots_are_the_chunk_states():
+    """The chunk-parallel pair's first kernel leaves, in the caller's workspace, the state
+    at the start of every 256-token chunk (rounded to half, stored transposed in pieces of
+    32 d_k rows: [head][chunk][piece][d_v][32]); each is checked against the oracle's state
+    after the chunk's prefix."""
+    w = wl(B=1, H=2, N=600, state_std=0.05)
+    x = W.make_inputs(w)
+    ws = ws_for(x["q"], x["v"], x["gamma"], x["theta"], 256, chunk_parallel=True)
+    rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"], 256,
+                                state_in=dev(x["state"]), workspace=ws, out_dtype=torch.float32,
+                                chunk_parallel=True)
+    torch.cuda.synchronize()
+    snap = ws[: 2 * 32 * 256 * 512 * 2].view(torch.float16).reshape(2, 32, 8, 512, 32)
+    for c in range(3):
+        # [head, piece, d_v, 32] -> [head, piece, 32, d_v] -> S [head, d_k, d_v]
+        got = snap[:, c].permute(0, 1, 3, 2).reshape(2, 256, 512).cpu().to(torch.float64).numpy()[None]
+        if c == 0:
+            ref = O.to64(x["state"])
+        else:
+            sl = slice(0, 256 * c)
+            _, ref = O.chunkwise(x["q"][:, :, sl], x["k"][:, :, sl], x["v"][:, :, sl], x["gamma"],
+                                 x["theta"], 256, 0, 1.0, x["state"])
+        assert rel_inf(got, ref) <= 1e-2, c
+
+
+def test_small_decay_runs_the_chunk_parallel_pair():
+    """A head with gamma^32 < 2^-6 (gamma = 0.8) is outside the sequential kernel's operand
+    range; the default call then takes the chunk-parallel pair, which applies the decay in
+    float32 and carries no such limit. Checked against the oracle, outputs and state."""
+    w = wl(N=300, state_std=0.05)
+    x = W.make_inputs(w)
+    gamma = np.array([0.8, 0.97], dtype=np.float32)
+    n_default = rn().rn_chunkwise_workspace_bytes(x["q"], x["v"], gamma, x["theta"], 64)
+    n_pair = rn().rn_chunkwise_workspace_bytes(x["q"], x["v"], gamma, x["theta"], 64, chunk_parallel=True)
+    assert n_default == n_pair
+    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), gamma, x["theta"], 64,
+                                         state_in=dev(x["state"]), state_out=True,
+                                         out_dtype=torch.float32)
+    ref, Sref = O.chunkwise(x["q"], x["k"], x["v"], gamma, x["theta"], 64, 0, 1.0, x["state"])
+    assert rel_inf(out.cpu(), ref) <= 1e-2
+    assert rel_inf(S.cpu(), Sref) <= 1e-2

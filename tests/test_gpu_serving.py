@@ -111,8 +111,8 @@ CASES = [
 
 
 @pytest.mark.parametrize("lengths,pos", CASES)
-@pytest.mark.parametrize("generic", [False, True])
-def test_chunkwise_varlen_outputs_and_states(lengths, pos, generic):
+@pytest.mark.parametrize("path", ["sequential", "pair", "generic"])
+def test_chunkwise_varlen_outputs_and_states(lengths, pos, path):
     """Each sequence's rows and final state against the oracle's chunkwise form on that
     sequence alone (its length, its positions, its initial state); padded rows keep the
     value they had; a length of 0 hands the initial state through."""
@@ -123,9 +123,10 @@ def test_chunkwise_varlen_outputs_and_states(lengths, pos, generic):
     _, S = rn().rn_retention_chunkwise_varlen(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
                                               x["theta"], 64, pos=posd, lengths=lens,
                                               state_in=dev(x["state"]), state_out=True, out=out,
-                                              out_dtype=torch.float32, force_generic=generic)
+                                              out_dtype=torch.float32, force_generic=path == "generic",
+                                              chunk_parallel=path == "pair")
     out, S = out.cpu(), S.cpu()
-    tol = 1e-4 if generic else 1e-2
+    tol = 1e-4 if path == "generic" else 1e-2
     for b, (L, p) in enumerate(zip(lengths, pos)):
         sb = slice(b, b + 1)
         assert (out[sb, :, L:] == SENTINEL).all(), f"padded rows of sequence {b} written"
