@@ -1,9 +1,13 @@
-"""fp64 CPU oracle for the retention forward pass — TEST INFRASTRUCTURE.
+"""fp64 CPU oracle for the retention forward pass and its gradients — TEST INFRASTRUCTURE.
 
-Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
-this package. It shares no code with the HIP path and the HIP path never calls
-it. Pinned by tests/test_oracle.py (brute force, closed forms, invariants,
-library special cases); no function here is left unpinned.
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import this
+package. It shares no code with the HIP path and the HIP path never calls it. Pinned
+by tests/test_oracle.py (brute force, closed forms, invariants, library special cases)
+and tests/test_oracle_backward.py (gradients against central finite differences of the
+forward oracle); no function here is left unpinned.
 """
 from .retention import *  # noqa: F401,F403
-from .retention import __all__  # noqa: F401
+from .retention import __all__ as _fwd_all
+from .backward import backward  # noqa: F401
+
+__all__ = list(_fwd_all) + ["backward"]
