@@ -196,6 +196,38 @@ rn_status rn_retention_recurrent_step_at(const rn_desc* desc, const int64_t* pos
                                          void* stream);
 
 /*
+ * Bytes of device workspace rn_retention_chunkwise_backward needs for `desc`: the state
+ * at every 256-token chunk start and the gradient reaching it (float32, d_k x d_v each,
+ * per head), and the gradient of the pre-GroupNorm output (float32 [B,H,N,d_v]).
+ * Returns 0 for an invalid descriptor.
+ */
+size_t rn_chunkwise_backward_workspace_bytes(const rn_desc* desc, int32_t chunk);
+
+/*
+ * Gradients of the chunkwise call (same descriptor, inputs and chunk as the forward call)
+ * given the gradient of a loss with respect to its output and, optionally, its final
+ * state: the chunkwise recurrence differentiated, the GroupNorm and gate included
+ * (hwhale notes: chunkwise and recurrent equations, ChunkwiseRetention listing; GroupNorm
+ * per head and swish gate of the multi-scale layer). Recomputes the forward pass
+ * internally; nothing from the forward call is needed.
+ * dout:       [B,H,N,d_v] in out_dtype; dstate_out: [B,H,d_k,d_v] float32 or NULL (zero).
+ * dq, dk:     [B,H,N,d_k], dv: [B,H,N,d_v], in in_dtype (written).
+ * dgate:      [B,H,N,d_v] in in_dtype, required iff RN_EPI_GATE (written).
+ * dstate_in:  [B,H,d_k,d_v] float32 or NULL (not computed); gradient for state_in.
+ * dgn_weight, dgn_bias: DEVICE float32 [H*d_v] or NULL, written when RN_EPI_GN (sums over
+ *             the batch and the rows); ignored otherwise.
+ * workspace:  at least rn_chunkwise_backward_workspace_bytes(desc, chunk), 256-byte aligned.
+ * Plain float32 arithmetic throughout (every shape and dtype the forward accepts).
+ */
+rn_status rn_retention_chunkwise_backward(const rn_desc* desc, int32_t chunk, const void* q,
+                                          const void* k, const void* v, const void* gate,
+                                          const float* state_in, const void* dout,
+                                          const float* dstate_out, void* dq, void* dk, void* dv,
+                                          void* dgate, float* dstate_in, float* dgn_weight,
+                                          float* dgn_bias, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/*
  * Standalone per-head GroupNorm (+ swish gate):
  *   y = (x - mean) / sqrt(var + eps) * w + b over the d_v channels of each (b,h,t),
  *   out = y * g * sigmoid(g) if gate != NULL, else y.

@@ -23,7 +23,8 @@ __all__ = [
     "RN_F32", "RN_BF16", "RN_NORM_D_ROW", "RN_NORM_R_ROW", "RN_EPI_GN", "RN_EPI_GATE",
     "RN_FORCE_GENERIC", "RN_CHUNK_PARALLEL", "RnError", "RnDesc", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
     "rn_retention_parallel", "rn_retention_chunkwise", "rn_retention_recurrent_step",
-    "rn_retention_chunkwise_varlen", "rn_retention_recurrent_step_at", "rn_groupnorm_gate", "rn_chunkwise_workspace_bytes", "rn_parallel_workspace_bytes",
+    "rn_retention_chunkwise_varlen", "rn_retention_recurrent_step_at", "rn_groupnorm_gate",
+    "rn_retention_chunkwise_backward", "rn_chunkwise_backward_workspace_bytes", "rn_chunkwise_workspace_bytes", "rn_parallel_workspace_bytes",
     "rn_version", "make_desc",
 ]
 
@@ -39,7 +40,7 @@ EXPORTED_SYMBOLS = (
     "rn_parallel_workspace_bytes", "rn_retention_parallel", "rn_chunkwise_workspace_bytes", "rn_retention_chunkwise",
     "rn_retention_recurrent_step", "rn_retention_chunkwise_varlen",
     "rn_retention_recurrent_step_at", "rn_groupnorm_gate", "rn_status_str", "rn_last_error",
-    "rn_version",
+    "rn_version", "rn_retention_chunkwise_backward", "rn_chunkwise_backward_workspace_bytes",
 )
 
 
@@ -82,6 +83,10 @@ def _load():
     L.rn_retention_chunkwise_varlen.restype = i32
     L.rn_retention_recurrent_step_at.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp]
     L.rn_retention_recurrent_step_at.restype = i32
+    L.rn_chunkwise_backward_workspace_bytes.argtypes = [D, i32]
+    L.rn_chunkwise_backward_workspace_bytes.restype = sz
+    L.rn_retention_chunkwise_backward.argtypes = [D, i32] + [vp] * 14 + [vp, sz, vp]
+    L.rn_retention_chunkwise_backward.restype = i32
     L.rn_groupnorm_gate.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                     ctypes.c_float, vp, vp]
     L.rn_groupnorm_gate.restype = i32
@@ -332,6 +337,53 @@ def rn_retention_recurrent_step_at(q, k, v, gamma, theta, state, pos, *, gate=No
     _check(lib.rn_retention_recurrent_step_at(ctypes.byref(d), pp, _ptr(q), _ptr(k), _ptr(v),
                                               _ptr(gate), _ptr(state), _ptr(out), _stream(q)))
     return out
+
+
+def rn_chunkwise_backward_workspace_bytes(q, v, gamma, theta, chunk, *, gn=False, gate=None,
+                                          out_dtype=None) -> int:
+    B, H, N, dk = q.shape
+    flags = _flags(False, False, gn, gate, False)
+    od = q.dtype if out_dtype is None else out_dtype
+    d, keep = make_desc(B, H, N, dk, v.shape[-1], _dtype_code(q.dtype), _dtype_code(od), gamma,
+                        theta, flags=flags)
+    return int(lib.rn_chunkwise_backward_workspace_bytes(ctypes.byref(d), chunk))
+
+
+def rn_retention_chunkwise_backward(q, k, v, gamma, theta, chunk, dout, *, gate=None,
+                                    state_in=None, dstate_out=None, want_dstate_in=False,
+                                    pos0=0, qk_scale=1.0, gn=False, gn_eps=1e-5, gn_weight=None,
+                                    gn_bias=None, workspace=None):
+    """Gradients of the chunkwise call with respect to q, k, v (and the gate, the initial
+    state, the GroupNorm weight and bias). ``dout`` has the forward output's dtype.
+    Returns a dict with dq, dk, dv and, when they apply, dgate, dstate_in, dgn_weight,
+    dgn_bias."""
+    flags = _flags(False, False, gn, gate, False)
+    d, keep, od = _qkv_desc(q, k, v, gamma, theta, dout.dtype, flags, pos0, qk_scale, gn_eps,
+                            gn_weight, gn_bias)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    if tuple(dout.shape) != tuple(v.shape):
+        raise ValueError("dout must have v's shape")
+    for s_ in (state_in, dstate_out):
+        if s_ is not None and (s_.dtype != torch.float32 or tuple(s_.shape) != (B, H, dk, dv)):
+            raise ValueError("states must be float32 [B,H,d_k,d_v]")
+    res = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v)}
+    if gate is not None:
+        res["dgate"] = torch.empty_like(gate)
+    if want_dstate_in:
+        res["dstate_in"] = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if gn:
+        res["dgn_weight"] = torch.empty(H * dv, dtype=torch.float32, device=q.device)
+        res["dgn_bias"] = torch.empty(H * dv, dtype=torch.float32, device=q.device)
+    need = int(lib.rn_chunkwise_backward_workspace_bytes(ctypes.byref(d), chunk))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib.rn_retention_chunkwise_backward(
+        ctypes.byref(d), chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(state_in),
+        _ptr(dout), _ptr(dstate_out), _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]),
+        _ptr(res.get("dgate")), _ptr(res.get("dstate_in")), _ptr(res.get("dgn_weight")),
+        _ptr(res.get("dgn_bias")), _ptr(workspace), workspace.numel(), _stream(q)))
+    return res
 
 
 def rn_groupnorm_gate(x, gate=None, weight=None, bias=None, eps=1e-5, *, out=None, out_dtype=None):

@@ -267,6 +267,46 @@ rn_status rn_retention_recurrent_step_at(const rn_desc* desc, const int64_t* pos
   return step_call(desc, pos, q, k, v, gate, state, out, stream);
 }
 
+size_t rn_chunkwise_backward_workspace_bytes(const rn_desc* desc, int32_t chunk) {
+  rn::CallArgs a;
+  if (chunk < 1 || check_desc(desc, Form::kChunkwise, &a) != RN_OK) return 0;
+  return align256(rn::backward_ws_bytes(a));
+}
+
+rn_status rn_retention_chunkwise_backward(const rn_desc* desc, int32_t chunk, const void* q,
+                                          const void* k, const void* v, const void* gate,
+                                          const float* state_in, const void* dout,
+                                          const float* dstate_out, void* dq, void* dk, void* dv,
+                                          void* dgate, float* dstate_in, float* dgn_weight,
+                                          float* dgn_bias, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  rn::CallArgs a;
+  rn_status s = check_desc(desc, Form::kChunkwise, &a);
+  if (s != RN_OK) return s;
+  if (chunk < 1) return fail(RN_ERR_INVALID_ARG, "chunk=%d must be >= 1", chunk);
+  if (int64_t(desc->B) * desc->H > 65535)
+    return fail(RN_ERR_UNSUPPORTED, "B*H=%lld > 65535 (one grid row per head)",
+                (long long)desc->B * desc->H);
+  if (!q || !k || !v || !dout || !dq || !dk || !dv)
+    return fail(RN_ERR_INVALID_ARG, "q/k/v/dout/dq/dk/dv pointer is NULL");
+  if ((desc->flags & RN_EPI_GATE) && (!gate || !dgate))
+    return fail(RN_ERR_INVALID_ARG, "RN_EPI_GATE needs gate and dgate");
+  const size_t need = align256(rn::backward_ws_bytes(a));
+  if (!workspace || workspace_bytes < need)
+    return fail(RN_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(RN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  a.chunk = chunk;
+  rn::BwArgs x{q, k, v, (desc->flags & RN_EPI_GATE) ? gate : nullptr, dout, state_in, dstate_out,
+               dq, dk, dv, (desc->flags & RN_EPI_GATE) ? dgate : nullptr, dstate_in,
+               (desc->flags & RN_EPI_GN) ? dgn_weight : nullptr,
+               (desc->flags & RN_EPI_GN) ? dgn_bias : nullptr};
+  g_err[0] = 0;
+  return hip_status(rn::launch_backward(a, desc->in_dtype, desc->out_dtype, x, workspace,
+                                        static_cast<hipStream_t>(stream)),
+                    "chunkwise backward launch");
+}
+
 rn_status rn_groupnorm_gate(int32_t B, int32_t H, int32_t N, int32_t d_v, rn_dtype in_dtype,
                             rn_dtype out_dtype, const void* x, const void* gate, const float* w,
                             const float* b, float eps, void* out, void* stream) {

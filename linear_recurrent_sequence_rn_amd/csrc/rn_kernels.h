@@ -35,6 +35,17 @@ hipError_t launch_chunkwise_cp(const CallArgs& a, int out_dt, const void* q, con
                                const void* v, const void* gate, const float* s_in, float* s_out,
                                void* out, void* ws, size_t ws_bytes, hipStream_t st);
 
+// Gradients of the chunkwise form (plain float32 kernels).
+struct BwArgs {
+  const void* q; const void* k; const void* v; const void* gate;
+  const void* dout; const float* state_in; const float* dstate_out;
+  void* dq; void* dk; void* dv; void* dgate; float* dstate_in;
+  float* dgn_w; float* dgn_b;
+};
+size_t backward_ws_bytes(const CallArgs& a);
+hipError_t launch_backward(const CallArgs& a, int in_dt, int out_dt, const BwArgs& x, void* ws,
+                           hipStream_t st);
+
 // MFMA parallel form (bf16 inputs, d_k = 256, d_v = 512).
 bool parallel_mfma_supported(const CallArgs& a, int in_dt);
 size_t parallel_mfma_ws_bytes(const CallArgs& a);

@@ -204,3 +204,24 @@ def test_binding_checks_sequence_arrays():
     with pytest.raises(ValueError):
         rn.rn_retention_recurrent_step_at(q[:, :, :1], q[:, :, :1], v[:, :, :1], [0.9], np.ones(8),
                                           torch.zeros(2, 1, 16, 16), None)
+
+
+def bwd(d, dgate=FAKE, ws=FAKE, ws_bytes=1 << 40, dq=FAKE):
+    return rn.lib.rn_retention_chunkwise_backward(
+        ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, dq, FAKE, FAKE, dgate,
+        None, None, None, ws, ws_bytes, None)
+
+
+def test_backward_errors():
+    d, keep = desc()
+    assert bwd(d, dq=None) == rn.RN_ERR_INVALID_ARG
+    need = rn.lib.rn_chunkwise_backward_workspace_bytes(ctypes.byref(d), 4)
+    assert need > 0
+    assert bwd(d, ws_bytes=need - 1) == rn.RN_ERR_WORKSPACE
+    assert bwd(d, ws=ctypes.c_void_p(0x1010), ws_bytes=need) == rn.RN_ERR_INVALID_ARG
+    d, keep = desc(flags=rn.RN_EPI_GN | rn.RN_EPI_GATE)
+    assert bwd(d, dgate=None) == rn.RN_ERR_INVALID_ARG       # gate flag needs dgate
+    d, keep = desc(B=600, H=128, gamma=np.full(128, 0.9))
+    assert bwd(d) == rn.RN_ERR_UNSUPPORTED                   # B*H above one grid dimension
+    d, keep = desc(flags=rn.RN_NORM_D_ROW)
+    assert bwd(d) == rn.RN_ERR_INVALID_ARG                   # rescalings: parallel form only
