@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3       # MI355X float32 vector
 
 
 CHUNKWISE_PROFILE = os.path.join(ROOT, "profiles", "chunkwise_fused_6p7b_training.md")
@@ -101,9 +102,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-parallel", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--source-hash", action="store_true",
                     help="print the chunkwise kernel's source hash (as recorded in its profile) and exit")
-    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "copy"], default=None,
+    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "backward", "copy"], default=None,
                     help="run one workload only (for profiling); 'copy' times a plain 1 GiB "
                          "device copy, the reference for the HBM byte counters")
     args = ap.parse_args()
@@ -139,7 +141,7 @@ def main():
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "copy_GBs": 2 * src.numel() * 4 / dt / 1e9}))
         return
-    if args.only in ("decode", "parallel"):
+    if args.only in ("decode", "parallel", "backward"):
         args.no_cpu_baseline = True
     w = W.WORKLOADS["chunkwise_6p7b"]
     x = W.make_inputs(w)
@@ -154,7 +156,7 @@ def main():
         rn.rn_retention_chunkwise(q, k, v, gamma, theta, w.chunk, gate=gate, gn=True,
                                   gn_eps=w.gn_eps, state_out=S_out, out=out, workspace=ws)
 
-    if args.only in ("decode", "parallel"):
+    if args.only in ("decode", "parallel", "backward"):
         args.steps = args.warmup = 1
     for _ in range(args.warmup):
         step()
@@ -201,6 +203,43 @@ def main():
                      "algorithmic_bytes": bytes_, "algorithmic_flops": flops,
                      "mfma_tflops": tfl, "mfma_frac": tfl / BF16_PEAK_TFLOPS},
     }
+
+    # ---- chunkwise backward on the same workload (secondary record) ------------------
+    # Gradients of q, k, v and the gate through GroupNorm + gate, given a random dout;
+    # float32 kernels. Algorithmic flops: twice the forward's (each product of the forward
+    # has two gradient products of the same size).
+    if args.only in ("chunkwise", "decode", "parallel"):
+        args.no_backward = True
+    if not args.no_backward:
+        dout = torch.randn(v.shape, generator=torch.Generator(device=dev).manual_seed(5),
+                           device=dev).to(torch.bfloat16)
+        wsb = torch.empty(rn.rn_chunkwise_backward_workspace_bytes(q, v, gamma, theta, w.chunk, gn=True, gate=gate),
+                          dtype=torch.uint8, device=dev)
+
+        def bstep():
+            rn.rn_retention_chunkwise_backward(q, k, v, gamma, theta, w.chunk, dout, gate=gate, gn=True,
+                                               workspace=wsb)
+
+        bstep()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        e0.record(stream)
+        for _ in range(reps):
+            bstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bs = e0.elapsed_time(e1) / reps / 1e3
+        bfl = 2 * flops
+        rec["backward"] = {"workload": "chunkwise_6p7b backward: dq, dk, dv, dgate through GroupNorm + gate",
+                           "ms": bs * 1e3, "tokens_per_s": tokens / bs,
+                           "algorithmic_flops": bfl, "tflops": bfl / bs / 1e12,
+                           "bound": "alu", "fp32_vector_frac": bfl / bs / 1e12 / FP32_PEAK_TFLOPS,
+                           "workspace_bytes": wsb.numel()}
+        del dout, wsb
+    if args.only == "backward":
+        args.no_parallel = True
+        args.no_decode = True
 
     # ---- parallel form, 1.3B shape (secondary record) --------------------------------
     if args.only in ("chunkwise", "decode"):

@@ -159,16 +159,54 @@ struct alignas(16) TileShared {
   float P[kBC][kLdA];
 };
 
-// acc += A (64 x K) B (K x 16 NCT); la(k0) fills As for k0..k0+15, lb(k0) fills Bs.
-// With FROMP, A is read from P (whose rows are the reduction index) and la is unused.
-template <int NCT, bool FROMP, class LA, class LB>
-__device__ __forceinline__ void tile_mm(float (&acc)[4][NCT], int K, TileShared& sm, LA la, LB lb) {
-  const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
+// acc += A (64 x K) B (K x 16 NCT). ga(row, k) and gb(...) return operand elements (zero
+// outside the operand); B is addressed gb(k, col) for BM = kBRows (reduction along the
+// source's rows) or gb(col, k) for BM = kBCols. With FROMP, A is read from P (whose rows are
+// the reduction index) and ga is unused. Each slice's elements are fetched into registers
+// one slice ahead, so their global loads overlap the previous slice's arithmetic.
+enum { kBRows = 0, kBCols = 1 };
+template <int NCT, bool FROMP, int BM, class GA, class GB>
+__device__ __forceinline__ void tile_mm(float (&acc)[4][NCT], int K, TileShared& sm, GA ga, GB gb) {
+  constexpr int NCB = 16 * NCT;        // B columns
+  constexpr int NBE = NCB / 16;        // B elements per thread and slice
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  float ra[4], rb[NBE];
+  auto fetch = [&](int k0) __attribute__((always_inline)) {
+    if constexpr (!FROMP) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = tid + 256 * i;
+        ra[i] = ga(e >> 4, k0 + (e & 15));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NBE; ++i) {
+      const int e = tid + 256 * i;
+      if constexpr (BM == kBRows) rb[i] = gb(k0 + e / NCB, e % NCB);
+      else rb[i] = gb(e >> 4, k0 + (e & 15));
+    }
+  };
+  auto put = [&]() __attribute__((always_inline)) {
+    if constexpr (!FROMP) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = tid + 256 * i;
+        sm.As[e & 15][e >> 4] = ra[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NBE; ++i) {
+      const int e = tid + 256 * i;
+      if constexpr (BM == kBRows) sm.Bs[e / NCB][e % NCB] = rb[i];
+      else sm.Bs[e & 15][e >> 4] = rb[i];
+    }
+  };
+  fetch(0);
   for (int k0 = 0; k0 < K; k0 += kKS) {
+    __syncthreads();   // the previous slice's reads of As / Bs are done
+    put();
     __syncthreads();
-    if constexpr (!FROMP) la(k0);
-    lb(k0);
-    __syncthreads();
+    if (k0 + kKS < K) fetch(k0 + kKS);
 #pragma unroll 4
     for (int kk = 0; kk < kKS; ++kk) {
       float4 av;
@@ -192,32 +230,6 @@ __device__ __forceinline__ void zero_acc(float (&acc)[4][NCT]) {
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int j = 0; j < NCT; ++j) acc[r][j] = 0.f;
-}
-
-// Loaders; `get` returns the operand element, zero outside it.
-// A from a row-major source: As[k][row] = get(row, k0 + k).
-template <class G>
-__device__ __forceinline__ void load_a(TileShared& sm, int k0, G get) {
-  for (int e = threadIdx.x; e < kKS * kR; e += 256) {
-    const int kk = e & 15, row = e >> 4;
-    sm.As[kk][row] = get(row, k0 + kk);
-  }
-}
-// B, reduction index along the source rows: Bs[k][col] = get(k0 + k, col).
-template <class G>
-__device__ __forceinline__ void load_b_rows(TileShared& sm, int k0, int nc, G get) {
-  for (int e = threadIdx.x; e < kKS * nc; e += 256) {
-    const int kk = e / nc, col = e % nc;
-    sm.Bs[kk][col] = get(k0 + kk, col);
-  }
-}
-// B, reduction index along the source columns: Bs[k][col] = get(col, k0 + k).
-template <class G>
-__device__ __forceinline__ void load_b_cols(TileShared& sm, int k0, int nc, G get) {
-  for (int e = threadIdx.x; e < kKS * nc; e += 256) {
-    const int kk = e & 15, col = e >> 4;
-    sm.Bs[kk][col] = get(col, k0 + kk);
-  }
 }
 
 // Decayed, masked score tile -> P (transposed): P[key - key0][row] for the tile's rows
@@ -312,23 +324,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nkey = T.r1 - T.c0;   // keys c0 .. r1-1
   float m[4][16];
   zero_acc(m);
-  tile_mm<16, false>(m, dk, sm,
-      [&](int k0) __attribute__((always_inline)) { load_a(sm, k0, [&](int row, int kk) __attribute__((always_inline)) {
-          return (T.r0 + row < T.r1 && kk < dk) ? Qb[int64_t(T.r0 + row) * dk + kk] : 0.f; }); },
-      [&](int k0) __attribute__((always_inline)) { load_b_cols(sm, k0, kBC, [&](int col, int kk) __attribute__((always_inline)) {
-          return (col < nkey && kk < dk) ? Kb[int64_t(T.c0 + col) * dk + kk] : 0.f; }); });
+  tile_mm<16, false, kBCols>(m, dk, sm,
+      [&](int row, int kk) __attribute__((always_inline)) {
+          return (T.r0 + row < T.r1 && kk < dk) ? Qb[int64_t(T.r0 + row) * dk + kk] : 0.f; },
+      [&](int col, int kk) __attribute__((always_inline)) {
+          return (col < nkey && kk < dk) ? Kb[int64_t(T.c0 + col) * dk + kk] : 0.f; });
   store_scores<true>(sm, m, T.r0, T.r1, T.c0, T.r1, lg, a.alpha);
   float o[4][32];
   zero_acc(o);
-  tile_mm<32, true>(o, (nkey + kKS - 1) / kKS * kKS, sm, [](int) {},
-      [&](int k0) __attribute__((always_inline)) { load_b_rows(sm, k0, dv, [&](int kk, int col) __attribute__((always_inline)) {
-          return kk < nkey ? Elem<IN>::load(v, (int64_t(bh) * N + T.c0 + kk) * dv + col) : 0.f; }); });
-  tile_mm<32, false>(o, dk, sm,
-      [&](int k0) __attribute__((always_inline)) { load_a(sm, k0, [&](int row, int kk) __attribute__((always_inline)) {
+  tile_mm<32, true, kBRows>(o, (nkey + kKS - 1) / kKS * kKS, sm, [](int, int) { return 0.f; },
+      [&](int kk, int col) __attribute__((always_inline)) {
+          return (kk < nkey && col < dv) ? Elem<IN>::load(v, (int64_t(bh) * N + T.c0 + kk) * dv + col) : 0.f; });
+  tile_mm<32, false, kBRows>(o, dk, sm,
+      [&](int row, int kk) __attribute__((always_inline)) {
           const int t = T.r0 + row;
-          return (t < T.r1 && kk < dk) ? a.alpha * gpow(lg, float(t - T.c0 + 1)) * Qb[int64_t(t) * dk + kk] : 0.f; }); },
-      [&](int k0) __attribute__((always_inline)) { load_b_rows(sm, k0, dv, [&](int kk, int col) __attribute__((always_inline)) {
-          return kk < dk ? Sc[int64_t(kk) * dv + col] : 0.f; }); });
+          return (t < T.r1 && kk < dk) ? a.alpha * gpow(lg, float(t - T.c0 + 1)) * Qb[int64_t(t) * dk + kk] : 0.f; },
+      [&](int kk, int col) __attribute__((always_inline)) {
+          return (kk < dk && col < dv) ? Sc[int64_t(kk) * dv + col] : 0.f; });
   const bool gn = a.flags & RN_EPI_GN, gt = a.flags & RN_EPI_GATE;
   if (!gn) {
 #pragma unroll
@@ -444,23 +456,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nkey = T.r1 - T.c0;
   float m[4][16];
   zero_acc(m);
-  tile_mm<16, false>(m, dv, sm,
-      [&](int k0) __attribute__((always_inline)) { load_a(sm, k0, [&](int row, int kk) __attribute__((always_inline)) {
-          return (T.r0 + row < T.r1 && kk < dv) ? Db[int64_t(T.r0 + row) * dv + kk] : 0.f; }); },
-      [&](int k0) __attribute__((always_inline)) { load_b_cols(sm, k0, kBC, [&](int col, int kk) __attribute__((always_inline)) {
-          return (col < nkey && kk < dv) ? Elem<IN>::load(v, (int64_t(bh) * N + T.c0 + col) * dv + kk) : 0.f; }); });
+  tile_mm<16, false, kBCols>(m, dv, sm,
+      [&](int row, int kk) __attribute__((always_inline)) {
+          return (T.r0 + row < T.r1 && kk < dv) ? Db[int64_t(T.r0 + row) * dv + kk] : 0.f; },
+      [&](int col, int kk) __attribute__((always_inline)) {
+          return (col < nkey && kk < dv) ? Elem<IN>::load(v, (int64_t(bh) * N + T.c0 + col) * dv + kk) : 0.f; });
   store_scores<true>(sm, m, T.r0, T.r1, T.c0, T.r1, lg, a.alpha);
   float g[4][16];
   zero_acc(g);
-  tile_mm<16, true>(g, (nkey + kKS - 1) / kKS * kKS, sm, [](int) {},
-      [&](int k0) __attribute__((always_inline)) { load_b_rows(sm, k0, kBC, [&](int kk, int col) __attribute__((always_inline)) {
-          return (kk < nkey && col < dk) ? Kb[int64_t(T.c0 + kk) * dk + col] : 0.f; }); });
-  tile_mm<16, false>(g, dv, sm,
-      [&](int k0) __attribute__((always_inline)) { load_a(sm, k0, [&](int row, int kk) __attribute__((always_inline)) {
+  tile_mm<16, true, kBRows>(g, (nkey + kKS - 1) / kKS * kKS, sm, [](int, int) { return 0.f; },
+      [&](int kk, int col) __attribute__((always_inline)) {
+          return (kk < nkey && col < dk) ? Kb[int64_t(T.c0 + kk) * dk + col] : 0.f; });
+  tile_mm<16, false, kBCols>(g, dv, sm,
+      [&](int row, int kk) __attribute__((always_inline)) {
           const int t = T.r0 + row;
-          return (t < T.r1 && kk < dv) ? a.alpha * gpow(lg, float(t - T.c0 + 1)) * Db[int64_t(t) * dv + kk] : 0.f; }); },
-      [&](int k0) __attribute__((always_inline)) { load_b_cols(sm, k0, kBC, [&](int col, int kk) __attribute__((always_inline)) {
-          return (col < dk && kk < dv) ? Sc[int64_t(col) * dv + kk] : 0.f; }); });
+          return (t < T.r1 && kk < dv) ? a.alpha * gpow(lg, float(t - T.c0 + 1)) * Db[int64_t(t) * dv + kk] : 0.f; },
+      [&](int col, int kk) __attribute__((always_inline)) {
+          return (col < dk && kk < dv) ? Sc[int64_t(col) * dv + kk] : 0.f; });
   store_rotated<IN>(sm, g, a, seq_pos0(a, bh / a.H), bh, T.r0, T.r1, dq);
 }
 
@@ -483,23 +495,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nlater = T.c1 - T.r0;   // rows r0 .. c1-1
   float m[4][16];
   zero_acc(m);
-  tile_mm<16, false>(m, dv, sm,
-      [&](int k0) __attribute__((always_inline)) { load_a(sm, k0, [&](int row, int kk) __attribute__((always_inline)) {
-          return (T.r0 + row < T.r1 && kk < dv) ? Elem<IN>::load(v, (int64_t(bh) * N + T.r0 + row) * dv + kk) : 0.f; }); },
-      [&](int k0) __attribute__((always_inline)) { load_b_cols(sm, k0, kBC, [&](int col, int kk) __attribute__((always_inline)) {
-          return (col < nlater && kk < dv) ? Db[int64_t(T.r0 + col) * dv + kk] : 0.f; }); });
+  tile_mm<16, false, kBCols>(m, dv, sm,
+      [&](int row, int kk) __attribute__((always_inline)) {
+          return (T.r0 + row < T.r1 && kk < dv) ? Elem<IN>::load(v, (int64_t(bh) * N + T.r0 + row) * dv + kk) : 0.f; },
+      [&](int col, int kk) __attribute__((always_inline)) {
+          return (col < nlater && kk < dv) ? Db[int64_t(T.r0 + col) * dv + kk] : 0.f; });
   store_scores<false>(sm, m, T.r0, T.r1, T.r0, T.c1, lg, a.alpha);
   float g[4][16];
   zero_acc(g);
-  tile_mm<16, true>(g, (nlater + kKS - 1) / kKS * kKS, sm, [](int) {},
-      [&](int k0) __attribute__((always_inline)) { load_b_rows(sm, k0, kBC, [&](int kk, int col) __attribute__((always_inline)) {
-          return (kk < nlater && col < dk) ? Qb[int64_t(T.r0 + kk) * dk + col] : 0.f; }); });
-  tile_mm<16, false>(g, dv, sm,
-      [&](int k0) __attribute__((always_inline)) { load_a(sm, k0, [&](int row, int kk) __attribute__((always_inline)) {
+  tile_mm<16, true, kBRows>(g, (nlater + kKS - 1) / kKS * kKS, sm, [](int, int) { return 0.f; },
+      [&](int kk, int col) __attribute__((always_inline)) {
+          return (kk < nlater && col < dk) ? Qb[int64_t(T.r0 + kk) * dk + col] : 0.f; });
+  tile_mm<16, false, kBCols>(g, dv, sm,
+      [&](int row, int kk) __attribute__((always_inline)) {
           const int s = T.r0 + row;
-          return (s < T.r1 && kk < dv) ? gpow(lg, float(T.c1 - 1 - s)) * Elem<IN>::load(v, (int64_t(bh) * N + s) * dv + kk) : 0.f; }); },
-      [&](int k0) __attribute__((always_inline)) { load_b_cols(sm, k0, kBC, [&](int col, int kk) __attribute__((always_inline)) {
-          return (col < dk && kk < dv) ? Gc[int64_t(col) * dv + kk] : 0.f; }); });
+          return (s < T.r1 && kk < dv) ? gpow(lg, float(T.c1 - 1 - s)) * Elem<IN>::load(v, (int64_t(bh) * N + s) * dv + kk) : 0.f; },
+      [&](int col, int kk) __attribute__((always_inline)) {
+          return (col < dk && kk < dv) ? Gc[int64_t(col) * dv + kk] : 0.f; });
   store_rotated<IN>(sm, g, a, seq_pos0(a, bh / a.H), bh, T.r0, T.r1, dk_);
 }
 
@@ -523,23 +535,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nlater = T.c1 - T.r0;
   float m[4][16];
   zero_acc(m);
-  tile_mm<16, false>(m, dk, sm,
-      [&](int k0) __attribute__((always_inline)) { load_a(sm, k0, [&](int row, int kk) __attribute__((always_inline)) {
-          return (T.r0 + row < T.r1 && kk < dk) ? Kb[int64_t(T.r0 + row) * dk + kk] : 0.f; }); },
-      [&](int k0) __attribute__((always_inline)) { load_b_cols(sm, k0, kBC, [&](int col, int kk) __attribute__((always_inline)) {
-          return (col < nlater && kk < dk) ? Qb[int64_t(T.r0 + col) * dk + kk] : 0.f; }); });
+  tile_mm<16, false, kBCols>(m, dk, sm,
+      [&](int row, int kk) __attribute__((always_inline)) {
+          return (T.r0 + row < T.r1 && kk < dk) ? Kb[int64_t(T.r0 + row) * dk + kk] : 0.f; },
+      [&](int col, int kk) __attribute__((always_inline)) {
+          return (col < nlater && kk < dk) ? Qb[int64_t(T.r0 + col) * dk + kk] : 0.f; });
   store_scores<false>(sm, m, T.r0, T.r1, T.r0, T.c1, lg, a.alpha);
   float o[4][32];
   zero_acc(o);
-  tile_mm<32, true>(o, (nlater + kKS - 1) / kKS * kKS, sm, [](int) {},
-      [&](int k0) __attribute__((always_inline)) { load_b_rows(sm, k0, dv, [&](int kk, int col) __attribute__((always_inline)) {
-          return kk < nlater ? Db[int64_t(T.r0 + kk) * dv + col] : 0.f; }); });
-  tile_mm<32, false>(o, dk, sm,
-      [&](int k0) __attribute__((always_inline)) { load_a(sm, k0, [&](int row, int kk) __attribute__((always_inline)) {
+  tile_mm<32, true, kBRows>(o, (nlater + kKS - 1) / kKS * kKS, sm, [](int, int) { return 0.f; },
+      [&](int kk, int col) __attribute__((always_inline)) {
+          return (kk < nlater && col < dv) ? Db[int64_t(T.r0 + kk) * dv + col] : 0.f; });
+  tile_mm<32, false, kBRows>(o, dk, sm,
+      [&](int row, int kk) __attribute__((always_inline)) {
           const int s = T.r0 + row;
-          return (s < T.r1 && kk < dk) ? gpow(lg, float(T.c1 - 1 - s)) * Kb[int64_t(s) * dk + kk] : 0.f; }); },
-      [&](int k0) __attribute__((always_inline)) { load_b_rows(sm, k0, dv, [&](int kk, int col) __attribute__((always_inline)) {
-          return kk < dk ? Gc[int64_t(kk) * dv + col] : 0.f; }); });
+          return (s < T.r1 && kk < dk) ? gpow(lg, float(T.c1 - 1 - s)) * Kb[int64_t(s) * dk + kk] : 0.f; },
+      [&](int kk, int col) __attribute__((always_inline)) {
+          return (kk < dk && col < dv) ? Gc[int64_t(kk) * dv + col] : 0.f; });
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int s = T.r0 + 4 * ty + r;
