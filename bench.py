@@ -6,7 +6,9 @@ A step is one chunkwise forward of the 6.7B-shaped training workload (B=2, H=16,
 N=8192, d_k=256, d_v=512, chunk 256, bf16 q/k/v/gate, GroupNorm + swish gate, bf16
 output, float32 final state) with inputs resident in HBM. The line also carries the
 decode step time of the 6.7B-shaped decode workload (batch 128, 16 heads, float32
-state updated in place; 1024 sequential steps timed back to back).
+state updated in place; 1024 sequential steps timed back to back), and secondary records
+for the chunkwise backward, the same forward with one decay per (head, coordinate pair)
+and the parallel form.
 
 Prints one JSON line. `roofline` describes the fused chunkwise kernel: its average
 duration is measured with HIP events recorded on the stream it runs on; achieved
@@ -103,9 +105,11 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-parallel", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-pair", action="store_true")
     ap.add_argument("--source-hash", action="store_true",
                     help="print the chunkwise kernel's source hash (as recorded in its profile) and exit")
-    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "backward", "copy"], default=None,
+    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "backward", "pair", "copy"],
+                    default=None,
                     help="run one workload only (for profiling); 'copy' times a plain 1 GiB "
                          "device copy, the reference for the HBM byte counters")
     args = ap.parse_args()
@@ -141,7 +145,7 @@ def main():
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "copy_GBs": 2 * src.numel() * 4 / dt / 1e9}))
         return
-    if args.only in ("decode", "parallel", "backward"):
+    if args.only in ("decode", "parallel", "backward", "pair"):
         args.no_cpu_baseline = True
     w = W.WORKLOADS["chunkwise_6p7b"]
     x = W.make_inputs(w)
@@ -156,7 +160,7 @@ def main():
         rn.rn_retention_chunkwise(q, k, v, gamma, theta, w.chunk, gate=gate, gn=True,
                                   gn_eps=w.gn_eps, state_out=S_out, out=out, workspace=ws)
 
-    if args.only in ("decode", "parallel", "backward"):
+    if args.only in ("decode", "parallel", "backward", "pair"):
         args.steps = args.warmup = 1
     for _ in range(args.warmup):
         step()
@@ -208,7 +212,7 @@ def main():
     # Gradients of q, k, v and the gate through GroupNorm + gate, given a random dout;
     # float32 kernels. Algorithmic flops: twice the forward's (each product of the forward
     # has two gradient products of the same size).
-    if args.only in ("chunkwise", "decode", "parallel"):
+    if args.only in ("chunkwise", "decode", "parallel", "pair"):
         args.no_backward = True
     if not args.no_backward:
         dout = torch.randn(v.shape, generator=torch.Generator(device=dev).manual_seed(5),
@@ -240,6 +244,51 @@ def main():
     if args.only == "backward":
         args.no_parallel = True
         args.no_decode = True
+        args.no_pair = True
+
+    # ---- the same forward with one decay per (head, coordinate pair) -------------------
+    # Chunk-parallel pair of kernels (state snapshots, then outputs) with the decays
+    # folded into the operands per coordinate; same algorithmic bytes and flops as the
+    # per-head-decay forward.
+    if args.only in ("chunkwise", "decode", "parallel"):
+        args.no_pair = True
+    if args.only == "pair":
+        args.no_parallel = True
+        args.no_decode = True
+    if not args.no_pair:
+        wv = W.WORKLOADS["chunkwise_6p7b_pair"]
+        xv = W.make_inputs(wv)
+        qv, kv, vv, gv = (xv[n].to(dev) for n in ("q", "k", "v", "gate"))
+        gpair = torch.from_numpy(xv["gamma"]).to(dev)
+        outv = torch.empty_like(vv)
+        Sv = torch.empty(wv.B, wv.H, wv.d_k, wv.d_v, dtype=torch.float32, device=dev)
+        wsv = torch.empty(rn.rn_chunkwise_workspace_bytes(qv, vv, gpair, xv["theta"], wv.chunk, gn=True,
+                                                          gate=gv), dtype=torch.uint8, device=dev)
+
+        def vstep():
+            rn.rn_retention_chunkwise(qv, kv, vv, gpair, xv["theta"], wv.chunk, gate=gv, gn=True,
+                                      gn_eps=wv.gn_eps, state_out=Sv, out=outv, workspace=wsv)
+
+        for _ in range(3):
+            vstep()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            vstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        vs = e0.elapsed_time(e1) / reps / 1e3
+        vfl, vby = chunkwise_work(wv.B, wv.H, wv.N, wv.d_k, wv.d_v, wv.chunk)
+        rec["pair_decay"] = {"workload": "chunkwise_6p7b_pair: the chunkwise_6p7b shape with one decay "
+                                         "per (head, coordinate pair), 1 - 2^-(5 + 4h/16 + 4j/127)",
+                             "ms": vs * 1e3, "tokens_per_s": wv.B * wv.N / vs,
+                             "bound": "hbm", "achieved_GBs": vby / vs / 1e9,
+                             "hbm_frac": vby / vs / 1e9 / HBM_PEAK_GBS,
+                             "algorithmic_bytes": vby, "algorithmic_flops": vfl,
+                             "mfma_tflops": vfl / vs / 1e12, "kernels": "cp_states + cp_outputs"}
+        del xv, qv, kv, vv, gv, outv, Sv, wsv
 
     # ---- parallel form, 1.3B shape (secondary record) --------------------------------
     if args.only in ("chunkwise", "decode"):

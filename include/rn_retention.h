@@ -26,7 +26,7 @@
  * Ownership: every tensor argument is a DEVICE pointer owned by the caller; the
  * library never allocates device memory on these paths (the chunkwise entry point
  * takes a caller-owned workspace). gamma and theta (in rn_desc) are HOST arrays
- * read during the call. gn_weight / gn_bias are DEVICE arrays [H*d_v] or NULL.
+ * read during the call. gn_weight / gn_bias / gamma_pair are DEVICE arrays or NULL.
  * Asynchrony: each call enqueues kernels on `stream` (a hipStream_t; NULL = the
  * null stream) and returns without synchronising; device faults surface at the
  * caller's next synchronisation.
@@ -85,6 +85,19 @@ typedef struct rn_desc {
     const float* theta;    /* HOST [d_k/2]: one angle per coordinate pair, finite */
     const float* gn_weight;/* DEVICE [H*d_v] GroupNorm scale, or NULL (= 1) */
     const float* gn_bias;  /* DEVICE [H*d_v] GroupNorm shift, or NULL (= 0) */
+    const float* gamma_pair;
+    /* DEVICE [H * d_k/2] float32, 4-byte aligned, or NULL. When set, each head keeps
+     * one decay per coordinate pair instead of one number: gamma_pair[h*d_k/2 + j]
+     * decays pair j (state rows 2j and 2j+1) of head h, and `gamma` is not read (it may
+     * be NULL). This is the form the pages state before simplifying the decay to a
+     * scalar (hwhale notes: A diagonalised as Λ(γe^{iθ})Λ^{-1}; m0nads notes,
+     * "Retention": γ and θ as two vectors), under which the score becomes
+     *     s_ts = alpha * Re sum_j gamma_j^(t-s) zq_{t,j} conj(zk_{s,j}).
+     * Values must lie in (0, 1]; they are read by the kernels, so the host cannot check
+     * them (other values give unspecified numbers, never an access outside the
+     * buffers). Accepted by the parallel form (not with RN_NORM_D_ROW, whose rescaling
+     * is defined by the scalar decay), the chunkwise forms and the decode steps; the
+     * chunkwise backward returns RN_ERR_UNSUPPORTED. */
 } rn_desc;
 
 /*

@@ -59,6 +59,7 @@ class RnDesc(ctypes.Structure):
         ("qk_scale", ctypes.c_float), ("gn_eps", ctypes.c_float),
         ("gamma", ctypes.POINTER(ctypes.c_float)), ("theta", ctypes.POINTER(ctypes.c_float)),
         ("gn_weight", ctypes.c_void_p), ("gn_bias", ctypes.c_void_p),
+        ("gamma_pair", ctypes.c_void_p),
     ]
 
 
@@ -149,21 +150,48 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _is_pair_decay(gamma) -> bool:
+    return isinstance(gamma, torch.Tensor) and gamma.dim() == 2 or \
+        isinstance(gamma, np.ndarray) and gamma.ndim == 2
+
+
 def make_desc(B: int, H: int, N: int, d_k: int, d_v: int, in_dtype: int, out_dtype: int,
-              gamma: Sequence[float], theta: Sequence[float], *, flags: int = 0, pos0: int = 0,
-              qk_scale: float = 1.0, gn_eps: float = 1e-5, gn_weight=None, gn_bias=None):
-    """Builds an rn_desc; returns (desc, keepalive) — keep both alive across the call."""
-    g = np.ascontiguousarray(np.asarray(gamma, dtype=np.float32))
+              gamma, theta: Sequence[float], *, flags: int = 0, pos0: int = 0,
+              qk_scale: float = 1.0, gn_eps: float = 1e-5, gn_weight=None, gn_bias=None,
+              device=None):
+    """Builds an rn_desc; returns (desc, keepalive) — keep both alive across the call.
+
+    ``gamma`` is either H per-head decays (host sequence) or one decay per (head,
+    coordinate pair): a float32 [H, d_k/2] tensor on the GPU, or a 2-D host array that is
+    copied to ``device`` (the descriptor's gamma_pair). With a CPU ``device`` the copy
+    stays on the host, which only calls that never read it may take (workspace sizes,
+    argument checks)."""
     th = np.ascontiguousarray(np.asarray(theta, dtype=np.float32))
     d = RnDesc()
     d.B, d.H, d.N, d.d_k, d.d_v = B, H, N, d_k, d_v
     d.in_dtype, d.out_dtype, d.flags, d.pos0 = in_dtype, out_dtype, flags, pos0
     d.qk_scale, d.gn_eps = qk_scale, gn_eps
-    d.gamma = g.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    if _is_pair_decay(gamma):
+        gp = gamma
+        if not isinstance(gp, torch.Tensor) or not gp.is_cuda:
+            host = gamma.detach().cpu().numpy() if isinstance(gamma, torch.Tensor) else gamma
+            dev = torch.device(device) if device is not None else torch.device("cpu")
+            gp = torch.as_tensor(np.asarray(host, dtype=np.float32), device=dev)
+        if gp.dtype != torch.float32 or tuple(gp.shape) != (H, d_k // 2):
+            raise ValueError(f"pair decays must be float32 [{H}, {d_k // 2}]")
+        gp = gp.contiguous()
+        g = None
+        d.gamma = None
+        d.gamma_pair = gp.data_ptr()
+    else:
+        gp = None
+        g = np.ascontiguousarray(np.asarray(gamma, dtype=np.float32))
+        d.gamma = g.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+        d.gamma_pair = None
     d.theta = th.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
     d.gn_weight = None if gn_weight is None else gn_weight.data_ptr()
     d.gn_bias = None if gn_bias is None else gn_bias.data_ptr()
-    return d, (g, th, gn_weight, gn_bias)
+    return d, (g, gp, th, gn_weight, gn_bias)
 
 
 def _flags(norm_d, norm_r, gn, gate, force_generic, chunk_parallel=False):
@@ -186,7 +214,7 @@ def _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos0, qk_scale, gn_eps, g
     B, H, N, dk = q.shape
     dv = v.shape[-1]
     if len(gamma) != H or len(theta) != dk // 2:
-        raise ValueError(f"need gamma[{H}] and theta[{dk // 2}]")
+        raise ValueError(f"need gamma[{H}] (or [{H}, {dk // 2}]) and theta[{dk // 2}]")
     od = q.dtype if out_dtype is None else out_dtype
     for t in (gn_weight, gn_bias):
         if t is not None:
@@ -195,7 +223,7 @@ def _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos0, qk_scale, gn_eps, g
                 raise ValueError("gn_weight/gn_bias must be float32 with H*d_v elements")
     d, keep = make_desc(B, H, N, dk, dv, _dtype_code(q.dtype), _dtype_code(od), gamma, theta,
                         flags=flags, pos0=pos0, qk_scale=qk_scale, gn_eps=gn_eps,
-                        gn_weight=gn_weight, gn_bias=gn_bias)
+                        gn_weight=gn_weight, gn_bias=gn_bias, device=q.device)
     return d, keep, od
 
 
@@ -223,7 +251,7 @@ def rn_parallel_workspace_bytes(q, v, gamma, theta, *, norm_d=False, norm_r=Fals
     flags = _flags(norm_d, norm_r, gn, gate, force_generic)
     od = q.dtype if out_dtype is None else out_dtype
     d, keep = make_desc(B, H, N, dk, v.shape[-1], _dtype_code(q.dtype), _dtype_code(od), gamma,
-                        theta, flags=flags)
+                        theta, flags=flags, device=q.device)
     return int(lib.rn_parallel_workspace_bytes(ctypes.byref(d)))
 
 
@@ -233,7 +261,7 @@ def rn_chunkwise_workspace_bytes(q, v, gamma, theta, chunk, *, gn=False, gate=No
     flags = _flags(False, False, gn, gate, force_generic, chunk_parallel)
     od = q.dtype if out_dtype is None else out_dtype
     d, keep = make_desc(B, H, N, dk, v.shape[-1], _dtype_code(q.dtype), _dtype_code(od), gamma,
-                        theta, flags=flags)
+                        theta, flags=flags, device=q.device)
     return int(lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), chunk))
 
 
@@ -345,7 +373,7 @@ def rn_chunkwise_backward_workspace_bytes(q, v, gamma, theta, chunk, *, gn=False
     flags = _flags(False, False, gn, gate, False)
     od = q.dtype if out_dtype is None else out_dtype
     d, keep = make_desc(B, H, N, dk, v.shape[-1], _dtype_code(q.dtype), _dtype_code(od), gamma,
-                        theta, flags=flags)
+                        theta, flags=flags, device=q.device)
     return int(lib.rn_chunkwise_backward_workspace_bytes(ctypes.byref(d), chunk))
 
 

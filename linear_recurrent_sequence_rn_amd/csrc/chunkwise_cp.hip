@@ -18,6 +18,24 @@
 // Both kernels compute with 16x16x32 f16 MFMA and float32 accumulation. Operands are
 // rounded to IEEE half after the float32 rotation and decay (half keeps 3 more bits
 // than bf16); they must stay within half's range, as must the state.
+//
+// One decay per coordinate pair (the form before the pages reduce the decay to a
+// scalar: hwhale notes, A diagonalised as Λ(γe^{iθ})Λ^{-1}; m0nads notes, "Retention",
+// γ and θ as two vectors). The decay of coordinate d can no longer be applied to a
+// score after the product over d_k, so it is folded into the operands per coordinate,
+// with every factor at most 1 wherever the fold allows it:
+//   carry   Kh_j scaled by gamma_d^(L-1-j), state row d by gamma_d^L;
+//   cross   Qh_t scaled by alpha gamma_d^(t-256c+1) before the product with S_c;
+//   keys before the workgroup's rows (s < t0):
+//           (alpha Qh_t gamma_d^(t-t0)) . (Kh_s gamma_d^(t0-s));
+//   keys among its rows, per 16x16 score tile with anchor A (the middle of a diagonal
+//   tile, the boundary between the two 16-row halves otherwise):
+//           (alpha Qh_t gamma_d^(t-A)) . (Kh_s gamma_d^(A-s)),
+//   formed in float32 from the unscaled half operands and multiplied as bf16 high and
+//   low parts (three bf16 MFMA, about 16 significant bits), so that factors up to
+//   gamma_d^-8 keep float32's exponent range; entries above the diagonal are dropped
+//   by selection. Inside a diagonal tile a decay below 2^-13 is taken as 2^-13, which
+//   changes a score term with t > s by less than 2^-13 of its undecayed size.
 #include "rn_device.h"
 #include "rn_kernels.h"
 
@@ -137,6 +155,7 @@ struct StateParams {
 constexpr int kLoads1 = 8 + 32;   // vector loads per thread and block
 constexpr int kStores1 = 16;      // snapshot stores per thread and block
 
+template <bool VEC>
 __global__ void __launch_bounds__(256) cp_states(StateParams P) {
   const CallArgs& a = P.a;
   const int xcd = blockIdx.x & 7, L8 = blockIdx.x >> 3;
@@ -183,6 +202,14 @@ __global__ void __launch_bounds__(256) cp_states(StateParams P) {
   // K: pair 32kq + pi of tokens 8tg .. 8tg+7 of a block
   const int pi = tid & 31, tg = tid >> 5;
   const float th = a.ap.theta[32 * kq + pi];
+  // decays: of this thread's K pair, and of its accumulator rows (rt, r): pair
+  // 32kq + 8rt + 2g + (r >> 1)
+  const float lgk = VEC ? pair_log2g(a, h, 32 * kq + pi) : lg;
+  float lgr[4][2];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int hr = 0; hr < 2; ++hr) lgr[rt][hr] = VEC ? pair_log2g(a, h, 32 * kq + 8 * rt + 2 * g + hr) : lg;
   float c1, s1, c64, s64;
   angle_cs(1, th, &c1, &s1);
   angle_cs(kT1, th, &c64, &s64);
@@ -216,7 +243,7 @@ __global__ void __launch_bounds__(256) cp_states(StateParams P) {
         const uint32_t x = kr[j + jj];
         const float x0 = bf_lo(x), x1 = bf_hi(x);
         const int jc = jc0 + j + jj;
-        const float z = jc < Lc ? exp2f(lg * float(Lc - 1 - jc)) : 0.f;
+        const float z = jc < Lc ? exp2f(lgk * float(Lc - 1 - jc)) : 0.f;
         y[jj][0] = (x0 * c - x1 * s) * z;
         y[jj][1] = (x0 * s + x1 * c) * z;
         const float cn = c * c1 - s * s1;
@@ -272,14 +299,20 @@ __global__ void __launch_bounds__(256) cp_states(StateParams P) {
     u32x2 snapv[4][4];
     const bool chunk_start = live && (b % kBlkPerChunk) == 0;
     if (chunk_start) {
-      const float gL = exp2f(lg * float(min(kC, len - kC * (b / kBlkPerChunk))));
+      const float Lf = float(min(kC, len - kC * (b / kBlkPerChunk)));
+      float gL[4][2];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int hr = 0; hr < 2; ++hr) gL[rt][hr] = exp2f(lgr[rt][hr] * Lf);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           snapv[rt][ct] = u32x2{pack_f16x2(acc[rt][ct][0], acc[rt][ct][1]),
                                 pack_f16x2(acc[rt][ct][2], acc[rt][ct][3])};
-          acc[rt][ct] *= gL;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[rt][ct][r] *= gL[rt][r >> 1];
         }
     } else {
 #pragma unroll
@@ -376,9 +409,23 @@ struct alignas(16) SharedO {
   uint16_t vt[kDV][32];      // V^T of the key step, or a snapshot piece (swizzled rows)
   uint16_t ps[kQ][32];       // P[q][key] (swizzled rows); GroupNorm partial sums at the end
   float gwb[2][kDV];         // GroupNorm weight and bias of the head
+  float lgp[kDK / 2];        // log2 of each pair's decay (one decay per pair only)
 };
 
-template <int OUT>
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// x -> (hi, lo) with hi = bf16(x), lo = bf16(x - hi): hi + lo keeps about 16 bits of x
+// over float32's exponent range. Element i of the two vectors.
+__device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int i) {
+  const __bf16 h = static_cast<__bf16>(x);
+  hi[i] = h;
+  lo[i] = static_cast<__bf16>(x - static_cast<float>(h));
+}
+
+template <int OUT, bool VEC>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 cp_outputs(OutParams P) {
   const CallArgs& a = P.a;
@@ -426,6 +473,7 @@ cp_outputs(OutParams P) {
   // Row loader/rotator for Q and K: pair pj of rows rg2 + 2i (i < 16) of a 32-row step.
   const int pj = tid & 127, rg2 = tid >> 7;
   const float th = a.ap.theta[pj];
+  const float lgq = VEC ? pair_log2g(a, h, pj) : 0.f;   // decay of the staged pair
   float c2, s2;
   angle_cs(2, th, &c2, &s2);
   auto load_rows = [&](__amdgpu_buffer_rsrc_t r, int row0, u32x4* dst) {
@@ -433,15 +481,20 @@ cp_outputs(OutParams P) {
     for (int i = 0; i < 16; ++i)
       dst[i >> 2][i & 3] = ld_b32(r, static_cast<uint32_t>(((row0 + rg2 + 2 * i) * kDK + 2 * pj) * 2));
   };
-  auto stage_rows = [&](int row0, const u32x4* src, uint16_t (*buf)[kLdQ], float scale) {
+  // Rows scaled by `scale`, and with one decay per pair by gamma^(row - anchor) as well
+  // (lgs = log2 gamma of the staged pair, or its negative for gamma^(anchor - row)).
+  auto stage_rows = [&](int row0, const u32x4* src, uint16_t (*buf)[kLdQ], float scale,
+                        float lgs = 0.f, int anchor = 0) {
     float c, s;
     angle_cs_fast(p0 + row0 + rg2, th, &c, &s);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const uint32_t word = src[i >> 2][i & 3];
       const float x0 = bf_lo(word), x1 = bf_hi(word);
+      float f = scale;
+      if constexpr (VEC) f *= exp2f(lgs * float(row0 + rg2 + 2 * i - anchor));
       *reinterpret_cast<uint32_t*>(&buf[rg2 + 2 * i][2 * pj]) =
-          pack_f16x2((x0 * c - x1 * s) * scale, (x0 * s + x1 * c) * scale);
+          pack_f16x2((x0 * c - x1 * s) * f, (x0 * s + x1 * c) * f);
       const float cn = c * c2 - s * s2;
       s = c * s2 + s * c2;
       c = cn;
@@ -545,7 +598,10 @@ cp_outputs(OutParams P) {
   load_rows(rq, t0, qx);
   load_piece(0, pre);
   wait_vm<0>();
-  stage_rows(t0, qx, sm.qs, a.alpha);
+  // cross operand: alpha Qh_t, with one decay per pair scaled by gamma^(t - c0 + 1) (xi)
+  stage_rows(t0, qx, sm.qs, a.alpha, lgq, c0 - 1);
+  if constexpr (VEC)
+    if (tid < kDK / 2) sm.lgp[tid] = lgq;
   sm.gwb[0][tid] = gwv[0];
   sm.gwb[0][tid + 256] = gwv[1];
   sm.gwb[1][tid] = gbv[0];
@@ -560,7 +616,7 @@ cp_outputs(OutParams P) {
     } else {
       load_rows(rk, c0, pre);
       load_v(c0, pre + 4);
-      load_gate(gt);
+      if constexpr (!VEC) load_gate(gt);   // with pair decays: after the key steps
     }
     lds_barrier();
     mma_vt(kPiece * ph, sm.qs, true);
@@ -574,18 +630,32 @@ cp_outputs(OutParams P) {
   cross_phase(Ic<5>{});
   cross_phase(Ic<6>{});
   cross_phase(Ic<7>{});
-  // xi_t = gamma^(t - c0 + 1) per query row (column of the transposed tiles)
+  // xi_t = gamma^(t - c0 + 1) per query row (column of the transposed tiles); with one
+  // decay per pair it was folded into the operand
+  if constexpr (!VEC) {
 #pragma unroll
-  for (int mq = 0; mq < 2; ++mq) {
-    const float xi = exp2f(lg * float(t0 + 16 * mq + l16 - c0 + 1));
+    for (int mq = 0; mq < 2; ++mq) {
+      const float xi = exp2f(lg * float(t0 + 16 * mq + l16 - c0 + 1));
 #pragma unroll
-    for (int tb = 0; tb < 8; ++tb) acc[tb][mq] *= xi;
+      for (int tb = 0; tb < 8; ++tb) acc[tb][mq] *= xi;
+    }
   }
 
   for (int st = 0; st < nsteps; ++st) {
     const int key0 = c0 + kKs * st;
+    const bool diag = st == nsteps - 1;     // keys t0 .. t0+31: the workgroup's own rows
     lds_barrier();
-    stage_rows(key0, pre, sm.ks, 1.f);
+    if constexpr (VEC) {
+      // keys before t0: Q by gamma^(t - t0), K by gamma^(t0 - s); own rows: unscaled
+      // (the score tiles scale them in registers)
+      if (diag)
+        stage_rows(t0, qx, sm.qs, a.alpha);
+      else if (st == 0)
+        stage_rows(t0, qx, sm.qs, a.alpha, lgq, t0);
+      stage_rows(key0, pre, sm.ks, 1.f, diag ? 0.f : -lgq, t0);
+    } else {
+      stage_rows(key0, pre, sm.ks, 1.f);
+    }
     stage_v(pre + 4);
     // the next step's rows (past the last step: rows the workgroup does not use)
     load_rows(rk, key0 + kKs, pre);
@@ -595,18 +665,46 @@ cp_outputs(OutParams P) {
     {
       const int mk = w >> 1, mq = w & 1;
       f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (!VEC || !diag) {
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const f16x8 A = as_f16x8(*reinterpret_cast<const u32x4*>(&sm.ks[16 * mk + l16][32 * kk + 8 * g]));
-        const f16x8 Bq = as_f16x8(*reinterpret_cast<const u32x4*>(&sm.qs[16 * mq + l16][32 * kk + 8 * g]));
-        sc = mfma(A, Bq, sc);
+        for (int kk = 0; kk < 8; ++kk) {
+          const f16x8 A = as_f16x8(*reinterpret_cast<const u32x4*>(&sm.ks[16 * mk + l16][32 * kk + 8 * g]));
+          const f16x8 Bq = as_f16x8(*reinterpret_cast<const u32x4*>(&sm.qs[16 * mq + l16][32 * kk + 8 * g]));
+          sc = mfma(A, Bq, sc);
+        }
+      } else if (mk <= mq) {   // (the tile with mk > mq lies above the diagonal)
+        // tile among the workgroup's rows: decays applied here per coordinate around the
+        // anchor A = t0 + 8 + 8 (mk + mq); A-operand row = key 16mk + l16, B-operand row
+        // = query 16mq + l16, k-elements 32kk + 8g .. +7 (pairs 16kk + 4g .. +3)
+        const int anc = 8 + 8 * (mk + mq);
+        const float ek = float(anc - 16 * mk - l16), eq = float(16 * mq + l16 - anc);
+        const float lo_lim = mk == mq ? -13.f : -__builtin_inff();
+#pragma clang loop unroll(disable)
+        for (int kk = 0; kk < 8; ++kk) {
+          const f16x8 kx = as_f16x8(*reinterpret_cast<const u32x4*>(&sm.ks[16 * mk + l16][32 * kk + 8 * g]));
+          const f16x8 qv = as_f16x8(*reinterpret_cast<const u32x4*>(&sm.qs[16 * mq + l16][32 * kk + 8 * g]));
+          bf16x8 kh, kl, qh, ql;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float lgv = fmaxf(sm.lgp[16 * kk + 4 * g + i], lo_lim);
+            const float fk = exp2f(lgv * ek), fq = exp2f(lgv * eq);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              split_bf16(static_cast<float>(kx[2 * i + e]) * fk, kh, kl, 2 * i + e);
+              split_bf16(static_cast<float>(qv[2 * i + e]) * fq, qh, ql, 2 * i + e);
+            }
+          }
+          sc = mfma_bf16(kh, qh, sc);
+          sc = mfma_bf16(kh, ql, sc);
+          sc = mfma_bf16(kl, qh, sc);
+        }
       }
       const int tq = t0 + 16 * mq + l16;
       float pvv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = key0 + 16 * mk + 4 * g + r;
-        const float e = exp2f(lg * float(max(tq - s, 0)));
+        const float e = VEC ? 1.f : exp2f(lg * float(max(tq - s, 0)));
         pvv[r] = s <= tq ? sc[r] * e : 0.f;
       }
       const int qrow = 16 * mq + l16;
@@ -618,6 +716,9 @@ cp_outputs(OutParams P) {
     mma_vt(0, sm.qs, false);
     wait_vm<0>();
   }
+  // with pair decays the gate rows are loaded here, behind the GroupNorm statistics,
+  // which keeps them out of the registers the key steps need
+  if constexpr (VEC) load_gate(gt);
 
   // ---- epilogue: GroupNorm over the 512 columns of each row, gate, store ----------------
   float y[8][2][4];
@@ -763,7 +864,10 @@ hipError_t launch_chunkwise_cp(const CallArgs& a, int out_dt, const void* q, con
       sp.dst = win + 1 == nwin ? s_out : carry;
       sp.dst_group = win + 1 == nwin ? 0 : 1;
       sp.snap = snap;
-      hipLaunchKernelGGL(cp_states, dim3(64 * ((heads + 7) / 8)), dim3(256), 0, st, sp);
+      if (a.gpair)
+        hipLaunchKernelGGL(cp_states<true>, dim3(64 * ((heads + 7) / 8)), dim3(256), 0, st, sp);
+      else
+        hipLaunchKernelGGL(cp_states<false>, dim3(64 * ((heads + 7) / 8)), dim3(256), 0, st, sp);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       OutParams op;
@@ -779,10 +883,17 @@ hipError_t launch_chunkwise_cp(const CallArgs& a, int out_dt, const void* q, con
       op.out = out;
       const int inst = heads * kWin;
       const dim3 grid(64 * ((inst + 7) / 8));
-      if (out_dt == RN_BF16)
-        hipLaunchKernelGGL(cp_outputs<RN_BF16>, grid, dim3(256), 0, st, op);
-      else
-        hipLaunchKernelGGL(cp_outputs<RN_F32>, grid, dim3(256), 0, st, op);
+      if (a.gpair) {
+        if (out_dt == RN_BF16)
+          hipLaunchKernelGGL((cp_outputs<RN_BF16, true>), grid, dim3(256), 0, st, op);
+        else
+          hipLaunchKernelGGL((cp_outputs<RN_F32, true>), grid, dim3(256), 0, st, op);
+      } else {
+        if (out_dt == RN_BF16)
+          hipLaunchKernelGGL((cp_outputs<RN_BF16, false>), grid, dim3(256), 0, st, op);
+        else
+          hipLaunchKernelGGL((cp_outputs<RN_F32, false>), grid, dim3(256), 0, st, op);
+      }
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

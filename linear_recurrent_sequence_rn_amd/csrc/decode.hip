@@ -1,7 +1,8 @@
 // One recurrent retention step (decode): S <- gamma S + Kh^T v in place, o = alpha Qh S
 // (hwhale notes: recurrent equations and the RecurrentRetention listing). The token of
 // sequence b sits at the descriptor's position, or at pos[b] when the call passes one
-// position per sequence (batched decode of sequences of different lengths).
+// position per sequence (batched decode of sequences of different lengths). With one
+// decay per coordinate pair, state rows 2j and 2j+1 are scaled by pair j's decay.
 //
 // HBM-bound: the float32 state is read and written once per step; everything else is
 // a few KB. One block owns one (b, h) state of d_k x d_v floats. Thread (group g,
@@ -31,6 +32,7 @@ __global__ void __launch_bounds__(256) decode_step(CallArgs a, const void* q, co
                                                    void* out) {
   __shared__ float qh[kMaxDk];
   __shared__ float kh[kMaxDk];
+  __shared__ float gd[kMaxDk];   // decay of each state row
   __shared__ float vv[kMaxDv];
   __shared__ float part[256 * 4];
   __shared__ float orow[kMaxDv];
@@ -49,11 +51,11 @@ __global__ void __launch_bounds__(256) decode_step(CallArgs a, const void* q, co
     qh[2 * j + 1] = q0 * s + q1 * c;
     kh[2 * j] = k0 * c - k1 * s;
     kh[2 * j + 1] = k0 * s + k1 * c;
+    gd[2 * j] = gd[2 * j + 1] = pair_gamma(a, h, j);
   }
   for (int c = threadIdx.x; c < dv; c += 256) vv[c] = Elem<IN>::load(v, static_cast<int64_t>(bh) * dv + c);
   __syncthreads();
 
-  const float g = a.hp.gamma[h];
   const int nq = dv / VEC;                 // column vectors per row
   const int G = nq >= 256 ? 1 : 256 / nq;  // row groups
   const int tid = threadIdx.x;
@@ -86,7 +88,7 @@ __global__ void __launch_bounds__(256) decode_step(CallArgs a, const void* q, co
       for (int u = 0; u < kBatch; ++u) {
         const int d = d0 + u * G;
         if (d < dk) {
-          const float kd = kh[d], qd = qh[d];
+          const float kd = kh[d], qd = qh[d], g = gd[d];
 #pragma unroll
           for (int i = 0; i < VEC; ++i) {
             float s = fmaf(g, sv[u][i], kd * vr[i]);
@@ -129,6 +131,7 @@ __global__ void __launch_bounds__(kFastThreads) decode_step_pipelined(CallArgs a
   constexpr int DV = 4 * NQ;
   __shared__ float qh[kMaxDk];
   __shared__ float kh[kMaxDk];
+  __shared__ float gd[kMaxDk];   // decay of each state row
   __shared__ float part[G * DV];
   __shared__ float orow[DV];
   __shared__ float red[kFastThreads / 64];
@@ -147,13 +150,13 @@ __global__ void __launch_bounds__(kFastThreads) decode_step_pipelined(CallArgs a
     qh[2 * j + 1] = q0 * s + q1 * c;
     kh[2 * j] = k0 * c - k1 * s;
     kh[2 * j + 1] = k0 * s + k1 * c;
+    gd[2 * j] = gd[2 * j + 1] = pair_gamma(a, h, j);
   }
   float vr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) vr[i] = Elem<IN>::load(v, static_cast<int64_t>(bh) * DV + 4 * cq + i);
   __syncthreads();
 
-  const float g = a.hp.gamma[h];
   const int nit = dk / (G * kFastBatch);
   float* S = state + static_cast<int64_t>(bh) * dk * DV + 4 * cq;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -168,7 +171,7 @@ __global__ void __launch_bounds__(kFastThreads) decode_step_pipelined(CallArgs a
 #pragma unroll
     for (int u = 0; u < kFastBatch; ++u) {
       const int d = d0 + u * G;
-      const float kd = kh[d], qd = qh[d];
+      const float kd = kh[d], qd = qh[d], g = gd[d];
       f32x4 x;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

@@ -1,7 +1,10 @@
 // Plain (non-MFMA) retention kernels for float32 inputs and for shapes outside the
 // MFMA kernels' tiles. They evaluate the pages' formulas directly, one 256-thread
 // block per output row (parallel form) or per head (chunkwise form), with every
-// product in float32 and the rotation angle reduced in float64.
+// product in float32 and the rotation angle reduced in float64. With one decay per
+// coordinate pair (the form before the pages reduce the decay to a scalar), the decay
+// of pair j enters the score inside the sum over coordinates, scales the cross term
+// per coordinate and the state per row.
 #include "rn_device.h"
 #include "rn_kernels.h"
 
@@ -28,6 +31,7 @@ template <int IN, int OUT>
 __global__ void __launch_bounds__(256) generic_parallel(CallArgs a, const void* q, const void* k,
                                                         const void* v, const void* gate, void* out) {
   __shared__ float qh[kMaxDk];
+  __shared__ float lgp[kMaxDk / 2];
   __shared__ float sc[kTile];
   __shared__ float orow[kMaxDv];
   __shared__ float red[4];
@@ -36,9 +40,12 @@ __global__ void __launch_bounds__(256) generic_parallel(CallArgs a, const void* 
   const int64_t bh = static_cast<int64_t>(b) * a.H + h;
   const int64_t qoff = (bh * a.N + t) * dk;
   const int64_t pt = a.pos0 + t;
-  for (int j = threadIdx.x; j < dk / 2; j += 256)
+  for (int j = threadIdx.x; j < dk / 2; j += 256) {
     rot_pair<IN>(q, qoff, j, pt, a.ap.theta[j], &qh[2 * j], &qh[2 * j + 1]);
+    lgp[j] = pair_log2g(a, h, j);
+  }
   const float lg = a.hp.log2g[h];
+  const bool per_pair = a.gpair != nullptr;
   float acc0 = 0.f, acc1 = 0.f, rs = 0.f;
   const int c0 = threadIdx.x, c1 = threadIdx.x + 256;
   __syncthreads();
@@ -52,9 +59,10 @@ __global__ void __launch_bounds__(256) generic_parallel(CallArgs a, const void* 
       for (int j = 0; j < dk / 2; ++j) {
         float k0, k1;
         rot_pair<IN>(k, koff, j, ps, a.ap.theta[j], &k0, &k1);
-        dot += qh[2 * j] * k0 + qh[2 * j + 1] * k1;
+        const float pj = qh[2 * j] * k0 + qh[2 * j + 1] * k1;
+        dot += per_pair ? pj * gpow(lgp[j], static_cast<float>(t - s)) : pj;
       }
-      val = a.alpha * dot * gpow(lg, static_cast<float>(t - s));
+      val = a.alpha * (per_pair ? dot : dot * gpow(lg, static_cast<float>(t - s)));
     }
     rs += val;
     sc[threadIdx.x] = val;
@@ -92,9 +100,12 @@ __global__ void __launch_bounds__(256) generic_parallel(CallArgs a, const void* 
 //   rows t:  O_t = alpha [ sum_{c0<=s<=t} gamma^(t-s) (Qh_t.Kh_s) V_s
 //                         + gamma^(t-c0+1) Qh_t S ]
 //   then     S <- gamma^L S + sum_j gamma^(L-1-j) Kh_j^T V_j
-// (hwhale notes: chunkwise equation and ChunkwiseRetention listing). Sequence b runs
-// over its own number of tokens and from its own starting position when the call
-// gives them; rows past its length are left untouched.
+// (hwhale notes: chunkwise equation and ChunkwiseRetention listing). With one decay per
+// coordinate pair, every power of gamma is taken per coordinate d inside the products
+// (gamma_d^(t-s) Qh_td Kh_sd, gamma_d^(t-c0+1) Qh_td, state row d scaled by gamma_d^L,
+// Kh_jd by gamma_d^(L-1-j)). Sequence b runs over its own number of tokens and from its
+// own starting position when the call gives them; rows past its length are left
+// untouched.
 template <int IN, int OUT>
 __global__ void __launch_bounds__(256) generic_chunkwise(CallArgs a, const void* q, const void* k,
                                                          const void* v, const void* gate,
@@ -102,6 +113,8 @@ __global__ void __launch_bounds__(256) generic_chunkwise(CallArgs a, const void*
                                                          void* out, float* ws) {
   constexpr int kJ = 16;  // key rows per state-update tile
   __shared__ float qh[kMaxDk];
+  __shared__ float qx[kMaxDk];     // Qh_t scaled by the cross-term decay of each coordinate
+  __shared__ float lgp[kMaxDk / 2];
   __shared__ float sc[kTile];
   __shared__ float orow[kMaxDv];
   __shared__ float kt[kJ][kMaxDk];
@@ -115,15 +128,22 @@ __global__ void __launch_bounds__(256) generic_chunkwise(CallArgs a, const void*
   const int64_t nS = static_cast<int64_t>(dk) * dv;
   float* S = ws + bh * nS;
   for (int64_t e = threadIdx.x; e < nS; e += 256) S[e] = state_in ? state_in[bh * nS + e] : 0.f;
+  for (int j = threadIdx.x; j < dk / 2; j += 256) lgp[j] = pair_log2g(a, h, j);
   __syncthreads();
   const float lg = a.hp.log2g[h];
+  const bool per_pair = a.gpair != nullptr;
   const int c0 = threadIdx.x, c1 = threadIdx.x + 256;
   for (int cs = 0; cs < len; cs += C) {
     const int L = min(C, len - cs);
     for (int t = cs; t < cs + L; ++t) {
       const int64_t pt = p0 + t;
-      for (int j = threadIdx.x; j < dk / 2; j += 256)
+      // cross-term decay xi = gamma^(t - cs + 1), per coordinate pair
+      for (int j = threadIdx.x; j < dk / 2; j += 256) {
         rot_pair<IN>(q, (bh * N + t) * dk, j, pt, a.ap.theta[j], &qh[2 * j], &qh[2 * j + 1]);
+        const float xi = gpow(lgp[j], static_cast<float>(t - cs + 1));
+        qx[2 * j] = qh[2 * j] * xi;
+        qx[2 * j + 1] = qh[2 * j + 1] * xi;
+      }
       __syncthreads();
       float acc0 = 0.f, acc1 = 0.f;
       for (int s0 = cs; s0 <= t; s0 += kTile) {
@@ -135,9 +155,10 @@ __global__ void __launch_bounds__(256) generic_chunkwise(CallArgs a, const void*
           for (int j = 0; j < dk / 2; ++j) {
             float k0, k1;
             rot_pair<IN>(k, koff, j, p0 + s, a.ap.theta[j], &k0, &k1);
-            dot += qh[2 * j] * k0 + qh[2 * j + 1] * k1;
+            const float pj = qh[2 * j] * k0 + qh[2 * j + 1] * k1;
+            dot += per_pair ? pj * gpow(lgp[j], static_cast<float>(t - s)) : pj;
           }
-          val = dot * gpow(lg, static_cast<float>(t - s));
+          val = per_pair ? dot : dot * gpow(lg, static_cast<float>(t - s));
         }
         sc[threadIdx.x] = val;
         __syncthreads();
@@ -149,27 +170,25 @@ __global__ void __launch_bounds__(256) generic_chunkwise(CallArgs a, const void*
         }
         __syncthreads();
       }
-      // cross-chunk term with xi_j = gamma^(j+1), j = t - cs
-      const float xi = gpow(lg, static_cast<float>(t - cs + 1));
+      // cross-chunk term: (Qh_t ⊙ xi) S
       float x0 = 0.f, x1 = 0.f;
       for (int d = 0; d < dk; ++d) {
-        if (c0 < dv) x0 += qh[d] * S[static_cast<int64_t>(d) * dv + c0];
-        if (c1 < dv) x1 += qh[d] * S[static_cast<int64_t>(d) * dv + c1];
+        if (c0 < dv) x0 += qx[d] * S[static_cast<int64_t>(d) * dv + c0];
+        if (c1 < dv) x1 += qx[d] * S[static_cast<int64_t>(d) * dv + c1];
       }
-      if (c0 < dv) orow[c0] = a.alpha * (acc0 + xi * x0);
-      if (c1 < dv) orow[c1] = a.alpha * (acc1 + xi * x1);
+      if (c0 < dv) orow[c0] = a.alpha * (acc0 + x0);
+      if (c1 < dv) orow[c1] = a.alpha * (acc1 + x1);
       __syncthreads();
       row_epilogue256<IN, OUT>(orow, dv, a, h, gate, (bh * N + t) * dv, out, red);
       __syncthreads();
     }
     // state update: S <- gamma^L S + sum_j zeta_j Kh_j^T V_j, zeta_j = gamma^(L-1-j)
-    const float gL = gpow(lg, static_cast<float>(L));
     for (int j0 = 0; j0 < L; j0 += kJ) {
       const int nj = min(kJ, L - j0);
       for (int e = threadIdx.x; e < nj * (dk / 2); e += 256) {
         const int jj = e / (dk / 2), p = e % (dk / 2);
         const int s = cs + j0 + jj;
-        const float zeta = gpow(lg, static_cast<float>(L - 1 - (j0 + jj)));
+        const float zeta = gpow(lgp[p], static_cast<float>(L - 1 - (j0 + jj)));
         float k0, k1;
         rot_pair<IN>(k, (bh * N + s) * dk, p, p0 + s, a.ap.theta[p], &k0, &k1);
         kt[jj][2 * p] = zeta * k0;
@@ -183,7 +202,7 @@ __global__ void __launch_bounds__(256) generic_chunkwise(CallArgs a, const void*
       for (int64_t e = threadIdx.x; e < nS; e += 256) {
         const int d = static_cast<int>(e / dv), c = static_cast<int>(e % dv);
         float s = S[e];
-        if (j0 == 0) s *= gL;
+        if (j0 == 0) s *= gpow(lgp[d >> 1], static_cast<float>(L));
         for (int jj = 0; jj < nj; ++jj) s += kt[jj][d] * vt[jj][c];
         S[e] = s;
       }

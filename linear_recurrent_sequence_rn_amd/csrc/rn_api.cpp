@@ -60,13 +60,23 @@ rn_status check_desc(const rn_desc* d, Form form, rn::CallArgs* a) {
   if (!std::isfinite(d->qk_scale)) return fail(RN_ERR_INVALID_ARG, "qk_scale is not finite");
   if ((d->flags & RN_EPI_GN) && !(d->gn_eps >= 0.f && std::isfinite(d->gn_eps)))
     return fail(RN_ERR_INVALID_ARG, "gn_eps must be finite and >= 0");
-  if (!d->gamma || !d->theta) return fail(RN_ERR_INVALID_ARG, "gamma/theta is NULL");
+  if (!d->theta) return fail(RN_ERR_INVALID_ARG, "theta is NULL");
   std::memset(a, 0, sizeof(*a));
-  for (int h = 0; h < d->H; ++h) {
-    const float g = d->gamma[h];
-    if (!(g > 0.f && g <= 1.f)) return fail(RN_ERR_INVALID_ARG, "gamma[%d]=%g not in (0, 1]", h, g);
-    a->hp.gamma[h] = g;
-    a->hp.log2g[h] = static_cast<float>(std::log2(static_cast<double>(g)));
+  if (d->gamma_pair) {
+    // one decay per (head, pair), read by the kernels from device memory
+    if (reinterpret_cast<uintptr_t>(d->gamma_pair) % alignof(float))
+      return fail(RN_ERR_INVALID_ARG, "gamma_pair must be 4-byte aligned");
+    if (d->flags & RN_NORM_D_ROW)
+      return fail(RN_ERR_INVALID_ARG, "RN_NORM_D_ROW is defined by a scalar decay; not with gamma_pair");
+    a->gpair = d->gamma_pair;
+  } else {
+    if (!d->gamma) return fail(RN_ERR_INVALID_ARG, "gamma is NULL");
+    for (int h = 0; h < d->H; ++h) {
+      const float g = d->gamma[h];
+      if (!(g > 0.f && g <= 1.f)) return fail(RN_ERR_INVALID_ARG, "gamma[%d]=%g not in (0, 1]", h, g);
+      a->hp.gamma[h] = g;
+      a->hp.log2g[h] = static_cast<float>(std::log2(static_cast<double>(g)));
+    }
   }
   for (int j = 0; j < d->d_k / 2; ++j) {
     if (!std::isfinite(d->theta[j])) return fail(RN_ERR_INVALID_ARG, "theta[%d] is not finite", j);
@@ -127,7 +137,7 @@ const char* rn_status_str(rn_status s) {
 }
 
 static bool use_mfma_parallel(const rn_desc* d, const rn::CallArgs& a) {
-  return !(d->flags & RN_FORCE_GENERIC) && rn::parallel_mfma_supported(a, d->in_dtype);
+  return !(d->flags & RN_FORCE_GENERIC) && !a.gpair && rn::parallel_mfma_supported(a, d->in_dtype);
 }
 
 size_t rn_parallel_workspace_bytes(const rn_desc* desc) {
@@ -162,13 +172,15 @@ rn_status rn_retention_parallel(const rn_desc* desc, const void* q, const void* 
 }
 
 // Chunkwise schedules: the sequential fused kernel (default where it applies), the
-// chunk-parallel pair (on request, or where the sequential kernel's decay range does not
-// hold), the generic float32 kernel (everything else).
+// chunk-parallel pair (on request, where the sequential kernel's decay range does not
+// hold, and for one decay per coordinate pair), the generic float32 kernel (everything
+// else).
 enum class ChunkPath { kParallelPair, kSequential, kGeneric };
 
 static ChunkPath chunk_path(const rn_desc* d, const rn::CallArgs& a) {
   if (d->flags & RN_FORCE_GENERIC) return ChunkPath::kGeneric;
   const bool pair = rn::chunkwise_cp_supported(a, d->in_dtype);
+  if (a.gpair) return pair ? ChunkPath::kParallelPair : ChunkPath::kGeneric;
   if ((d->flags & RN_CHUNK_PARALLEL) && pair) return ChunkPath::kParallelPair;
   if (rn::chunkwise_mfma_supported(a, d->in_dtype)) return ChunkPath::kSequential;
   if (pair) return ChunkPath::kParallelPair;
@@ -269,7 +281,7 @@ rn_status rn_retention_recurrent_step_at(const rn_desc* desc, const int64_t* pos
 
 size_t rn_chunkwise_backward_workspace_bytes(const rn_desc* desc, int32_t chunk) {
   rn::CallArgs a;
-  if (chunk < 1 || check_desc(desc, Form::kChunkwise, &a) != RN_OK) return 0;
+  if (chunk < 1 || check_desc(desc, Form::kChunkwise, &a) != RN_OK || a.gpair) return 0;
   return align256(rn::backward_ws_bytes(a));
 }
 
@@ -284,6 +296,8 @@ rn_status rn_retention_chunkwise_backward(const rn_desc* desc, int32_t chunk, co
   rn_status s = check_desc(desc, Form::kChunkwise, &a);
   if (s != RN_OK) return s;
   if (chunk < 1) return fail(RN_ERR_INVALID_ARG, "chunk=%d must be >= 1", chunk);
+  if (desc->gamma_pair)
+    return fail(RN_ERR_UNSUPPORTED, "the backward takes one decay per head (gamma_pair is set)");
   if (int64_t(desc->B) * desc->H > 65535)
     return fail(RN_ERR_UNSUPPORTED, "B*H=%lld > 65535 (one grid row per head)",
                 (long long)desc->B * desc->H);

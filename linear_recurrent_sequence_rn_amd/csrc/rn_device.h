@@ -121,9 +121,21 @@ struct CallArgs {
   const float* gn_b;   // device [H*dv] or null
   const int64_t* pos;  // device [B]: position of each sequence's token 0, or null (pos0)
   const int32_t* lens; // device [B]: tokens of each sequence, or null (N)
+  const float* gpair;  // device [H * dk/2]: one decay per (head, coordinate pair), or null
   HeadParams hp;
   AngleParams ap;
 };
+
+// log2 of the decay of coordinate pair j of head h: the pair's own decay when the call
+// gives one per pair (log2 formed in float64, as the host does for the per-head decay),
+// else the head's.
+__device__ __forceinline__ float pair_log2g(const CallArgs& a, int h, int j) {
+  if (a.gpair) return static_cast<float>(log2(static_cast<double>(a.gpair[h * (a.dk / 2) + j])));
+  return a.hp.log2g[h];
+}
+__device__ __forceinline__ float pair_gamma(const CallArgs& a, int h, int j) {
+  return a.gpair ? a.gpair[h * (a.dk / 2) + j] : a.hp.gamma[h];
+}
 
 // Absolute position of token 0 of sequence b.
 __device__ __forceinline__ int64_t seq_pos0(const CallArgs& a, int b) {

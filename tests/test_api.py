@@ -225,3 +225,31 @@ def test_backward_errors():
     assert bwd(d) == rn.RN_ERR_UNSUPPORTED                   # B*H above one grid dimension
     d, keep = desc(flags=rn.RN_NORM_D_ROW)
     assert bwd(d) == rn.RN_ERR_INVALID_ARG                   # rescalings: parallel form only
+
+
+def test_pair_decay_descriptor():
+    """One decay per (head, coordinate pair) travels as a device array (gamma_pair); the
+    host checks its alignment and the combinations the forms accept, never its values.
+    Here the array is a host copy, which only calls that fail or size a workspace see."""
+    big = dict(d_k=256, d_v=512, theta=np.ones(128), H=4, N=1000)
+    gp = np.full((4, 128), 0.9, dtype=np.float32)
+    d, keep = desc(**big, gamma=gp)
+    assert not d.gamma and d.gamma_pair
+    # chunkwise runs the chunk-parallel pair at this shape: its workspace, not the
+    # sequential kernel's
+    dcp, keep_cp = desc(**big, gamma=np.full(4, 0.9), flags=rn.RN_CHUNK_PARALLEL)
+    assert rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), 256) == \
+        rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(dcp), 256) > 0
+    assert rn.lib.rn_parallel_workspace_bytes(ctypes.byref(d)) == 0       # generic parallel
+    assert chk(d, ws_bytes=1000) == rn.RN_ERR_WORKSPACE
+    dn, keep_n = desc(**big, gamma=gp, flags=rn.RN_NORM_D_ROW)
+    assert par(dn) == rn.RN_ERR_INVALID_ARG                               # scalar-decay rescaling
+    assert b"RN_NORM_D_ROW" in rn.lib.rn_last_error()
+    assert bwd(d) == rn.RN_ERR_UNSUPPORTED                                # backward: per-head decay
+    assert rn.lib.rn_chunkwise_backward_workspace_bytes(ctypes.byref(d), 256) == 0
+    d.gamma_pair = 0x1002
+    assert chk(d) == rn.RN_ERR_INVALID_ARG                                # misaligned
+    d.gamma_pair = None
+    assert chk(d) == rn.RN_ERR_INVALID_ARG                                # no decay at all
+    with pytest.raises(ValueError):
+        desc(**big, gamma=np.full((4, 127), 0.9, dtype=np.float32))

@@ -1,0 +1,228 @@
+"""GPU parity with one decay per (head, coordinate pair) — the form before the pages reduce
+the decay to a scalar — against the pair-decay oracle (oracle/vector_decay.py).
+
+Paths: the chunk-parallel MFMA pair (bf16 q/k/v, d_k 256, d_v 512; the decays folded into
+the half operands per coordinate, the score tiles among a workgroup's own rows as bf16
+high/low parts), the generic float32 kernels, and the decode kernels.
+
+Tolerances, as for the per-head decay paths:
+  * MFMA pair: raw outputs and final states per (b, h) ||gpu - ref||_inf <= 1e-2
+    ||ref||_inf (operands rounded to half, relative 2^-11, summed over many terms; inside
+    the diagonal score tiles a decay below 2^-13 is taken as 2^-13, which moves a score
+    term by less than 2^-13 of its undecayed size); after GroupNorm max-abs 2e-2, times
+    max(1, |swish(g)|) with the gate, plus half a bf16 ulp for bf16 output.
+  * float32 kernels (generic, decode): 1e-4 relative per (b, h).
+Decays: "pair_spread" draws them log-uniformly from 0.99999 down to 4.5e-5 with one pair
+at 1e-6 and one at exactly 1, so every fold limit is crossed; "pair_wide" is the
+RetNet-like range used at the 6.7B shape.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def rn():
+    import linear_recurrent_sequence_rn_amd as m
+    return m
+
+
+def rel_inf(gpu, ref):
+    g, r = O.to64(gpu), O.to64(ref)
+    err = np.abs(g - r).reshape(r.shape[0], r.shape[1], -1).max(-1)
+    nrm = np.abs(r).reshape(r.shape[0], r.shape[1], -1).max(-1)
+    return float((err / np.maximum(nrm, 1e-30)).max())
+
+
+def dev(x):
+    return None if x is None else x.to(DEV)
+
+
+def gdev(g):
+    return torch.from_numpy(np.ascontiguousarray(g)).to(DEV)
+
+
+def wl(**kw):
+    base = dict(name="t", form="chunkwise", B=1, H=2, N=200, d_k=256, d_v=512, dtype="bf16",
+                chunk=64, gamma_kind="pair_spread", qkv_std=1 / 16, seed=41)
+    base.update(kw)
+    return W.Workload(**base)
+
+
+def check_gated(out, ref, gate):
+    sw = np.abs(O.swish(gate)) if gate is not None else 1.0
+    bound = 2e-2 * np.maximum(1.0, sw)
+    d = np.abs(O.to64(out) - ref)
+    if out.dtype == torch.bfloat16:
+        bound = bound + np.abs(ref) * 2.0 ** -8
+    assert (d <= bound).all(), float((d / bound).max())
+
+
+@pytest.mark.parametrize("N,pos0,kind", [(200, 0, "pair_spread"), (700, 11, "pair_spread"),
+                                         (1, 70000, "pair_wide"), (513, 3, "pair_wide"),
+                                         (64, 5, "pair_spread"), (1000, 0, "pair_wide")])
+def test_mfma_pair_raw_output_and_state(N, pos0, kind):
+    w = wl(N=N, state_std=0.05, gamma_kind=kind)
+    x = W.make_inputs(w)
+    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), gdev(x["gamma"]),
+                                         x["theta"], 64, state_in=dev(x["state"]), state_out=True,
+                                         out_dtype=torch.float32, pos0=pos0)
+    ref, Sref = O.chunkwise_vec(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 64, pos0, 1.0,
+                                x["state"])
+    assert rel_inf(out.cpu(), ref) <= 1e-2
+    assert rel_inf(S.cpu(), Sref) <= 1e-2
+
+
+def test_mfma_pair_gn_gate_affine_fp32_and_bf16_out():
+    w = wl(N=333, gate=True, H=3)
+    x = W.make_inputs(w)
+    H, dv = 3, 512
+    gw = torch.randn(H * dv, generator=torch.Generator().manual_seed(5)) * 0.5 + 1
+    gb = torch.randn(H * dv, generator=torch.Generator().manual_seed(6)) * 0.1
+    raw, _ = O.chunkwise_vec(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 128)
+    ref = O.groupnorm_gate(raw, x["gate"], 1e-5, gw.reshape(H, dv), gb.reshape(H, dv))
+    for od in (torch.float32, torch.bfloat16):
+        out, _ = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]),
+                                             gdev(x["gamma"]), x["theta"], 128,
+                                             gate=dev(x["gate"]), gn=True, gn_weight=dev(gw),
+                                             gn_bias=dev(gb), out_dtype=od)
+        check_gated(out.cpu(), ref, x["gate"])
+
+
+def test_mfma_pair_equal_decays_match_the_per_head_path():
+    """Pair decays all equal to the head's decay give the per-head result (both schedules
+    are checked against their own oracles elsewhere; here against each other)."""
+    w = wl(N=600, gamma_kind="wide", H=4)
+    x = W.make_inputs(w)
+    gp = np.repeat(x["gamma"][:, None], 128, axis=1)
+    a, Sa = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), gdev(gp),
+                                        x["theta"], 256, state_out=True, out_dtype=torch.float32)
+    b, Sb = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
+                                        x["theta"], 256, state_out=True, out_dtype=torch.float32)
+    assert rel_inf(a.cpu(), b.cpu()) <= 1e-2
+    assert rel_inf(Sa.cpu(), Sb.cpu()) <= 1e-2
+
+
+def test_mfma_pair_varlen_batch():
+    """Padded batch with per-sequence lengths and first positions: each sequence equals the
+    oracle on its own rows; rows past a length stay zero."""
+    w = wl(B=3, N=700, gamma_kind="pair_spread", gate=True)
+    x = W.make_inputs(w)
+    lens = [700, 1, 300]
+    pos = [0, 5, 1234]
+    out, S = rn().rn_retention_chunkwise_varlen(
+        dev(x["q"]), dev(x["k"]), dev(x["v"]), gdev(x["gamma"]), x["theta"], 256,
+        pos=torch.tensor(pos, dtype=torch.int64, device=DEV),
+        lengths=torch.tensor(lens, dtype=torch.int32, device=DEV), state_out=True,
+        out_dtype=torch.float32)
+    out, S = out.cpu(), S.cpu()
+    for b, (L, p0) in enumerate(zip(lens, pos)):
+        sl = (slice(b, b + 1), slice(None), slice(0, L))
+        ref, Sref = O.chunkwise_vec(x["q"][sl], x["k"][sl], x["v"][sl], x["gamma"], x["theta"],
+                                    256, p0)
+        assert rel_inf(out[sl], ref) <= 1e-2, b
+        assert rel_inf(S[b:b + 1], Sref) <= 1e-2, b
+        assert (out[b, :, L:] == 0).all()
+
+
+@pytest.mark.parametrize("chunk", [16, 5, 64])
+@pytest.mark.parametrize("gn", [False, True])
+def test_generic_fp32_chunkwise(chunk, gn):
+    w = wl(N=64, d_k=16, d_v=16, dtype="f32", qkv_std=1.0, state_std=0.3, H=3, B=2)
+    x = W.make_inputs(w)
+    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), gdev(x["gamma"]),
+                                         x["theta"], chunk, state_in=dev(x["state"]),
+                                         state_out=True, gn=gn, pos0=9, qk_scale=0.7)
+    ref, Sref = O.chunkwise_vec(x["q"], x["k"], x["v"], x["gamma"], x["theta"], chunk, 9, 0.7,
+                                x["state"])
+    assert rel_inf(out.cpu(), O.apply_epilogue(ref, gn=gn)) <= 1e-4
+    assert rel_inf(S.cpu(), Sref) <= 1e-4
+
+
+def test_generic_chunkwise_bf16_other_shape():
+    """bf16 inputs outside the MFMA pair's shapes run the float32 generic kernel."""
+    w = wl(N=90, d_k=64, d_v=48, H=2)
+    x = W.make_inputs(w)
+    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), gdev(x["gamma"]),
+                                         x["theta"], 32, state_out=True, out_dtype=torch.float32)
+    ref, Sref = O.chunkwise_vec(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 32)
+    assert rel_inf(out.cpu(), ref) <= 1e-4
+    assert rel_inf(S.cpu(), Sref) <= 1e-4
+
+
+@pytest.mark.parametrize("norm_r", [False, True])
+def test_generic_fp32_parallel(norm_r):
+    w = wl(N=50, d_k=16, d_v=16, dtype="f32", qkv_std=1.0, H=2, B=2)
+    x = W.make_inputs(w)
+    out = rn().rn_retention_parallel(dev(x["q"]), dev(x["k"]), dev(x["v"]), gdev(x["gamma"]),
+                                     x["theta"], norm_r=norm_r, qk_scale=0.5, pos0=3)
+    ref = O.parallel_vec(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 3, 0.5, norm_r=norm_r)
+    assert rel_inf(out.cpu(), ref) <= 1e-4
+
+
+@pytest.mark.parametrize("shape", [(256, 512, "bf16"), (16, 20, "f32"), (64, 128, "bf16")])
+def test_decode_steps(shape):
+    dk, dv, dt = shape
+    w = wl(B=3, H=16 if dk == 256 else 3, N=1, d_k=dk, d_v=dv, dtype=dt, state_std=0.1)
+    x = W.make_inputs(w)
+    S = x["state"].clone().to(DEV)
+    Sref = x["state"]
+    for st in range(3):
+        y = W.make_inputs(w, seed=100 + st)
+        out = rn().rn_retention_recurrent_step(dev(y["q"]), dev(y["k"]), dev(y["v"]),
+                                               gdev(x["gamma"]), x["theta"], S, 77 + st,
+                                               out_dtype=torch.float32)
+        o_ref, Sref = O.recurrent_step_vec(y["q"], y["k"], y["v"], x["gamma"], x["theta"], 77 + st,
+                                           1.0, Sref)
+        assert rel_inf(out.cpu()[:, :, 0], o_ref) <= 1e-4, st
+    assert rel_inf(S.cpu(), Sref) <= 1e-4
+
+
+def test_prefill_then_decode():
+    """Chunkwise prefill (MFMA pair) hands its state to per-sequence decode steps; the
+    outputs follow the recurrence over the whole sequence."""
+    w = wl(B=2, N=300, gamma_kind="pair_wide")
+    x = W.make_inputs(w)
+    g = gdev(x["gamma"])
+    _, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), g, x["theta"], 256,
+                                       state_out=True, out_dtype=torch.float32)
+    y = W.make_inputs(w, N=3, seed=501)
+    pos = torch.tensor([300, 300], dtype=torch.int64, device=DEV)
+    outs = []
+    for t in range(3):
+        o = rn().rn_retention_recurrent_step_at(dev(y["q"][:, :, t:t + 1]), dev(y["k"][:, :, t:t + 1]),
+                                                dev(y["v"][:, :, t:t + 1]), g, x["theta"], S, pos,
+                                                out_dtype=torch.float32)
+        outs.append(o.cpu())
+        pos += 1
+    qa = torch.cat([x["q"], y["q"]], 2)
+    ka = torch.cat([x["k"], y["k"]], 2)
+    va = torch.cat([x["v"], y["v"]], 2)
+    ref, Sref = O.recurrent_vec(qa, ka, va, x["gamma"], x["theta"])
+    assert rel_inf(torch.cat(outs, 2), ref[:, :, 300:]) <= 1e-2
+    assert rel_inf(S.cpu(), Sref) <= 1e-2
+
+
+def test_full_6p7b_pair_shape_sampled_heads():
+    """The 6.7B training shape (2 x 16 heads x 8192 tokens, GroupNorm + gate, bf16 out) in the
+    launch configuration the benchmark times; two heads are checked in full against the
+    oracle's recurrence (one head's recurrence finishes in seconds), with the final state."""
+    w = W.WORKLOADS["chunkwise_6p7b_pair"]
+    x = W.make_inputs(w)
+    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), gdev(x["gamma"]),
+                                         x["theta"], w.chunk, gate=dev(x["gate"]), gn=True,
+                                         state_out=True)
+    torch.cuda.synchronize()
+    out, S = out.cpu(), S.cpu()
+    for b, h in ((0, 0), (1, 15), (1, 6)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        raw, Sref = O.recurrent_vec(x["q"][sl], x["k"][sl], x["v"][sl], x["gamma"][h:h + 1],
+                                    x["theta"])
+        ref = O.groupnorm_gate(raw, x["gate"][sl], w.gn_eps)
+        check_gated(out[sl], ref, x["gate"][sl])
+        assert rel_inf(S[sl], Sref) <= 1e-2, (b, h)

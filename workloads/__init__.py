@@ -26,7 +26,7 @@ import torch
 
 __all__ = [
     "Workload", "WORKLOADS", "theta_default", "gamma_small", "gamma_wide",
-    "make_inputs", "make_decode_step_inputs",
+    "gamma_pairs_wide", "gamma_pairs_spread", "make_inputs", "make_decode_step_inputs",
 ]
 
 
@@ -48,6 +48,41 @@ def gamma_wide(H: int) -> np.ndarray:
     return (1.0 - 2.0 ** (-5.0 - 4.0 * h / H)).astype(np.float32)
 
 
+def gamma_pairs_wide(H: int, d_k: int) -> np.ndarray:
+    """One decay per (head, coordinate pair): 1 - 2^-(5 + 4h/H + 4j/(P-1)), P = d_k/2.
+    Each head spans four octaves of 1 - gamma across its pairs, the heads together the
+    range 1 - 2^-5 .. 1 - 2^-13 (float32 [H, P])."""
+    P = d_k // 2
+    h = np.arange(H, dtype=np.float64)[:, None]
+    j = np.arange(P, dtype=np.float64)[None, :]
+    return (1.0 - 2.0 ** (-(5.0 + 4.0 * h / H + 4.0 * j / max(P - 1, 1)))).astype(np.float32)
+
+
+def gamma_pairs_spread(H: int, d_k: int, seed: int) -> np.ndarray:
+    """Pair decays over a wide range, for checking robustness: gamma = exp(-u) with u
+    log-uniform in [1e-5, 10] (gamma from 0.99999 down to 4.5e-5), pair 0 of head 0 set to
+    1e-6 and pair 1 of head 0 to exactly 1 (float32 [H, d_k/2])."""
+    rng = np.random.default_rng([seed, 77])
+    u = np.exp(rng.uniform(np.log(1e-5), np.log(10.0), (H, d_k // 2)))
+    g = np.exp(-u)
+    g[0, 0] = 1e-6
+    if d_k >= 4:
+        g[0, 1] = 1.0
+    return g.astype(np.float32)
+
+
+def _gamma(kind: str, H: int, d_k: int, seed: int) -> np.ndarray:
+    if kind == "small":
+        return gamma_small(H)
+    if kind == "wide":
+        return gamma_wide(H)
+    if kind == "pair_wide":
+        return gamma_pairs_wide(H, d_k)
+    if kind == "pair_spread":
+        return gamma_pairs_spread(H, d_k, seed)
+    raise ValueError(kind)
+
+
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
@@ -65,14 +100,14 @@ class Workload:
     gn: bool = False
     gate: bool = False
     gn_eps: float = 1e-5
-    gamma_kind: str = "small"   # "small" | "wide"
+    gamma_kind: str = "small"   # "small" | "wide" (per head) | "pair_wide" | "pair_spread" (per pair)
     qkv_std: float = 1.0        # q,k,v ~ N(0, qkv_std^2)
     state_std: float = 0.0      # initial state ~ N(0, state_std^2); 0 = no state
     steps: int = 0              # decode steps (recurrent workload)
     seed: int = 0
 
     def gamma(self) -> np.ndarray:
-        return gamma_small(self.H) if self.gamma_kind == "small" else gamma_wide(self.H)
+        return _gamma(self.gamma_kind, self.H, self.d_k, self.seed)
 
     def theta(self) -> np.ndarray:
         return theta_default(self.d_k)
@@ -97,6 +132,10 @@ WORKLOADS = {
     "decode_6p7b": Workload("decode_6p7b", "recurrent", B=128, H=16, N=1, d_k=256,
                             d_v=512, dtype="bf16", gamma_kind="wide", qkv_std=_S,
                             state_std=0.1, steps=1024, seed=4),
+    # the 6.7B training shape with one decay per (head, coordinate pair)
+    "chunkwise_6p7b_pair": Workload("chunkwise_6p7b_pair", "chunkwise", B=2, H=16, N=8192,
+                                    d_k=256, d_v=512, dtype="bf16", chunk=256, gn=True,
+                                    gate=True, gamma_kind="pair_wide", qkv_std=_S, seed=6),
     # long-sequence chunkwise: 128 chunks of 512, GroupNorm
     "chunkwise_long": Workload("chunkwise_long", "chunkwise", B=1, H=16, N=65536,
                                d_k=256, d_v=512, dtype="bf16", chunk=512, gn=True,
@@ -114,7 +153,8 @@ def make_inputs(w: Workload, *, N: Optional[int] = None, B: Optional[int] = None
     """Draw q, k, v, gate, state for workload ``w`` (optionally resized).
 
     Returns CPU torch tensors in the workload dtype (q, k, v, gate) and float32
-    (state, or None), plus float32 numpy ``gamma`` [H] and ``theta`` [d_k/2].
+    (state, or None), plus float32 numpy ``gamma`` ([H], or [H, d_k/2] for the pair
+    kinds) and ``theta`` [d_k/2].
     """
     B = w.B if B is None else B
     H = w.H if H is None else H
@@ -127,7 +167,7 @@ def make_inputs(w: Workload, *, N: Optional[int] = None, B: Optional[int] = None
     state = None
     if w.state_std > 0:
         state = rng.standard_normal((B, H, w.d_k, w.d_v), dtype=np.float32) * np.float32(w.state_std)
-    gamma = w.gamma() if H == w.H else (gamma_small(H) if w.gamma_kind == "small" else gamma_wide(H))
+    gamma = _gamma(w.gamma_kind, H, w.d_k, w.seed)
     return {
         "q": _round(q, w.dtype), "k": _round(k, w.dtype), "v": _round(v, w.dtype),
         "gate": None if gate is None else _round(gate, w.dtype),
