@@ -67,7 +67,8 @@ typedef int32_t rn_dtype;
                                        tokens, then all chunks' outputs in parallel) instead of the
                                        single sequential kernel; same result, another workspace size.
                                        It is also what runs where the sequential kernel does not
-                                       apply (gamma^32 < 2^-6) at d_k 256, d_v 512 */
+                                       apply (gamma^32 < 2^-6, or gamma_pair set) at d_k 256,
+                                       d_v 512 */
 
 typedef struct rn_desc {
     int32_t B;             /* batch, >= 1 */
