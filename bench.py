@@ -7,8 +7,9 @@ N=8192, d_k=256, d_v=512, chunk 256, bf16 q/k/v/gate, GroupNorm + swish gate, bf
 output, float32 final state) with inputs resident in HBM. The line also carries the
 decode step time of the 6.7B-shaped decode workload (batch 128, 16 heads, float32
 state updated in place; 1024 sequential steps timed back to back), and secondary records
-for the chunkwise backward, the same forward with one decay per (head, coordinate pair)
-and the parallel form.
+for the chunkwise backward, the same forward with one decay per (head, coordinate pair),
+the gated multi-scale layer around it (projections and output projection) and the
+parallel form.
 
 Prints one JSON line. `roofline` describes the fused chunkwise kernel: its average
 duration is measured with HIP events recorded on the stream it runs on; achieved
@@ -106,9 +107,11 @@ def main():
     ap.add_argument("--no-parallel", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-pair", action="store_true")
+    ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--source-hash", action="store_true",
                     help="print the chunkwise kernel's source hash (as recorded in its profile) and exit")
-    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "backward", "pair", "copy"],
+    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "backward", "pair", "layer",
+                                       "copy"],
                     default=None,
                     help="run one workload only (for profiling); 'copy' times a plain 1 GiB "
                          "device copy, the reference for the HBM byte counters")
@@ -145,7 +148,7 @@ def main():
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "copy_GBs": 2 * src.numel() * 4 / dt / 1e9}))
         return
-    if args.only in ("decode", "parallel", "backward", "pair"):
+    if args.only in ("decode", "parallel", "backward", "pair", "layer"):
         args.no_cpu_baseline = True
     w = W.WORKLOADS["chunkwise_6p7b"]
     x = W.make_inputs(w)
@@ -160,7 +163,7 @@ def main():
         rn.rn_retention_chunkwise(q, k, v, gamma, theta, w.chunk, gate=gate, gn=True,
                                   gn_eps=w.gn_eps, state_out=S_out, out=out, workspace=ws)
 
-    if args.only in ("decode", "parallel", "backward", "pair"):
+    if args.only in ("decode", "parallel", "backward", "pair", "layer"):
         args.steps = args.warmup = 1
     for _ in range(args.warmup):
         step()
@@ -212,7 +215,7 @@ def main():
     # Gradients of q, k, v and the gate through GroupNorm + gate, given a random dout;
     # float32 kernels. Algorithmic flops: twice the forward's (each product of the forward
     # has two gradient products of the same size).
-    if args.only in ("chunkwise", "decode", "parallel", "pair"):
+    if args.only in ("chunkwise", "decode", "parallel", "pair", "layer"):
         args.no_backward = True
     if not args.no_backward:
         dout = torch.randn(v.shape, generator=torch.Generator(device=dev).manual_seed(5),
@@ -245,16 +248,18 @@ def main():
         args.no_parallel = True
         args.no_decode = True
         args.no_pair = True
+        args.no_layer = True
 
     # ---- the same forward with one decay per (head, coordinate pair) -------------------
     # Chunk-parallel pair of kernels (state snapshots, then outputs) with the decays
     # folded into the operands per coordinate; same algorithmic bytes and flops as the
     # per-head-decay forward.
-    if args.only in ("chunkwise", "decode", "parallel"):
+    if args.only in ("chunkwise", "decode", "parallel", "layer"):
         args.no_pair = True
     if args.only == "pair":
         args.no_parallel = True
         args.no_decode = True
+        args.no_layer = True
     if not args.no_pair:
         wv = W.WORKLOADS["chunkwise_6p7b_pair"]
         xv = W.make_inputs(wv)
@@ -289,6 +294,52 @@ def main():
                              "algorithmic_bytes": vby, "algorithmic_flops": vfl,
                              "mfma_tflops": vfl / vs / 1e12, "kernels": "cp_states + cp_outputs"}
         del xv, qv, kv, vv, gv, outv, Sv, wsv
+
+    # ---- the gated multi-scale layer around the same retention ---------------------------
+    # x [2, 8192, 4096] -> projections (rocBLAS bf16 GEMMs) -> fused chunkwise retention
+    # with GroupNorm + gate -> heads regrouped by token -> W_O. Algorithmic flops: the five
+    # projections plus the retention's.
+    if args.only in ("chunkwise", "decode", "parallel"):
+        args.no_layer = True
+    if args.only == "layer":
+        args.no_parallel = True
+        args.no_decode = True
+    if not args.no_layer:
+        D = W.LAYER_D_MODEL
+        xl = W.make_layer_inputs(w, D)
+        lt = {n: xl[n].to(dev) for n in ("x", "w_q", "w_k", "w_v", "w_g", "w_o")}
+        outl = torch.empty(w.B, w.N, D, dtype=torch.bfloat16, device=dev)
+        wsl = torch.empty(rn.rn_msr_layer_workspace_bytes(lt["x"], w.H, w.d_k, w.d_v, xl["gamma"],
+                                                          xl["theta"], w.chunk), dtype=torch.uint8,
+                          device=dev)
+
+        def lstep():
+            rn.rn_msr_layer_forward(lt["x"], lt["w_q"], lt["w_k"], lt["w_v"], lt["w_g"], lt["w_o"],
+                                    xl["gamma"], xl["theta"], w.H, w.d_k, w.d_v, w.chunk,
+                                    out=outl, workspace=wsl)
+
+        for _ in range(3):
+            lstep()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            lstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ls = e0.elapsed_time(e1) / reps / 1e3
+        tok = w.B * w.N
+        gemm_fl = 2 * tok * D * (2 * w.H * w.d_k + 2 * w.H * w.d_v) + 2 * tok * w.H * w.d_v * D
+        lfl = gemm_fl + flops
+        rec["layer"] = {"workload": f"gated multi-scale layer on chunkwise_6p7b: x [2, 8192, {D}] bf16, "
+                                    "W_Q/W_K [4096, 4096], W_V/W_G [4096, 8192], W_O [8192, 4096], "
+                                    "GroupNorm + swish gate, bf16 out",
+                        "ms": ls * 1e3, "tokens_per_s": tok / ls, "bound": "mfma",
+                        "algorithmic_flops": lfl, "gemm_flops": gemm_fl, "tflops": lfl / ls / 1e12,
+                        "mfma_frac": lfl / ls / 1e12 / BF16_PEAK_TFLOPS,
+                        "workspace_bytes": wsl.numel()}
+        del xl, lt, outl, wsl
 
     # ---- parallel form, 1.3B shape (secondary record) --------------------------------
     if args.only in ("chunkwise", "decode"):

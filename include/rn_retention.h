@@ -242,6 +242,38 @@ rn_status rn_retention_chunkwise_backward(const rn_desc* desc, int32_t chunk, co
                                           size_t workspace_bytes, void* stream);
 
 /*
+ * Gated multi-scale retention layer (m0nads notes and hwhale notes, "Gated Multi-Scale
+ * Retention"; sdkjxy walkthrough, the MSR block):
+ *     Q = X W_Q,  K = X W_K,  V = X W_V,  G = X W_G
+ *     Y_h = GroupNorm_h(Retention_h(Q_h, K_h, V_h))      (chunkwise form, this desc)
+ *     out = (swish(G) ⊙ Concat_h Y_h) W_O
+ * where head h owns columns [h d_k, (h+1) d_k) of Q and K and [h d_v, (h+1) d_v) of V
+ * and G. The pages state W_G and W_O as d x d; here they are d_model x (H d_v) and
+ * (H d_v) x d_model, which is d x d when H d_v = d_model.
+ * Arguments (DEVICE, row-major, caller-owned):
+ *     x    [B, N, d_model] bf16            w_q, w_k [d_model, H*d_k] bf16
+ *     w_v, w_g [d_model, H*d_v] bf16       w_o  [H*d_v, d_model] bf16
+ *     out  [B, N, d_model] in desc->out_dtype (bf16 or float32)
+ *     state_in / state_out [B, H, d_k, d_v] float32 or NULL, as for rn_retention_chunkwise.
+ * desc: B, H, N, d_k, d_v, decays (gamma or gamma_pair), theta, pos0, qk_scale, GroupNorm
+ * parameters and flags as for rn_retention_chunkwise; in_dtype must be RN_BF16 (else
+ * RN_ERR_UNSUPPORTED); RN_EPI_GN applies the per-head GroupNorm, RN_EPI_GATE the gate
+ * (w_g is then required; without the flag w_g is not read). d_v must be a multiple of 8.
+ * The four projections and W_O run as rocBLAS GEMMs with bf16 operands and float32
+ * accumulation; Q, K, V, G and the heads' outputs are held in bf16 in the workspace
+ * (rn_msr_layer_workspace_bytes, linear in B*N), then the retention kernels run as in
+ * rn_retention_chunkwise. The first call on a host thread and device creates a rocBLAS
+ * handle, which keeps its own device memory for the life of the process.
+ * Errors: as for rn_retention_chunkwise; a rocBLAS failure returns RN_ERR_HIP.
+ */
+size_t rn_msr_layer_workspace_bytes(const rn_desc* desc, int32_t d_model, int32_t chunk);
+rn_status rn_msr_layer_forward(const rn_desc* desc, int32_t d_model, int32_t chunk,
+                               const void* x, const void* w_q, const void* w_k,
+                               const void* w_v, const void* w_g, const void* w_o,
+                               const float* state_in, float* state_out, void* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Standalone per-head GroupNorm (+ swish gate):
  *   y = (x - mean) / sqrt(var + eps) * w + b over the d_v channels of each (b,h,t),
  *   out = y * g * sigmoid(g) if gate != NULL, else y.

@@ -25,7 +25,7 @@ __all__ = [
     "rn_retention_parallel", "rn_retention_chunkwise", "rn_retention_recurrent_step",
     "rn_retention_chunkwise_varlen", "rn_retention_recurrent_step_at", "rn_groupnorm_gate",
     "rn_retention_chunkwise_backward", "rn_chunkwise_backward_workspace_bytes", "rn_chunkwise_workspace_bytes", "rn_parallel_workspace_bytes",
-    "rn_version", "make_desc",
+    "rn_version", "make_desc", "rn_msr_layer_forward", "rn_msr_layer_workspace_bytes",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "librn_retention.so"
@@ -41,6 +41,7 @@ EXPORTED_SYMBOLS = (
     "rn_retention_recurrent_step", "rn_retention_chunkwise_varlen",
     "rn_retention_recurrent_step_at", "rn_groupnorm_gate", "rn_status_str", "rn_last_error",
     "rn_version", "rn_retention_chunkwise_backward", "rn_chunkwise_backward_workspace_bytes",
+    "rn_msr_layer_workspace_bytes", "rn_msr_layer_forward",
 )
 
 
@@ -88,6 +89,10 @@ def _load():
     L.rn_chunkwise_backward_workspace_bytes.restype = sz
     L.rn_retention_chunkwise_backward.argtypes = [D, i32] + [vp] * 14 + [vp, sz, vp]
     L.rn_retention_chunkwise_backward.restype = i32
+    L.rn_msr_layer_workspace_bytes.argtypes = [D, i32, i32]
+    L.rn_msr_layer_workspace_bytes.restype = sz
+    L.rn_msr_layer_forward.argtypes = [D, i32, i32] + [vp] * 9 + [vp, sz, vp]
+    L.rn_msr_layer_forward.restype = i32
     L.rn_groupnorm_gate.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                     ctypes.c_float, vp, vp]
     L.rn_groupnorm_gate.restype = i32
@@ -412,6 +417,68 @@ def rn_retention_chunkwise_backward(q, k, v, gamma, theta, chunk, dout, *, gate=
         _ptr(res.get("dgate")), _ptr(res.get("dstate_in")), _ptr(res.get("dgn_weight")),
         _ptr(res.get("dgn_bias")), _ptr(workspace), workspace.numel(), _stream(q)))
     return res
+
+
+def _layer_desc(x, H, d_k, d_v, gamma, theta, flags, pos0, qk_scale, gn_eps, gn_weight, gn_bias,
+                out_dtype):
+    if x.dim() != 3 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16 [B, N, d_model]")
+    B, N, _ = x.shape
+    if len(gamma) != H or len(theta) != d_k // 2:
+        raise ValueError(f"need gamma[{H}] (or [{H}, {d_k // 2}]) and theta[{d_k // 2}]")
+    od = torch.bfloat16 if out_dtype is None else out_dtype
+    for t in (gn_weight, gn_bias):
+        if t is not None:
+            _ptr(t)
+            if t.dtype != torch.float32 or t.numel() != H * d_v:
+                raise ValueError("gn_weight/gn_bias must be float32 with H*d_v elements")
+    d, keep = make_desc(B, H, N, d_k, d_v, RN_BF16, _dtype_code(od), gamma, theta, flags=flags,
+                        pos0=pos0, qk_scale=qk_scale, gn_eps=gn_eps, gn_weight=gn_weight,
+                        gn_bias=gn_bias, device=x.device)
+    return d, keep, od
+
+
+def rn_msr_layer_workspace_bytes(x, H, d_k, d_v, gamma, theta, chunk, *, gn=True, gate=True,
+                                 out_dtype=None) -> int:
+    d, keep, _ = _layer_desc(x, H, d_k, d_v, gamma, theta, _flags(False, False, gn, gate or None, False),
+                             0, 1.0, 1e-5, None, None, out_dtype)
+    return int(lib.rn_msr_layer_workspace_bytes(ctypes.byref(d), x.shape[-1], chunk))
+
+
+def rn_msr_layer_forward(x, w_q, w_k, w_v, w_g, w_o, gamma, theta, H, d_k, d_v, chunk, *,
+                         state_in=None, state_out=None, out=None, out_dtype=None, workspace=None,
+                         pos0=0, qk_scale=1.0, gn=True, gn_eps=1e-5, gn_weight=None,
+                         gn_bias=None):
+    """Gated multi-scale retention layer: (swish(X W_G) ⊙ GN_h(Retention_h)) W_O with the
+    heads' Q, K, V projected from x [B, N, d_model] (bf16). Weights: w_q, w_k
+    [d_model, H*d_k], w_v, w_g [d_model, H*d_v], w_o [H*d_v, d_model] (bf16); w_g=None
+    leaves the gate out. Returns (out [B, N, d_model], state_out)."""
+    B, N, D = x.shape
+    gate = w_g is not None
+    for name, w, shape in (("w_q", w_q, (D, H * d_k)), ("w_k", w_k, (D, H * d_k)),
+                           ("w_v", w_v, (D, H * d_v)), ("w_g", w_g, (D, H * d_v)),
+                           ("w_o", w_o, (H * d_v, D))):
+        if w is not None and (tuple(w.shape) != shape or w.dtype != torch.bfloat16):
+            raise ValueError(f"{name} must be bfloat16 {shape}")
+    flags = _flags(False, False, gn, True if gate else None, False)
+    d, keep, od = _layer_desc(x, H, d_k, d_v, gamma, theta, flags, pos0, qk_scale, gn_eps,
+                              gn_weight, gn_bias, out_dtype)
+    out = _out(out, (B, N, D), od, x.device)
+    if state_out is True:
+        state_out = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=x.device)
+    elif state_out is False:
+        state_out = None
+    for s_ in (state_in, state_out):
+        if s_ is not None and (s_.dtype != torch.float32 or tuple(s_.shape) != (B, H, d_k, d_v)):
+            raise ValueError("states must be float32 [B,H,d_k,d_v]")
+    need = int(lib.rn_msr_layer_workspace_bytes(ctypes.byref(d), D, chunk))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _check(lib.rn_msr_layer_forward(ctypes.byref(d), D, chunk, _ptr(x), _ptr(w_q), _ptr(w_k),
+                                    _ptr(w_v), _ptr(w_g), _ptr(w_o), _ptr(state_in),
+                                    _ptr(state_out), _ptr(out), _ptr(workspace),
+                                    workspace.numel(), _stream(x)))
+    return out, state_out
 
 
 def rn_groupnorm_gate(x, gate=None, weight=None, bias=None, eps=1e-5, *, out=None, out_dtype=None):

@@ -3,6 +3,7 @@
 // nothing; failures return a status and leave a thread-local message.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -319,6 +320,92 @@ rn_status rn_retention_chunkwise_backward(const rn_desc* desc, int32_t chunk, co
   return hip_status(rn::launch_backward(a, desc->in_dtype, desc->out_dtype, x, workspace,
                                         static_cast<hipStream_t>(stream)),
                     "chunkwise backward launch");
+}
+
+// ---- gated multi-scale retention layer ---------------------------------------------------
+
+namespace {
+
+struct LayerPlan {
+  rn::LayerArgs L;
+  bool gate;
+  size_t off_q, off_k, off_v, off_g, off_o, off_ret, ret_bytes, total;
+  rn_desc ret_desc;   // the retention call: bf16 head outputs
+};
+
+rn_status plan_layer(const rn_desc* d, int32_t d_model, int32_t chunk, LayerPlan* p) {
+  rn::CallArgs a;
+  rn_status s = check_desc(d, Form::kChunkwise, &a);
+  if (s != RN_OK) return s;
+  if (chunk < 1) return fail(RN_ERR_INVALID_ARG, "chunk=%d must be >= 1", chunk);
+  if (d_model < 1) return fail(RN_ERR_INVALID_ARG, "d_model=%d must be >= 1", d_model);
+  if (d->in_dtype != RN_BF16)
+    return fail(RN_ERR_UNSUPPORTED, "the layer takes bf16 input and weights (in_dtype)");
+  if (d->d_v % 8) return fail(RN_ERR_UNSUPPORTED, "the layer needs d_v %% 8 == 0 (got %d)", d->d_v);
+  const int64_t cols = int64_t(d->H) * std::max(d->d_k, d->d_v);
+  if (cols > (int64_t(1) << 30) || int64_t(d->B) * d->N > (int64_t(1) << 30) ||
+      d_model > (1 << 30))
+    return fail(RN_ERR_UNSUPPORTED, "layer dimensions beyond 32-bit GEMM sizes");
+  p->L = rn::LayerArgs{d->B, d->H, d->N, d_model, d->d_k, d->d_v};
+  p->gate = (d->flags & RN_EPI_GATE) != 0;
+  p->ret_desc = *d;
+  p->ret_desc.out_dtype = RN_BF16;
+  const size_t tok = size_t(d->B) * d->H * d->N;
+  const size_t bq = align256(tok * d->d_k * 2), bv = align256(tok * d->d_v * 2);
+  p->off_q = 0;
+  p->off_k = bq;
+  p->off_v = 2 * bq;
+  p->off_g = 2 * bq + bv;
+  p->off_o = p->off_g + (p->gate ? bv : 0);
+  p->off_ret = p->off_o + bv;
+  p->ret_bytes = rn_chunkwise_workspace_bytes(&p->ret_desc, chunk);
+  p->total = p->off_ret + align256(p->ret_bytes);
+  return RN_OK;
+}
+
+rn_status blas_status(int st, const char* what) {
+  if (st == 0) return RN_OK;
+  return fail(RN_ERR_HIP, "%s: %s", what, rn::blas_status_string(st));
+}
+
+}  // namespace
+
+size_t rn_msr_layer_workspace_bytes(const rn_desc* desc, int32_t d_model, int32_t chunk) {
+  LayerPlan p;
+  if (plan_layer(desc, d_model, chunk, &p) != RN_OK) return 0;
+  return p.total;
+}
+
+rn_status rn_msr_layer_forward(const rn_desc* desc, int32_t d_model, int32_t chunk, const void* x,
+                               const void* w_q, const void* w_k, const void* w_v, const void* w_g,
+                               const void* w_o, const float* state_in, float* state_out,
+                               void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  LayerPlan p;
+  rn_status s = plan_layer(desc, d_model, chunk, &p);
+  if (s != RN_OK) return s;
+  if (!x || !w_q || !w_k || !w_v || !w_o || !out)
+    return fail(RN_ERR_INVALID_ARG, "x/w_q/w_k/w_v/w_o/out pointer is NULL");
+  if (p.gate && !w_g) return fail(RN_ERR_INVALID_ARG, "RN_EPI_GATE needs w_g");
+  if (!workspace || workspace_bytes < p.total)
+    return fail(RN_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, p.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(RN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  g_err[0] = 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  void *q = ws + p.off_q, *k = ws + p.off_k, *v = ws + p.off_v, *o = ws + p.off_o;
+  void* g = p.gate ? ws + p.off_g : nullptr;
+  if ((s = blas_status(rn::layer_project(p.L, x, w_q, desc->d_k, q, st), "projection X W_Q")) ||
+      (s = blas_status(rn::layer_project(p.L, x, w_k, desc->d_k, k, st), "projection X W_K")) ||
+      (s = blas_status(rn::layer_project(p.L, x, w_v, desc->d_v, v, st), "projection X W_V")))
+    return s;
+  if (p.gate && (s = blas_status(rn::layer_project(p.L, x, w_g, desc->d_v, g, st), "projection X W_G")))
+    return s;
+  if ((s = chunkwise_call(&p.ret_desc, chunk, nullptr, nullptr, q, k, v, g, state_in, state_out, o,
+                          ws + p.off_ret, p.ret_bytes, stream)) != RN_OK)
+    return s;
+  // the regrouped heads go to v's region (v is no longer needed; same size)
+  return blas_status(rn::layer_output(p.L, o, v, w_o, out, desc->out_dtype, st), "output projection");
 }
 
 rn_status rn_groupnorm_gate(int32_t B, int32_t H, int32_t N, int32_t d_v, rn_dtype in_dtype,

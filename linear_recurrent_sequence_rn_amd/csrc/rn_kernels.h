@@ -53,4 +53,15 @@ hipError_t launch_parallel_mfma(const CallArgs& a, int out_dt, const void* q, co
                                 const void* v, const void* gate, void* out, void* ws,
                                 hipStream_t st);
 
+// Gated multi-scale retention layer: rocBLAS projections and output projection (return
+// values are rocblas_status codes; 0 = success).
+struct LayerArgs {
+  int B, H, N, d_model, dk, dv;
+};
+int layer_project(const LayerArgs& L, const void* x, const void* w, int d, void* y,
+                  hipStream_t stream);
+int layer_output(const LayerArgs& L, const void* o, void* ot, const void* w_o, void* out,
+                 int out_dtype, hipStream_t stream);
+const char* blas_status_string(int status);
+
 }  // namespace rn

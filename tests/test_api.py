@@ -253,3 +253,32 @@ def test_pair_decay_descriptor():
     assert chk(d) == rn.RN_ERR_INVALID_ARG                                # no decay at all
     with pytest.raises(ValueError):
         desc(**big, gamma=np.full((4, 127), 0.9, dtype=np.float32))
+
+
+def layer(d, d_model=64, chunk=16, ws=FAKE, ws_bytes=1 << 40, w_g=FAKE, x=FAKE):
+    return rn.lib.rn_msr_layer_forward(ctypes.byref(d), d_model, chunk, x, FAKE, FAKE, FAKE, w_g,
+                                       FAKE, None, None, FAKE, ws, ws_bytes, None)
+
+
+def test_layer_errors_and_workspace():
+    d, keep = desc(flags=rn.RN_EPI_GN | rn.RN_EPI_GATE)
+    need = rn.lib.rn_msr_layer_workspace_bytes(ctypes.byref(d), 64, 16)
+    # q, k (d_k) + v, g, head outputs (d_v), each 256-aligned, + the retention workspace
+    tok = 1 * 2 * 8
+    a = lambda n: (n + 255) // 256 * 256
+    d_ret, keep_ret = desc(flags=rn.RN_EPI_GN | rn.RN_EPI_GATE, out_dtype=rn.RN_BF16)
+    ret = rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(d_ret), 16)
+    assert need == 2 * a(tok * 16 * 2) + 3 * a(tok * 16 * 2) + a(ret)
+    assert layer(d, ws_bytes=need - 1) == rn.RN_ERR_WORKSPACE
+    assert layer(d, ws=ctypes.c_void_p(0x1010), ws_bytes=need) == rn.RN_ERR_INVALID_ARG
+    assert layer(d, w_g=None) == rn.RN_ERR_INVALID_ARG          # gate flag needs w_g
+    assert layer(d, x=None) == rn.RN_ERR_INVALID_ARG
+    assert layer(d, d_model=0) == rn.RN_ERR_INVALID_ARG
+    assert layer(d, chunk=0) == rn.RN_ERR_INVALID_ARG
+    d32, keep32 = desc(in_dtype=rn.RN_F32)
+    assert layer(d32) == rn.RN_ERR_UNSUPPORTED                  # bf16 GEMM operands only
+    dodd, keep_odd = desc(d_v=12)
+    assert layer(dodd) == rn.RN_ERR_UNSUPPORTED                 # d_v % 8
+    dbad, keep_bad = desc(B=0)
+    assert layer(dbad) == rn.RN_ERR_INVALID_ARG
+    assert rn.lib.rn_msr_layer_workspace_bytes(ctypes.byref(dbad), 64, 16) == 0

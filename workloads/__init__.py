@@ -27,6 +27,7 @@ import torch
 __all__ = [
     "Workload", "WORKLOADS", "theta_default", "gamma_small", "gamma_wide",
     "gamma_pairs_wide", "gamma_pairs_spread", "make_inputs", "make_decode_step_inputs",
+    "LAYER_D_MODEL", "make_layer_inputs",
 ]
 
 
@@ -192,3 +193,35 @@ def initial_state(w: Workload, *, B: Optional[int] = None) -> torch.Tensor:
     rng = np.random.default_rng([w.seed, 1 << 20])
     s = rng.standard_normal((B, w.H, w.d_k, w.d_v), dtype=np.float32) * np.float32(w.state_std)
     return torch.from_numpy(s)
+
+
+# Model width of the 6.7B-shaped layer (16 heads of d_k = 256 -> H d_k = 4096).
+LAYER_D_MODEL = 4096
+
+
+def make_layer_inputs(w: Workload, d_model: int, *, N: Optional[int] = None,
+                      B: Optional[int] = None, seed: Optional[int] = None) -> dict:
+    """Input and synthetic weights of the gated multi-scale layer on workload ``w``'s heads.
+
+    x ~ N(0, 1) [B, N, d_model]; W_Q, W_K, W_V ~ N(0, 1/(d_k d_model)) so that q, k, v have
+    the retention workloads' scale N(0, 1/d_k); W_G ~ N(0, 1/d_model) (gate ~ N(0, 1));
+    W_O ~ N(0, 1/(H d_v)). All drawn as float32 in the order x, W_Q, W_K, W_V, W_G, W_O from
+    ``default_rng([seed, 9])`` and rounded to bf16. Returns CPU tensors plus ``gamma`` and
+    ``theta`` as make_inputs does."""
+    B = w.B if B is None else B
+    N = w.N if N is None else N
+    rng = np.random.default_rng([w.seed if seed is None else seed, 9])
+    H, dk, dv = w.H, w.d_k, w.d_v
+
+    def draw(shape, std):
+        return _round(rng.standard_normal(shape, dtype=np.float32) * np.float32(std), "bf16")
+
+    x = draw((B, N, d_model), 1.0)
+    s_qkv = 1.0 / math.sqrt(dk * d_model)
+    return {
+        "x": x,
+        "w_q": draw((d_model, H * dk), s_qkv), "w_k": draw((d_model, H * dk), s_qkv),
+        "w_v": draw((d_model, H * dv), s_qkv), "w_g": draw((d_model, H * dv), 1.0 / math.sqrt(d_model)),
+        "w_o": draw((H * dv, d_model), 1.0 / math.sqrt(H * dv)),
+        "gamma": _gamma(w.gamma_kind, H, dk, w.seed), "theta": w.theta(),
+    }
