@@ -26,23 +26,22 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// o [B, H, N, dv] -> ot [B, N, H, dv]; one thread per 16 bytes (8 bf16); dv % 8 == 0.
+// o [B, H, N, dv] -> ot [B, N, H, dv]; dv % 8 == 0. Block (row group, h, b) copies
+// kRows consecutive rows of one head, 16 bytes (8 bf16) per thread and step. (Putting
+// the heads of a row group in neighbouring blocks instead measured 15 % slower.)
+constexpr int kRows = 16;
 __global__ void __launch_bounds__(256) heads_to_tokens(const uint16_t* __restrict__ o,
-                                                       uint16_t* __restrict__ ot, int B, int H,
-                                                       int N, int dv) {
+                                                       uint16_t* __restrict__ ot, int H, int N,
+                                                       int dv) {
   const int vpr = dv / 8;                              // 16-byte pieces per row
-  const int64_t total = int64_t(B) * H * N * vpr;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-       i += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t row = i / vpr;                       // (b, h, t) in head-major order
-    const int piece = static_cast<int>(i - row * vpr);
-    const int t = static_cast<int>(row % N);
-    const int64_t bh = row / N;
-    const int h = static_cast<int>(bh % H);
-    const int64_t b = bh / H;
-    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o) + i);
-    const int64_t dst = ((b * N + t) * H + h) * vpr + piece;
-    __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(ot) + dst);
+  const int h = blockIdx.y, b = blockIdx.z, t0 = blockIdx.x * kRows;
+  const int rows = min(kRows, N - t0);
+  const u32x4* src = reinterpret_cast<const u32x4*>(o) + ((int64_t(b) * H + h) * N + t0) * vpr;
+  u32x4* dst = reinterpret_cast<u32x4*>(ot) + ((int64_t(b) * N + t0) * H + h) * vpr;
+  for (int p = threadIdx.x; p < rows * vpr; p += 256) {
+    const int r = p / vpr, c = p - r * vpr;
+    const u32x4 x = __builtin_nontemporal_load(src + p);
+    __builtin_nontemporal_store(x, dst + int64_t(r) * H * vpr + c);
   }
 }
 
@@ -97,10 +96,8 @@ int layer_project(const LayerArgs& L, const void* x, const void* w, int d, void*
 // out [B N, d_model] = regroup(o) [B N, H dv] W_O; `ot` receives the regrouped heads.
 int layer_output(const LayerArgs& L, const void* o, void* ot, const void* w_o, void* out,
                  int out_dtype, hipStream_t stream) {
-  const int64_t pieces = int64_t(L.B) * L.H * L.N * (L.dv / 8);
-  const int blocks = static_cast<int>(std::min<int64_t>((pieces + 255) / 256, 8192));
-  hipLaunchKernelGGL(heads_to_tokens, dim3(blocks), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(o), static_cast<uint16_t*>(ot), L.B, L.H, L.N,
+  hipLaunchKernelGGL(heads_to_tokens, dim3((L.N + kRows - 1) / kRows, L.H, L.B), dim3(256), 0,
+                     stream, static_cast<const uint16_t*>(o), static_cast<uint16_t*>(ot), L.H, L.N,
                      L.dv);
   if (hipGetLastError() != hipSuccess) return rocblas_status_internal_error;
   int dev = 0;
