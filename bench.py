@@ -32,7 +32,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-FP32_PEAK_TFLOPS = 157.3       # MI355X float32 vector
 
 
 CHUNKWISE_PROFILE = os.path.join(ROOT, "profiles", "chunkwise_fused_6p7b_training.md")
@@ -212,9 +211,10 @@ def main():
     }
 
     # ---- chunkwise backward on the same workload (secondary record) ------------------
-    # Gradients of q, k, v and the gate through GroupNorm + gate, given a random dout;
-    # float32 kernels. Algorithmic flops: twice the forward's (each product of the forward
-    # has two gradient products of the same size).
+    # Gradients of q, k, v and the gate through GroupNorm + gate, given a random dout; the
+    # tile products on matrix cores (f16 operands), the state scans in float32.
+    # Algorithmic flops: twice the forward's (each product of the forward has two gradient
+    # products of the same size).
     if args.only in ("chunkwise", "decode", "parallel", "pair", "layer"):
         args.no_backward = True
     if not args.no_backward:
@@ -241,7 +241,7 @@ def main():
         rec["backward"] = {"workload": "chunkwise_6p7b backward: dq, dk, dv, dgate through GroupNorm + gate",
                            "ms": bs * 1e3, "tokens_per_s": tokens / bs,
                            "algorithmic_flops": bfl, "tflops": bfl / bs / 1e12,
-                           "bound": "alu", "fp32_vector_frac": bfl / bs / 1e12 / FP32_PEAK_TFLOPS,
+                           "bound": "mfma", "mfma_frac": bfl / bs / 1e12 / BF16_PEAK_TFLOPS,
                            "workspace_bytes": wsb.numel()}
         del dout, wsb
     if args.only == "backward":

@@ -232,11 +232,123 @@ __device__ __forceinline__ void zero_acc(float (&acc)[4][NCT]) {
     for (int j = 0; j < NCT; ++j) acc[r][j] = 0.f;
 }
 
+// ---- the same tile products on matrix cores (bf16 inputs) ------------------------------
+// 16x16x32 f16 MFMA with float32 accumulation. The accumulator layout of a 16x16 tile
+// (lane: column l16, rows 4g..4g+3) is the layout above: thread 64w + 16g + l16 holds
+// rows 16w + 4g + r, i.e. ty = 4w + g, tx = l16. Operands are rounded to IEEE half when
+// they are staged: A as As[row][k], B as Bs[col][k] (32 k-values per slice, 8 per lane
+// and 16 bytes per read), a score tile as P[row][key].
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kKH = 32;             // reduction slice
+constexpr int kLdH = kKH + 8;       // LDS pitch (half) of As and Bs rows
+constexpr int kLdPH = kBC + 8;      // LDS pitch (half) of P rows
+
+struct alignas(16) TileSharedH {
+  union {
+    struct {
+      _Float16 As[kR][kLdH];
+      _Float16 Bs[kMaxDv][kLdH];
+      _Float16 P[kR][kLdPH];
+    } m;
+    float rot[kR][kMaxDk + 4];             // rows rotated back before their store
+    struct {
+      float sw[16][kLdB];                  // per-thread sums of the GroupNorm backward
+      float sb[16][kLdB];
+    } gn;
+  };
+};
+
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  f16x2 v;
+  v[0] = static_cast<_Float16>(lo);
+  v[1] = static_cast<_Float16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc += A (64 x K) B (K x 16 NCT) as in tile_mm. Each thread stages runs of 8 consecutive
+// k-values: A row tid/4, k 8 (tid%4) ..; B runs are spread so that consecutive threads
+// read consecutive source addresses (for BM = kBRows consecutive columns, for kBCols the
+// four runs of one column). The next slice is fetched into registers while the MFMAs of
+// the current one run.
+template <int NCT, bool FROMP, int BM, class GA, class GB>
+__device__ __forceinline__ void tile_mm_h(float (&acc)[4][NCT], int K, TileSharedH& sm, GA ga, GB gb) {
+  constexpr int NCB = 16 * NCT;            // B columns
+  constexpr int NRUN = NCB * 4 / 256;      // B runs of 8 per thread and slice
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, g = l >> 4;
+  float ra[8], rb[NRUN][8];
+  auto bcol = [&](int u) { const int run = tid + 256 * u; return BM == kBRows ? run % NCB : run >> 2; };
+  auto bq = [&](int u) { const int run = tid + 256 * u; return BM == kBRows ? run / NCB : run & 3; };
+  auto fetch = [&](int k0) __attribute__((always_inline)) {
+    if constexpr (!FROMP) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ra[i] = ga(tid >> 2, k0 + 8 * (tid & 3) + i);
+    }
+#pragma unroll
+    for (int u = 0; u < NRUN; ++u) {
+      const int col = bcol(u), kq = k0 + 8 * bq(u);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rb[u][i] = BM == kBRows ? gb(kq + i, col) : gb(col, kq + i);
+    }
+  };
+  auto put = [&]() __attribute__((always_inline)) {
+    if constexpr (!FROMP)
+      *reinterpret_cast<u32x4*>(&sm.m.As[tid >> 2][8 * (tid & 3)]) =
+          u32x4{pack_h2(ra[0], ra[1]), pack_h2(ra[2], ra[3]), pack_h2(ra[4], ra[5]), pack_h2(ra[6], ra[7])};
+#pragma unroll
+    for (int u = 0; u < NRUN; ++u)
+      *reinterpret_cast<u32x4*>(&sm.m.Bs[bcol(u)][8 * bq(u)]) =
+          u32x4{pack_h2(rb[u][0], rb[u][1]), pack_h2(rb[u][2], rb[u][3]), pack_h2(rb[u][4], rb[u][5]),
+                pack_h2(rb[u][6], rb[u][7])};
+  };
+  f32x4 t[NCT];
+#pragma unroll
+  for (int j = 0; j < NCT; ++j) t[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  fetch(0);
+  for (int k0 = 0; k0 < K; k0 += kKH) {
+    __syncthreads();   // the previous slice's reads of As / Bs are done
+    put();
+    __syncthreads();
+    if (k0 + kKH < K) fetch(k0 + kKH);
+    f16x8 av;
+    if constexpr (FROMP) av = *reinterpret_cast<const f16x8*>(&sm.m.P[16 * w + l16][k0 + 8 * g]);
+    else av = *reinterpret_cast<const f16x8*>(&sm.m.As[16 * w + l16][8 * g]);
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const f16x8 bv = *reinterpret_cast<const f16x8*>(&sm.m.Bs[16 * j + l16][8 * g]);
+      t[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, t[j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NCT; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r][j] += t[j][r];
+}
+
+// Shared memory and the tile product of one input type: float32 VALU for float32 inputs,
+// matrix cores for bf16 inputs.
+template <int IN> struct TileOf { using type = TileShared; };
+template <> struct TileOf<RN_BF16> { using type = TileSharedH; };
+
+template <int IN, int NCT, bool FROMP, int BM, class SM, class GA, class GB>
+__device__ __forceinline__ void tmm(float (&acc)[4][NCT], int K, SM& sm, GA ga, GB gb) {
+  if constexpr (IN == RN_BF16) tile_mm_h<NCT, FROMP, BM>(acc, K, sm, ga, gb);
+  else tile_mm<NCT, FROMP, BM>(acc, K, sm, ga, gb);
+}
+__device__ __forceinline__ float* rot_buf(TileShared& sm) { return &sm.P[0][0]; }
+__device__ __forceinline__ float* rot_buf(TileSharedH& sm) { return &sm.rot[0][0]; }
+__device__ __forceinline__ float* gn_sw(TileShared& sm) { return &sm.Bs[0][0]; }
+__device__ __forceinline__ float* gn_sw(TileSharedH& sm) { return &sm.gn.sw[0][0]; }
+__device__ __forceinline__ float* gn_sb(TileShared& sm) { return &sm.P[0][0]; }
+__device__ __forceinline__ float* gn_sb(TileSharedH& sm) { return &sm.gn.sb[0][0]; }
+
 // Decayed, masked score tile -> P (transposed): P[key - key0][row] for the tile's rows
 // row0 + 4ty + r and keys key0 + tx + 16 j < key_end. FORWARD: keys s <= t (o, dq);
 // otherwise later rows t >= s (dk, dv: the tile's rows are the keys s).
-template <bool FORWARD>
-__device__ __forceinline__ void store_scores(TileShared& sm, const float (&m)[4][16], int row0,
+template <bool FORWARD, class SM>
+__device__ __forceinline__ void store_scores(SM& sm, const float (&m)[4][16], int row0,
                                              int row_end, int key0, int key_end, float lg,
                                              float alpha) {
   const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
@@ -248,7 +360,9 @@ __device__ __forceinline__ void store_scores(TileShared& sm, const float (&m)[4]
       const int row = row0 + 4 * ty + r, key = key0 + tx + 16 * j;
       const int dist = FORWARD ? row - key : key - row;
       const bool ok = row < row_end && key < key_end && dist >= 0;
-      sm.P[tx + 16 * j][4 * ty + r] = ok ? alpha * m[r][j] * gpow(lg, float(dist)) : 0.f;
+      const float x = ok ? alpha * m[r][j] * gpow(lg, float(dist)) : 0.f;
+      if constexpr (__is_same(SM, TileSharedH)) sm.m.P[4 * ty + r][tx + 16 * j] = static_cast<_Float16>(x);
+      else sm.P[tx + 16 * j][4 * ty + r] = x;
     }
 }
 
@@ -277,11 +391,11 @@ __device__ __forceinline__ TileRows tile_rows(int N) {
 
 // Rotates a row tile of gradients back by -p and stores it: the tile goes through LDS
 // (P, free after the products) so that each thread then takes whole coordinate pairs.
-template <int IN>
-__device__ __forceinline__ void store_rotated(TileShared& sm, const float (&g)[4][16], const CallArgs& a,
+template <int IN, class SM>
+__device__ __forceinline__ void store_rotated(SM& sm, const float (&g)[4][16], const CallArgs& a,
                                               int64_t p0, int bh, int r0, int r1, void* dst) {
   const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15, dk = a.dk;
-  float* buf = &sm.P[0][0];   // [64 rows][kMaxDk + 4]
+  float* buf = rot_buf(sm);   // [64 rows][kMaxDk + 4]
   constexpr int ld = kMaxDk + 4;
   __syncthreads();
 #pragma unroll
@@ -310,7 +424,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                                                const void* v, const void* gate, const void* dout,
                                                const float* S, float* dO, void* dgate,
                                                float* dgn_w, float* dgn_b) {
-  __shared__ TileShared sm;
+  __shared__ typename TileOf<IN>::type sm;
   const int dk = a.dk, dv = a.dv, N = a.N;
   const TileRows T = tile_rows(N);
   if (T.r0 >= T.r1) return;
@@ -324,7 +438,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nkey = T.r1 - T.c0;   // keys c0 .. r1-1
   float m[4][16];
   zero_acc(m);
-  tile_mm<16, false, kBCols>(m, dk, sm,
+  tmm<IN, 16, false, kBCols>(m, dk, sm,
       [&](int row, int kk) __attribute__((always_inline)) {
           return (T.r0 + row < T.r1 && kk < dk) ? Qb[int64_t(T.r0 + row) * dk + kk] : 0.f; },
       [&](int col, int kk) __attribute__((always_inline)) {
@@ -332,10 +446,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   store_scores<true>(sm, m, T.r0, T.r1, T.c0, T.r1, lg, a.alpha);
   float o[4][32];
   zero_acc(o);
-  tile_mm<32, true, kBRows>(o, (nkey + kKS - 1) / kKS * kKS, sm, [](int, int) { return 0.f; },
+  tmm<IN, 32, true, kBRows>(o, (nkey + kKS - 1) / kKS * kKS, sm, [](int, int) { return 0.f; },
       [&](int kk, int col) __attribute__((always_inline)) {
           return (kk < nkey && col < dv) ? Elem<IN>::load(v, (int64_t(bh) * N + T.c0 + kk) * dv + col) : 0.f; });
-  tile_mm<32, false, kBRows>(o, dk, sm,
+  tmm<IN, 32, false, kBRows>(o, dk, sm,
       [&](int row, int kk) __attribute__((always_inline)) {
           const int t = T.r0 + row;
           return (t < T.r1 && kk < dk) ? a.alpha * gpow(lg, float(t - T.c0 + 1)) * Qb[int64_t(t) * dk + kk] : 0.f; },
@@ -354,8 +468,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
   // GroupNorm / gate backward, row by row. Per-column sums of dy * xh and dy (for dgn_w,
   // dgn_b) gather in this thread's own LDS cells: Bs[ty][col] and P viewed as [16][kLdB].
-  float* sw = &sm.Bs[0][0];
-  float* sb = &sm.P[0][0];
+  float* sw = gn_sw(sm);
+  float* sb = gn_sb(sm);
   __syncthreads();
 #pragma clang loop unroll(full)
   for (int j = 0; j < 32; ++j) {
@@ -443,7 +557,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 template <int IN>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) bw_dq(CallArgs a, const float* Kh, const void* v,
                                              const float* dO, const float* S, void* dq) {
-  __shared__ TileShared sm;
+  __shared__ typename TileOf<IN>::type sm;
   const int dk = a.dk, dv = a.dv, N = a.N;
   const TileRows T = tile_rows(N);
   if (T.r0 >= T.r1) return;
@@ -456,7 +570,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nkey = T.r1 - T.c0;
   float m[4][16];
   zero_acc(m);
-  tile_mm<16, false, kBCols>(m, dv, sm,
+  tmm<IN, 16, false, kBCols>(m, dv, sm,
       [&](int row, int kk) __attribute__((always_inline)) {
           return (T.r0 + row < T.r1 && kk < dv) ? Db[int64_t(T.r0 + row) * dv + kk] : 0.f; },
       [&](int col, int kk) __attribute__((always_inline)) {
@@ -464,10 +578,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   store_scores<true>(sm, m, T.r0, T.r1, T.c0, T.r1, lg, a.alpha);
   float g[4][16];
   zero_acc(g);
-  tile_mm<16, true, kBRows>(g, (nkey + kKS - 1) / kKS * kKS, sm, [](int, int) { return 0.f; },
+  tmm<IN, 16, true, kBRows>(g, (nkey + kKS - 1) / kKS * kKS, sm, [](int, int) { return 0.f; },
       [&](int kk, int col) __attribute__((always_inline)) {
           return (kk < nkey && col < dk) ? Kb[int64_t(T.c0 + kk) * dk + col] : 0.f; });
-  tile_mm<16, false, kBCols>(g, dv, sm,
+  tmm<IN, 16, false, kBCols>(g, dv, sm,
       [&](int row, int kk) __attribute__((always_inline)) {
           const int t = T.r0 + row;
           return (t < T.r1 && kk < dv) ? a.alpha * gpow(lg, float(t - T.c0 + 1)) * Db[int64_t(t) * dv + kk] : 0.f; },
@@ -482,7 +596,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 template <int IN>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) bw_dk(CallArgs a, const float* Qh, const void* v,
                                              const float* dO, const float* G, void* dk_) {
-  __shared__ TileShared sm;
+  __shared__ typename TileOf<IN>::type sm;
   const int dk = a.dk, dv = a.dv, N = a.N;
   const TileRows T = tile_rows(N);
   if (T.r0 >= T.r1) return;
@@ -495,7 +609,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nlater = T.c1 - T.r0;   // rows r0 .. c1-1
   float m[4][16];
   zero_acc(m);
-  tile_mm<16, false, kBCols>(m, dv, sm,
+  tmm<IN, 16, false, kBCols>(m, dv, sm,
       [&](int row, int kk) __attribute__((always_inline)) {
           return (T.r0 + row < T.r1 && kk < dv) ? Elem<IN>::load(v, (int64_t(bh) * N + T.r0 + row) * dv + kk) : 0.f; },
       [&](int col, int kk) __attribute__((always_inline)) {
@@ -503,10 +617,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   store_scores<false>(sm, m, T.r0, T.r1, T.r0, T.c1, lg, a.alpha);
   float g[4][16];
   zero_acc(g);
-  tile_mm<16, true, kBRows>(g, (nlater + kKS - 1) / kKS * kKS, sm, [](int, int) { return 0.f; },
+  tmm<IN, 16, true, kBRows>(g, (nlater + kKS - 1) / kKS * kKS, sm, [](int, int) { return 0.f; },
       [&](int kk, int col) __attribute__((always_inline)) {
           return (kk < nlater && col < dk) ? Qb[int64_t(T.r0 + kk) * dk + col] : 0.f; });
-  tile_mm<16, false, kBCols>(g, dv, sm,
+  tmm<IN, 16, false, kBCols>(g, dv, sm,
       [&](int row, int kk) __attribute__((always_inline)) {
           const int s = T.r0 + row;
           return (s < T.r1 && kk < dv) ? gpow(lg, float(T.c1 - 1 - s)) * Elem<IN>::load(v, (int64_t(bh) * N + s) * dv + kk) : 0.f; },
@@ -520,7 +634,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 template <int IN>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) bw_dv(CallArgs a, const float* Qh, const float* Kh,
                                              const float* dO, const float* G, void* dv_) {
-  __shared__ TileShared sm;
+  __shared__ typename TileOf<IN>::type sm;
   const int dk = a.dk, dv = a.dv, N = a.N;
   const TileRows T = tile_rows(N);
   if (T.r0 >= T.r1) return;
@@ -535,7 +649,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nlater = T.c1 - T.r0;
   float m[4][16];
   zero_acc(m);
-  tile_mm<16, false, kBCols>(m, dk, sm,
+  tmm<IN, 16, false, kBCols>(m, dk, sm,
       [&](int row, int kk) __attribute__((always_inline)) {
           return (T.r0 + row < T.r1 && kk < dk) ? Kb[int64_t(T.r0 + row) * dk + kk] : 0.f; },
       [&](int col, int kk) __attribute__((always_inline)) {
@@ -543,10 +657,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   store_scores<false>(sm, m, T.r0, T.r1, T.r0, T.c1, lg, a.alpha);
   float o[4][32];
   zero_acc(o);
-  tile_mm<32, true, kBRows>(o, (nlater + kKS - 1) / kKS * kKS, sm, [](int, int) { return 0.f; },
+  tmm<IN, 32, true, kBRows>(o, (nlater + kKS - 1) / kKS * kKS, sm, [](int, int) { return 0.f; },
       [&](int kk, int col) __attribute__((always_inline)) {
           return (kk < nlater && col < dv) ? Db[int64_t(T.r0 + kk) * dv + col] : 0.f; });
-  tile_mm<32, false, kBRows>(o, dk, sm,
+  tmm<IN, 32, false, kBRows>(o, dk, sm,
       [&](int row, int kk) __attribute__((always_inline)) {
           const int s = T.r0 + row;
           return (s < T.r1 && kk < dk) ? gpow(lg, float(T.c1 - 1 - s)) * Kb[int64_t(s) * dk + kk] : 0.f; },

@@ -1,10 +1,15 @@
 """GPU parity of the chunkwise backward (rn_retention_chunkwise_backward) against the
 gradient oracle (oracle/backward.py, pinned by finite differences of the forward oracle).
 
-Tolerances: the kernels compute in float32.
-  * float32 inputs and gradients: per (b, h), ||gpu - ref||_inf <= 1e-4 ||ref||_inf.
-  * bf16 inputs: gradients are stored in bf16, so each element may also differ by half a
-    bf16 ulp of the reference: |gpu - ref| <= 1e-4 ||ref||_inf + 2^-8 |ref|.
+Tolerances:
+  * float32 inputs: the products run in float32; per (b, h),
+    ||gpu - ref||_inf <= 1e-4 ||ref||_inf.
+  * bf16 inputs: the tile products run on matrix cores with their operands rounded to IEEE
+    half (relative 2^-11) and float32 accumulation, as the forward's matrix-core paths do;
+    a gradient element is a signed sum of many such terms, so the bar is the forward's
+    raw-output bar, 1e-2 of the slice maximum, plus half a bf16 ulp of the reference for
+    the bf16 store: |gpu - ref| <= 1e-2 ||ref||_inf + 2^-8 |ref|. (The state scans stay in
+    float32.)
 """
 import numpy as np
 import pytest
@@ -89,4 +94,36 @@ def test_bf16_6p7b_head_shape():
         gate=dev(x["gate"]), gn=True)
     ref = O.backward(x["q"], x["k"], x["v"], x["gamma"], x["theta"], x["dout"], gate=x["gate"], gn=True)
     for n in ("dq", "dk", "dv", "dgate"):
-        assert close(got[n].cpu(), ref[n], bf16=True) <= 1.0, n
+        assert close(got[n].cpu(), ref[n], bf16=True, rel=1e-2) <= 1.0, n
+
+
+@pytest.mark.parametrize("N,pos0,dk,dv", [(513, 70000, 64, 96), (77, 3, 48, 40), (600, 0, 256, 512)])
+def test_bf16_state_positions_other_shapes(N, pos0, dk, dv):
+    """Matrix-core path with an initial state, a gradient for the final state, positions
+    and ragged tiles; head shapes below the 6.7B one are zero-padded in the products."""
+    x = make("bf16", 2, 2, N, dk, dv, seed=N + dk, state=True)
+    got = rn().rn_retention_chunkwise_backward(
+        dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"], 64, dev(x["dout"]),
+        state_in=dev(x["state"]), dstate_out=dev(x["dstate_out"]), want_dstate_in=True,
+        pos0=pos0, qk_scale=0.5)
+    ref = O.backward(x["q"], x["k"], x["v"], x["gamma"], x["theta"], x["dout"], pos0=pos0,
+                     alpha=0.5, state0=x["state"], dstate_out=x["dstate_out"])
+    for n, rname in (("dq", "dq"), ("dk", "dk"), ("dv", "dv")):
+        assert close(got[n].cpu(), ref[rname], bf16=True, rel=1e-2) <= 1.0, n
+    assert close(got["dstate_in"].cpu(), ref["dstate0"], rel=1e-2) <= 1.0
+
+
+def test_bf16_gn_affine_gradients():
+    x = make("bf16", 1, 2, 300, 256, 512, seed=21, gate=True)
+    H, dv = 2, 512
+    gw = torch.randn(H * dv, generator=torch.Generator().manual_seed(18)) * 0.3 + 1
+    gb = torch.randn(H * dv, generator=torch.Generator().manual_seed(19)) * 0.1
+    got = rn().rn_retention_chunkwise_backward(
+        dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"], 256, dev(x["dout"]),
+        gate=dev(x["gate"]), gn=True, gn_weight=dev(gw), gn_bias=dev(gb))
+    ref = O.backward(x["q"], x["k"], x["v"], x["gamma"], x["theta"], x["dout"], gate=x["gate"],
+                     gn=True, weight=gw.reshape(H, dv), bias=gb.reshape(H, dv))
+    for n in ("dq", "dk", "dv", "dgate"):
+        assert close(got[n].cpu(), ref[n], bf16=True, rel=1e-2) <= 1.0, n
+    assert close(got["dgn_weight"].cpu().reshape(1, H, dv), ref["dweight"][None], rel=1e-2) <= 1.0
+    assert close(got["dgn_bias"].cpu().reshape(1, H, dv), ref["dbias"][None], rel=1e-2) <= 1.0
