@@ -1,0 +1,498 @@
+// Matrix-core path of the chunkwise backward for bf16 inputs with d_k and d_v multiples of
+// 8: the same gradients as the float32 path (the chunkwise recurrence differentiated; hwhale
+// notes: chunkwise equation and ChunkwiseRetention listing; GroupNorm per head and swish
+// gate of the multi-scale layer), with every product on 16x16x32 f16 MFMA and float32
+// accumulation.
+//
+// Every product operand is a row-major half matrix whose reduction index is contiguous,
+// so that each lane stages 8 consecutive values with one 16-byte load. The reductions run
+// over d_k, d_v or tokens, so a prep pass writes the rotated rows of q and k in half both
+// row-major ([N][d_k]) and transposed ([d_k][Np], tokens contiguous), and v transposed;
+// the GroupNorm backward writes dO row-major and a second pass transposes it; the state
+// scans write each chunk's state in both orientations. Np is N rounded up to 64 and the
+// transposed copies are zero past N, so a reduction over tokens may read up to the next
+// multiple of 32 (the scores or weights there are zero).
+//
+// Per head (chunks of 256 tokens, c0 its first token, c1 one past its last):
+//   scan (forward)  S_c for every chunk: S <- gamma^L S + sum_s gamma^(c1-1-s) Kh_s^T V_s
+//   dout            o recomputed per 64-row tile, then the GroupNorm / gate backward -> dO
+//   scan (reverse)  G_{c+1} for every chunk: G <- gamma^L G + alpha sum_t gamma^(t-c0+1) Qh_t^T dO_t
+//   dq  = [alpha (dO V^T) (.) D] Kh + alpha xi dO S_c^T,   rotated back
+//   dk  = [alpha (V dO^T) (.) D'] Qh + zeta V G_{c+1}^T,   rotated back
+//   dv  = [alpha (Kh Qh^T) (.) D'] dO + zeta Kh G_{c+1}
+#include "backward_tiles.h"
+#include "rn_device.h"
+#include "rn_kernels.h"
+
+namespace rn {
+namespace {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Row-major source of half (or, for the input v, bf16) values: element (r, c) at
+// p[r * pitch + c]; rows at or past `rows` read as zeros.
+struct Src {
+  const uint16_t* p;
+  int64_t pitch;
+  int rows;
+  bool bf;
+};
+
+__device__ __forceinline__ uint16_t h_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+__device__ __forceinline__ uint32_t bf2_to_h2(uint32_t x) {
+  return pack_h2(__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u));
+}
+__device__ __forceinline__ u32x4 bf8_to_h8(u32x4 x) {
+  const uint32_t x0 = x[0], x1 = x[1], x2 = x[2], x3 = x[3];
+  return u32x4{bf2_to_h2(x0), bf2_to_h2(x1), bf2_to_h2(x2), bf2_to_h2(x3)};
+}
+// (The halves are taken apart with integer shifts: a bit_cast of each vector element to a
+// pair of halves, in an unrolled loop, was compiled to reuse element 0 for all four.)
+__device__ __forceinline__ float h_to_f(uint32_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xffffu)));
+}
+__device__ __forceinline__ u32x4 scale8(u32x4 x, const float* f) {
+  const uint32_t x0 = x[0], x1 = x[1], x2 = x[2], x3 = x[3];
+  return u32x4{pack_h2(h_to_f(x0) * f[0], h_to_f(x0 >> 16) * f[1]),
+               pack_h2(h_to_f(x1) * f[2], h_to_f(x1 >> 16) * f[3]),
+               pack_h2(h_to_f(x2) * f[4], h_to_f(x2 >> 16) * f[5]),
+               pack_h2(h_to_f(x3) * f[6], h_to_f(x3 >> 16) * f[7])};
+}
+// 8 values (r, c .. c+7) as half; zero for rows past the source or when `live` is false.
+__device__ __forceinline__ u32x4 run8(const Src& s, int r, int64_t c, bool live = true) {
+  if (!live || r >= s.rows) return u32x4{0u, 0u, 0u, 0u};
+  const u32x4 x = *reinterpret_cast<const u32x4*>(s.p + r * s.pitch + c);
+  return s.bf ? bf8_to_h8(x) : x;
+}
+
+// acc += A B over k < K, A (64 x K) either P (FROMP) or rows ar0 + i of A scaled by
+// amul * gamma^(ae0 + aesg i) (log2 gamma = alg), B (K x 16 NCT) given by its columns:
+// column n is row br0 + n of B, read from column bc0 on. Without FROMP, K is a multiple of
+// 8 and runs at or past K read as zeros; with FROMP the scores past the product's extent
+// are zero. The next slice is fetched into registers while the MFMAs of the current run.
+template <int NCT, bool FROMP>
+__device__ __forceinline__ void tmm16(float (&acc)[4][NCT], int K, TileSharedH& sm, const Src& A,
+                                      int ar0, float amul, float alg, int ae0, int aesg,
+                                      const Src& B, int br0, int bc0) {
+  constexpr int NRUN = NCT / 4;   // B runs of 8 per thread and slice (16 NCT columns x 4 runs)
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, g = l >> 4;
+  const int arow = tid >> 2, aq = tid & 3;
+  const bool scaled = !FROMP && (aesg != 0 || amul != 1.f);
+  float af[8];
+  {
+    const float f = amul * exp2f(alg * float(ae0 + aesg * arow));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) af[i] = f;
+  }
+  u32x4 ra = u32x4{0u, 0u, 0u, 0u}, rb[NRUN];
+  auto fetch = [&](int k0) __attribute__((always_inline)) {
+    if constexpr (!FROMP) ra = run8(A, ar0 + arow, k0 + 8 * aq, k0 + 8 * aq < K);
+#pragma unroll
+    for (int u = 0; u < NRUN; ++u) {
+      const int run = tid + 256 * u, n = run >> 2, kq = k0 + 8 * (run & 3);
+      rb[u] = run8(B, br0 + n, int64_t(bc0) + kq, FROMP || kq < K);
+    }
+  };
+  auto put = [&]() __attribute__((always_inline)) {
+    if constexpr (!FROMP)
+      *reinterpret_cast<u32x4*>(&sm.m.As[arow][8 * aq]) = scaled ? scale8(ra, af) : ra;
+#pragma unroll
+    for (int u = 0; u < NRUN; ++u) {
+      const int run = tid + 256 * u;
+      *reinterpret_cast<u32x4*>(&sm.m.Bs[run >> 2][8 * (run & 3)]) = rb[u];
+    }
+  };
+  f32x4 t[NCT];
+#pragma unroll
+  for (int j = 0; j < NCT; ++j) t[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  fetch(0);
+  for (int k0 = 0; k0 < K; k0 += kKH) {
+    __syncthreads();   // the previous slice's reads of As / Bs are done
+    put();
+    __syncthreads();
+    if (k0 + kKH < K) fetch(k0 + kKH);
+    f16x8 av;
+    if constexpr (FROMP) av = *reinterpret_cast<const f16x8*>(&sm.m.P[16 * w + l16][k0 + 8 * g]);
+    else av = *reinterpret_cast<const f16x8*>(&sm.m.As[16 * w + l16][8 * g]);
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const f16x8 bv = *reinterpret_cast<const f16x8*>(&sm.m.Bs[16 * j + l16][8 * g]);
+      t[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, t[j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NCT; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r][j] += t[j][r];
+}
+
+// Workspace (half), per head: row-major rotated q and k, their transposes, v transposed,
+// dO row-major and transposed, and the chunk states S and G in both orientations.
+struct MLayout {
+  int Np, nch;
+  size_t QR, KR, QT, KT, VT, DR, DT, S, ST, G, GT, total;   // byte offsets
+};
+size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
+MLayout m_layout(const CallArgs& a) {
+  MLayout L;
+  L.Np = (a.N + 63) / 64 * 64;
+  L.nch = (a.N + kBC - 1) / kBC;
+  const size_t BH = size_t(a.B) * a.H;
+  const size_t rowk = a256(BH * a.N * a.dk * 2), rowv = a256(BH * a.N * a.dv * 2);
+  const size_t tk = a256(BH * a.dk * L.Np * 2), tv = a256(BH * a.dv * L.Np * 2);
+  const size_t st = a256(BH * L.nch * a.dk * a.dv * 2);
+  size_t o = 0;
+  L.QR = o; o += rowk;
+  L.KR = o; o += rowk;
+  L.QT = o; o += tk;
+  L.KT = o; o += tk;
+  L.VT = o; o += tv;
+  L.DR = o; o += rowv;
+  L.DT = o; o += tv;
+  L.S = o; o += st;
+  L.ST = o; o += st;
+  L.G = o; o += st;
+  L.GT = o; o += st;
+  L.total = o;
+  return L;
+}
+
+// ---- prep: rotated q, k (row-major and transposed) and v transposed, per 64 tokens ------
+// Grid (Np/64, b*H + h); the transposes go through LDS, [column][token].
+__global__ void __launch_bounds__(256) bm_prep(CallArgs a, const uint16_t* q, const uint16_t* k,
+                                               const uint16_t* v, uint16_t* QR, uint16_t* KR,
+                                               uint16_t* QT, uint16_t* KT, uint16_t* VT, int Np) {
+  __shared__ __attribute__((aligned(16))) uint16_t tb[kMaxDv][64 + 8];
+  const int dk = a.dk, dv = a.dv, N = a.N;
+  const int t0 = blockIdx.x * 64, bh = blockIdx.y;
+  const int64_t p0 = seq_pos0(a, bh / a.H);
+  for (int which = 0; which < 2; ++which) {
+    const uint16_t* x = which ? k : q;
+    uint16_t* R = (which ? KR : QR) + int64_t(bh) * N * dk;
+    uint16_t* T = (which ? KT : QT) + int64_t(bh) * dk * Np;
+    for (int e = threadIdx.x; e < 64 * (dk / 2); e += 256) {
+      const int tt = e / (dk / 2), j = e - tt * (dk / 2), t = t0 + tt;
+      float r0 = 0.f, r1 = 0.f;
+      if (t < N) {
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(x + (int64_t(bh) * N + t) * dk + 2 * j);
+        const float x0 = __uint_as_float(u << 16), x1 = __uint_as_float(u & 0xffff0000u);
+        float c, s;
+        angle_cs(p0 + t, a.ap.theta[j], &c, &s);
+        r0 = x0 * c - x1 * s;
+        r1 = x0 * s + x1 * c;
+        *reinterpret_cast<uint32_t*>(R + int64_t(t) * dk + 2 * j) = pack_h2(r0, r1);
+      }
+      tb[2 * j][tt] = h_bits(r0);
+      tb[2 * j + 1][tt] = h_bits(r1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < dk * 8; e += 256) {
+      const int d = e >> 3, pc = e & 7;
+      *reinterpret_cast<u32x4*>(T + int64_t(d) * Np + t0 + 8 * pc) = *reinterpret_cast<const u32x4*>(&tb[d][8 * pc]);
+    }
+    __syncthreads();
+  }
+  uint16_t* T = VT + int64_t(bh) * dv * Np;
+  for (int e = threadIdx.x; e < 64 * dv; e += 256) {
+    const int tt = e / dv, c = e - tt * dv, t = t0 + tt;
+    const float x = t < N ? __uint_as_float(uint32_t(v[(int64_t(bh) * N + t) * dv + c]) << 16) : 0.f;
+    tb[c][tt] = h_bits(x);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < dv * 8; e += 256) {
+    const int c = e >> 3, pc = e & 7;
+    *reinterpret_cast<u32x4*>(T + int64_t(c) * Np + t0 + 8 * pc) = *reinterpret_cast<const u32x4*>(&tb[c][8 * pc]);
+  }
+}
+
+// dO [N][d_v] -> dO^T [d_v][Np] (zero past N). Grid (Np/64, b*H + h).
+__global__ void __launch_bounds__(256) bm_transpose(const uint16_t* R, uint16_t* T, int N, int dv,
+                                                    int Np) {
+  __shared__ __attribute__((aligned(16))) uint16_t tb[kMaxDv][64 + 8];
+  const int t0 = blockIdx.x * 64, bh = blockIdx.y;
+  const uint16_t* Rb = R + int64_t(bh) * N * dv;
+  for (int e = threadIdx.x; e < 64 * (dv / 8); e += 256) {
+    const int tt = e / (dv / 8), cq = e - tt * (dv / 8), t = t0 + tt;
+    u32x4 x = u32x4{0u, 0u, 0u, 0u};
+    if (t < N) x = *reinterpret_cast<const u32x4*>(Rb + int64_t(t) * dv + 8 * cq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tb[8 * cq + 2 * i][tt] = uint16_t(x[i] & 0xffffu);
+      tb[8 * cq + 2 * i + 1][tt] = uint16_t(x[i] >> 16);
+    }
+  }
+  __syncthreads();
+  uint16_t* Tb = T + int64_t(bh) * dv * Np;
+  for (int e = threadIdx.x; e < dv * 8; e += 256) {
+    const int c = e >> 3, pc = e & 7;
+    *reinterpret_cast<u32x4*>(Tb + int64_t(c) * Np + t0 + 8 * pc) = *reinterpret_cast<const u32x4*>(&tb[c][8 * pc]);
+  }
+}
+
+// ---- state scans on matrix cores ---------------------------------------------------------
+// REV = 0: S (chunk states) from X = Kh^T weighted by zeta, Y = V^T, from state_in.
+// REV = 1: G (gradients reaching the chunk ends) from X = Qh^T weighted by alpha xi, Y = dO^T,
+//          chunks in reverse, from dstate_out; the final value goes to dstate_in.
+// Workgroup: a 64 (d_k) x 128 (d_v) tile of the state in MFMA accumulators, wave w rows
+// 16w.. of the tile. Per 32-token slice: X^T rows (tokens weighted on staging) times Y^T
+// rows. Each chunk's boundary value is stored in half as [d_k][d_v] and [d_v][d_k].
+struct alignas(16) ScanShared {
+  _Float16 As[64][kLdH];
+  _Float16 Bs[128][kLdH];
+  float wt[kBC];
+};
+
+template <int REV>
+__global__ void __launch_bounds__(256) bm_scan(CallArgs a, const uint16_t* XT, const uint16_t* YT,
+                                               const float* init, uint16_t* Sr, uint16_t* St,
+                                               float* final_out, int Np) {
+  __shared__ ScanShared sm;
+  const int dk = a.dk, dv = a.dv, N = a.N;
+  const int nte = (dv + 127) / 128;
+  const int d0 = 64 * (blockIdx.x / nte), e0 = 128 * (blockIdx.x % nte);
+  const int bh = blockIdx.y, h = bh % a.H;
+  const float lg = a.hp.log2g[h];
+  const int nch = (N + kBC - 1) / kBC;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, g = l >> 4;
+  const Src X{XT + int64_t(bh) * dk * Np, Np, dk, false};
+  const Src Y{YT + int64_t(bh) * dv * Np, Np, dv, false};
+  const int64_t nS = int64_t(dk) * dv;
+  f32x4 t[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int d = d0 + 16 * w + 4 * g + r, e = e0 + 16 * j + l16;
+      t[j][r] = (init && d < dk && e < dv) ? init[bh * nS + int64_t(d) * dv + e] : 0.f;
+    }
+  const int arow = tid >> 2, aq = tid & 3;
+  u32x4 ra, rb[2];
+  for (int step = 0; step < nch; ++step) {
+    const int c = REV ? nch - 1 - step : step;
+    const int c0 = c * kBC, L = min(N, c0 + kBC) - c0;
+    // the chunk's boundary value, in both orientations
+    uint16_t* Sc = Sr + (int64_t(bh) * nch + c) * nS;
+    uint16_t* STc = St + (int64_t(bh) * nch + c) * nS;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = e0 + 16 * j + l16, d = d0 + 16 * w + 4 * g;
+      if (e < dv && d < dk) {
+        *reinterpret_cast<u32x2*>(STc + int64_t(e) * dk + d) =
+            u32x2{pack_h2(t[j][0], t[j][1]), pack_h2(t[j][2], t[j][3])};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Sc[int64_t(d + r) * dv + e] = h_bits(t[j][r]);
+      }
+    }
+    const float gL = gpow(lg, float(L));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] *= gL;
+    __syncthreads();   // the previous chunk's reads of wt are done
+    for (int jj = tid; jj < kBC; jj += 256)
+      sm.wt[jj] = jj < L ? (REV ? a.alpha * gpow(lg, float(jj + 1)) : gpow(lg, float(L - 1 - jj))) : 0.f;
+    auto fetch = [&](int k0) __attribute__((always_inline)) {
+      ra = run8(X, d0 + arow, int64_t(c0) + k0 + 8 * aq);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int run = tid + 256 * u;
+        rb[u] = run8(Y, e0 + (run >> 2), int64_t(c0) + k0 + 8 * (run & 3));
+      }
+    };
+    fetch(0);
+    for (int k0 = 0; k0 < L; k0 += kKH) {
+      __syncthreads();   // previous slice's reads done; the weights are written
+      *reinterpret_cast<u32x4*>(&sm.As[arow][8 * aq]) = scale8(ra, &sm.wt[k0 + 8 * aq]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int run = tid + 256 * u;
+        *reinterpret_cast<u32x4*>(&sm.Bs[run >> 2][8 * (run & 3)]) = rb[u];
+      }
+      __syncthreads();
+      if (k0 + kKH < L) fetch(k0 + kKH);
+      const f16x8 av = *reinterpret_cast<const f16x8*>(&sm.As[16 * w + l16][8 * g]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f16x8 bv = *reinterpret_cast<const f16x8*>(&sm.Bs[16 * j + l16][8 * g]);
+        t[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, t[j], 0, 0, 0);
+      }
+    }
+  }
+  if (final_out) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = d0 + 16 * w + 4 * g + r, e = e0 + 16 * j + l16;
+        if (d < dk && e < dv) final_out[bh * nS + int64_t(d) * dv + e] = t[j][r];
+      }
+  }
+}
+
+// ---- tile kernels (grid: (64-row tiles of the chunks, b*H + h)) ----------------------------
+struct Heads {
+  const uint16_t *QR, *KR, *QT, *KT, *VT, *DR, *DT, *S, *ST, *G, *GT;
+  int Np, nch;
+};
+
+// o recomputed: alpha (Qh Kh^T (.) D) V + alpha xi Qh S_c, then the GroupNorm / gate backward.
+template <int OUTD>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bm_dout(CallArgs a, Heads Hd, const void* gate, const void* dout, uint16_t* DR, void* dgate,
+        float* dgn_w, float* dgn_b) {
+  __shared__ TileSharedH sm;
+  const int dk = a.dk, dv = a.dv, N = a.N, Np = Hd.Np;
+  const TileRows T = tile_rows(N);
+  if (T.r0 >= T.r1) return;
+  const int bh = blockIdx.y, h = bh % a.H;
+  const float lg = a.hp.log2g[h];
+  const Src Q{Hd.QR + int64_t(bh) * N * dk, dk, N, false};
+  const Src K{Hd.KR + int64_t(bh) * N * dk, dk, N, false};
+  const Src VT{Hd.VT + int64_t(bh) * dv * Np, Np, dv, false};
+  const Src ST{Hd.ST + (int64_t(bh) * Hd.nch + T.c) * dk * dv, dk, dv, false};
+  float m[4][16];
+  zero_acc(m);
+  tmm16<16, false>(m, dk, sm, Q, T.r0, 1.f, 0.f, 0, 0, K, T.c0, 0);
+  store_scores<true>(sm, m, T.r0, T.r1, T.c0, T.r1, lg, a.alpha);
+  float o[4][32];
+  zero_acc(o);
+  tmm16<32, true>(o, T.r1 - T.c0, sm, Q, 0, 1.f, 0.f, 0, 0, VT, 0, T.c0);
+  tmm16<32, false>(o, dk, sm, Q, T.r0, a.alpha, lg, T.r0 - T.c0 + 1, 1, ST, 0, 0);
+  gn_backward_tile<RN_BF16, OUTD>(sm, o, a, h, bh, T.r0, T.r1, gate, dout, dgate, dgn_w, dgn_b,
+      [&](int64_t i, float x) __attribute__((always_inline)) { DR[i] = h_bits(x); });
+}
+
+// dQh = [alpha (dO V^T) (.) D] Kh + alpha xi dO S_c^T, rotated back.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bm_dq(CallArgs a, Heads Hd, const uint16_t* v, void* dq) {
+  __shared__ TileSharedH sm;
+  const int dk = a.dk, dv = a.dv, N = a.N, Np = Hd.Np;
+  const TileRows T = tile_rows(N);
+  if (T.r0 >= T.r1) return;
+  const int bh = blockIdx.y, h = bh % a.H;
+  const float lg = a.hp.log2g[h];
+  const Src D{Hd.DR + int64_t(bh) * N * dv, dv, N, false};
+  const Src V{v + int64_t(bh) * N * dv, dv, N, true};
+  const Src KT{Hd.KT + int64_t(bh) * dk * Np, Np, dk, false};
+  const Src S{Hd.S + (int64_t(bh) * Hd.nch + T.c) * dk * dv, dv, dk, false};
+  float m[4][16];
+  zero_acc(m);
+  tmm16<16, false>(m, dv, sm, D, T.r0, 1.f, 0.f, 0, 0, V, T.c0, 0);
+  store_scores<true>(sm, m, T.r0, T.r1, T.c0, T.r1, lg, a.alpha);
+  float gq[4][16];
+  zero_acc(gq);
+  tmm16<16, true>(gq, T.r1 - T.c0, sm, D, 0, 1.f, 0.f, 0, 0, KT, 0, T.c0);
+  tmm16<16, false>(gq, dv, sm, D, T.r0, a.alpha, lg, T.r0 - T.c0 + 1, 1, S, 0, 0);
+  store_rotated<RN_BF16>(sm, gq, a, seq_pos0(a, bh / a.H), bh, T.r0, T.r1, dq);
+}
+
+// Tile rows are keys s; later rows t in [s, c1): dKh = [alpha (V dO^T) (.) D'] Qh + zeta V G^T.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bm_dk(CallArgs a, Heads Hd, const uint16_t* v, void* dk_) {
+  __shared__ TileSharedH sm;
+  const int dk = a.dk, dv = a.dv, N = a.N, Np = Hd.Np;
+  const TileRows T = tile_rows(N);
+  if (T.r0 >= T.r1) return;
+  const int bh = blockIdx.y, h = bh % a.H;
+  const float lg = a.hp.log2g[h];
+  const Src V{v + int64_t(bh) * N * dv, dv, N, true};
+  const Src D{Hd.DR + int64_t(bh) * N * dv, dv, N, false};
+  const Src QT{Hd.QT + int64_t(bh) * dk * Np, Np, dk, false};
+  const Src G{Hd.G + (int64_t(bh) * Hd.nch + T.c) * dk * dv, dv, dk, false};
+  float m[4][16];
+  zero_acc(m);
+  tmm16<16, false>(m, dv, sm, V, T.r0, 1.f, 0.f, 0, 0, D, T.r0, 0);
+  store_scores<false>(sm, m, T.r0, T.r1, T.r0, T.c1, lg, a.alpha);
+  float gk[4][16];
+  zero_acc(gk);
+  tmm16<16, true>(gk, T.c1 - T.r0, sm, V, 0, 1.f, 0.f, 0, 0, QT, 0, T.r0);
+  tmm16<16, false>(gk, dv, sm, V, T.r0, 1.f, lg, T.c1 - 1 - T.r0, -1, G, 0, 0);
+  store_rotated<RN_BF16>(sm, gk, a, seq_pos0(a, bh / a.H), bh, T.r0, T.r1, dk_);
+}
+
+// dV = [alpha (Kh Qh^T) (.) D'] dO + zeta Kh G.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bm_dv(CallArgs a, Heads Hd, void* dv_) {
+  __shared__ TileSharedH sm;
+  const int dk = a.dk, dv = a.dv, N = a.N, Np = Hd.Np;
+  const TileRows T = tile_rows(N);
+  if (T.r0 >= T.r1) return;
+  const int bh = blockIdx.y, h = bh % a.H;
+  const float lg = a.hp.log2g[h];
+  const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
+  const Src K{Hd.KR + int64_t(bh) * N * dk, dk, N, false};
+  const Src Q{Hd.QR + int64_t(bh) * N * dk, dk, N, false};
+  const Src DT{Hd.DT + int64_t(bh) * dv * Np, Np, dv, false};
+  const Src GT{Hd.GT + (int64_t(bh) * Hd.nch + T.c) * dk * dv, dk, dv, false};
+  float m[4][16];
+  zero_acc(m);
+  tmm16<16, false>(m, dk, sm, K, T.r0, 1.f, 0.f, 0, 0, Q, T.r0, 0);
+  store_scores<false>(sm, m, T.r0, T.r1, T.r0, T.c1, lg, a.alpha);
+  float o[4][32];
+  zero_acc(o);
+  tmm16<32, true>(o, T.c1 - T.r0, sm, K, 0, 1.f, 0.f, 0, 0, DT, 0, T.r0);
+  tmm16<32, false>(o, dk, sm, K, T.r0, 1.f, lg, T.c1 - 1 - T.r0, -1, GT, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int s = T.r0 + 4 * ty + r;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int col = tx + 16 * j;
+      if (s < T.r1 && col < dv) Elem<RN_BF16>::store(dv_, (int64_t(bh) * N + s) * dv + col, o[r][j]);
+    }
+  }
+}
+
+__global__ void fill_zero_m(float* p, int64_t n) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0.f;
+}
+
+template <int OUTD>
+hipError_t launch_t(const CallArgs& a, const BwArgs& x, void* ws, hipStream_t st) {
+  const MLayout L = m_layout(a);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  auto at = [&](size_t off) { return reinterpret_cast<uint16_t*>(w + off); };
+  const int BH = a.B * a.H;
+  Heads Hd{at(L.QR), at(L.KR), at(L.QT), at(L.KT), at(L.VT), at(L.DR), at(L.DT),
+           at(L.S), at(L.ST), at(L.G), at(L.GT), L.Np, L.nch};
+  const dim3 gblk(L.Np / 64, BH);
+  const dim3 gscan(((a.dk + 63) / 64) * ((a.dv + 127) / 128), BH);
+  const dim3 gtiles(L.nch * (kBC / kR), BH);
+  hipLaunchKernelGGL(bm_prep, gblk, dim3(256), 0, st, a, static_cast<const uint16_t*>(x.q),
+                     static_cast<const uint16_t*>(x.k), static_cast<const uint16_t*>(x.v), at(L.QR),
+                     at(L.KR), at(L.QT), at(L.KT), at(L.VT), L.Np);
+  hipLaunchKernelGGL(bm_scan<0>, gscan, dim3(256), 0, st, a, static_cast<const uint16_t*>(at(L.KT)),
+                     static_cast<const uint16_t*>(at(L.VT)), x.state_in, at(L.S), at(L.ST),
+                     static_cast<float*>(nullptr), L.Np);
+  if (a.flags & RN_EPI_GN) {
+    if (x.dgn_w) hipLaunchKernelGGL(fill_zero_m, dim3(8), dim3(256), 0, st, x.dgn_w, int64_t(a.H) * a.dv);
+    if (x.dgn_b) hipLaunchKernelGGL(fill_zero_m, dim3(8), dim3(256), 0, st, x.dgn_b, int64_t(a.H) * a.dv);
+  }
+  hipLaunchKernelGGL((bm_dout<OUTD>), gtiles, dim3(256), 0, st, a, Hd, x.gate, x.dout, at(L.DR),
+                     x.dgate, x.dgn_w, x.dgn_b);
+  hipLaunchKernelGGL(bm_transpose, gblk, dim3(256), 0, st, static_cast<const uint16_t*>(at(L.DR)),
+                     at(L.DT), a.N, a.dv, L.Np);
+  hipLaunchKernelGGL(bm_scan<1>, gscan, dim3(256), 0, st, a, static_cast<const uint16_t*>(at(L.QT)),
+                     static_cast<const uint16_t*>(at(L.DT)), x.dstate_out, at(L.G), at(L.GT),
+                     x.dstate_in, L.Np);
+  hipLaunchKernelGGL(bm_dq, gtiles, dim3(256), 0, st, a, Hd, static_cast<const uint16_t*>(x.v), x.dq);
+  hipLaunchKernelGGL(bm_dk, gtiles, dim3(256), 0, st, a, Hd, static_cast<const uint16_t*>(x.v), x.dk);
+  hipLaunchKernelGGL(bm_dv, gtiles, dim3(256), 0, st, a, Hd, x.dv);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool backward_mfma_supported(const CallArgs& a, int in_dt) {
+  return in_dt == RN_BF16 && a.dk % 8 == 0 && a.dv % 8 == 0;
+}
+
+size_t backward_mfma_ws_bytes(const CallArgs& a) { return m_layout(a).total; }
+
+hipError_t launch_backward_mfma(const CallArgs& a, int out_dt, const BwArgs& x, void* ws,
+                                hipStream_t st) {
+  return out_dt == RN_F32 ? launch_t<RN_F32>(a, x, ws, st) : launch_t<RN_BF16>(a, x, ws, st);
+}
+
+}  // namespace rn

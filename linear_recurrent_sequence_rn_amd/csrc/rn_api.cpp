@@ -280,10 +280,18 @@ rn_status rn_retention_recurrent_step_at(const rn_desc* desc, const int64_t* pos
   return step_call(desc, pos, q, k, v, gate, state, out, stream);
 }
 
+// Workspace of the gradients: the matrix-core path's where it may run (it is chosen per
+// call, by the pointers' alignment), never less than the float32 path's.
+static size_t backward_need(const rn_desc* desc, const rn::CallArgs& a) {
+  size_t n = rn::backward_ws_bytes(a);
+  if (rn::backward_mfma_supported(a, desc->in_dtype)) n = std::max(n, rn::backward_mfma_ws_bytes(a));
+  return align256(n);
+}
+
 size_t rn_chunkwise_backward_workspace_bytes(const rn_desc* desc, int32_t chunk) {
   rn::CallArgs a;
   if (chunk < 1 || check_desc(desc, Form::kChunkwise, &a) != RN_OK || a.gpair) return 0;
-  return align256(rn::backward_ws_bytes(a));
+  return backward_need(desc, a);
 }
 
 rn_status rn_retention_chunkwise_backward(const rn_desc* desc, int32_t chunk, const void* q,
@@ -306,7 +314,7 @@ rn_status rn_retention_chunkwise_backward(const rn_desc* desc, int32_t chunk, co
     return fail(RN_ERR_INVALID_ARG, "q/k/v/dout/dq/dk/dv pointer is NULL");
   if ((desc->flags & RN_EPI_GATE) && (!gate || !dgate))
     return fail(RN_ERR_INVALID_ARG, "RN_EPI_GATE needs gate and dgate");
-  const size_t need = align256(rn::backward_ws_bytes(a));
+  const size_t need = backward_need(desc, a);
   if (!workspace || workspace_bytes < need)
     return fail(RN_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
@@ -317,6 +325,13 @@ rn_status rn_retention_chunkwise_backward(const rn_desc* desc, int32_t chunk, co
                (desc->flags & RN_EPI_GN) ? dgn_weight : nullptr,
                (desc->flags & RN_EPI_GN) ? dgn_bias : nullptr};
   g_err[0] = 0;
+  const bool mfma = rn::backward_mfma_supported(a, desc->in_dtype) &&
+                    reinterpret_cast<uintptr_t>(v) % 16 == 0 && reinterpret_cast<uintptr_t>(q) % 4 == 0 &&
+                    reinterpret_cast<uintptr_t>(k) % 4 == 0;
+  if (mfma)
+    return hip_status(rn::launch_backward_mfma(a, desc->out_dtype, x, workspace,
+                                               static_cast<hipStream_t>(stream)),
+                      "chunkwise backward (matrix cores) launch");
   return hip_status(rn::launch_backward(a, desc->in_dtype, desc->out_dtype, x, workspace,
                                         static_cast<hipStream_t>(stream)),
                     "chunkwise backward launch");

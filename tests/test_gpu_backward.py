@@ -97,10 +97,13 @@ def test_bf16_6p7b_head_shape():
         assert close(got[n].cpu(), ref[n], bf16=True, rel=1e-2) <= 1.0, n
 
 
-@pytest.mark.parametrize("N,pos0,dk,dv", [(513, 70000, 64, 96), (77, 3, 48, 40), (600, 0, 256, 512)])
+@pytest.mark.parametrize("N,pos0,dk,dv", [(513, 70000, 64, 96), (77, 3, 48, 40), (600, 0, 256, 512),
+                                         (130, 5, 20, 12)])
 def test_bf16_state_positions_other_shapes(N, pos0, dk, dv):
-    """Matrix-core path with an initial state, a gradient for the final state, positions
-    and ragged tiles; head shapes below the 6.7B one are zero-padded in the products."""
+    """Matrix-core paths with an initial state, a gradient for the final state, positions
+    and ragged tiles; head shapes below the 6.7B one are zero-padded in the products (d_k
+    and d_v multiples of 8 take the half-operand path with transposed copies, 20 / 12 the
+    one that stages float32 operands)."""
     x = make("bf16", 2, 2, N, dk, dv, seed=N + dk, state=True)
     got = rn().rn_retention_chunkwise_backward(
         dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"], 64, dev(x["dout"]),
