@@ -160,75 +160,113 @@ MLayout m_layout(const CallArgs& a) {
 }
 
 // ---- prep: rotated q, k (row-major and transposed) and v transposed, per 64 tokens ------
-// Grid (Np/64, b*H + h); the transposes go through LDS, [column][token].
+// Grid (Np/64, b*H + h); the transposes go through LDS, [column][token] with a pitch of
+// 66 halves (33 words, odd: the 64 lanes of a wave writing one token of consecutive
+// columns hit distinct banks), read back 4 bytes at a time.
+constexpr int kTp = 66;
+__device__ __forceinline__ void store_t_rows(uint16_t (*tb)[kTp], int rows, uint16_t* T, int Np, int t0) {
+  for (int e = threadIdx.x; e < rows * 8; e += 256) {
+    const int c = e >> 3, pc = e & 7;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(&tb[c][8 * pc]);
+    *reinterpret_cast<u32x4*>(T + int64_t(c) * Np + t0 + 8 * pc) = u32x4{src[0], src[1], src[2], src[3]};
+  }
+}
 __global__ void __launch_bounds__(256) bm_prep(CallArgs a, const uint16_t* q, const uint16_t* k,
                                                const uint16_t* v, uint16_t* QR, uint16_t* KR,
                                                uint16_t* QT, uint16_t* KT, uint16_t* VT, int Np) {
-  __shared__ __attribute__((aligned(16))) uint16_t tb[kMaxDv][64 + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t tb[kMaxDv][kTp];
   const int dk = a.dk, dv = a.dv, N = a.N;
   const int t0 = blockIdx.x * 64, bh = blockIdx.y;
   const int64_t p0 = seq_pos0(a, bh / a.H);
+  // Runs of 8 values: lane e takes token e % 64 of column group e / 64, so that its
+  // writes of one column into tb fall in consecutive halves; all of a thread's loads are
+  // issued before the first is used (up to 8 runs of q or k, 16 of v at the 6.7B shape).
+  constexpr int kMaxRunsK = 64 * (kMaxDk / 8) / 256;
+  constexpr int kMaxRunsV = 64 * (kMaxDv / 8) / 256;
   for (int which = 0; which < 2; ++which) {
-    const uint16_t* x = which ? k : q;
+    const uint16_t* x = (which ? k : q) + int64_t(bh) * N * dk;
     uint16_t* R = (which ? KR : QR) + int64_t(bh) * N * dk;
     uint16_t* T = (which ? KT : QT) + int64_t(bh) * dk * Np;
-    for (int e = threadIdx.x; e < 64 * (dk / 2); e += 256) {
-      const int tt = e / (dk / 2), j = e - tt * (dk / 2), t = t0 + tt;
-      float r0 = 0.f, r1 = 0.f;
-      if (t < N) {
-        const uint32_t u = *reinterpret_cast<const uint32_t*>(x + (int64_t(bh) * N + t) * dk + 2 * j);
+    const int nrun = 64 * (dk / 8);
+    u32x4 raw[kMaxRunsK];
+#pragma unroll
+    for (int i = 0; i < kMaxRunsK; ++i) {
+      const int e = threadIdx.x + 256 * i, cq = e >> 6, t = t0 + (e & 63);
+      raw[i] = (e < nrun && t < N) ? *reinterpret_cast<const u32x4*>(x + int64_t(t) * dk + 8 * cq)
+                                    : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxRunsK; ++i) {
+      const int e = threadIdx.x + 256 * i, cq = e >> 6, tt = e & 63, t = t0 + tt;
+      if (e >= nrun) break;
+      const uint32_t w4[4] = {raw[i][0], raw[i][1], raw[i][2], raw[i][3]};
+      uint32_t o[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t u = w4[m];
         const float x0 = __uint_as_float(u << 16), x1 = __uint_as_float(u & 0xffff0000u);
-        float c, s;
-        angle_cs(p0 + t, a.ap.theta[j], &c, &s);
-        r0 = x0 * c - x1 * s;
-        r1 = x0 * s + x1 * c;
-        *reinterpret_cast<uint32_t*>(R + int64_t(t) * dk + 2 * j) = pack_h2(r0, r1);
+        float c, sn;
+        angle_cs(p0 + t, a.ap.theta[4 * cq + m], &c, &sn);
+        const float r0 = x0 * c - x1 * sn, r1 = x0 * sn + x1 * c;
+        o[m] = pack_h2(r0, r1);
+        tb[8 * cq + 2 * m][tt] = uint16_t(o[m] & 0xffffu);
+        tb[8 * cq + 2 * m + 1][tt] = uint16_t(o[m] >> 16);
       }
-      tb[2 * j][tt] = h_bits(r0);
-      tb[2 * j + 1][tt] = h_bits(r1);
+      if (t < N) *reinterpret_cast<u32x4*>(R + int64_t(t) * dk + 8 * cq) = u32x4{o[0], o[1], o[2], o[3]};
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < dk * 8; e += 256) {
-      const int d = e >> 3, pc = e & 7;
-      *reinterpret_cast<u32x4*>(T + int64_t(d) * Np + t0 + 8 * pc) = *reinterpret_cast<const u32x4*>(&tb[d][8 * pc]);
-    }
+    store_t_rows(tb, dk, T, Np, t0);
     __syncthreads();
   }
-  uint16_t* T = VT + int64_t(bh) * dv * Np;
-  for (int e = threadIdx.x; e < 64 * dv; e += 256) {
-    const int tt = e / dv, c = e - tt * dv, t = t0 + tt;
-    const float x = t < N ? __uint_as_float(uint32_t(v[(int64_t(bh) * N + t) * dv + c]) << 16) : 0.f;
-    tb[c][tt] = h_bits(x);
+  const uint16_t* vb = v + int64_t(bh) * N * dv;
+  const int nrun = 64 * (dv / 8);
+  u32x4 raw[kMaxRunsV];
+#pragma unroll
+  for (int i = 0; i < kMaxRunsV; ++i) {
+    const int e = threadIdx.x + 256 * i, cq = e >> 6, t = t0 + (e & 63);
+    raw[i] = (e < nrun && t < N) ? *reinterpret_cast<const u32x4*>(vb + int64_t(t) * dv + 8 * cq)
+                                  : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxRunsV; ++i) {
+    const int e = threadIdx.x + 256 * i, cq = e >> 6, tt = e & 63;
+    if (e >= nrun) break;
+    const uint32_t w4[4] = {raw[i][0], raw[i][1], raw[i][2], raw[i][3]};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t hh = bf2_to_h2(w4[m]);
+      tb[8 * cq + 2 * m][tt] = uint16_t(hh & 0xffffu);
+      tb[8 * cq + 2 * m + 1][tt] = uint16_t(hh >> 16);
+    }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < dv * 8; e += 256) {
-    const int c = e >> 3, pc = e & 7;
-    *reinterpret_cast<u32x4*>(T + int64_t(c) * Np + t0 + 8 * pc) = *reinterpret_cast<const u32x4*>(&tb[c][8 * pc]);
-  }
+  store_t_rows(tb, dv, VT + int64_t(bh) * dv * Np, Np, t0);
 }
 
-// dO [N][d_v] -> dO^T [d_v][Np] (zero past N). Grid (Np/64, b*H + h).
+// dO [N][d_v] -> dO^T [d_v][Np] (zero past N). Grid (Np/64, b*H + h). Lanes take
+// consecutive tokens of one 8-column group (16-byte loads from consecutive rows), so that
+// their LDS writes of one column fall in consecutive halves.
 __global__ void __launch_bounds__(256) bm_transpose(const uint16_t* R, uint16_t* T, int N, int dv,
                                                     int Np) {
-  __shared__ __attribute__((aligned(16))) uint16_t tb[kMaxDv][64 + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t tb[kMaxDv][kTp];
   const int t0 = blockIdx.x * 64, bh = blockIdx.y;
   const uint16_t* Rb = R + int64_t(bh) * N * dv;
   for (int e = threadIdx.x; e < 64 * (dv / 8); e += 256) {
-    const int tt = e / (dv / 8), cq = e - tt * (dv / 8), t = t0 + tt;
+    const int cq = e >> 6, tt = e & 63, t = t0 + tt;
     u32x4 x = u32x4{0u, 0u, 0u, 0u};
     if (t < N) x = *reinterpret_cast<const u32x4*>(Rb + int64_t(t) * dv + 8 * cq);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tb[8 * cq + 2 * i][tt] = uint16_t(x[i] & 0xffffu);
-      tb[8 * cq + 2 * i + 1][tt] = uint16_t(x[i] >> 16);
-    }
+    const uint32_t x0 = x[0], x1 = x[1], x2 = x[2], x3 = x[3];
+    tb[8 * cq + 0][tt] = uint16_t(x0 & 0xffffu);
+    tb[8 * cq + 1][tt] = uint16_t(x0 >> 16);
+    tb[8 * cq + 2][tt] = uint16_t(x1 & 0xffffu);
+    tb[8 * cq + 3][tt] = uint16_t(x1 >> 16);
+    tb[8 * cq + 4][tt] = uint16_t(x2 & 0xffffu);
+    tb[8 * cq + 5][tt] = uint16_t(x2 >> 16);
+    tb[8 * cq + 6][tt] = uint16_t(x3 & 0xffffu);
+    tb[8 * cq + 7][tt] = uint16_t(x3 >> 16);
   }
   __syncthreads();
-  uint16_t* Tb = T + int64_t(bh) * dv * Np;
-  for (int e = threadIdx.x; e < dv * 8; e += 256) {
-    const int c = e >> 3, pc = e & 7;
-    *reinterpret_cast<u32x4*>(Tb + int64_t(c) * Np + t0 + 8 * pc) = *reinterpret_cast<const u32x4*>(&tb[c][8 * pc]);
-  }
+  store_t_rows(tb, dv, T + int64_t(bh) * dv * Np, Np, t0);
 }
 
 // ---- state scans on matrix cores ---------------------------------------------------------

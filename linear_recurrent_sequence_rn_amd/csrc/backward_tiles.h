@@ -311,17 +311,21 @@ __device__ __forceinline__ void gn_backward_tile(SM& sm, const float (&o)[4][32]
     return;
   }
   // GroupNorm / gate backward, row by row. Per-column sums of dy * xh and dy (for dgn_w,
-  // dgn_b) gather in this thread's own LDS cells: Bs[ty][col] and P viewed as [16][kLdB].
-  float* sw = gn_sw(sm);
-  float* sb = gn_sb(sm);
-  __syncthreads();
+  // dgn_b) gather in registers over this thread's four rows, then in its own LDS cells
+  // (two [16][kLdB] float arrays) for the reduction over the tile.
+  const bool sums = dgn_w || dgn_b;
+  float swa[32], sba[32];
+#pragma clang loop unroll(full)
+  for (int j = 0; j < 32; ++j) swa[j] = sba[j] = 0.f;
+  // affine parameters of this thread's 32 columns; dout, gate and the sigmoid are taken
+  // once per element
+  float wv[32], bv[32];
 #pragma clang loop unroll(full)
   for (int j = 0; j < 32; ++j) {
-    sw[ty * kLdB + tx + 16 * j] = 0.f;
-    sb[ty * kLdB + tx + 16 * j] = 0.f;
+    const int col = tx + 16 * j;
+    wv[j] = (a.gn_w && col < dv) ? a.gn_w[h * dv + col] : 1.f;
+    bv[j] = (a.gn_b && col < dv) ? a.gn_b[h * dv + col] : 0.f;
   }
-  auto gnw = [&](int col) { return a.gn_w ? a.gn_w[h * dv + col] : 1.f; };
-  auto gnb = [&](int col) { return a.gn_b ? a.gn_b[h * dv + col] : 0.f; };
 #pragma clang loop unroll(full)
   for (int r = 0; r < 4; ++r) {
     const int t = T.r0 + 4 * ty + r;
@@ -338,36 +342,30 @@ __device__ __forceinline__ void gn_backward_tile(SM& sm, const float (&o)[4][32]
       s2 += (tx + 16 * j < dv) ? dd * dd : 0.f;
     }
     const float rstd = 1.0f / sqrtf(row16_sum(s2) / dv + a.eps);
-    // dy = dout (* swish(g)); dxh = dy * w; the row means of dxh and dxh * xh
-    auto dy_of = [&](int j, float xh) {
-      const int col = tx + 16 * j;
-      float dy = Elem<OUTD>::load(dout, roff + col);
-      if (gt) {
-        const float g = Elem<IN>::load(gate, roff + col);
-        const float sg = 1.0f / (1.0f + expf(-g));
-        dy *= g * sg;
-      }
-      (void)xh;
-      return dy;
-    };
+    // dy = dout (* swish(g)); dgate = dout y swish'(g); the row means of dxh = dy w and
+    // of dxh xh
+    float dyv[32];
     float m1 = 0.f, m2 = 0.f;
 #pragma clang loop unroll(full)
     for (int j = 0; j < 32; ++j) {
       const int col = tx + 16 * j;
+      dyv[j] = 0.f;
       if (live && col < dv) {
-      const float xh = (o[r][j] - mean) * rstd;
-      const float dy = dy_of(j, xh);
-      const float dxh = dy * gnw(col);
-      m1 += dxh;
-      m2 += dxh * xh;
-      sw[ty * kLdB + col] += dy * xh;
-      sb[ty * kLdB + col] += dy;
-      if (gt) {
-        const float g = Elem<IN>::load(gate, roff + col);
-        const float sg = 1.0f / (1.0f + expf(-g));
+        const float xh = (o[r][j] - mean) * rstd;
         const float d0 = Elem<OUTD>::load(dout, roff + col);
-        Elem<IN>::store(dgate, roff + col, d0 * (xh * gnw(col) + gnb(col)) * sg * (1.0f + g * (1.0f - sg)));
-      }
+        float dy = d0;
+        if (gt) {
+          const float g = Elem<IN>::load(gate, roff + col);
+          const float sg = 1.0f / (1.0f + expf(-g));
+          dy = d0 * g * sg;
+          Elem<IN>::store(dgate, roff + col, d0 * (xh * wv[j] + bv[j]) * sg * (1.0f + g * (1.0f - sg)));
+        }
+        dyv[j] = dy;
+        const float dxh = dy * wv[j];
+        m1 += dxh;
+        m2 += dxh * xh;
+        swa[j] += dy * xh;
+        sba[j] += dy;
       }
     }
     m1 = row16_sum(m1) / dv;
@@ -377,12 +375,19 @@ __device__ __forceinline__ void gn_backward_tile(SM& sm, const float (&o)[4][32]
       const int col = tx + 16 * j;
       if (live && col < dv) {
         const float xh = (o[r][j] - mean) * rstd;
-        const float dxh = dy_of(j, xh) * gnw(col);
-        store_dO(roff + col, rstd * (dxh - m1 - xh * m2));
+        store_dO(roff + col, rstd * (dyv[j] * wv[j] - m1 - xh * m2));
       }
     }
   }
-  if (dgn_w || dgn_b) {
+  if (sums) {
+    float* sw = gn_sw(sm);
+    float* sb = gn_sb(sm);
+    __syncthreads();   // the products' reads of shared memory are done
+#pragma clang loop unroll(full)
+    for (int j = 0; j < 32; ++j) {
+      sw[ty * kLdB + tx + 16 * j] = swa[j];
+      sb[ty * kLdB + tx + 16 * j] = sba[j];
+    }
     __syncthreads();
     for (int col = threadIdx.x; col < dv; col += 256) {
       float xw = 0.f, xb = 0.f;
