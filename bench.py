@@ -106,6 +106,7 @@ def main():
     ap.add_argument("--no-parallel", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-pair", action="store_true")
+    ap.add_argument("--no-schedules", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--source-hash", action="store_true",
                     help="print the chunkwise kernel's source hash (as recorded in its profile) and exit")
@@ -209,6 +210,36 @@ def main():
                      "algorithmic_bytes": bytes_, "algorithmic_flops": flops,
                      "mfma_tflops": tfl, "mfma_frac": tfl / BF16_PEAK_TFLOPS},
     }
+
+    # ---- the other chunkwise schedules on the same workload (secondary record) ------------
+    # Same inputs and outputs, same result: the segmented schedule (segment-local states,
+    # scan, outputs) and the chunk-parallel pair (state snapshots, outputs).
+    if args.only is not None:
+        args.no_schedules = True
+    if not args.no_schedules:
+        sched = {"workload": "chunkwise_6p7b, the headline call with another schedule flag",
+                 "sequential_ms": kern_s * 1e3}
+        for name, kw in (("segmented", dict(segmented=True)), ("pair", dict(chunk_parallel=True))):
+            wss = torch.empty(rn.rn_chunkwise_workspace_bytes(q, v, gamma, theta, w.chunk, gn=True, gate=gate, **kw),
+                              dtype=torch.uint8, device=dev)
+
+            def sstep():
+                rn.rn_retention_chunkwise(q, k, v, gamma, theta, w.chunk, gate=gate, gn=True,
+                                          gn_eps=w.gn_eps, state_out=S_out, out=out, workspace=wss, **kw)
+
+            for _ in range(3):
+                sstep()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 10
+            e0.record(stream)
+            for _ in range(reps):
+                sstep()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            sched[name + "_ms"] = e0.elapsed_time(e1) / reps
+            del wss
+        rec["schedules"] = sched
 
     # ---- chunkwise backward on the same workload (secondary record) ------------------
     # Gradients of q, k, v and the gate through GroupNorm + gate, given a random dout; the

@@ -63,12 +63,18 @@ typedef int32_t rn_dtype;
 #define RN_EPI_GN     (1u << 2) /* per-(token, head) GroupNorm over d_v (hwhale notes, multi-head paragraph) */
 #define RN_EPI_GATE   (1u << 3) /* out = GN(.) * swish(gate); requires RN_EPI_GN (m0nads notes, swish gate) */
 #define RN_FORCE_GENERIC (1u << 8) /* use the plain (non-MFMA) kernels; for testing and unusual shapes */
-#define RN_CHUNK_PARALLEL (1u << 9) /* chunkwise: the two-kernel schedule (state snapshots per 256
-                                       tokens, then all chunks' outputs in parallel) instead of the
-                                       single sequential kernel; same result, another workspace size.
-                                       It is also what runs where the sequential kernel does not
-                                       apply (gamma^32 < 2^-6, or gamma_pair set) at d_k 256,
-                                       d_v 512 */
+#define RN_CHUNK_PARALLEL (1u << 9) /* chunkwise: the two-kernel chunk-parallel pair (state
+                                       snapshots per 256 tokens, then all chunks' outputs in
+                                       parallel) instead of the single sequential kernel; same
+                                       result, another workspace size. It is also what runs where
+                                       the sequential kernel does not apply (gamma^32 < 2^-6, or
+                                       gamma_pair set) at d_k 256, d_v 512 */
+#define RN_CHUNK_SEGMENTED (1u << 10) /* chunkwise, bf16 with d_k 256, d_v 512 and one decay per
+                                       head: the segmented schedule (segment-local states per
+                                       2048 tokens, a scan over segments, then all chunks'
+                                       outputs in parallel); same result, another workspace size,
+                                       no limit on gamma. Elsewhere the flag is ignored. At most
+                                       one of RN_CHUNK_PARALLEL and RN_CHUNK_SEGMENTED may be set. */
 
 typedef struct rn_desc {
     int32_t B;             /* batch, >= 1 */

@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "RN_OK", "RN_ERR_INVALID_ARG", "RN_ERR_UNSUPPORTED", "RN_ERR_HIP", "RN_ERR_WORKSPACE",
     "RN_F32", "RN_BF16", "RN_NORM_D_ROW", "RN_NORM_R_ROW", "RN_EPI_GN", "RN_EPI_GATE",
-    "RN_FORCE_GENERIC", "RN_CHUNK_PARALLEL", "RnError", "RnDesc", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
+    "RN_FORCE_GENERIC", "RN_CHUNK_PARALLEL", "RN_CHUNK_SEGMENTED", "RnError", "RnDesc", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
     "rn_retention_parallel", "rn_retention_chunkwise", "rn_retention_recurrent_step",
     "rn_retention_chunkwise_varlen", "rn_retention_recurrent_step_at", "rn_groupnorm_gate",
     "rn_retention_chunkwise_backward", "rn_chunkwise_backward_workspace_bytes", "rn_chunkwise_workspace_bytes", "rn_parallel_workspace_bytes",
@@ -35,6 +35,7 @@ RN_F32, RN_BF16 = 0, 1
 RN_NORM_D_ROW, RN_NORM_R_ROW, RN_EPI_GN, RN_EPI_GATE = 1, 2, 4, 8
 RN_FORCE_GENERIC = 1 << 8
 RN_CHUNK_PARALLEL = 1 << 9
+RN_CHUNK_SEGMENTED = 1 << 10
 
 EXPORTED_SYMBOLS = (
     "rn_parallel_workspace_bytes", "rn_retention_parallel", "rn_chunkwise_workspace_bytes", "rn_retention_chunkwise",
@@ -199,9 +200,10 @@ def make_desc(B: int, H: int, N: int, d_k: int, d_v: int, in_dtype: int, out_dty
     return d, (g, gp, th, gn_weight, gn_bias)
 
 
-def _flags(norm_d, norm_r, gn, gate, force_generic, chunk_parallel=False):
+def _flags(norm_d, norm_r, gn, gate, force_generic, chunk_parallel=False, segmented=False):
     f = 0
     if chunk_parallel: f |= RN_CHUNK_PARALLEL
+    if segmented: f |= RN_CHUNK_SEGMENTED
     if norm_d: f |= RN_NORM_D_ROW
     if norm_r: f |= RN_NORM_R_ROW
     if gn: f |= RN_EPI_GN
@@ -261,9 +263,10 @@ def rn_parallel_workspace_bytes(q, v, gamma, theta, *, norm_d=False, norm_r=Fals
 
 
 def rn_chunkwise_workspace_bytes(q, v, gamma, theta, chunk, *, gn=False, gate=None,
-                                 out_dtype=None, force_generic=False, chunk_parallel=False) -> int:
+                                 out_dtype=None, force_generic=False, chunk_parallel=False,
+                                 segmented=False) -> int:
     B, H, N, dk = q.shape
-    flags = _flags(False, False, gn, gate, force_generic, chunk_parallel)
+    flags = _flags(False, False, gn, gate, force_generic, chunk_parallel, segmented)
     od = q.dtype if out_dtype is None else out_dtype
     d, keep = make_desc(B, H, N, dk, v.shape[-1], _dtype_code(q.dtype), _dtype_code(od), gamma,
                         theta, flags=flags, device=q.device)
@@ -281,20 +284,21 @@ def _seq_array(t, B, dtype, name):
 def rn_retention_chunkwise(q, k, v, gamma, theta, chunk, *, gate=None, state_in=None,
                            state_out=None, out=None, out_dtype=None, workspace=None, pos0=0,
                            qk_scale=1.0, gn=False, gn_eps=1e-5, gn_weight=None, gn_bias=None,
-                           force_generic=False, chunk_parallel=False):
+                           force_generic=False, chunk_parallel=False, segmented=False):
     """Chunkwise form; returns (out, state_out). ``state_out`` may be a tensor (written),
     True (allocated), or None/False (discarded). ``chunk_parallel`` selects the two-kernel
-    schedule (RN_CHUNK_PARALLEL)."""
+    chunk-parallel pair (RN_CHUNK_PARALLEL), ``segmented`` the segmented schedule
+    (RN_CHUNK_SEGMENTED); by default the sequential kernel runs where it applies."""
     return _chunkwise(q, k, v, gamma, theta, chunk, None, None, gate, state_in, state_out, out,
                       out_dtype, workspace, pos0, qk_scale, gn, gn_eps, gn_weight, gn_bias,
-                      force_generic, chunk_parallel)
+                      force_generic, chunk_parallel, segmented)
 
 
 def rn_retention_chunkwise_varlen(q, k, v, gamma, theta, chunk, *, pos=None, lengths=None,
                                   gate=None, state_in=None, state_out=None, out=None,
                                   out_dtype=None, workspace=None, pos0=0, qk_scale=1.0, gn=False,
                                   gn_eps=1e-5, gn_weight=None, gn_bias=None, force_generic=False,
-                                  chunk_parallel=False):
+                                  chunk_parallel=False, segmented=False):
     """Chunkwise form over a padded batch: sequence b holds ``lengths[b]`` tokens
     (device int32 [B]) starting at position ``pos[b]`` (device int64 [B]); either may be
     None (N tokens / ``pos0``). Rows past a sequence's length are not written (a new
@@ -304,13 +308,13 @@ def rn_retention_chunkwise_varlen(q, k, v, gamma, theta, chunk, *, pos=None, len
         out = _out(None, v.shape, od, v.device, fill=0)
     return _chunkwise(q, k, v, gamma, theta, chunk, pos, lengths, gate, state_in, state_out, out,
                       out_dtype, workspace, pos0, qk_scale, gn, gn_eps, gn_weight, gn_bias,
-                      force_generic, chunk_parallel)
+                      force_generic, chunk_parallel, segmented)
 
 
 def _chunkwise(q, k, v, gamma, theta, chunk, pos, lengths, gate, state_in, state_out, out,
                out_dtype, workspace, pos0, qk_scale, gn, gn_eps, gn_weight, gn_bias,
-               force_generic, chunk_parallel):
-    flags = _flags(False, False, gn, gate, force_generic, chunk_parallel)
+               force_generic, chunk_parallel, segmented=False):
+    flags = _flags(False, False, gn, gate, force_generic, chunk_parallel, segmented)
     d, keep, od = _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos0, qk_scale, gn_eps,
                             gn_weight, gn_bias)
     B, H, N, dk = q.shape

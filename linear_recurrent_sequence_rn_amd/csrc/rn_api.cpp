@@ -32,7 +32,7 @@ rn_status hip_status(hipError_t e, const char* what) {
 enum class Form { kParallel, kChunkwise, kStep };
 
 constexpr uint32_t kKnownFlags = RN_NORM_D_ROW | RN_NORM_R_ROW | RN_EPI_GN | RN_EPI_GATE |
-                                 RN_FORCE_GENERIC | RN_CHUNK_PARALLEL;
+                                 RN_FORCE_GENERIC | RN_CHUNK_PARALLEL | RN_CHUNK_SEGMENTED;
 
 bool dtype_ok(rn_dtype d) { return d == RN_F32 || d == RN_BF16; }
 
@@ -52,6 +52,8 @@ rn_status check_desc(const rn_desc* d, Form form, rn::CallArgs* a) {
   if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype))
     return fail(RN_ERR_INVALID_ARG, "unknown dtype (in=%d out=%d)", d->in_dtype, d->out_dtype);
   if (d->flags & ~kKnownFlags) return fail(RN_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
+  if ((d->flags & RN_CHUNK_PARALLEL) && (d->flags & RN_CHUNK_SEGMENTED))
+    return fail(RN_ERR_INVALID_ARG, "RN_CHUNK_PARALLEL and RN_CHUNK_SEGMENTED are exclusive");
   if ((d->flags & RN_EPI_GATE) && !(d->flags & RN_EPI_GN))
     return fail(RN_ERR_INVALID_ARG, "RN_EPI_GATE requires RN_EPI_GN");
   if (form != Form::kParallel && (d->flags & (RN_NORM_D_ROW | RN_NORM_R_ROW)))
@@ -173,17 +175,20 @@ rn_status rn_retention_parallel(const rn_desc* desc, const void* q, const void* 
 }
 
 // Chunkwise schedules: the sequential fused kernel (default where it applies), the
-// chunk-parallel pair (on request, where the sequential kernel's decay range does not
-// hold, and for one decay per coordinate pair), the generic float32 kernel (everything
-// else).
-enum class ChunkPath { kParallelPair, kSequential, kGeneric };
+// segmented schedule (on request, and where the sequential kernel's decay range does not
+// hold), the chunk-parallel pair (on request, and for one decay per coordinate pair), the
+// generic float32 kernel (everything else).
+enum class ChunkPath { kSegmented, kParallelPair, kSequential, kGeneric };
 
 static ChunkPath chunk_path(const rn_desc* d, const rn::CallArgs& a) {
   if (d->flags & RN_FORCE_GENERIC) return ChunkPath::kGeneric;
   const bool pair = rn::chunkwise_cp_supported(a, d->in_dtype);
+  const bool seg = rn::chunkwise_seg_supported(a, d->in_dtype);
   if (a.gpair) return pair ? ChunkPath::kParallelPair : ChunkPath::kGeneric;
   if ((d->flags & RN_CHUNK_PARALLEL) && pair) return ChunkPath::kParallelPair;
+  if ((d->flags & RN_CHUNK_SEGMENTED) && seg) return ChunkPath::kSegmented;
   if (rn::chunkwise_mfma_supported(a, d->in_dtype)) return ChunkPath::kSequential;
+  if (seg) return ChunkPath::kSegmented;
   if (pair) return ChunkPath::kParallelPair;
   return ChunkPath::kGeneric;
 }
@@ -192,6 +197,7 @@ size_t rn_chunkwise_workspace_bytes(const rn_desc* desc, int32_t chunk) {
   rn::CallArgs a;
   if (chunk < 1 || check_desc(desc, Form::kChunkwise, &a) != RN_OK) return 0;
   switch (chunk_path(desc, a)) {
+    case ChunkPath::kSegmented: return align256(rn::chunkwise_seg_ws_bytes(a));
     case ChunkPath::kParallelPair: return align256(rn::chunkwise_cp_ws_bytes(a));
     case ChunkPath::kSequential: return align256(rn::chunkwise_mfma_ws_bytes(a));
     default: return generic_ws_bytes(desc);
@@ -218,6 +224,10 @@ static rn_status chunkwise_call(const rn_desc* desc, int32_t chunk, const int64_
   g_err[0] = 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const ChunkPath path = chunk_path(desc, a);
+  if (path == ChunkPath::kSegmented)
+    return hip_status(rn::launch_chunkwise_seg(a, desc->out_dtype, q, k, v, gate, state_in,
+                                               state_out, out, workspace, workspace_bytes, st),
+                      "chunkwise (segmented) launch");
   if (path == ChunkPath::kParallelPair)
     return hip_status(rn::launch_chunkwise_cp(a, desc->out_dtype, q, k, v, gate, state_in,
                                               state_out, out, workspace, workspace_bytes, st),

@@ -35,6 +35,14 @@ hipError_t launch_chunkwise_cp(const CallArgs& a, int out_dt, const void* q, con
                                const void* v, const void* gate, const float* s_in, float* s_out,
                                void* out, void* ws, size_t ws_bytes, hipStream_t st);
 
+// Segmented chunkwise schedule: segment-local states, a scan over segments, then the
+// outputs of all chunks (bf16, d_k 256, d_v 512, one decay per head).
+bool chunkwise_seg_supported(const CallArgs& a, int in_dt);
+size_t chunkwise_seg_ws_bytes(const CallArgs& a);
+hipError_t launch_chunkwise_seg(const CallArgs& a, int out_dt, const void* q, const void* k,
+                                const void* v, const void* gate, const float* s_in, float* s_out,
+                                void* out, void* ws, size_t ws_bytes, hipStream_t st);
+
 // Gradients of the chunkwise form (plain float32 kernels).
 struct BwArgs {
   const void* q; const void* k; const void* v; const void* gate;

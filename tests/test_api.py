@@ -140,6 +140,25 @@ def test_workspace_independent_of_sequence_length():
     assert len(sizes) == 1 and sizes.pop() > 0
 
 
+def test_chunkwise_schedule_flags():
+    """The two explicit schedules are exclusive; each has its own workspace size, which does
+    not grow with N (windows of 32 chunks carry the state between them)."""
+    big = dict(d_k=256, d_v=512, theta=np.ones(128), H=16, gamma=np.full(16, 0.9))
+    d, keep = desc(**big, flags=rn.RN_CHUNK_PARALLEL | rn.RN_CHUNK_SEGMENTED)
+    assert chk(d) == rn.RN_ERR_INVALID_ARG
+    assert b"exclusive" in rn.lib.rn_last_error()
+    assert rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), 256) == 0
+    sizes = {}
+    for name, flags in (("sequential", 0), ("pair", rn.RN_CHUNK_PARALLEL), ("segmented", rn.RN_CHUNK_SEGMENTED)):
+        got = set()
+        for N in (64, 8192, 65536):
+            d, keep = desc(**dict(big, N=N), flags=flags)
+            got.add(rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), 256))
+        assert len(got) == 1 and min(got) > 0, name
+        sizes[name] = got.pop()
+    assert len(set(sizes.values())) == 3, sizes
+
+
 def test_parallel_workspace():
     big = dict(d_k=256, d_v=512, theta=np.ones(128), H=8, gamma=np.full(8, 0.9), N=2048)
     d, keep = desc(**big)

@@ -1,6 +1,7 @@
 """GPU parity of the MFMA chunkwise schedules (bf16 q/k/v, d_k = 256): the sequential
-single kernel (the default) and the chunk-parallel pair (RN_CHUNK_PARALLEL: state
-snapshots, then outputs; d_v = 512).
+single kernel (the default), the segmented schedule (RN_CHUNK_SEGMENTED: segment-local
+states, a scan over segments, then the outputs; d_v = 512) and the chunk-parallel pair
+(RN_CHUNK_PARALLEL: state snapshots, then outputs; d_v = 512).
 
 Tolerances (half-precision MFMA operands, fp32 accumulation):
   * raw outputs and final states: per (b, h), ||gpu - ref||_inf <= 1e-2 ||ref||_inf.
@@ -65,7 +66,12 @@ def counters(ws, heads):
     return c
 
 
-SCHEDULES = [False, True]   # chunk-parallel pair?
+SCHEDULES = ["segmented", "sequential", "pair"]
+
+
+def sk(schedule):
+    """Binding keywords that select a schedule."""
+    return dict(chunk_parallel=schedule == "pair", segmented=schedule == "segmented")
 
 
 @pytest.mark.parametrize("cp", SCHEDULES)
@@ -75,7 +81,7 @@ def test_raw_output_and_state(N, pos0, cp):
     x = W.make_inputs(w)
     out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
                                          x["theta"], 64, state_in=dev(x["state"]), state_out=True,
-                                         out_dtype=torch.float32, pos0=pos0, chunk_parallel=cp)
+                                         out_dtype=torch.float32, pos0=pos0, **sk(cp))
     ref, Sref = O.chunkwise(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 64, pos0, 1.0, x["state"])
     assert rel_inf(out.cpu(), ref) <= 1e-2
     assert rel_inf(S.cpu(), Sref) <= 1e-2
@@ -94,7 +100,7 @@ def test_gn_gate_affine_fp32_and_bf16_out(cp):
         out, _ = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
                                              x["theta"], 256, gate=dev(x["gate"]), gn=True,
                                              gn_weight=dev(gw), gn_bias=dev(gb), out_dtype=od,
-                                             chunk_parallel=cp)
+                                             **sk(cp))
         check_gated(out.cpu(), ref, x["gate"])
 
 
@@ -113,7 +119,7 @@ def test_value_dims(dv):
 
 
 def test_exchange_diagnostics_and_determinism():
-    """Every slice of a head reports the same XCD (the L2 exchange path is the one in
+    """Sequential kernel: every slice of a head reports the same XCD (the L2 exchange path is the one in
     use), no wait hit its time limit, and two runs agree bit for bit."""
     w = wl(N=300, H=4, gate=True)
     x = W.make_inputs(w)
@@ -144,7 +150,7 @@ def test_more_heads_than_one_launch(cp):
     x = W.make_inputs(w)
     out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
                                          x["theta"], 64, state_out=True, out_dtype=torch.float32,
-                                         chunk_parallel=cp)
+                                         **sk(cp))
     ref, Sref = O.chunkwise(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 64)
     assert rel_inf(out.cpu(), ref) <= 1e-2
     assert rel_inf(S.cpu(), Sref) <= 1e-2
@@ -159,7 +165,7 @@ def test_6p7b_training_shape_sampled_heads(cp):
     x = W.make_inputs(w)
     out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
                                          x["theta"], w.chunk, gate=dev(x["gate"]), gn=True,
-                                         state_out=True, out_dtype=torch.float32, chunk_parallel=cp)
+                                         state_out=True, out_dtype=torch.float32, **sk(cp))
     out, S = out.cpu(), S.cpu()
     assert torch.isfinite(out).all()
     for b, h in ((0, 0), (1, 15), (0, 9)):
@@ -178,11 +184,11 @@ def test_long_sequence_sampled_head(cp):
     w = W.WORKLOADS["chunkwise_long"]
     x = W.make_inputs(w)
     sizes = [rn().rn_chunkwise_workspace_bytes(x["q"][:, :, :n], x["v"][:, :, :n], x["gamma"],
-                                               x["theta"], 512, gn=True, chunk_parallel=cp)
+                                               x["theta"], 512, gn=True, **sk(cp))
              for n in (8192 + 256, 65536)]
     assert sizes[0] == sizes[1]
     args = (dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"], w.chunk)
-    kw = dict(gn=True, state_out=True, out_dtype=torch.float32, chunk_parallel=cp)
+    kw = dict(gn=True, state_out=True, out_dtype=torch.float32, **sk(cp))
     out, S = rn().rn_retention_chunkwise(*args, **kw)
     out2, S2 = rn().rn_retention_chunkwise(*args, **kw)
     assert torch.equal(out, out2) and torch.equal(S, S2), "runs differ: exchange race"
@@ -220,19 +226,57 @@ def test_chunk_parallel_snapshots_are_the_chunk_states():
         assert rel_inf(got, ref) <= 1e-2, c
 
 
-def test_small_decay_runs_the_chunk_parallel_pair():
+def test_small_decay_takes_a_schedule_without_a_decay_limit():
     """A head with gamma^32 < 2^-6 (gamma = 0.8) is outside the sequential kernel's operand
-    range; the default call then takes the chunk-parallel pair, which applies the decay in
-    float32 and carries no such limit. Checked against the oracle, outputs and state."""
+    range; the default call then takes the segmented schedule, which applies the decay in
+    float32 (as does the chunk-parallel pair). Both checked against the oracle, outputs and
+    state."""
     w = wl(N=300, state_std=0.05)
     x = W.make_inputs(w)
     gamma = np.array([0.8, 0.97], dtype=np.float32)
     n_default = rn().rn_chunkwise_workspace_bytes(x["q"], x["v"], gamma, x["theta"], 64)
-    n_pair = rn().rn_chunkwise_workspace_bytes(x["q"], x["v"], gamma, x["theta"], 64, chunk_parallel=True)
-    assert n_default == n_pair
-    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), gamma, x["theta"], 64,
-                                         state_in=dev(x["state"]), state_out=True,
-                                         out_dtype=torch.float32)
+    n_seg = rn().rn_chunkwise_workspace_bytes(x["q"], x["v"], gamma, x["theta"], 64, segmented=True)
+    assert n_default == n_seg
     ref, Sref = O.chunkwise(x["q"], x["k"], x["v"], gamma, x["theta"], 64, 0, 1.0, x["state"])
-    assert rel_inf(out.cpu(), ref) <= 1e-2
-    assert rel_inf(S.cpu(), Sref) <= 1e-2
+    for kw in (dict(), dict(chunk_parallel=True)):
+        out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), gamma, x["theta"],
+                                             64, state_in=dev(x["state"]), state_out=True,
+                                             out_dtype=torch.float32, **kw)
+        assert rel_inf(out.cpu(), ref) <= 1e-2, kw
+        assert rel_inf(S.cpu(), Sref) <= 1e-2, kw
+
+
+def test_segmented_states_in_the_workspace():
+    """The segmented schedule's intermediate states, read back from the caller's workspace
+    ([heads][32 chunks][d_v][d_k] half L, then [heads][4][d_v][d_k] float32 E, then
+    [heads][4][d_v][d_k] half T): T_g is the state at segment g's start (2048 tokens
+    apart), and L at a chunk start plus gamma^(c0 - s_g) T_g is the state there."""
+    w = wl(B=1, H=2, N=2048 + 600, state_std=0.05)
+    x = W.make_inputs(w)
+    ws = ws_for(x["q"], x["v"], x["gamma"], x["theta"], 256, segmented=True)
+    rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"], 256,
+                                state_in=dev(x["state"]), workspace=ws, out_dtype=torch.float32,
+                                segmented=True)
+    torch.cuda.synchronize()
+    heads, snap = 2, 256 * 512
+    L = ws[: heads * 32 * snap * 2].view(torch.float16).reshape(heads, 32, 512, 256)
+    off = heads * 32 * snap * 2 + heads * 4 * snap * 4
+    T = ws[off: off + heads * 4 * snap * 2].view(torch.float16).reshape(heads, 4, 512, 256)
+
+    def state_at(t):
+        if t == 0:
+            return O.to64(x["state"])
+        sl = slice(0, t)
+        return O.chunkwise(x["q"][:, :, sl], x["k"][:, :, sl], x["v"][:, :, sl], x["gamma"],
+                           x["theta"], 256, 0, 1.0, x["state"])[1]
+
+    def host(t):   # [heads, d_v, d_k] half -> [1, heads, d_k, d_v] float64
+        return t.permute(0, 2, 1).cpu().to(torch.float64).numpy()[None]
+
+    g = np.asarray(x["gamma"], dtype=np.float64)[None, :, None, None]
+    for seg in (0, 1):
+        assert rel_inf(host(T[:, seg]), state_at(2048 * seg)) <= 1e-2, seg
+    for c in (1, 5, 9, 10):
+        c0, s0 = 256 * c, 2048 * (c // 8)
+        got = host(L[:, c]) + g ** (c0 - s0) * host(T[:, c // 8])
+        assert rel_inf(got, state_at(c0)) <= 1e-2, c

@@ -111,7 +111,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("lengths,pos", CASES)
-@pytest.mark.parametrize("path", ["sequential", "pair", "generic"])
+@pytest.mark.parametrize("path", ["segmented", "sequential", "pair", "generic"])
 def test_chunkwise_varlen_outputs_and_states(lengths, pos, path):
     """Each sequence's rows and final state against the oracle's chunkwise form on that
     sequence alone (its length, its positions, its initial state); padded rows keep the
@@ -124,7 +124,8 @@ def test_chunkwise_varlen_outputs_and_states(lengths, pos, path):
                                               x["theta"], 64, pos=posd, lengths=lens,
                                               state_in=dev(x["state"]), state_out=True, out=out,
                                               out_dtype=torch.float32, force_generic=path == "generic",
-                                              chunk_parallel=path == "pair")
+                                              chunk_parallel=path == "pair",
+                                              segmented=path == "segmented")
     out, S = out.cpu(), S.cpu()
     tol = 1e-4 if path == "generic" else 1e-2
     for b, (L, p) in enumerate(zip(lengths, pos)):
