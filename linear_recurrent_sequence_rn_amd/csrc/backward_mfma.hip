@@ -374,7 +374,7 @@ struct Heads {
 };
 
 // o recomputed: alpha (Qh Kh^T (.) D) V + alpha xi Qh S_c, then the GroupNorm / gate backward.
-template <int OUTD>
+template <int OUTD, bool AFF>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bm_dout(CallArgs a, Heads Hd, const void* gate, const void* dout, uint16_t* DR, void* dgate,
         float* dgn_w, float* dgn_b) {
@@ -396,8 +396,12 @@ bm_dout(CallArgs a, Heads Hd, const void* gate, const void* dout, uint16_t* DR, 
   zero_acc(o);
   tmm16<32, true>(o, T.r1 - T.c0, sm, Q, 0, 1.f, 0.f, 0, 0, VT, 0, T.c0);
   tmm16<32, false>(o, dk, sm, Q, T.r0, a.alpha, lg, T.r0 - T.c0 + 1, 1, ST, 0, 0);
-  gn_backward_tile<RN_BF16, OUTD>(sm, o, a, h, bh, T.r0, T.r1, gate, dout, dgate, dgn_w, dgn_b,
-      [&](int64_t i, float x) __attribute__((always_inline)) { DR[i] = h_bits(x); });
+  // dO rows of this head through a buffer resource (element stores without branches)
+  const __amdgpu_buffer_rsrc_t rdr = head_rsrc(DR + int64_t(bh) * a.N * a.dv, int64_t(a.N) * a.dv * 2);
+  gn_backward_tile<RN_BF16, OUTD, AFF>(sm, o, a, h, bh, T.r0, T.r1, gate, dout, dgate, dgn_w, dgn_b,
+      [&](int64_t, int i, bool ok, float x) __attribute__((always_inline)) {
+        __builtin_amdgcn_raw_buffer_store_b16(h_bits(x), rdr, ok ? static_cast<uint32_t>(i) * 2 : kGnSink, 0, 0);
+      });
 }
 
 // dQh = [alpha (dO V^T) (.) D] Kh + alpha xi dO S_c^T, rotated back.
@@ -507,8 +511,12 @@ hipError_t launch_t(const CallArgs& a, const BwArgs& x, void* ws, hipStream_t st
     if (x.dgn_w) hipLaunchKernelGGL(fill_zero_m, dim3(8), dim3(256), 0, st, x.dgn_w, int64_t(a.H) * a.dv);
     if (x.dgn_b) hipLaunchKernelGGL(fill_zero_m, dim3(8), dim3(256), 0, st, x.dgn_b, int64_t(a.H) * a.dv);
   }
-  hipLaunchKernelGGL((bm_dout<OUTD>), gtiles, dim3(256), 0, st, a, Hd, x.gate, x.dout, at(L.DR),
-                     x.dgate, x.dgn_w, x.dgn_b);
+  if (a.gn_w || a.gn_b || x.dgn_w || x.dgn_b)
+    hipLaunchKernelGGL((bm_dout<OUTD, true>), gtiles, dim3(256), 0, st, a, Hd, x.gate, x.dout, at(L.DR),
+                       x.dgate, x.dgn_w, x.dgn_b);
+  else
+    hipLaunchKernelGGL((bm_dout<OUTD, false>), gtiles, dim3(256), 0, st, a, Hd, x.gate, x.dout, at(L.DR),
+                       x.dgate, x.dgn_w, x.dgn_b);
   hipLaunchKernelGGL(bm_transpose, gblk, dim3(256), 0, st, static_cast<const uint16_t*>(at(L.DR)),
                      at(L.DT), a.N, a.dv, L.Np);
   hipLaunchKernelGGL(bm_scan<1>, gscan, dim3(256), 0, st, a, static_cast<const uint16_t*>(at(L.QT)),

@@ -288,10 +288,65 @@ __device__ __forceinline__ void store_rotated(SM& sm, const float (&g)[4][16], c
 // GroupNorm / gate backward of a 64-row tile whose pre-GroupNorm output o (64 x d_v, in
 // the accumulator layout) has been recomputed: per row the gradient before GroupNorm,
 // dO = rstd (dxh - mean(dxh) - xh mean(dxh xh)) with dxh = dy w and dy = dout (* swish(g)),
-// is passed to store_dO(element index, value); the gate's gradient is stored; the tile's
+// is passed to store_dO(head offset, element offset within the head, whether the element
+// exists, value); the gate's gradient is stored; the tile's
 // per-column sums of dy xh and dy are added to dgn_w and dgn_b. Without GroupNorm dO is
 // dout.
-template <int IN, int OUTD, class SM, class STORE>
+// Element stores through a buffer resource over one head's rows: a store with ok false
+// goes to an offset past the range and is dropped, so the stores of a row need no branch
+// (a branch would make every later wait also wait for the stores already issued).
+constexpr uint32_t kGnSink = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           static_cast<int>(bytes > 0x7fffffff ? 0x7fffffff : bytes), 0x00020000);
+}
+template <int DT>
+__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int i, bool ok, float x) {
+  if constexpr (DT == RN_F32) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, ok ? static_cast<uint32_t>(i) * 4 : kGnSink, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), r, ok ? static_cast<uint32_t>(i) * 2 : kGnSink, 0, 0);
+  }
+}
+
+// dout (and gate) of one row at columns tx + 16 j: all 32 (64) loads are issued before any
+// is used, at addresses clamped into the row (columns past d_v read a valid element that
+// the caller discards), so no branch separates a load from the others in flight.
+template <int DT>
+__device__ __forceinline__ float load_elem(__amdgpu_buffer_rsrc_t r, uint32_t voff, int j) {
+  if constexpr (DT == RN_F32)
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff * 4 + 64 * j, 0, 0));
+  else
+    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, voff * 2 + 32 * j, 0, 0));
+}
+// dout (and gate) of one row (elements roff + tx + 16 j of the head; the row differs
+// between the lane groups of a wave): all 32 (64) loads are issued before any is used,
+// through buffer resources over the head with one per-lane offset and the column step in
+// the immediate, so no branch and no per-element address separates a load from the
+// others in flight. Columns past d_v (d_v < 512) read an element of the next row or past
+// the range (0); the caller discards them.
+template <int IN, int OUTD>
+__device__ __forceinline__ void gn_load_row(float (&dov)[32], float (&gav)[32], __amdgpu_buffer_rsrc_t rdo,
+                                            __amdgpu_buffer_rsrc_t rga, bool gt, int roff, int tx) {
+  const uint32_t voff = static_cast<uint32_t>(roff + tx);
+  if (gt) {
+#pragma clang loop unroll(full)
+    for (int j = 0; j < 32; ++j) {
+      dov[j] = load_elem<OUTD>(rdo, voff, j);
+      gav[j] = load_elem<IN>(rga, voff, j);
+    }
+  } else {
+#pragma clang loop unroll(full)
+    for (int j = 0; j < 32; ++j) {
+      dov[j] = load_elem<OUTD>(rdo, voff, j);
+      gav[j] = 0.f;
+    }
+  }
+}
+
+// AFF: the GroupNorm has an affine weight or bias, or their gradients are asked for;
+// without it the weights are 1 and 0 and no column sums are kept (128 fewer registers).
+template <int IN, int OUTD, bool AFF = true, class SM, class STORE>
 __device__ __forceinline__ void gn_backward_tile(SM& sm, const float (&o)[4][32], const CallArgs& a,
                                                  int h, int bh, int r0, int r1, const void* gate,
                                                  const void* dout, void* dgate, float* dgn_w,
@@ -300,20 +355,28 @@ __device__ __forceinline__ void gn_backward_tile(SM& sm, const float (&o)[4][32]
   const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
   const struct { int r0, r1; } T{r0, r1};
   const bool gn = a.flags & RN_EPI_GN, gt = a.flags & RN_EPI_GATE;
+  // the head's rows (uniform bases: element offsets within a head fit 32 bits)
+  const int64_t hoff = int64_t(bh) * N * dv;
+  dout = static_cast<const char*>(dout) + hoff * (OUTD == RN_F32 ? 4 : 2);
+  if (gate) gate = static_cast<const char*>(gate) + hoff * (IN == RN_F32 ? 4 : 2);
+  if (dgate) dgate = static_cast<char*>(dgate) + hoff * (IN == RN_F32 ? 4 : 2);
+  const __amdgpu_buffer_rsrc_t rdg = head_rsrc(dgate, int64_t(N) * dv * (IN == RN_F32 ? 4 : 2));
+  const __amdgpu_buffer_rsrc_t rdo = head_rsrc(dout, int64_t(N) * dv * (OUTD == RN_F32 ? 4 : 2));
+  const __amdgpu_buffer_rsrc_t rga = head_rsrc(gate, int64_t(N) * dv * (IN == RN_F32 ? 4 : 2));
   if (!gn) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = T.r0 + 4 * ty + r;
       if (t >= T.r1) continue;
-      const int64_t roff = (int64_t(bh) * N + t) * dv;
-      for (int col = tx; col < dv; col += 16) store_dO(roff + col, Elem<OUTD>::load(dout, roff + col));
+      const int roff = t * dv;
+      for (int col = tx; col < dv; col += 16) store_dO(hoff, roff + col, true, Elem<OUTD>::load(dout, roff + col));
     }
     return;
   }
   // GroupNorm / gate backward, row by row. Per-column sums of dy * xh and dy (for dgn_w,
   // dgn_b) gather in registers over this thread's four rows, then in its own LDS cells
   // (two [16][kLdB] float arrays) for the reduction over the tile.
-  const bool sums = dgn_w || dgn_b;
+  const bool sums = AFF && (dgn_w || dgn_b);
   float swa[32], sba[32];
 #pragma clang loop unroll(full)
   for (int j = 0; j < 32; ++j) swa[j] = sba[j] = 0.f;
@@ -323,6 +386,11 @@ __device__ __forceinline__ void gn_backward_tile(SM& sm, const float (&o)[4][32]
 #pragma clang loop unroll(full)
   for (int j = 0; j < 32; ++j) {
     const int col = tx + 16 * j;
+    if constexpr (!AFF) {
+      wv[j] = 1.f;
+      bv[j] = 0.f;
+      continue;
+    }
     wv[j] = (a.gn_w && col < dv) ? a.gn_w[h * dv + col] : 1.f;
     bv[j] = (a.gn_b && col < dv) ? a.gn_b[h * dv + col] : 0.f;
   }
@@ -330,7 +398,9 @@ __device__ __forceinline__ void gn_backward_tile(SM& sm, const float (&o)[4][32]
   for (int r = 0; r < 4; ++r) {
     const int t = T.r0 + 4 * ty + r;
     const bool live = t < T.r1;
-    const int64_t roff = (int64_t(bh) * N + (live ? t : T.r0)) * dv;
+    const int roff = (live ? t : T.r0) * dv;
+    float dov[32], gav[32];
+    gn_load_row<IN, OUTD>(dov, gav, rdo, rga, gt, roff, tx);
     float s1 = 0.f;
 #pragma clang loop unroll(full)
     for (int j = 0; j < 32; ++j) s1 += (tx + 16 * j < dv) ? o[r][j] : 0.f;
@@ -344,26 +414,27 @@ __device__ __forceinline__ void gn_backward_tile(SM& sm, const float (&o)[4][32]
     const float rstd = 1.0f / sqrtf(row16_sum(s2) / dv + a.eps);
     // dy = dout (* swish(g)); dgate = dout y swish'(g); the row means of dxh = dy w and
     // of dxh xh
+    // (all of the row's loads were issued above, so the stores here cost at most one wait)
     float dyv[32];
     float m1 = 0.f, m2 = 0.f;
 #pragma clang loop unroll(full)
     for (int j = 0; j < 32; ++j) {
-      const int col = tx + 16 * j;
-      dyv[j] = 0.f;
-      if (live && col < dv) {
-        const float xh = (o[r][j] - mean) * rstd;
-        const float d0 = Elem<OUTD>::load(dout, roff + col);
-        float dy = d0;
-        if (gt) {
-          const float g = Elem<IN>::load(gate, roff + col);
-          const float sg = 1.0f / (1.0f + expf(-g));
-          dy = d0 * g * sg;
-          Elem<IN>::store(dgate, roff + col, d0 * (xh * wv[j] + bv[j]) * sg * (1.0f + g * (1.0f - sg)));
-        }
-        dyv[j] = dy;
-        const float dxh = dy * wv[j];
-        m1 += dxh;
-        m2 += dxh * xh;
+      const bool ok = live && tx + 16 * j < dv;
+      const float xh = (o[r][j] - mean) * rstd;
+      const float d0 = dov[j];
+      float dy = d0;
+      if (gt) {
+        const float g = gav[j];
+        const float sg = 1.0f / (1.0f + expf(-g));
+        dy = d0 * g * sg;
+        store_elem<IN>(rdg, roff + tx + 16 * j, ok, d0 * (xh * wv[j] + bv[j]) * sg * (1.0f + g * (1.0f - sg)));
+      }
+      dy = ok ? dy : 0.f;
+      dyv[j] = dy;
+      const float dxh = dy * wv[j];
+      m1 += dxh;
+      m2 += dxh * xh;
+      if constexpr (AFF) {
         swa[j] += dy * xh;
         sba[j] += dy;
       }
@@ -373,10 +444,8 @@ __device__ __forceinline__ void gn_backward_tile(SM& sm, const float (&o)[4][32]
 #pragma clang loop unroll(full)
     for (int j = 0; j < 32; ++j) {
       const int col = tx + 16 * j;
-      if (live && col < dv) {
-        const float xh = (o[r][j] - mean) * rstd;
-        store_dO(roff + col, rstd * (dyv[j] * wv[j] - m1 - xh * m2));
-      }
+      const float xh = (o[r][j] - mean) * rstd;
+      store_dO(hoff, roff + col, live && col < dv, rstd * (dyv[j] * wv[j] - m1 - xh * m2));
     }
   }
   if (sums) {
