@@ -66,13 +66,26 @@ __device__ __forceinline__ u32x4 run8(const Src& s, int r, int64_t c, bool live 
   const u32x4 x = *reinterpret_cast<const u32x4*>(s.p + r * s.pitch + c);
   return s.bf ? bf8_to_h8(x) : x;
 }
+// Raw 16 bytes (r, c .. c+7) through a buffer resource over the source: rows past it read
+// as zero, and so does a run that is not `live` (sent past the range). No branch, so the
+// loads of a slice stay in flight together; the bf16 -> half conversion is the caller's.
+constexpr uint32_t kRunSink = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t src_rsrc(const Src& s) {
+  const int64_t bytes = int64_t(s.rows) * s.pitch * 2;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(s.p), 0,
+                                           static_cast<int>(bytes > 0x7fffffff ? 0x7fffffff : bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 raw8(__amdgpu_buffer_rsrc_t r, int64_t pitch, int row, int64_t c, bool live) {
+  const uint32_t off = live ? static_cast<uint32_t>((row * pitch + c) * 2) : kRunSink;
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 
 // acc += A B over k < K, A (64 x K) either P (FROMP) or rows ar0 + i of A scaled by
 // amul * gamma^(ae0 + aesg i) (log2 gamma = alg), B (K x 16 NCT) given by its columns:
 // column n is row br0 + n of B, read from column bc0 on. Without FROMP, K is a multiple of
 // 8 and runs at or past K read as zeros; with FROMP the scores past the product's extent
 // are zero. The next slice is fetched into registers while the MFMAs of the current run.
-template <int NCT, bool FROMP>
+template <int NCT, bool FROMP, int NSET = 1>
 __device__ __forceinline__ void tmm16(float (&acc)[4][NCT], int K, TileSharedH& sm, const Src& A,
                                       int ar0, float amul, float alg, int ae0, int aesg,
                                       const Src& B, int br0, int bc0) {
@@ -86,33 +99,40 @@ __device__ __forceinline__ void tmm16(float (&acc)[4][NCT], int K, TileSharedH& 
 #pragma unroll
     for (int i = 0; i < 8; ++i) af[i] = f;
   }
-  u32x4 ra = u32x4{0u, 0u, 0u, 0u}, rb[NRUN];
-  auto fetch = [&](int k0) __attribute__((always_inline)) {
-    if constexpr (!FROMP) ra = run8(A, ar0 + arow, k0 + 8 * aq, k0 + 8 * aq < K);
+  // NSET register sets: the NSET slices after slice k0 are in flight while it computes
+  static_assert(NSET == 1 || NSET == 2, "one or two register sets");
+  u32x4 ra[NSET], rb[NSET][NRUN];
+#pragma unroll
+  for (int i = 0; i < NSET; ++i) ra[i] = u32x4{0u, 0u, 0u, 0u};
+  const __amdgpu_buffer_rsrc_t rsa = src_rsrc(A), rsb = src_rsrc(B);
+  auto fetch = [&](int k0, int set) __attribute__((always_inline)) {
+    if constexpr (!FROMP) ra[set] = raw8(rsa, A.pitch, ar0 + arow, k0 + 8 * aq, k0 + 8 * aq < K);
 #pragma unroll
     for (int u = 0; u < NRUN; ++u) {
       const int run = tid + 256 * u, n = run >> 2, kq = k0 + 8 * (run & 3);
-      rb[u] = run8(B, br0 + n, int64_t(bc0) + kq, FROMP || kq < K);
+      rb[set][u] = raw8(rsb, B.pitch, br0 + n, int64_t(bc0) + kq, kq < K);
     }
   };
-  auto put = [&]() __attribute__((always_inline)) {
-    if constexpr (!FROMP)
-      *reinterpret_cast<u32x4*>(&sm.m.As[arow][8 * aq]) = scaled ? scale8(ra, af) : ra;
+  auto put = [&](int set) __attribute__((always_inline)) {
+    if constexpr (!FROMP) {
+      const u32x4 x = A.bf ? bf8_to_h8(ra[set]) : ra[set];
+      *reinterpret_cast<u32x4*>(&sm.m.As[arow][8 * aq]) = scaled ? scale8(x, af) : x;
+    }
 #pragma unroll
     for (int u = 0; u < NRUN; ++u) {
       const int run = tid + 256 * u;
-      *reinterpret_cast<u32x4*>(&sm.m.Bs[run >> 2][8 * (run & 3)]) = rb[u];
+      *reinterpret_cast<u32x4*>(&sm.m.Bs[run >> 2][8 * (run & 3)]) = B.bf ? bf8_to_h8(rb[set][u]) : rb[set][u];
     }
   };
   f32x4 t[NCT];
 #pragma unroll
   for (int j = 0; j < NCT; ++j) t[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  fetch(0);
-  for (int k0 = 0; k0 < K; k0 += kKH) {
+  // one slice: stage the set, refill it with the slice NSET ahead, multiply
+  auto slice = [&](int k0, int set) __attribute__((always_inline)) {
     __syncthreads();   // the previous slice's reads of As / Bs are done
-    put();
+    put(set);
     __syncthreads();
-    if (k0 + kKH < K) fetch(k0 + kKH);
+    fetch(k0 + NSET * kKH, set);
     f16x8 av;
     if constexpr (FROMP) av = *reinterpret_cast<const f16x8*>(&sm.m.P[16 * w + l16][k0 + 8 * g]);
     else av = *reinterpret_cast<const f16x8*>(&sm.m.As[16 * w + l16][8 * g]);
@@ -121,6 +141,19 @@ __device__ __forceinline__ void tmm16(float (&acc)[4][NCT], int K, TileSharedH& 
       const f16x8 bv = *reinterpret_cast<const f16x8*>(&sm.m.Bs[16 * j + l16][8 * g]);
       t[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, t[j], 0, 0, 0);
     }
+  };
+  // with two sets, slices go in pairs with no branch between them: K is rounded up to 64,
+  // the runs past K read as zeros (and, with FROMP, so do the scores past the product's
+  // extent)
+  fetch(0, 0);
+  if constexpr (NSET == 2) {
+    fetch(kKH, 1);
+    for (int k0 = 0; k0 < K; k0 += 2 * kKH) {
+      slice(k0, 0);
+      slice(k0 + kKH, 1);
+    }
+  } else {
+    for (int k0 = 0; k0 < K; k0 += kKH) slice(k0, 0);
   }
 #pragma unroll
   for (int j = 0; j < NCT; ++j)
@@ -419,12 +452,12 @@ bm_dq(CallArgs a, Heads Hd, const uint16_t* v, void* dq) {
   const Src S{Hd.S + (int64_t(bh) * Hd.nch + T.c) * dk * dv, dv, dk, false};
   float m[4][16];
   zero_acc(m);
-  tmm16<16, false>(m, dv, sm, D, T.r0, 1.f, 0.f, 0, 0, V, T.c0, 0);
+  tmm16<16, false, 2>(m, dv, sm, D, T.r0, 1.f, 0.f, 0, 0, V, T.c0, 0);
   store_scores<true>(sm, m, T.r0, T.r1, T.c0, T.r1, lg, a.alpha);
   float gq[4][16];
   zero_acc(gq);
-  tmm16<16, true>(gq, T.r1 - T.c0, sm, D, 0, 1.f, 0.f, 0, 0, KT, 0, T.c0);
-  tmm16<16, false>(gq, dv, sm, D, T.r0, a.alpha, lg, T.r0 - T.c0 + 1, 1, S, 0, 0);
+  tmm16<16, true, 2>(gq, T.r1 - T.c0, sm, D, 0, 1.f, 0.f, 0, 0, KT, 0, T.c0);
+  tmm16<16, false, 2>(gq, dv, sm, D, T.r0, a.alpha, lg, T.r0 - T.c0 + 1, 1, S, 0, 0);
   store_rotated<RN_BF16>(sm, gq, a, seq_pos0(a, bh / a.H), bh, T.r0, T.r1, dq);
 }
 
@@ -443,12 +476,12 @@ bm_dk(CallArgs a, Heads Hd, const uint16_t* v, void* dk_) {
   const Src G{Hd.G + (int64_t(bh) * Hd.nch + T.c) * dk * dv, dv, dk, false};
   float m[4][16];
   zero_acc(m);
-  tmm16<16, false>(m, dv, sm, V, T.r0, 1.f, 0.f, 0, 0, D, T.r0, 0);
+  tmm16<16, false, 2>(m, dv, sm, V, T.r0, 1.f, 0.f, 0, 0, D, T.r0, 0);
   store_scores<false>(sm, m, T.r0, T.r1, T.r0, T.c1, lg, a.alpha);
   float gk[4][16];
   zero_acc(gk);
-  tmm16<16, true>(gk, T.c1 - T.r0, sm, V, 0, 1.f, 0.f, 0, 0, QT, 0, T.r0);
-  tmm16<16, false>(gk, dv, sm, V, T.r0, 1.f, lg, T.c1 - 1 - T.r0, -1, G, 0, 0);
+  tmm16<16, true, 2>(gk, T.c1 - T.r0, sm, V, 0, 1.f, 0.f, 0, 0, QT, 0, T.r0);
+  tmm16<16, false, 2>(gk, dv, sm, V, T.r0, 1.f, lg, T.c1 - 1 - T.r0, -1, G, 0, 0);
   store_rotated<RN_BF16>(sm, gk, a, seq_pos0(a, bh / a.H), bh, T.r0, T.r1, dk_);
 }
 
@@ -531,7 +564,9 @@ hipError_t launch_t(const CallArgs& a, const BwArgs& x, void* ws, hipStream_t st
 }  // namespace
 
 bool backward_mfma_supported(const CallArgs& a, int in_dt) {
-  return in_dt == RN_BF16 && a.dk % 8 == 0 && a.dv % 8 == 0;
+  // (every per-head operand array is read through a buffer resource: under 2 GB)
+  return in_dt == RN_BF16 && a.dk % 8 == 0 && a.dv % 8 == 0 &&
+         (int64_t(a.N) + 64) * max(a.dk, a.dv) * 2 < (int64_t(1) << 31);
 }
 
 size_t backward_mfma_ws_bytes(const CallArgs& a) { return m_layout(a).total; }
