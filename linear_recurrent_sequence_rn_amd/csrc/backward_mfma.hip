@@ -339,21 +339,46 @@ __global__ void __launch_bounds__(256) bm_scan(CallArgs a, const uint16_t* XT, c
       t[j][r] = (init && d < dk && e < dv) ? init[bh * nS + int64_t(d) * dv + e] : 0.f;
     }
   const int arow = tid >> 2, aq = tid & 3;
-  u32x4 ra, rb[2];
+  // Slices of 32 tokens are numbered across chunks (slice u: chunk u >> 3 in scan order,
+  // tokens 32 (u & 7) .. of it) and loaded four ahead through a ring of register sets,
+  // branch-free: runs past a chunk's end or past the last chunk read as zeros.
+  constexpr int kSets = 4;
+  const __amdgpu_buffer_rsrc_t rx = src_rsrc(X), ry = src_rsrc(Y);
+  u32x4 ra[kSets], rb[kSets][2];
+  auto fetch = [&](int u, int set) __attribute__((always_inline)) {
+    const int cu = REV ? nch - 1 - (u >> 3) : (u >> 3);
+    const int c0u = cu * kBC, Lu = (u >> 3) < nch ? min(N, c0u + kBC) - c0u : 0;
+    const int k = kKH * (u & 7);
+    ra[set] = raw8(rx, X.pitch, d0 + arow, int64_t(c0u) + k + 8 * aq, k + 8 * aq < Lu);
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int run = tid + 256 * v, kq = k + 8 * (run & 3);
+      rb[set][v] = raw8(ry, Y.pitch, e0 + (run >> 2), int64_t(c0u) + kq, kq < Lu);
+    }
+  };
+  // chunk boundary values through buffer resources over the head's states: lanes past
+  // d_k or d_v store to a dropped offset (no branch)
+  const __amdgpu_buffer_rsrc_t rS = src_rsrc(Src{Sr + int64_t(bh) * nch * nS, 1, int(nch * nS), false});
+  const __amdgpu_buffer_rsrc_t rST = src_rsrc(Src{St + int64_t(bh) * nch * nS, 1, int(nch * nS), false});
+  for (int u = 0; u < kSets; ++u) fetch(u, u);
   for (int step = 0; step < nch; ++step) {
     const int c = REV ? nch - 1 - step : step;
     const int c0 = c * kBC, L = min(N, c0 + kBC) - c0;
     // the chunk's boundary value, in both orientations
-    uint16_t* Sc = Sr + (int64_t(bh) * nch + c) * nS;
-    uint16_t* STc = St + (int64_t(bh) * nch + c) * nS;
+    const uint32_t cbase = static_cast<uint32_t>(int64_t(c) * nS);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int e = e0 + 16 * j + l16, d = d0 + 16 * w + 4 * g;
-      if (e < dv && d < dk) {
-        *reinterpret_cast<u32x2*>(STc + int64_t(e) * dk + d) =
-            u32x2{pack_h2(t[j][0], t[j][1]), pack_h2(t[j][2], t[j][3])};
+      const bool ok = e < dv && d < dk;
+      const uint32_t ot = ok ? (cbase + uint32_t(e) * dk + d) * 2 : kRunSink;
+      __builtin_amdgcn_raw_buffer_store_b64(
+          __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
+                             u32x2{pack_h2(t[j][0], t[j][1]), pack_h2(t[j][2], t[j][3])}),
+          rST, ot, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Sc[int64_t(d + r) * dv + e] = h_bits(t[j][r]);
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t orow = ok ? (cbase + uint32_t(d + r) * dv + e) * 2 : kRunSink;
+        __builtin_amdgcn_raw_buffer_store_b16(h_bits(t[j][r]), rS, orow, 0, 0);
       }
     }
     const float gL = gpow(lg, float(L));
@@ -362,25 +387,18 @@ __global__ void __launch_bounds__(256) bm_scan(CallArgs a, const uint16_t* XT, c
     __syncthreads();   // the previous chunk's reads of wt are done
     for (int jj = tid; jj < kBC; jj += 256)
       sm.wt[jj] = jj < L ? (REV ? a.alpha * gpow(lg, float(jj + 1)) : gpow(lg, float(L - 1 - jj))) : 0.f;
-    auto fetch = [&](int k0) __attribute__((always_inline)) {
-      ra = run8(X, d0 + arow, int64_t(c0) + k0 + 8 * aq);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int run = tid + 256 * u;
-        rb[u] = run8(Y, e0 + (run >> 2), int64_t(c0) + k0 + 8 * (run & 3));
-      }
-    };
-    fetch(0);
-    for (int k0 = 0; k0 < L; k0 += kKH) {
+    for (int i = 0; i < 8; ++i) {
+      const int k0 = kKH * i;
       __syncthreads();   // previous slice's reads done; the weights are written
-      *reinterpret_cast<u32x4*>(&sm.As[arow][8 * aq]) = scale8(ra, &sm.wt[k0 + 8 * aq]);
+      *reinterpret_cast<u32x4*>(&sm.As[arow][8 * aq]) = scale8(ra[i % kSets], &sm.wt[k0 + 8 * aq]);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int run = tid + 256 * u;
-        *reinterpret_cast<u32x4*>(&sm.Bs[run >> 2][8 * (run & 3)]) = rb[u];
+      for (int v = 0; v < 2; ++v) {
+        const int run = tid + 256 * v;
+        *reinterpret_cast<u32x4*>(&sm.Bs[run >> 2][8 * (run & 3)]) = rb[i % kSets][v];
       }
       __syncthreads();
-      if (k0 + kKH < L) fetch(k0 + kKH);
+      fetch(8 * step + i + kSets, i % kSets);
       const f16x8 av = *reinterpret_cast<const f16x8*>(&sm.As[16 * w + l16][8 * g]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
