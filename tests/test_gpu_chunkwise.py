@@ -280,3 +280,21 @@ def test_segmented_states_in_the_workspace():
         c0, s0 = 256 * c, 2048 * (c // 8)
         got = host(L[:, c]) + g ** (c0 - s0) * host(T[:, c // 8])
         assert rel_inf(got, state_at(c0)) <= 1e-2, c
+
+
+@pytest.mark.parametrize("gammas", [(1.0, 0.999), (0.5, 1e-6)])
+def test_segmented_decays_without_a_limit(gammas):
+    """The segmented schedule applies the decay only as factors at most 1 (operands) or in
+    float32 (scores, row scales), so decays from 1 down to 1e-6 hold, across segment
+    boundaries (2048 tokens) and a window boundary (8192): N = 8192 + 300 with an initial
+    state, raw outputs and final state against the oracle."""
+    w = wl(N=8192 + 300, state_std=0.05)
+    x = W.make_inputs(w)
+    gamma = np.array(gammas, dtype=np.float32)
+    out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), gamma, x["theta"], 256,
+                                         state_in=dev(x["state"]), state_out=True,
+                                         out_dtype=torch.float32, segmented=True)
+    ref, Sref = O.chunkwise(x["q"], x["k"], x["v"], gamma, x["theta"], 256, 0, 1.0, x["state"])
+    assert torch.isfinite(out).all() and torch.isfinite(S).all()
+    assert rel_inf(out.cpu(), ref) <= 1e-2
+    assert rel_inf(S.cpu(), Sref) <= 1e-2
