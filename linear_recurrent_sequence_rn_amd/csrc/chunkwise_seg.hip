@@ -11,11 +11,11 @@
 // segment-start states chain as T_{g+1} = gamma^(len_g) T_g + E_g, E_g being the local
 // state at segment g's end. Three kernels per window of 32 chunks (8192 tokens) and group
 // of up to 64 heads:
-//   seg_states   one wave per (head, 2048-token segment, 64 state rows, 64 state columns)
-//                walks its segment in 64-token blocks from a zero state, the float32 tile in
-//                MFMA accumulators, and writes L at every chunk start inside the segment
-//                (half) and E at the segment's end (float32). The waves share nothing, so
-//                there are no barriers; K and V are transposed in registers.
+//   seg_states   one 8-wave workgroup per (head, 2048-token segment, 128 state rows) walks
+//                its segment in 32-token steps from a zero state, each wave holding a
+//                128 x 64 float32 tile in MFMA accumulators; K is rotated once per step for
+//                all waves into LDS, V is transposed in registers. It writes L at every
+//                chunk start inside the segment (half) and E at the segment's end (float32).
 //   seg_scan     per state element: T_g for every segment (half) and the float32 state
 //                leaving the window.
 //   seg_outputs  one 512-thread workgroup per (head, chunk, 64 query rows):
