@@ -184,7 +184,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       [&](int kk, int col) __attribute__((always_inline)) {
           return (kk < dk && col < dv) ? Sc[int64_t(kk) * dv + col] : 0.f; });
   gn_backward_tile<IN, OUTD>(sm, o, a, h, bh, T.r0, T.r1, gate, dout, dgate, dgn_w, dgn_b,
-      [&](int64_t hoff, int i, bool ok, float x) __attribute__((always_inline)) {
+      [&](int64_t hoff, int i, bool ok, float x, int, int) __attribute__((always_inline)) {
         if (ok) dO[hoff + i] = x;
       });
 }

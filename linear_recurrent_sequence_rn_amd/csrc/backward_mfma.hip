@@ -276,32 +276,6 @@ __global__ void __launch_bounds__(256) bm_prep(CallArgs a, const uint16_t* q, co
   store_t_rows(tb, dv, VT + int64_t(bh) * dv * Np, Np, t0);
 }
 
-// dO [N][d_v] -> dO^T [d_v][Np] (zero past N). Grid (Np/64, b*H + h). Lanes take
-// consecutive tokens of one 8-column group (16-byte loads from consecutive rows), so that
-// their LDS writes of one column fall in consecutive halves.
-__global__ void __launch_bounds__(256) bm_transpose(const uint16_t* R, uint16_t* T, int N, int dv,
-                                                    int Np) {
-  __shared__ __attribute__((aligned(16))) uint16_t tb[kMaxDv][kTp];
-  const int t0 = blockIdx.x * 64, bh = blockIdx.y;
-  const uint16_t* Rb = R + int64_t(bh) * N * dv;
-  for (int e = threadIdx.x; e < 64 * (dv / 8); e += 256) {
-    const int cq = e >> 6, tt = e & 63, t = t0 + tt;
-    u32x4 x = u32x4{0u, 0u, 0u, 0u};
-    if (t < N) x = *reinterpret_cast<const u32x4*>(Rb + int64_t(t) * dv + 8 * cq);
-    const uint32_t x0 = x[0], x1 = x[1], x2 = x[2], x3 = x[3];
-    tb[8 * cq + 0][tt] = uint16_t(x0 & 0xffffu);
-    tb[8 * cq + 1][tt] = uint16_t(x0 >> 16);
-    tb[8 * cq + 2][tt] = uint16_t(x1 & 0xffffu);
-    tb[8 * cq + 3][tt] = uint16_t(x1 >> 16);
-    tb[8 * cq + 4][tt] = uint16_t(x2 & 0xffffu);
-    tb[8 * cq + 5][tt] = uint16_t(x2 >> 16);
-    tb[8 * cq + 6][tt] = uint16_t(x3 & 0xffffu);
-    tb[8 * cq + 7][tt] = uint16_t(x3 >> 16);
-  }
-  __syncthreads();
-  store_t_rows(tb, dv, T + int64_t(bh) * dv * Np, Np, t0);
-}
-
 // ---- state scans on matrix cores ---------------------------------------------------------
 // REV = 0: S (chunk states) from X = Kh^T weighted by zeta, Y = V^T, from state_in.
 // REV = 1: G (gradients reaching the chunk ends) from X = Qh^T weighted by alpha xi, Y = dO^T,
@@ -427,9 +401,12 @@ struct Heads {
 // o recomputed: alpha (Qh Kh^T (.) D) V + alpha xi Qh S_c, then the GroupNorm / gate backward.
 template <int OUTD, bool AFF>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-bm_dout(CallArgs a, Heads Hd, const void* gate, const void* dout, uint16_t* DR, void* dgate,
-        float* dgn_w, float* dgn_b) {
+bm_dout(CallArgs a, Heads Hd, const void* gate, const void* dout, uint16_t* DR, uint16_t* DT,
+        void* dgate, float* dgn_w, float* dgn_b) {
   __shared__ TileSharedH sm;
+  // dO of the tile in half (rows past the tile's end hold zeros), copied out at the end in
+  // 16-byte runs, row-major to DR and transposed to DT
+  __shared__ __attribute__((aligned(16))) uint16_t dtile[kR][kMaxDv + 8];
   const int dk = a.dk, dv = a.dv, N = a.N, Np = Hd.Np;
   const TileRows T = tile_rows(N);
   if (T.r0 >= T.r1) return;
@@ -447,12 +424,30 @@ bm_dout(CallArgs a, Heads Hd, const void* gate, const void* dout, uint16_t* DR, 
   zero_acc(o);
   tmm16<32, true>(o, T.r1 - T.c0, sm, Q, 0, 1.f, 0.f, 0, 0, VT, 0, T.c0);
   tmm16<32, false>(o, dk, sm, Q, T.r0, a.alpha, lg, T.r0 - T.c0 + 1, 1, ST, 0, 0);
-  // dO rows of this head through a buffer resource (element stores without branches)
-  const __amdgpu_buffer_rsrc_t rdr = head_rsrc(DR + int64_t(bh) * a.N * a.dv, int64_t(a.N) * a.dv * 2);
   gn_backward_tile<RN_BF16, OUTD, AFF>(sm, o, a, h, bh, T.r0, T.r1, gate, dout, dgate, dgn_w, dgn_b,
-      [&](int64_t, int i, bool ok, float x) __attribute__((always_inline)) {
-        __builtin_amdgcn_raw_buffer_store_b16(h_bits(x), rdr, ok ? static_cast<uint32_t>(i) * 2 : kGnSink, 0, 0);
+      [&](int64_t, int, bool ok, float x, int rloc, int col) __attribute__((always_inline)) {
+        dtile[rloc][col] = ok ? h_bits(x) : uint16_t(0);
       });
+  __syncthreads();
+  // row-major: the tile's rows below its end
+  const int rows = T.r1 - T.r0, runs = dv / 8;
+  uint16_t* DRh = DR + (int64_t(bh) * N + T.r0) * dv;
+  for (int e = threadIdx.x; e < rows * runs; e += 256) {
+    const int rr = e / runs, c8 = e - rr * runs;
+    *reinterpret_cast<u32x4*>(DRh + int64_t(rr) * dv + 8 * c8) =
+        *reinterpret_cast<const u32x4*>(&dtile[rr][8 * c8]);
+  }
+  // transposed: 8 tokens of one column per run, all 64 columns of the tile (the rows past
+  // the sequence's end are zeros, as the padded layout wants)
+  uint16_t* DTh = DT + int64_t(bh) * dv * Np + T.r0;
+  for (int e = threadIdx.x; e < dv * 8; e += 256) {
+    const int col = e >> 3, tg = e & 7;
+    uint32_t wds[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      wds[k] = uint32_t(dtile[8 * tg + 2 * k][col]) | (uint32_t(dtile[8 * tg + 2 * k + 1][col]) << 16);
+    *reinterpret_cast<u32x4*>(DTh + int64_t(col) * Np + 8 * tg) = u32x4{wds[0], wds[1], wds[2], wds[3]};
+  }
 }
 
 // dQh = [alpha (dO V^T) (.) D] Kh + alpha xi dO S_c^T, rotated back.
@@ -564,12 +559,10 @@ hipError_t launch_t(const CallArgs& a, const BwArgs& x, void* ws, hipStream_t st
   }
   if (a.gn_w || a.gn_b || x.dgn_w || x.dgn_b)
     hipLaunchKernelGGL((bm_dout<OUTD, true>), gtiles, dim3(256), 0, st, a, Hd, x.gate, x.dout, at(L.DR),
-                       x.dgate, x.dgn_w, x.dgn_b);
+                       at(L.DT), x.dgate, x.dgn_w, x.dgn_b);
   else
     hipLaunchKernelGGL((bm_dout<OUTD, false>), gtiles, dim3(256), 0, st, a, Hd, x.gate, x.dout, at(L.DR),
-                       x.dgate, x.dgn_w, x.dgn_b);
-  hipLaunchKernelGGL(bm_transpose, gblk, dim3(256), 0, st, static_cast<const uint16_t*>(at(L.DR)),
-                     at(L.DT), a.N, a.dv, L.Np);
+                       at(L.DT), x.dgate, x.dgn_w, x.dgn_b);
   hipLaunchKernelGGL(bm_scan<1>, gscan, dim3(256), 0, st, a, static_cast<const uint16_t*>(at(L.QT)),
                      static_cast<const uint16_t*>(at(L.DT)), x.dstate_out, at(L.G), at(L.GT),
                      x.dstate_in, L.Np);

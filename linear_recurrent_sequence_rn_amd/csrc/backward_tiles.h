@@ -289,7 +289,7 @@ __device__ __forceinline__ void store_rotated(SM& sm, const float (&g)[4][16], c
 // the accumulator layout) has been recomputed: per row the gradient before GroupNorm,
 // dO = rstd (dxh - mean(dxh) - xh mean(dxh xh)) with dxh = dy w and dy = dout (* swish(g)),
 // is passed to store_dO(head offset, element offset within the head, whether the element
-// exists, value); the gate's gradient is stored; the tile's
+// exists, value, row within the tile, column); the gate's gradient is stored; the tile's
 // per-column sums of dy xh and dy are added to dgn_w and dgn_b. Without GroupNorm dO is
 // dout.
 // Element stores through a buffer resource over one head's rows: a store with ok false
@@ -367,9 +367,10 @@ __device__ __forceinline__ void gn_backward_tile(SM& sm, const float (&o)[4][32]
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = T.r0 + 4 * ty + r;
-      if (t >= T.r1) continue;
-      const int roff = t * dv;
-      for (int col = tx; col < dv; col += 16) store_dO(hoff, roff + col, true, Elem<OUTD>::load(dout, roff + col));
+      const bool live = t < T.r1;
+      const int roff = (live ? t : T.r0) * dv;
+      for (int col = tx; col < dv; col += 16)
+        store_dO(hoff, roff + col, live, live ? Elem<OUTD>::load(dout, roff + col) : 0.f, 4 * ty + r, col);
     }
     return;
   }
@@ -445,7 +446,7 @@ __device__ __forceinline__ void gn_backward_tile(SM& sm, const float (&o)[4][32]
     for (int j = 0; j < 32; ++j) {
       const int col = tx + 16 * j;
       const float xh = (o[r][j] - mean) * rstd;
-      store_dO(hoff, roff + col, live && col < dv, rstd * (dyv[j] * wv[j] - m1 - xh * m2));
+      store_dO(hoff, roff + col, live && col < dv, rstd * (dyv[j] * wv[j] - m1 - xh * m2), 4 * ty + r, col);
     }
   }
   if (sums) {
