@@ -87,7 +87,8 @@ __host__ __device__ constexpr int vt_pos(int s) {
 // ---- prep: one 256-thread block per (64-row block, head) ------------------------------
 // bf16 inputs only. q and k: thread = (group of 4 coordinate pairs = 16 bytes, group of
 // 8 rows); 16-byte loads, angles by recurrence along the rows. v: thread = 8 rows x 8
-// columns, transposed in registers and written as 8 rows of V^T (keys in vt_pos order).
+// columns, transposed in registers, assembled as V^T (keys in vt_pos order) in LDS and
+// written out as one contiguous run.
 __global__ void __launch_bounds__(256) parallel_prep(CallArgs a, const uint16_t* q,
                                                      const uint16_t* k, const uint16_t* v,
                                                      uint16_t* ws) {
@@ -148,7 +149,11 @@ __global__ void __launch_bounds__(256) parallel_prep(CallArgs a, const uint16_t*
       *reinterpret_cast<u32x4*>(base + L.k + size_t(t) * kDK + 8 * pg) = ok;
     }
   }
-  uint16_t* vt = base + L.v + size_t(jb) * kDV * kT;
+  // V^T of the block (512 rows of 64 keys in vt_pos order, 64 KB) is assembled in LDS
+  // and written out as one contiguous run of 16-byte pieces. LDS row c holds its eight
+  // 16-byte pieces in the order piece ^ ((c >> 3) & 7), which spreads the 8-byte
+  // writes of a wave (rows 8 apart) over the banks and keeps the read-out conflict free.
+  __shared__ __attribute__((aligned(16))) uint16_t tv[kDV * kT];
 #pragma unroll
   for (int rep = 0; rep < 2; ++rep) {
     const int tile = tid + 256 * rep;
@@ -161,14 +166,23 @@ __global__ void __launch_bounds__(256) parallel_prep(CallArgs a, const uint16_t*
         f[i][2 * j] = __uint_as_float(xv[rep][i][j] << 16);
         f[i][2 * j + 1] = __uint_as_float(xv[rep][i][j] & 0xffff0000u);
       }
-    // rows 8sg..8sg+3 and 8sg+4..8sg+7 land at positions p0 and p0 + 8
-    const int p0 = vt_pos(8 * sg);
+    // rows 8sg..8sg+3 and 8sg+4..8sg+7 land at key positions p0 and p0 + 8
+    const int p0 = vt_pos(8 * sg), sw = (cg & 7) << 3;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      uint16_t* row = vt + size_t(8 * cg + j) * kT;
-      *reinterpret_cast<u32x2*>(row + p0) = u32x2{pack_f16x2(f[0][j], f[1][j]), pack_f16x2(f[2][j], f[3][j])};
-      *reinterpret_cast<u32x2*>(row + p0 + 8) = u32x2{pack_f16x2(f[4][j], f[5][j]), pack_f16x2(f[6][j], f[7][j])};
+      uint16_t* row = tv + (8 * cg + j) * kT;
+      *reinterpret_cast<u32x2*>(row + (p0 ^ sw)) = u32x2{pack_f16x2(f[0][j], f[1][j]), pack_f16x2(f[2][j], f[3][j])};
+      *reinterpret_cast<u32x2*>(row + ((p0 + 8) ^ sw)) = u32x2{pack_f16x2(f[4][j], f[5][j]), pack_f16x2(f[6][j], f[7][j])};
     }
+  }
+  __syncthreads();
+  uint16_t* vt = base + L.v + size_t(jb) * kDV * kT;
+#pragma unroll
+  for (int r = 0; r < kDV * kT / 8 / 256; ++r) {
+    const int piece = tid + 256 * r;   // 16-byte piece of the block's V^T
+    const int c = piece >> 3, pc = piece & 7;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(tv + c * kT + ((pc ^ ((c >> 3) & 7)) << 3));
+    *reinterpret_cast<u32x4*>(vt + size_t(piece) * 8) = x;
   }
 }
 
