@@ -193,15 +193,18 @@ MLayout m_layout(const CallArgs& a) {
 }
 
 // ---- prep: rotated q, k (row-major and transposed) and v transposed, per 64 tokens ------
-// Grid (Np/64, b*H + h); the transposes go through LDS, [column][token] with a pitch of
-// 66 halves (33 words, odd: the 64 lanes of a wave writing one token of consecutive
-// columns hit distinct banks), read back 4 bytes at a time.
-constexpr int kTp = 66;
+// Grid (Np/64, b*H + h); the transposes go through LDS, [column][token].
+// Transposed tile of a 64-token block: row c (a coordinate) holds the 64 tokens as eight
+// 16-byte pieces, piece j stored at slot j ^ ((c >> 3) & 7). The swizzle spreads the
+// 2-byte writes of a wave (coordinates 8 rows apart in consecutive lanes) over the banks
+// and leaves the 16-byte read-out conflict free.
+constexpr int kTp = 64;
+__device__ __forceinline__ int tswz(int c, int tt) { return tt ^ (((c >> 3) & 7) << 3); }
 __device__ __forceinline__ void store_t_rows(uint16_t (*tb)[kTp], int rows, uint16_t* T, int Np, int t0) {
   for (int e = threadIdx.x; e < rows * 8; e += 256) {
     const int c = e >> 3, pc = e & 7;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(&tb[c][8 * pc]);
-    *reinterpret_cast<u32x4*>(T + int64_t(c) * Np + t0 + 8 * pc) = u32x4{src[0], src[1], src[2], src[3]};
+    *reinterpret_cast<u32x4*>(T + int64_t(c) * Np + t0 + 8 * pc) =
+        *reinterpret_cast<const u32x4*>(&tb[c][8 * (pc ^ ((c >> 3) & 7))]);
   }
 }
 __global__ void __launch_bounds__(256) bm_prep(CallArgs a, const uint16_t* q, const uint16_t* k,
@@ -211,65 +214,80 @@ __global__ void __launch_bounds__(256) bm_prep(CallArgs a, const uint16_t* q, co
   const int dk = a.dk, dv = a.dv, N = a.N;
   const int t0 = blockIdx.x * 64, bh = blockIdx.y;
   const int64_t p0 = seq_pos0(a, bh / a.H);
-  // Runs of 8 values: lane e takes token e % 64 of column group e / 64, so that its
-  // writes of one column into tb fall in consecutive halves; all of a thread's loads are
-  // issued before the first is used (up to 8 runs of q or k, 16 of v at the 6.7B shape).
+  // The block's rows of q, k and v are contiguous in memory: element run e (16 bytes) of
+  // a tile is token e / runs-per-row, coordinates 8 (e % runs-per-row) .. +8, so a wave
+  // reads and writes one contiguous 1 KB span. All of a thread's loads are issued before
+  // the first is used (8 runs each of q and k, 16 of v at the 6.7B shape).
   constexpr int kMaxRunsK = 64 * (kMaxDk / 8) / 256;
   constexpr int kMaxRunsV = 64 * (kMaxDv / 8) / 256;
-  for (int which = 0; which < 2; ++which) {
-    const uint16_t* x = (which ? k : q) + int64_t(bh) * N * dk;
-    uint16_t* R = (which ? KR : QR) + int64_t(bh) * N * dk;
-    uint16_t* T = (which ? KT : QT) + int64_t(bh) * dk * Np;
-    const int nrun = 64 * (dk / 8);
-    u32x4 raw[kMaxRunsK];
+  {
+    // q and k together: one angle per (token, pair); rotated q goes to tile rows
+    // 0..dk-1, rotated k to rows dk..2dk-1 (2 dk <= kMaxDv)
+    const int rpr = dk >> 3, nrun = 64 * rpr;
+    const uint16_t* xq = q + (int64_t(bh) * N + t0) * dk;
+    const uint16_t* xk = k + (int64_t(bh) * N + t0) * dk;
+    const int nval = (min(N - t0, 64)) * rpr;   // runs inside the sequence
+    u32x4 rq[kMaxRunsK], rk[kMaxRunsK];
 #pragma unroll
     for (int i = 0; i < kMaxRunsK; ++i) {
-      const int e = threadIdx.x + 256 * i, cq = e >> 6, t = t0 + (e & 63);
-      raw[i] = (e < nrun && t < N) ? *reinterpret_cast<const u32x4*>(x + int64_t(t) * dk + 8 * cq)
-                                    : u32x4{0u, 0u, 0u, 0u};
+      const int e = threadIdx.x + 256 * i;
+      const bool in = e < nval;
+      rq[i] = in ? *reinterpret_cast<const u32x4*>(xq + 8 * e) : u32x4{0u, 0u, 0u, 0u};
+      rk[i] = in ? *reinterpret_cast<const u32x4*>(xk + 8 * e) : u32x4{0u, 0u, 0u, 0u};
     }
+    uint16_t* Rq = QR + (int64_t(bh) * N + t0) * dk;
+    uint16_t* Rk = KR + (int64_t(bh) * N + t0) * dk;
 #pragma unroll
     for (int i = 0; i < kMaxRunsK; ++i) {
-      const int e = threadIdx.x + 256 * i, cq = e >> 6, tt = e & 63, t = t0 + tt;
+      const int e = threadIdx.x + 256 * i;
       if (e >= nrun) break;
-      const uint32_t w4[4] = {raw[i][0], raw[i][1], raw[i][2], raw[i][3]};
-      uint32_t o[4];
+      const int tt = e / rpr, cq = e - tt * rpr;
+      uint32_t oq[4], ok[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint32_t u = w4[m];
-        const float x0 = __uint_as_float(u << 16), x1 = __uint_as_float(u & 0xffff0000u);
         float c, sn;
-        angle_cs(p0 + t, a.ap.theta[4 * cq + m], &c, &sn);
-        const float r0 = x0 * c - x1 * sn, r1 = x0 * sn + x1 * c;
-        o[m] = pack_h2(r0, r1);
-        tb[8 * cq + 2 * m][tt] = uint16_t(o[m] & 0xffffu);
-        tb[8 * cq + 2 * m + 1][tt] = uint16_t(o[m] >> 16);
+        angle_cs(p0 + t0 + tt, a.ap.theta[4 * cq + m], &c, &sn);
+        const float q0 = __uint_as_float(rq[i][m] << 16), q1 = __uint_as_float(rq[i][m] & 0xffff0000u);
+        const float k0 = __uint_as_float(rk[i][m] << 16), k1 = __uint_as_float(rk[i][m] & 0xffff0000u);
+        oq[m] = pack_h2(q0 * c - q1 * sn, q0 * sn + q1 * c);
+        ok[m] = pack_h2(k0 * c - k1 * sn, k0 * sn + k1 * c);
+        const int r0 = 8 * cq + 2 * m, r1 = dk + r0;
+        tb[r0][tswz(r0, tt)] = uint16_t(oq[m] & 0xffffu);
+        tb[r0 + 1][tswz(r0 + 1, tt)] = uint16_t(oq[m] >> 16);
+        // (the k tile is read out from row dk on, so it swizzles by its own row index)
+        tb[r1][tswz(r0, tt)] = uint16_t(ok[m] & 0xffffu);
+        tb[r1 + 1][tswz(r0 + 1, tt)] = uint16_t(ok[m] >> 16);
       }
-      if (t < N) *reinterpret_cast<u32x4*>(R + int64_t(t) * dk + 8 * cq) = u32x4{o[0], o[1], o[2], o[3]};
+      if (e < nval) {
+        *reinterpret_cast<u32x4*>(Rq + 8 * e) = u32x4{oq[0], oq[1], oq[2], oq[3]};
+        *reinterpret_cast<u32x4*>(Rk + 8 * e) = u32x4{ok[0], ok[1], ok[2], ok[3]};
+      }
     }
     __syncthreads();
-    store_t_rows(tb, dk, T, Np, t0);
+    store_t_rows(tb, dk, QT + int64_t(bh) * dk * Np, Np, t0);
+    store_t_rows(tb + dk, dk, KT + int64_t(bh) * dk * Np, Np, t0);
     __syncthreads();
   }
-  const uint16_t* vb = v + int64_t(bh) * N * dv;
-  const int nrun = 64 * (dv / 8);
+  const int rpv = dv >> 3, nrun = 64 * rpv;
+  const int nval = (min(N - t0, 64)) * rpv;
+  const uint16_t* xv = v + (int64_t(bh) * N + t0) * dv;
   u32x4 raw[kMaxRunsV];
 #pragma unroll
   for (int i = 0; i < kMaxRunsV; ++i) {
-    const int e = threadIdx.x + 256 * i, cq = e >> 6, t = t0 + (e & 63);
-    raw[i] = (e < nrun && t < N) ? *reinterpret_cast<const u32x4*>(vb + int64_t(t) * dv + 8 * cq)
-                                  : u32x4{0u, 0u, 0u, 0u};
+    const int e = threadIdx.x + 256 * i;
+    raw[i] = e < nval ? *reinterpret_cast<const u32x4*>(xv + 8 * e) : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int i = 0; i < kMaxRunsV; ++i) {
-    const int e = threadIdx.x + 256 * i, cq = e >> 6, tt = e & 63;
+    const int e = threadIdx.x + 256 * i;
     if (e >= nrun) break;
-    const uint32_t w4[4] = {raw[i][0], raw[i][1], raw[i][2], raw[i][3]};
+    const int tt = e / rpv, cq = e - tt * rpv;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const uint32_t hh = bf2_to_h2(w4[m]);
-      tb[8 * cq + 2 * m][tt] = uint16_t(hh & 0xffffu);
-      tb[8 * cq + 2 * m + 1][tt] = uint16_t(hh >> 16);
+      const uint32_t hh = bf2_to_h2(raw[i][m]);
+      const int r0 = 8 * cq + 2 * m;
+      tb[r0][tswz(r0, tt)] = uint16_t(hh & 0xffffu);
+      tb[r0 + 1][tswz(r0 + 1, tt)] = uint16_t(hh >> 16);
     }
   }
   __syncthreads();
