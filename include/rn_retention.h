@@ -49,9 +49,16 @@ extern "C" {
 typedef int32_t rn_status;
 #define RN_OK               0
 #define RN_ERR_INVALID_ARG (-1) /* null pointer, size < 1, odd d_k, chunk < 1, bad flags, eps < 0 ... */
-#define RN_ERR_UNSUPPORTED (-2) /* valid but outside what is built: d_k > 256, d_v > 512, N > 2^30 ... */
+#define RN_ERR_UNSUPPORTED (-2) /* valid but outside what is built: d_k > 256, d_v > 512, N > 2^30, H > 128 ... */
 #define RN_ERR_HIP         (-3) /* HIP runtime / launch error; text via rn_last_error() */
 #define RN_ERR_WORKSPACE   (-4) /* workspace NULL or smaller than rn_chunkwise_workspace_bytes() */
+#define RN_ERR_EXCHANGE    (-5) /* reported by rn_chunkwise_check: a wait between the workgroups of
+                                   the sequential chunkwise kernel hit its time limit (1 s); the
+                                   call's out and state_out hold NaN where they were written */
+#define RN_ERR_NONFINITE   (-6) /* reported by rn_chunkwise_check: the sequential chunkwise kernel
+                                   produced a non-finite output or final state: a non-finite input,
+                                   or a value beyond its half-precision operand range (see
+                                   rn_retention_chunkwise) */
 
 typedef int32_t rn_dtype;
 #define RN_F32  0   /* IEEE float32 */
@@ -66,15 +73,21 @@ typedef int32_t rn_dtype;
 #define RN_CHUNK_PARALLEL (1u << 9) /* chunkwise: the two-kernel chunk-parallel pair (state
                                        snapshots per 256 tokens, then all chunks' outputs in
                                        parallel) instead of the single sequential kernel; same
-                                       result, another workspace size. It is also what runs where
-                                       the sequential kernel does not apply (gamma^32 < 2^-6, or
-                                       gamma_pair set) at d_k 256, d_v 512 */
+                                       result, another workspace size. Without any schedule flag
+                                       it runs only for gamma_pair at d_k 256, d_v 512 (where the
+                                       sequential kernel does not apply because gamma^32 < 2^-6,
+                                       the segmented schedule runs) */
 #define RN_CHUNK_SEGMENTED (1u << 10) /* chunkwise, bf16 with d_k 256, d_v 512 and one decay per
                                        head: the segmented schedule (segment-local states per
                                        2048 tokens, a scan over segments, then all chunks'
                                        outputs in parallel); same result, another workspace size,
                                        no limit on gamma. Elsewhere the flag is ignored. At most
                                        one of RN_CHUNK_PARALLEL and RN_CHUNK_SEGMENTED may be set. */
+#define RN_TEST_FORCE_TIMEOUT (1u << 12) /* testing only: every cross-workgroup wait of the
+                                       sequential chunkwise kernel gives up at once, as if its time
+                                       limit had passed, so that the error path (NaN outputs,
+                                       RN_ERR_EXCHANGE from rn_chunkwise_check) can be exercised
+                                       while every kernel still ends normally; other paths ignore it */
 
 typedef struct rn_desc {
     int32_t B;             /* batch, >= 1 */
@@ -152,6 +165,16 @@ size_t rn_chunkwise_workspace_bytes(const rn_desc* desc, int32_t chunk);
  * workspace: device buffer of at least rn_chunkwise_workspace_bytes(desc, chunk)
  *            bytes, 256-byte aligned; contents on entry are ignored.
  * RN_NORM_D_ROW / RN_NORM_R_ROW are rejected (parallel form only).
+ * Precision and range. float32 inputs run float32 kernels. bf16 inputs with d_k = 256 and
+ * d_v in {256, 512} (the sequential kernel, the default) or d_v = 512 (the segmented and
+ * chunk-parallel schedules) take matrix-core products whose operands are rounded to IEEE
+ * half with float32 accumulation: the rotated q and k, v, the decayed scores and the copy
+ * of the state used by the cross term must stay below 65504 in magnitude. In the
+ * sequential kernel the rotated rows also carry decay factors up to gamma^-32 (at most 64,
+ * since that kernel takes gamma^32 >= 2^-6), so |alpha q|, |k| < 1000 and |state| < 2^15
+ * keep every operand in range; RetNet-scaled data sits many orders of magnitude below.
+ * Outside that range the result is not finite; rn_chunkwise_check then reports
+ * RN_ERR_NONFINITE for the sequential kernel.
  */
 rn_status rn_retention_chunkwise(const rn_desc* desc, int32_t chunk, const void* q,
                                  const void* k, const void* v, const void* gate,
@@ -237,7 +260,12 @@ size_t rn_chunkwise_backward_workspace_bytes(const rn_desc* desc, int32_t chunk)
  * dgn_weight, dgn_bias: DEVICE float32 [H*d_v] or NULL, written when RN_EPI_GN (sums over
  *             the batch and the rows); ignored otherwise.
  * workspace:  at least rn_chunkwise_backward_workspace_bytes(desc, chunk), 256-byte aligned.
- * Plain float32 arithmetic throughout (every shape and dtype the forward accepts).
+ * Arithmetic: float32 inputs take float32 products throughout (held to 1e-4 relative).
+ * bf16 inputs take matrix-core products (16x16x32 f16 MFMA, float32 accumulation): with
+ * d_k and d_v multiples of 8 and v 16-byte, q and k 4-byte aligned, every operand is
+ * rounded to IEEE half (so, as for the forward, operands must stay below 65504 in
+ * magnitude); other bf16 shapes stage float32 operands and take the same products. Every
+ * shape and dtype the forward accepts is accepted.
  */
 rn_status rn_retention_chunkwise_backward(const rn_desc* desc, int32_t chunk, const void* q,
                                           const void* k, const void* v, const void* gate,
@@ -292,6 +320,21 @@ rn_status rn_groupnorm_gate(int32_t B, int32_t H, int32_t N, int32_t d_v,
                             rn_dtype in_dtype, rn_dtype out_dtype, const void* x,
                             const void* gate, const float* w, const float* b, float eps,
                             void* out, void* stream);
+
+/*
+ * Status of a completed rn_retention_chunkwise / rn_retention_chunkwise_varlen call (same
+ * desc and chunk), read from its workspace: RN_OK; RN_ERR_EXCHANGE if a wait between the
+ * workgroups of the sequential kernel hit its time limit (its outputs are then NaN);
+ * RN_ERR_NONFINITE if that kernel produced a non-finite output or final state. Other
+ * schedules (segmented, chunk-parallel, float32) record nothing and give RN_OK.
+ * workspace: the call's device workspace, in which case `stream` (the call's stream) is
+ * synchronised and the status word copied to the host; or a host copy of at least its
+ * first 256 bytes, read directly. Must be called before the workspace is reused.
+ * (Host calls that cannot block until the GPU finishes should keep using the outputs'
+ * own checks instead.)
+ */
+rn_status rn_chunkwise_check(const rn_desc* desc, int32_t chunk, const void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* Static name of a status code. */
 const char* rn_status_str(rn_status s);

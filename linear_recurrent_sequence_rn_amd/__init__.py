@@ -20,8 +20,10 @@ import torch
 
 __all__ = [
     "RN_OK", "RN_ERR_INVALID_ARG", "RN_ERR_UNSUPPORTED", "RN_ERR_HIP", "RN_ERR_WORKSPACE",
+    "RN_ERR_EXCHANGE", "RN_ERR_NONFINITE",
     "RN_F32", "RN_BF16", "RN_NORM_D_ROW", "RN_NORM_R_ROW", "RN_EPI_GN", "RN_EPI_GATE",
-    "RN_FORCE_GENERIC", "RN_CHUNK_PARALLEL", "RN_CHUNK_SEGMENTED", "RnError", "RnDesc", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
+    "RN_FORCE_GENERIC", "RN_CHUNK_PARALLEL", "RN_CHUNK_SEGMENTED", "RN_TEST_FORCE_TIMEOUT",
+    "RnError", "RnDesc", "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "rn_chunkwise_check",
     "rn_retention_parallel", "rn_retention_chunkwise", "rn_retention_recurrent_step",
     "rn_retention_chunkwise_varlen", "rn_retention_recurrent_step_at", "rn_groupnorm_gate",
     "rn_retention_chunkwise_backward", "rn_chunkwise_backward_workspace_bytes", "rn_chunkwise_workspace_bytes", "rn_parallel_workspace_bytes",
@@ -31,18 +33,20 @@ __all__ = [
 LIB_PATH = Path(__file__).resolve().parent / "librn_retention.so"
 
 RN_OK, RN_ERR_INVALID_ARG, RN_ERR_UNSUPPORTED, RN_ERR_HIP, RN_ERR_WORKSPACE = 0, -1, -2, -3, -4
+RN_ERR_EXCHANGE, RN_ERR_NONFINITE = -5, -6
 RN_F32, RN_BF16 = 0, 1
 RN_NORM_D_ROW, RN_NORM_R_ROW, RN_EPI_GN, RN_EPI_GATE = 1, 2, 4, 8
 RN_FORCE_GENERIC = 1 << 8
 RN_CHUNK_PARALLEL = 1 << 9
 RN_CHUNK_SEGMENTED = 1 << 10
+RN_TEST_FORCE_TIMEOUT = 1 << 12
 
 EXPORTED_SYMBOLS = (
     "rn_parallel_workspace_bytes", "rn_retention_parallel", "rn_chunkwise_workspace_bytes", "rn_retention_chunkwise",
     "rn_retention_recurrent_step", "rn_retention_chunkwise_varlen",
     "rn_retention_recurrent_step_at", "rn_groupnorm_gate", "rn_status_str", "rn_last_error",
     "rn_version", "rn_retention_chunkwise_backward", "rn_chunkwise_backward_workspace_bytes",
-    "rn_msr_layer_workspace_bytes", "rn_msr_layer_forward",
+    "rn_msr_layer_workspace_bytes", "rn_msr_layer_forward", "rn_chunkwise_check",
 )
 
 
@@ -94,6 +98,8 @@ def _load():
     L.rn_msr_layer_workspace_bytes.restype = sz
     L.rn_msr_layer_forward.argtypes = [D, i32, i32] + [vp] * 9 + [vp, sz, vp]
     L.rn_msr_layer_forward.restype = i32
+    L.rn_chunkwise_check.argtypes = [D, i32, vp, sz, vp]
+    L.rn_chunkwise_check.restype = i32
     L.rn_groupnorm_gate.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                     ctypes.c_float, vp, vp]
     L.rn_groupnorm_gate.restype = i32
@@ -200,8 +206,10 @@ def make_desc(B: int, H: int, N: int, d_k: int, d_v: int, in_dtype: int, out_dty
     return d, (g, gp, th, gn_weight, gn_bias)
 
 
-def _flags(norm_d, norm_r, gn, gate, force_generic, chunk_parallel=False, segmented=False):
+def _flags(norm_d, norm_r, gn, gate, force_generic, chunk_parallel=False, segmented=False,
+           test_force_timeout=False):
     f = 0
+    if test_force_timeout: f |= RN_TEST_FORCE_TIMEOUT
     if chunk_parallel: f |= RN_CHUNK_PARALLEL
     if segmented: f |= RN_CHUNK_SEGMENTED
     if norm_d: f |= RN_NORM_D_ROW
@@ -212,22 +220,33 @@ def _flags(norm_d, norm_r, gn, gate, force_generic, chunk_parallel=False, segmen
     return f
 
 
-def _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos0, qk_scale, gn_eps, gn_weight, gn_bias):
+def _check_affine(gn_weight, gn_bias, n, device):
+    """GroupNorm weight and bias: float32 with n elements, on the call's device."""
+    for t in (gn_weight, gn_bias):
+        if t is not None:
+            if t.dtype != torch.float32 or t.numel() != n or t.device != device:
+                raise ValueError(f"gn_weight/gn_bias must be float32 with {n} elements on {device}")
+            _ptr(t)
+
+
+def _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos0, qk_scale, gn_eps, gn_weight, gn_bias,
+              gate=None):
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError(f"expected q,k [B,H,N,d_k] and v [B,H,N,d_v]; got {tuple(q.shape)}, "
                          f"{tuple(k.shape)}, {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share one dtype")
+    if not (k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on one device")
+    if gate is not None and (gate.shape != v.shape or gate.dtype != q.dtype or gate.device != q.device):
+        raise ValueError(f"gate must match v: {q.dtype} {tuple(v.shape)} on {q.device}; got "
+                         f"{gate.dtype} {tuple(gate.shape)} on {gate.device}")
     B, H, N, dk = q.shape
     dv = v.shape[-1]
     if len(gamma) != H or len(theta) != dk // 2:
         raise ValueError(f"need gamma[{H}] (or [{H}, {dk // 2}]) and theta[{dk // 2}]")
     od = q.dtype if out_dtype is None else out_dtype
-    for t in (gn_weight, gn_bias):
-        if t is not None:
-            _ptr(t)
-            if t.dtype != torch.float32 or t.numel() != H * dv:
-                raise ValueError("gn_weight/gn_bias must be float32 with H*d_v elements")
+    _check_affine(gn_weight, gn_bias, H * dv, q.device)
     d, keep = make_desc(B, H, N, dk, dv, _dtype_code(q.dtype), _dtype_code(od), gamma, theta,
                         flags=flags, pos0=pos0, qk_scale=qk_scale, gn_eps=gn_eps,
                         gn_weight=gn_weight, gn_bias=gn_bias, device=q.device)
@@ -241,7 +260,7 @@ def rn_retention_parallel(q, k, v, gamma, theta, *, gate=None, out=None, out_dty
     """Parallel form; returns out [B,H,N,d_v]."""
     flags = _flags(norm_d, norm_r, gn, gate, force_generic)
     d, keep, od = _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos0, qk_scale, gn_eps,
-                            gn_weight, gn_bias)
+                            gn_weight, gn_bias, gate)
     out = _out(out, v.shape, od, v.device)
     need = int(lib.rn_parallel_workspace_bytes(ctypes.byref(d)))
     if workspace is None and need > 0:
@@ -284,14 +303,16 @@ def _seq_array(t, B, dtype, name):
 def rn_retention_chunkwise(q, k, v, gamma, theta, chunk, *, gate=None, state_in=None,
                            state_out=None, out=None, out_dtype=None, workspace=None, pos0=0,
                            qk_scale=1.0, gn=False, gn_eps=1e-5, gn_weight=None, gn_bias=None,
-                           force_generic=False, chunk_parallel=False, segmented=False):
+                           force_generic=False, chunk_parallel=False, segmented=False,
+                           test_force_timeout=False):
     """Chunkwise form; returns (out, state_out). ``state_out`` may be a tensor (written),
     True (allocated), or None/False (discarded). ``chunk_parallel`` selects the two-kernel
     chunk-parallel pair (RN_CHUNK_PARALLEL), ``segmented`` the segmented schedule
-    (RN_CHUNK_SEGMENTED); by default the sequential kernel runs where it applies."""
+    (RN_CHUNK_SEGMENTED); by default the sequential kernel runs where it applies.
+    ``test_force_timeout`` sets RN_TEST_FORCE_TIMEOUT (exercises the error path)."""
     return _chunkwise(q, k, v, gamma, theta, chunk, None, None, gate, state_in, state_out, out,
                       out_dtype, workspace, pos0, qk_scale, gn, gn_eps, gn_weight, gn_bias,
-                      force_generic, chunk_parallel, segmented)
+                      force_generic, chunk_parallel, segmented, test_force_timeout)
 
 
 def rn_retention_chunkwise_varlen(q, k, v, gamma, theta, chunk, *, pos=None, lengths=None,
@@ -313,10 +334,11 @@ def rn_retention_chunkwise_varlen(q, k, v, gamma, theta, chunk, *, pos=None, len
 
 def _chunkwise(q, k, v, gamma, theta, chunk, pos, lengths, gate, state_in, state_out, out,
                out_dtype, workspace, pos0, qk_scale, gn, gn_eps, gn_weight, gn_bias,
-               force_generic, chunk_parallel, segmented=False):
-    flags = _flags(False, False, gn, gate, force_generic, chunk_parallel, segmented)
+               force_generic, chunk_parallel, segmented=False, test_force_timeout=False):
+    flags = _flags(False, False, gn, gate, force_generic, chunk_parallel, segmented,
+                   test_force_timeout)
     d, keep, od = _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos0, qk_scale, gn_eps,
-                            gn_weight, gn_bias)
+                            gn_weight, gn_bias, gate)
     B, H, N, dk = q.shape
     dv = v.shape[-1]
     out = _out(out, v.shape, od, v.device)
@@ -348,7 +370,7 @@ def rn_retention_recurrent_step(q, k, v, gamma, theta, state, pos, *, gate=None,
     place. q, k: [B,H,1,d_k]; v: [B,H,1,d_v]. Returns out [B,H,1,d_v]."""
     flags = _flags(False, False, gn, gate, False)
     d, keep, od = _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos, qk_scale, gn_eps,
-                            gn_weight, gn_bias)
+                            gn_weight, gn_bias, gate)
     if state.dtype != torch.float32 or tuple(state.shape) != (q.shape[0], q.shape[1], q.shape[3], v.shape[3]):
         raise ValueError("state must be float32 [B,H,d_k,d_v]")
     out = _out(out, v.shape, od, v.device)
@@ -364,7 +386,7 @@ def rn_retention_recurrent_step_at(q, k, v, gamma, theta, state, pos, *, gate=No
     [B]); otherwise as rn_retention_recurrent_step. Returns out [B,H,1,d_v]."""
     flags = _flags(False, False, gn, gate, False)
     d, keep, od = _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, 0, qk_scale, gn_eps,
-                            gn_weight, gn_bias)
+                            gn_weight, gn_bias, gate)
     if state.dtype != torch.float32 or tuple(state.shape) != (q.shape[0], q.shape[1], q.shape[3], v.shape[3]):
         raise ValueError("state must be float32 [B,H,d_k,d_v]")
     pp = _seq_array(pos, q.shape[0], torch.int64, "pos")
@@ -396,7 +418,7 @@ def rn_retention_chunkwise_backward(q, k, v, gamma, theta, chunk, dout, *, gate=
     dgn_bias."""
     flags = _flags(False, False, gn, gate, False)
     d, keep, od = _qkv_desc(q, k, v, gamma, theta, dout.dtype, flags, pos0, qk_scale, gn_eps,
-                            gn_weight, gn_bias)
+                            gn_weight, gn_bias, gate)
     B, H, N, dk = q.shape
     dv = v.shape[-1]
     if tuple(dout.shape) != tuple(v.shape):
@@ -490,8 +512,31 @@ def rn_groupnorm_gate(x, gate=None, weight=None, bias=None, eps=1e-5, *, out=Non
     B, H, N, dv = x.shape
     od = x.dtype if out_dtype is None else out_dtype
     out = _out(out, x.shape, od, x.device)
-    if gate is not None and (gate.shape != x.shape or gate.dtype != x.dtype):
-        raise ValueError("gate must match x in shape and dtype")
+    if gate is not None and (gate.shape != x.shape or gate.dtype != x.dtype or gate.device != x.device):
+        raise ValueError("gate must match x in shape, dtype and device")
+    _check_affine(weight, bias, H * dv, x.device)
     _check(lib.rn_groupnorm_gate(B, H, N, dv, _dtype_code(x.dtype), _dtype_code(od), _ptr(x),
                                  _ptr(gate), _ptr(weight), _ptr(bias), eps, _ptr(out), _stream(x)))
     return out
+
+
+def rn_chunkwise_check(q, v, gamma, theta, chunk, workspace, *, gn=False, gate=None,
+                       out_dtype=None, force_generic=False, chunk_parallel=False,
+                       segmented=False) -> int:
+    """Status of a completed chunkwise call (same arguments as the call) read from its
+    ``workspace``: a GPU tensor (the call's stream is synchronised first) or a CPU copy of
+    its first bytes. Returns the status code (RN_OK, RN_ERR_EXCHANGE, RN_ERR_NONFINITE);
+    argument errors raise."""
+    B, H, N, dk = q.shape
+    flags = _flags(False, False, gn, gate, force_generic, chunk_parallel, segmented)
+    od = q.dtype if out_dtype is None else out_dtype
+    d, keep = make_desc(B, H, N, dk, v.shape[-1], _dtype_code(q.dtype), _dtype_code(od), gamma,
+                        theta, flags=flags, device=q.device)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    stream = _stream(workspace) if workspace.is_cuda else None
+    st = int(lib.rn_chunkwise_check(ctypes.byref(d), chunk, ctypes.c_void_p(workspace.data_ptr()),
+                                    workspace.numel() * workspace.element_size(), stream))
+    if st not in (RN_OK, RN_ERR_EXCHANGE, RN_ERR_NONFINITE):
+        _check(st)
+    return st

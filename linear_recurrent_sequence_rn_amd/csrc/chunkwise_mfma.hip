@@ -216,19 +216,34 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
-// Thread 0 waits until cnt[word] >= target, then the block synchronises. A wait that
-// exceeds kWaitTicks raises cnt[kError]; once raised, every later wait of every
-// workgroup of the head returns at once, so a broken exchange costs one time limit.
-__device__ __forceinline__ void wait_count(uint32_t* cnt, int word, uint32_t target) {
+// Bits of the call's status word (first word of the workspace, cleared at the start of
+// every call): a wait hit its time limit; an output or the final state is not finite.
+constexpr uint32_t kStatusTimeout = kChunkwiseStatusTimeout, kStatusNonFinite = kChunkwiseStatusNonFinite;
+constexpr size_t kStatusBytes = 256;   // status region at the start of the workspace
+
+// A wait that hit its time limit: raises the head's error word (every later wait of
+// every workgroup of the head then returns at once, so a broken exchange costs one time
+// limit, and every workgroup writes NaN outputs at its end) and the call's status word.
+__device__ __forceinline__ void raise_timeout(uint32_t* cnt, uint32_t* status) {
+  __hip_atomic_fetch_or(cnt + kError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_fetch_or(status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0 waits until cnt[word] >= target, then the block synchronises. With `force`
+// (the RN_TEST_FORCE_TIMEOUT flag) the wait gives up at once, as if its limit had passed.
+__device__ __forceinline__ void wait_count(uint32_t* cnt, int word, uint32_t target,
+                                           uint32_t* status, bool force) {
   if (threadIdx.x == 0) {
     uint32_t* p = cnt + word;
-    if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    if (force) {
+      raise_timeout(cnt, status);
+    } else if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       const uint64_t t0 = wall_clock64();
       while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
         if (__hip_atomic_load(cnt + kError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
         __builtin_amdgcn_s_sleep(1);
         if (wall_clock64() - t0 > kWaitTicks) {
-          __hip_atomic_fetch_or(cnt + kError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          raise_timeout(cnt, status);
           break;
         }
       }
@@ -250,7 +265,8 @@ struct Params {
   const float* s_in;
   float* s_out;
   void* out;
-  uint8_t* ws;
+  uint8_t* ws;          // this launch group's counters, statistics and ring
+  uint32_t* status;     // the call's status word
 };
 
 template <int C> struct Ic { static constexpr int value = C; };
@@ -293,7 +309,7 @@ chunkwise_fused(Params P) {
     __threadfence();
     __hip_atomic_fetch_add(cnt + kArrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  wait_count(cnt, kArrive, nS);
+  wait_count(cnt, kArrive, nS, P.status, (a.flags & RN_TEST_FORCE_TIMEOUT) != 0);
   if (tid == 0) {
     uint32_t m = __hip_atomic_load(cnt + kXccMask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm.mode = (__builtin_popcount(m) == 1) ? 0u : 1u;
@@ -330,7 +346,7 @@ chunkwise_fused(Params P) {
           if (x >= target || err) break;
           __builtin_amdgcn_s_sleep(1);
           if (wall_clock64() - t0 > kWaitTicks) {
-            if (l == 0) __hip_atomic_fetch_or(cnt + kError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (l == 0) raise_timeout(cnt, P.status);
             break;
           }
         }
@@ -501,8 +517,13 @@ chunkwise_fused(Params P) {
       }
     }
 
+    // A wait of this head that hit its time limit leaves the exchange, hence the
+    // state, invalid: the slice's final state is then written as NaN.
+    const bool failed = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(cnt + kError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0u;
     if (P.s_out) {
       const float gi32 = exp2f(-lg * 32.f);
+      uint32_t bad = 0u;   // set by a non-finite state value
 #pragma unroll
       for (int ta = 0; ta < 4; ++ta)
 #pragma unroll
@@ -511,8 +532,12 @@ chunkwise_fused(Params P) {
           for (int r = 0; r < 4; ++r) {
             const int dk = 64 * w + 32 * (ta >> 1) + 8 * g + 4 * (ta & 1) + r;
             const int dv = sl * kSl + 16 * tb + l16;
-            P.s_out[(size_t(bh) * kDK + dk) * DV + dv] = Sacc[ta][tb][r] * gi32;
+            const float x = Sacc[ta][tb][r] * gi32;
+            bad |= __builtin_isfinite(x) ? 0u : 1u;
+            P.s_out[(size_t(bh) * kDK + dk) * DV + dv] = failed ? __builtin_nanf("") : x;
           }
+      if (__builtin_amdgcn_ballot_w64(bad != 0u) != 0 && l == 0)
+        __hip_atomic_fetch_or(P.status, kStatusNonFinite, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else {
     // =============================== E waves ===========================================
@@ -649,6 +674,7 @@ chunkwise_fused(Params P) {
     // eb < nS reads slice eb's mean and M2 of rows 2ea, 2ea+1), gates and stores
     // (blocks outside the sequence: offsets past the end, stores dropped).
     const float inv_dv = 1.0f / float(DV);
+    uint32_t nonfinite = 0u;   // set by a non-finite output of the sequence
     auto finalize = [&](int b, const float (*o)[8], const u32x4* gt, int sbuf) {
       float y[2][8];
       if (use_gn) {
@@ -680,6 +706,16 @@ chunkwise_fused(Params P) {
         for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
           for (int c = 0; c < 8; ++c) y[rr][c] = o[rr][c];
+      }
+      {
+        // (a class test per value: x - x would not do, since the compiler may contract
+        // the product that forms x with the subtraction, leaving its rounding error)
+        uint32_t bad = 0u;
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) bad |= __builtin_isfinite(y[rr][c]) ? 0u : 1u;
+        nonfinite |= (b >= 0 && b < nb) ? bad : 0u;
       }
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
@@ -822,6 +858,28 @@ chunkwise_fused(Params P) {
       iter(Ic<2>{}, i0 + 2);
       iter(Ic<3>{}, i0 + 3);
     }
+    if (__builtin_amdgcn_ballot_w64(nonfinite != 0u) != 0 && l == 0)
+      __hip_atomic_fetch_or(P.status, kStatusNonFinite, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // A wait of this head that hit its time limit leaves the exchange invalid: every row
+    // this thread stored is written again as NaN (same thread, same addresses, so the
+    // NaN stores land after the earlier ones).
+    if (__builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(cnt + kError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0u) {
+      const float qn = __builtin_nanf("");
+      for (int b = 0; b < nb; ++b)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const uint32_t ooff = static_cast<uint32_t>(((b * kT + 2 * ea + rr) * DV + 8 * eb) * osz);
+          if constexpr (OUT == RN_BF16) {
+            const uint32_t nn = pack_bf16x2(qn, qn);
+            st_b128(r_o, ooff, u32x4{nn, nn, nn, nn});
+          } else {
+            const u32x4 nn = __builtin_bit_cast(u32x4, f32x4{qn, qn, qn, qn});
+            st_b128(r_o, ooff, nn);
+            st_b128(r_o, ooff + 16, nn);
+          }
+        }
+    }
   }
 }
 
@@ -884,7 +942,7 @@ size_t chunkwise_mfma_ws_bytes(const CallArgs& a) {
   int G = heads_per_group(nS);
   if (G <= 0) G = 8 * (256 / (8 * nS));  // no device visible: size for a 256-CU part
   G = min(G, a.B * a.H);
-  return size_t(G) * (kCntWords * 4 + kStatsPerHead + kRingPerHead);
+  return kStatusBytes + size_t(G) * (kCntWords * 4 + kStatsPerHead + kRingPerHead);
 }
 
 hipError_t launch_chunkwise_mfma(const CallArgs& a, int out_dt, const void* q, const void* k,
@@ -905,16 +963,20 @@ hipError_t launch_chunkwise_mfma(const CallArgs& a, int out_dt, const void* q, c
   p.s_in = s_in;
   p.s_out = s_out;
   p.out = out;
-  p.ws = static_cast<uint8_t*>(ws);
+  // the call's status word first, then the launch group's counters, statistics and ring
+  p.status = static_cast<uint32_t*>(ws);
+  p.ws = static_cast<uint8_t*>(ws) + kStatusBytes;
   for (int h0 = 0; h0 < total; h0 += G) {
     const int heads = min(G, total - h0);
-    if (size_t(heads) * (kCntWords * 4 + kStatsPerHead + kRingPerHead) > ws_bytes)
+    if (kStatusBytes + size_t(heads) * (kCntWords * 4 + kStatsPerHead + kRingPerHead) > ws_bytes)
       return hipErrorInvalidValue;
     p.head0 = h0;
     p.heads = heads;
-    const int nwords = heads * int(kCntWords);
+    // the first group also clears the status word (which later groups only raise)
+    const int first = h0 == 0 ? int(kStatusBytes / 4) : 0;
+    const int nwords = first + heads * int(kCntWords);
     hipLaunchKernelGGL(zero_words, dim3((nwords + 255) / 256), dim3(256), 0, st,
-                       static_cast<uint32_t*>(ws), nwords);
+                       reinterpret_cast<uint32_t*>(p.ws) - first, nwords);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int grid = 8 * nS * ((heads + 7) / 8);

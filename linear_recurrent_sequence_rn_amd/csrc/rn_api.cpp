@@ -32,7 +32,8 @@ rn_status hip_status(hipError_t e, const char* what) {
 enum class Form { kParallel, kChunkwise, kStep };
 
 constexpr uint32_t kKnownFlags = RN_NORM_D_ROW | RN_NORM_R_ROW | RN_EPI_GN | RN_EPI_GATE |
-                                 RN_FORCE_GENERIC | RN_CHUNK_PARALLEL | RN_CHUNK_SEGMENTED;
+                                 RN_FORCE_GENERIC | RN_CHUNK_PARALLEL | RN_CHUNK_SEGMENTED |
+                                 RN_TEST_FORCE_TIMEOUT;
 
 bool dtype_ok(rn_dtype d) { return d == RN_F32 || d == RN_BF16; }
 
@@ -47,6 +48,7 @@ rn_status check_desc(const rn_desc* d, Form form, rn::CallArgs* a) {
   if (d->d_v > rn::kMaxDv) return fail(RN_ERR_UNSUPPORTED, "d_v=%d > %d", d->d_v, rn::kMaxDv);
   if (d->H > rn::kMaxHeads) return fail(RN_ERR_UNSUPPORTED, "H=%d > %d", d->H, rn::kMaxHeads);
   if (d->B > 65535) return fail(RN_ERR_UNSUPPORTED, "B=%d > 65535", d->B);
+  if (d->N > (1 << 30)) return fail(RN_ERR_UNSUPPORTED, "N=%d > 2^30", d->N);
   if (form == Form::kStep && d->N != 1)
     return fail(RN_ERR_INVALID_ARG, "recurrent step needs N == 1 (got %d)", d->N);
   if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype))
@@ -135,6 +137,8 @@ const char* rn_status_str(rn_status s) {
     case RN_ERR_UNSUPPORTED: return "RN_ERR_UNSUPPORTED";
     case RN_ERR_HIP: return "RN_ERR_HIP";
     case RN_ERR_WORKSPACE: return "RN_ERR_WORKSPACE";
+    case RN_ERR_EXCHANGE: return "RN_ERR_EXCHANGE";
+    case RN_ERR_NONFINITE: return "RN_ERR_NONFINITE";
     default: return "RN_ERR_UNKNOWN";
   }
 }
@@ -248,6 +252,40 @@ rn_status rn_retention_chunkwise(const rn_desc* desc, int32_t chunk, const void*
                                  size_t workspace_bytes, void* stream) {
   return chunkwise_call(desc, chunk, nullptr, nullptr, q, k, v, gate, state_in, state_out, out,
                         workspace, workspace_bytes, stream);
+}
+
+rn_status rn_chunkwise_check(const rn_desc* desc, int32_t chunk, const void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  rn::CallArgs a;
+  rn_status s = check_desc(desc, Form::kChunkwise, &a);
+  if (s != RN_OK) return s;
+  if (chunk < 1) return fail(RN_ERR_INVALID_ARG, "chunk=%d must be >= 1", chunk);
+  if (chunk_path(desc, a) != ChunkPath::kSequential) return RN_OK;   // nothing recorded
+  if (!workspace) return fail(RN_ERR_INVALID_ARG, "workspace is NULL");
+  if (workspace_bytes < sizeof(uint32_t))
+    return fail(RN_ERR_WORKSPACE, "workspace %zu bytes holds no status word", workspace_bytes);
+  // The status word is the first word of the sequential kernel's workspace. A device
+  // pointer is read after the call's stream has finished; anything else (a host copy of
+  // the workspace) is read directly.
+  uint32_t word = 0;
+  hipPointerAttribute_t attr;
+  const bool on_device = hipPointerGetAttributes(&attr, workspace) == hipSuccess &&
+                         attr.type == hipMemoryTypeDevice;
+  (void)hipGetLastError();   // a host pointer leaves an error behind on some runtimes
+  if (on_device) {
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_status(e, "reading the chunkwise status word");
+  } else {
+    std::memcpy(&word, workspace, sizeof(word));
+  }
+  g_err[0] = 0;
+  if (word & rn::kChunkwiseStatusTimeout)
+    return fail(RN_ERR_EXCHANGE, "a cross-workgroup wait of the sequential chunkwise kernel "
+                                 "hit its time limit; its outputs are NaN");
+  if (word & rn::kChunkwiseStatusNonFinite)
+    return fail(RN_ERR_NONFINITE, "the sequential chunkwise kernel produced non-finite values");
+  return RN_OK;
 }
 
 rn_status rn_retention_chunkwise_varlen(const rn_desc* desc, int32_t chunk, const int64_t* pos,

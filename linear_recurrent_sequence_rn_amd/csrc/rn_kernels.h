@@ -21,6 +21,9 @@ hipError_t launch_groupnorm_gate(int B, int H, int N, int dv, int in_dt, int out
                                  float eps, void* out, hipStream_t st);
 
 // Fused MFMA chunkwise kernel (bf16 inputs, d_k = 256, d_v in {64,128,256,512}).
+// Its workspace starts with the call's status word: these bits.
+constexpr uint32_t kChunkwiseStatusTimeout = 1u;     // a cross-workgroup wait timed out
+constexpr uint32_t kChunkwiseStatusNonFinite = 2u;   // a non-finite output or final state
 bool chunkwise_mfma_supported(const CallArgs& a, int in_dt);
 size_t chunkwise_mfma_ws_bytes(const CallArgs& a);
 hipError_t launch_chunkwise_mfma(const CallArgs& a, int out_dt, const void* q, const void* k,

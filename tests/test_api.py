@@ -301,3 +301,100 @@ def test_layer_errors_and_workspace():
     dbad, keep_bad = desc(B=0)
     assert layer(dbad) == rn.RN_ERR_INVALID_ARG
     assert rn.lib.rn_msr_layer_workspace_bytes(ctypes.byref(dbad), 64, 16) == 0
+
+
+SEQ = dict(d_k=256, d_v=512, theta=np.ones(128), H=2, gamma=np.full(2, 0.99), N=300)
+
+
+def status_image(word, nbytes):
+    """A host copy of a sequential-kernel workspace whose status word is ``word``."""
+    img = np.zeros(nbytes // 4, dtype=np.uint32)
+    img[0] = word
+    return img
+
+
+def chk_status(d, img, chunk=64, nbytes=None):
+    nb = img.nbytes if nbytes is None else nbytes
+    return rn.lib.rn_chunkwise_check(ctypes.byref(d), chunk, img.ctypes.data_as(ctypes.c_void_p),
+                                     nb, None)
+
+
+def test_chunkwise_check_reads_the_status_word():
+    """The status word leads the sequential kernel's workspace: bit 0 is an exchange wait
+    that hit its time limit, bit 1 a non-finite output or state. A host copy of the
+    workspace is read directly, so every code is reachable without a GPU."""
+    d, keep = desc(**SEQ)
+    n = rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), 64)
+    assert n >= 256
+    assert chk_status(d, status_image(0, n)) == rn.RN_OK
+    assert chk_status(d, status_image(1, n)) == rn.RN_ERR_EXCHANGE
+    assert b"time limit" in rn.lib.rn_last_error()
+    assert chk_status(d, status_image(2, n)) == rn.RN_ERR_NONFINITE
+    assert chk_status(d, status_image(3, n)) == rn.RN_ERR_EXCHANGE     # the time-out wins
+    assert rn.lib.rn_status_str(rn.RN_ERR_EXCHANGE) == b"RN_ERR_EXCHANGE"
+    assert rn.lib.rn_status_str(rn.RN_ERR_NONFINITE) == b"RN_ERR_NONFINITE"
+    # argument errors
+    assert rn.lib.rn_chunkwise_check(ctypes.byref(d), 64, None, n, None) == rn.RN_ERR_INVALID_ARG
+    assert chk_status(d, status_image(0, n), nbytes=2) == rn.RN_ERR_WORKSPACE
+    assert chk_status(d, status_image(0, n), chunk=0) == rn.RN_ERR_INVALID_ARG
+    assert rn.lib.rn_chunkwise_check(None, 64, FAKE, n, None) == rn.RN_ERR_INVALID_ARG
+
+
+def test_chunkwise_check_other_schedules_record_nothing():
+    """Schedules other than the sequential kernel keep no status word: the check is RN_OK
+    whatever the workspace holds (their waits are kernel boundaries, not time-limited)."""
+    for flags in (rn.RN_CHUNK_PARALLEL, rn.RN_CHUNK_SEGMENTED, rn.RN_FORCE_GENERIC):
+        d, keep = desc(**SEQ, flags=flags)
+        assert chk_status(d, status_image(3, 1024)) == rn.RN_OK, flags
+    d, keep = desc(**dict(SEQ, gamma=np.full(2, 0.8)))       # gamma^32 < 2^-6: not sequential
+    assert chk_status(d, status_image(3, 1024)) == rn.RN_OK
+
+
+def test_chunkwise_check_binding_with_a_host_copy():
+    import torch
+    q = torch.zeros(1, 2, 300, 256, dtype=torch.bfloat16)
+    v = torch.zeros(1, 2, 300, 512, dtype=torch.bfloat16)
+    g, th = [0.99, 0.99], np.ones(128)
+    n = rn.rn_chunkwise_workspace_bytes(q, v, g, th, 64)
+    for word, code in ((0, rn.RN_OK), (1, rn.RN_ERR_EXCHANGE), (2, rn.RN_ERR_NONFINITE)):
+        img = torch.from_numpy(status_image(word, n).view(np.uint8))
+        assert rn.rn_chunkwise_check(q, v, g, th, 64, img) == code
+    with pytest.raises(RuntimeError):
+        rn.rn_chunkwise_check(q, v, g, th, 0, img)
+
+
+def test_test_force_timeout_flag_is_known():
+    d, keep = desc(flags=rn.RN_TEST_FORCE_TIMEOUT)
+    assert rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), 4) > 0
+    d, keep = desc(flags=1 << 30)
+    assert rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), 4) == 0
+
+
+def test_sequence_length_limit():
+    d, keep = desc(N=(1 << 30) + 1)
+    assert chk(d) == rn.RN_ERR_UNSUPPORTED
+    assert b"2^30" in rn.lib.rn_last_error()
+
+
+def test_binding_checks_gate_and_affine():
+    """The gate must match v (shape, dtype, device) and the GroupNorm weight and bias
+    must be float32 with H*d_v elements on the call's device; all rejected before any call."""
+    import torch
+    q = torch.zeros(1, 2, 8, 16, dtype=torch.bfloat16)
+    v = torch.zeros(1, 2, 8, 32, dtype=torch.bfloat16)
+    g, th = [0.9, 0.8], np.ones(8)
+    base = (q, q, v, g, th, None, 0, 0, 1.0, 1e-5)
+    for gate in (torch.zeros(1, 2, 8, 16, dtype=torch.bfloat16),          # shape
+                 torch.zeros(1, 2, 8, 32, dtype=torch.float32),           # dtype
+                 torch.zeros(1, 2, 8, 32, dtype=torch.bfloat16, device="meta")):   # device
+        with pytest.raises(ValueError, match="gate"):
+            rn._qkv_desc(*base, None, None, gate)
+    for w in (torch.ones(64, dtype=torch.bfloat16), torch.ones(63), torch.ones(64, device="meta")):
+        with pytest.raises(ValueError, match="gn_weight"):
+            rn._qkv_desc(*base, w, None)
+        with pytest.raises(ValueError, match="gn_weight"):
+            rn._qkv_desc(*base, None, w)
+    with pytest.raises(ValueError, match="gate"):
+        rn.rn_groupnorm_gate(v, gate=torch.zeros(1, 2, 8, 32, dtype=torch.bfloat16, device="meta"))
+    with pytest.raises(ValueError, match="gn_weight"):
+        rn.rn_groupnorm_gate(v, weight=torch.ones(63))

@@ -1,21 +1,21 @@
 """GPU parity of the chunkwise backward (rn_retention_chunkwise_backward) against the
 gradient oracle (oracle/backward.py, pinned by finite differences of the forward oracle).
 
-Tolerances:
+Tolerances (about five times the largest error measured):
   * float32 inputs: the products run in float32; per (b, h),
-    ||gpu - ref||_inf <= 1e-4 ||ref||_inf.
+    ||gpu - ref||_inf <= 5e-6 ||ref||_inf (measured at most 8.9e-7).
   * bf16 inputs: the tile products run on matrix cores with their operands rounded to IEEE
     half (relative 2^-11) and float32 accumulation, as the forward's matrix-core paths do;
-    a gradient element is a signed sum of many such terms, so the bar is the forward's
-    raw-output bar, 1e-2 of the slice maximum, plus half a bf16 ulp of the reference for
-    the bf16 store: |gpu - ref| <= 1e-2 ||ref||_inf + 2^-8 |ref|. (The state scans stay in
-    float32.)
+    a gradient element is a signed sum of many such terms, plus half a bf16 ulp of the
+    reference for the bf16 store: |gpu - ref| <= 1e-2 ||ref||_inf + 2^-8 |ref| (measured
+    at most 0.26 of that bound). (The state scans stay in float32.)
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
+from errlog import record
 import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -31,14 +31,16 @@ def dev(x):
     return None if x is None else x.to(DEV)
 
 
-def close(gpu, ref, bf16=False, rel=1e-4):
+def close(gpu, ref, bf16=False, rel=5e-6):
     g, r = O.to64(gpu), O.to64(ref)
     lead = r.shape[:2] if r.ndim >= 3 else (1,)
     nrm = np.abs(r).reshape(*lead, -1).max(-1).reshape(*lead, *([1] * (r.ndim - len(lead))))
     bound = rel * np.maximum(nrm, 1e-30)
     if bf16:
         bound = bound + np.abs(r) * 2.0 ** -8
-    return float((np.abs(g - r) / bound).max())
+    e = float((np.abs(g - r) / bound).max())
+    record(f"bw_ratio_at_{rel:g}", e)
+    return e
 
 
 def make(dtype, B, H, N, dk, dv, seed, gate=False, state=False):

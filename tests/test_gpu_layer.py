@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import oracle as O
+from errlog import record
 import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -37,8 +38,10 @@ def check(out, ref):
         bound = 2e-2 * np.abs(ref[b]).max()
         if out.dtype == torch.bfloat16:
             err = err - np.abs(ref[b]) * 2.0 ** -9
+        record("layer_max", err.max() / np.abs(ref[b]).max())
         assert err.max() <= bound, (b, float(err.max() / bound))
         rms = np.sqrt(((g[b] - ref[b]) ** 2).mean())
+        record("layer_rms", rms / np.sqrt((ref[b] ** 2).mean()))
         assert rms <= 1e-2 * np.sqrt((ref[b] ** 2).mean()), (b, rms)
 
 

@@ -1,19 +1,24 @@
 """GPU parity of the MFMA parallel form (bf16 q/k/v, d_k = 256, d_v = 512).
 
-Tolerances (half-precision MFMA operands, fp32 accumulation): raw outputs per (b, h)
-||gpu - ref||_inf <= 1e-2 ||ref||_inf (Qh, Kh, V and the decayed scores are rounded to
-half, relative 2^-11 each); after GroupNorm (fp32 output) max-abs 2e-2, with the gate
-2e-2 * max(1, |swish(g)|); bf16 output adds half a bf16 ulp of the reference.
+Tolerances (half-precision MFMA operands, fp32 accumulation), about five times the
+largest error measured: raw outputs per (b, h) ||gpu - ref||_inf <= MFMA_BAR ||ref||_inf
+(Qh, Kh, V and the decayed scores are rounded to half, relative 2^-11 each; measured at
+most 5.4e-4); after GroupNorm (fp32 output) max-abs GN_BAR, with the gate GN_BAR *
+max(1, |swish(g)|) (measured at most 2.2e-4, all 64 heads of the 1.3B shape); bf16
+output adds half a bf16 ulp of the reference.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
+from errlog import record
 import workloads as W
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+MFMA_BAR = 3e-3
+GN_BAR = 1e-3
 
 
 def rn():
@@ -25,7 +30,9 @@ def rel_inf(gpu, ref):
     g, r = O.to64(gpu), O.to64(ref)
     err = np.abs(g - r).reshape(r.shape[0], r.shape[1], -1).max(-1)
     nrm = np.abs(r).reshape(r.shape[0], r.shape[1], -1).max(-1)
-    return float((err / np.maximum(nrm, 1e-30)).max())
+    e = float((err / np.maximum(nrm, 1e-30)).max())
+    record("rel", e)
+    return e
 
 
 def dev(x):
@@ -34,8 +41,10 @@ def dev(x):
 
 def check_gated(out, ref, gate):
     sw = np.abs(O.swish(gate)) if gate is not None else 1.0
-    bound = 2e-2 * np.maximum(1.0, sw)
+    bound = GN_BAR * np.maximum(1.0, sw)
     d = np.abs(O.to64(out) - ref)
+    record("gated", ((d - (np.abs(ref) * 2.0 ** -8 if out.dtype == torch.bfloat16 else 0.0))
+                     / np.maximum(1.0, sw)).max())
     if out.dtype == torch.bfloat16:
         bound = bound + np.abs(ref) * 2.0 ** -8
     assert (d <= bound).all(), float((d / bound).max())
@@ -57,7 +66,7 @@ def test_raw_output(N, pos0, alpha, nd, nr):
                                      out_dtype=torch.float32, pos0=pos0, qk_scale=alpha,
                                      norm_d=nd, norm_r=nr)
     ref = O.parallel(x["q"], x["k"], x["v"], x["gamma"], x["theta"], pos0, alpha, nd, nr)
-    assert rel_inf(out.cpu(), ref) <= 1e-2
+    assert rel_inf(out.cpu(), ref) <= MFMA_BAR
 
 
 def test_gn_gate_affine_and_bf16_out():
@@ -82,12 +91,12 @@ def test_matches_plain_kernel():
     a = rn().rn_retention_parallel(*args, out_dtype=torch.float32, qk_scale=0.5, norm_r=True)
     b = rn().rn_retention_parallel(*args, out_dtype=torch.float32, qk_scale=0.5, norm_r=True,
                                    force_generic=True)
-    assert rel_inf(a.cpu(), b.cpu()) <= 1e-2
+    assert rel_inf(a.cpu(), b.cpu()) <= MFMA_BAR
 
 
-def test_1p3b_shape_sampled_heads():
+def test_1p3b_shape_all_heads():
     """The 1.3B-shaped workload (B=8, H=8, N=2048, alpha = 1/16, D and R normalisation,
-    GroupNorm) in the launch configuration of the full call; three (b, h) checked in full."""
+    GroupNorm) in the launch configuration of the full call; all 64 (b, h) checked in full."""
     w = W.WORKLOADS["parallel_1p3b"]
     x = W.make_inputs(w)
     out = rn().rn_retention_parallel(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"],
@@ -95,8 +104,13 @@ def test_1p3b_shape_sampled_heads():
                                      norm_r=True, gn=True)
     out = out.cpu()
     assert torch.isfinite(out).all()
-    for b, h in ((0, 0), (7, 7), (3, 5)):
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        raw = O.parallel(x["q"][sl], x["k"][sl], x["v"][sl], x["gamma"][h:h + 1], x["theta"], 0,
-                         w.qk_scale, True, True)
-        check_gated(out[sl], O.group_norm(raw), None)
+    worst = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            raw = O.parallel(x["q"][sl], x["k"][sl], x["v"][sl], x["gamma"][h:h + 1], x["theta"], 0,
+                             w.qk_scale, True, True)
+            ref = O.group_norm(raw)
+            check_gated(out[sl], ref, None)
+            worst = max(worst, float(np.abs(O.to64(out[sl]) - ref).max()))
+    print(f"1.3B parallel shape: worst |out - ref| after GroupNorm {worst:.2e}")

@@ -1,21 +1,24 @@
 """GPU parity: the HIP kernels against the fp64 oracle on the same seeded inputs.
 
-Tolerances:
-  * float32 arithmetic paths: per (b, h) slice, ||gpu - ref||_inf <= 1e-4 ||ref||_inf
-    (raw outputs, GroupNorm outputs and final states alike).
-  * bf16 MFMA paths: 2e-2 max-abs after GroupNorm (fp32 output); raw outputs and
-    states at a relative bound derived from bf16 operand rounding (see each test).
+Tolerances (about five times the largest error measured over the GPU suite):
+  * float32 arithmetic paths (generic kernels, decode, GroupNorm): per (b, h) slice,
+    ||gpu - ref||_inf <= F32_BAR ||ref||_inf (raw outputs, GroupNorm outputs and final
+    states alike). Measured at most 1.0e-6 (the generic parallel kernel; the full decode
+    workload over 1024 steps: 6.8e-7 for outputs, 5.7e-7 for the final states).
+  * a bf16 output after GroupNorm: 2e-2 max-abs plus half a bf16 ulp of the reference.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
+from errlog import record
 import workloads as W
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
+F32_BAR = 5e-6
 
 
 def rn():
@@ -29,7 +32,9 @@ def rel_inf(gpu, ref):
     r = O.to64(ref)
     err = np.abs(g - r).reshape(r.shape[0], r.shape[1], -1).max(-1)
     nrm = np.abs(r).reshape(r.shape[0], r.shape[1], -1).max(-1)
-    return float((err / np.maximum(nrm, 1e-30)).max())
+    e = float((err / np.maximum(nrm, 1e-30)).max())
+    record("rel", e)
+    return e
 
 
 def dev(x):
@@ -51,7 +56,7 @@ def test_tiny_parallel_fp32(gn):
                                      gn=gn, gn_eps=w.gn_eps)
     ref = O.brute_force(x["q"], x["k"], x["v"], x["gamma"], x["theta"])
     ref = O.apply_epilogue(ref, gn=gn, eps=w.gn_eps)
-    assert rel_inf(out.cpu(), ref) <= 1e-4
+    assert rel_inf(out.cpu(), ref) <= F32_BAR
 
 
 @pytest.mark.parametrize("gn", [False, True])
@@ -62,8 +67,8 @@ def test_tiny_chunkwise_fp32(gn, chunk):
                                          x["theta"], chunk, state_out=True, gn=gn, gn_eps=w.gn_eps)
     ref = O.brute_force(x["q"], x["k"], x["v"], x["gamma"], x["theta"])
     _, Sref = O.recurrent(x["q"], x["k"], x["v"], x["gamma"], x["theta"])
-    assert rel_inf(out.cpu(), O.apply_epilogue(ref, gn=gn, eps=w.gn_eps)) <= 1e-4
-    assert rel_inf(S.cpu(), Sref) <= 1e-4
+    assert rel_inf(out.cpu(), O.apply_epilogue(ref, gn=gn, eps=w.gn_eps)) <= F32_BAR
+    assert rel_inf(S.cpu(), Sref) <= F32_BAR
 
 
 @pytest.mark.parametrize("gn", [False, True])
@@ -83,8 +88,8 @@ def test_tiny_recurrent_fp32(gn):
     out = torch.cat(outs, 2).cpu()
     ref = O.brute_force(x["q"], x["k"], x["v"], x["gamma"], x["theta"])
     _, Sref = O.recurrent(x["q"], x["k"], x["v"], x["gamma"], x["theta"])
-    assert rel_inf(out, O.apply_epilogue(ref, gn=gn, eps=w.gn_eps)) <= 1e-4
-    assert rel_inf(S.cpu(), Sref) <= 1e-4
+    assert rel_inf(out, O.apply_epilogue(ref, gn=gn, eps=w.gn_eps)) <= F32_BAR
+    assert rel_inf(S.cpu(), Sref) <= F32_BAR
 
 
 def test_tiny_parallel_rescaled_fp32():
@@ -96,11 +101,11 @@ def test_tiny_parallel_rescaled_fp32():
         out = rn().rn_retention_parallel(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
                                          x["theta"], qk_scale=a, norm_d=nd, norm_r=nr)
         ref = O.parallel(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 0, a, nd, nr)
-        assert rel_inf(out.cpu(), ref) <= 1e-4, (nd, nr)
+        assert rel_inf(out.cpu(), ref) <= F32_BAR, (nd, nr)
     out = rn().rn_retention_parallel(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"],
                                      qk_scale=a, norm_d=True, norm_r=True, gn=True)
     ref = O.group_norm(O.parallel(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 0, a, True, True))
-    assert rel_inf(out.cpu(), ref) <= 1e-4
+    assert rel_inf(out.cpu(), ref) <= F32_BAR
 
 
 def test_tiny_state_in_pos0_gate_affine_fp32():
@@ -118,8 +123,8 @@ def test_tiny_state_in_pos0_gate_affine_fp32():
                                          gn=True, gn_weight=dev(gw), gn_bias=dev(gb))
     raw, Sref = O.chunkwise(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 7, pos0, 1.0, x["state"])
     ref = O.groupnorm_gate(raw, x["gate"], 1e-5, gw.reshape(H, dv), gb.reshape(H, dv))
-    assert rel_inf(out.cpu(), ref) <= 1e-4
-    assert rel_inf(S.cpu(), Sref) <= 1e-4
+    assert rel_inf(out.cpu(), ref) <= F32_BAR
+    assert rel_inf(S.cpu(), Sref) <= F32_BAR
 
 
 # ---- decode step ---------------------------------------------------------------------
@@ -138,29 +143,50 @@ def test_decode_steps_match_oracle(dtype):
         out = rn().rn_retention_recurrent_step(dev(x["q"]), dev(x["k"]), dev(x["v"]), w.gamma(),
                                                w.theta(), S, pos, out_dtype=torch.float32)
         o_ref, Sref = O.recurrent_step(x["q"], x["k"], x["v"], w.gamma(), w.theta(), pos, 1.0, Sref)
-        assert rel_inf(out.cpu()[:, :, 0], o_ref) <= 1e-4
-    assert rel_inf(S.cpu(), Sref) <= 1e-4
+        assert rel_inf(out.cpu()[:, :, 0], o_ref) <= F32_BAR
+    assert rel_inf(S.cpu(), Sref) <= F32_BAR
 
 
-def test_decode_full_batch_sampled():
-    """Full decode shape (batch 128, 16 heads, 256 x 512 state): one step, checked on 16
-    sampled (b, h) pairs, in the launch configuration the benchmark uses."""
+def test_decode_1024_steps_full_shape():
+    """The full decode workload in the benchmark's launch configuration: batch 128, 16
+    heads, 256 x 512 float32 states updated in place over 1024 steps at positions 0..1023.
+    After the first step every (b, h) output and state is checked; at every step, the
+    outputs of 16 sampled (b, h), whose states the oracle carries along in float64; after
+    the last step, those 16 states."""
     w = W.WORKLOADS["decode_6p7b"]
+    g, th = w.gamma(), w.theta()
     S0 = W.initial_state(w)
     S = dev(S0)
-    x = W.make_decode_step_inputs(w, 0)
-    out = rn().rn_retention_recurrent_step(dev(x["q"]), dev(x["k"]), dev(x["v"]), w.gamma(),
-                                           w.theta(), S, 0, out_dtype=torch.float32)
-    torch.cuda.synchronize()
     rng = np.random.default_rng(0)
-    pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, 128, 16), rng.integers(0, 16, 16))]
-    Sg = S.cpu()
-    for b, h in pairs:
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        o_ref, s_ref = O.recurrent_step(x["q"][sl], x["k"][sl], x["v"][sl], w.gamma()[h:h + 1],
-                                        w.theta(), 0, 1.0, S0[sl])
-        assert rel_inf(out.cpu()[sl][:, :, 0], o_ref) <= 1e-4
-        assert rel_inf(Sg[sl], s_ref) <= 1e-4
+    bs = rng.choice(w.B, 16, replace=False)
+    hs = rng.integers(0, w.H, 16)
+    bi, hi = torch.as_tensor(bs, device=DEV), torch.as_tensor(hs, device=DEV)
+    Sref = [S0[b:b + 1, h:h + 1] for b, h in zip(bs, hs)]
+    worst_o = 0.0
+    for i in range(w.steps):
+        x = W.make_decode_step_inputs(w, i)
+        out = rn().rn_retention_recurrent_step(dev(x["q"]), dev(x["k"]), dev(x["v"]), g, th, S, i,
+                                               out_dtype=torch.float32)
+        osel = out[bi, hi].cpu()                      # [16, 1, d_v]
+        if i == 0:
+            oall, Sall = out.cpu(), S.cpu()
+            for b0 in range(0, w.B, 16):
+                sl = (slice(b0, b0 + 16),)
+                o_ref, s_ref = O.recurrent_step(x["q"][sl], x["k"][sl], x["v"][sl], g, th, 0, 1.0,
+                                                S0[sl])
+                assert rel_inf(oall[sl][:, :, 0], o_ref) <= F32_BAR, b0
+                assert rel_inf(Sall[sl], s_ref) <= F32_BAR, b0
+            del oall, Sall
+        for j, (b, h) in enumerate(zip(bs, hs)):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            o_ref, Sref[j] = O.recurrent_step(x["q"][sl], x["k"][sl], x["v"][sl], g[h:h + 1], th, i,
+                                              1.0, Sref[j])
+            worst_o = max(worst_o, rel_inf(osel[j:j + 1], o_ref))
+        assert worst_o <= F32_BAR, (i, worst_o)
+    Sfin = S[bi, hi].cpu()                            # [16, d_k, d_v]
+    worst_s = max(rel_inf(Sfin[j][None, None], Sref[j]) for j in range(16))
+    print(f"decode 1024 steps: worst output {worst_o:.2e}, worst final state {worst_s:.2e}")
+    assert worst_s <= F32_BAR
 
 
 @pytest.mark.parametrize("dk,dv", [(256, 256), (128, 128), (64, 256), (48, 512), (256, 384)])
@@ -177,8 +203,8 @@ def test_decode_other_shapes(dk, dv):
         out = rn().rn_retention_recurrent_step(dev(x["q"]), dev(x["k"]), dev(x["v"]), w.gamma(),
                                                w.theta(), S, 100 + i, out_dtype=torch.float32)
         o_ref, Sref = O.recurrent_step(x["q"], x["k"], x["v"], w.gamma(), w.theta(), 100 + i, 1.0, Sref)
-        assert rel_inf(out.cpu()[:, :, 0], o_ref) <= 1e-4
-    assert rel_inf(S.cpu(), Sref) <= 1e-4
+        assert rel_inf(out.cpu()[:, :, 0], o_ref) <= F32_BAR
+    assert rel_inf(S.cpu(), Sref) <= F32_BAR
 
 
 def test_decode_gn_gate_bf16_out():
@@ -208,9 +234,9 @@ def test_groupnorm_gate(dt, dv):
     b = torch.randn(3 * dv, generator=gen)
     out = rn().rn_groupnorm_gate(dev(x), dev(g), dev(w), dev(b), 1e-5, out_dtype=torch.float32)
     ref = O.groupnorm_gate(x, g, 1e-5, w.reshape(3, dv), b.reshape(3, dv))
-    assert rel_inf(out.cpu(), ref) <= 1e-4
+    assert rel_inf(out.cpu(), ref) <= F32_BAR
     out2 = rn().rn_groupnorm_gate(dev(x), None, None, None, 1e-5, out_dtype=torch.float32)
-    assert rel_inf(out2.cpu(), O.group_norm(x, 1e-5)) <= 1e-4
+    assert rel_inf(out2.cpu(), O.group_norm(x, 1e-5)) <= F32_BAR
 
 
 # ---- generic path with bf16 inputs ---------------------------------------------------
@@ -223,8 +249,8 @@ def test_generic_bf16_inputs_fp32_accuracy():
                                          x["theta"], 8, state_out=True, out_dtype=torch.float32,
                                          pos0=3, force_generic=True)
     ref, Sref = O.chunkwise(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 8, 3)
-    assert rel_inf(out.cpu(), ref) <= 1e-4
-    assert rel_inf(S.cpu(), Sref) <= 1e-4
+    assert rel_inf(out.cpu(), ref) <= F32_BAR
+    assert rel_inf(S.cpu(), Sref) <= F32_BAR
     out = rn().rn_retention_parallel(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"],
                                      out_dtype=torch.float32, pos0=3, force_generic=True)
-    assert rel_inf(out.cpu(), O.parallel(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 3)) <= 1e-4
+    assert rel_inf(out.cpu(), O.parallel(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 3)) <= F32_BAR

@@ -6,20 +6,24 @@ own positions, no padding.
 
 Tolerances are those of the other GPU parity files:
   * decode and the generic chunkwise kernel (float32 arithmetic): per (b, h),
-    ||gpu - ref||_inf <= 1e-4 ||ref||_inf;
-  * fused MFMA chunkwise kernel (half operands): raw outputs and states at 1e-2 of the
-    slice maximum; after GroupNorm, 2e-2 * max(1, |swish(gate)|) max-abs. A decode step
-    that continues from an MFMA-made state inherits that state's 1e-2 bound.
+    ||gpu - ref||_inf <= F32_BAR ||ref||_inf;
+  * fused MFMA chunkwise kernel (half operands): raw outputs and states at MFMA_BAR of the
+    slice maximum (measured at most 3.9e-4 here); after GroupNorm, 2e-2 * max(1,
+    |swish(gate)|) max-abs (measured 2.0e-3). A decode step that continues from an
+    MFMA-made state inherits that state's MFMA_BAR bound.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
+from errlog import record
 import workloads as W
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+F32_BAR = 5e-6
+MFMA_BAR = 3e-3
 SENTINEL = 1234.5   # value of padded output rows before the call; must survive it
 
 
@@ -32,7 +36,9 @@ def rel_inf(gpu, ref):
     g, r = O.to64(gpu), O.to64(ref)
     err = np.abs(g - r).reshape(r.shape[0], r.shape[1], -1).max(-1)
     nrm = np.abs(r).reshape(r.shape[0], r.shape[1], -1).max(-1)
-    return float((err / np.maximum(nrm, 1e-30)).max())
+    e = float((err / np.maximum(nrm, 1e-30)).max())
+    record("rel", e)
+    return e
 
 
 def dev(x):
@@ -55,6 +61,7 @@ def check_gated(out, ref, gate):
     sw = np.abs(O.swish(gate)) if gate is not None else 1.0
     bound = 2e-2 * np.maximum(1.0, sw)
     d = np.abs(O.to64(out) - ref)
+    record("gated", (d / np.maximum(1.0, sw)).max())
     assert (d <= bound).all(), float((d / bound).max())
 
 
@@ -79,11 +86,11 @@ def test_decode_step_at_per_sequence_positions(dk, dv):
         for b in range(4):
             o_ref, Sref[b] = O.recurrent_step(x["q"][b:b + 1], x["k"][b:b + 1], x["v"][b:b + 1],
                                               w.gamma(), w.theta(), p0[b] + i, 1.0, Sref[b])
-            assert rel_inf(out[b:b + 1, :, 0], o_ref) <= 1e-4, (b, i)
+            assert rel_inf(out[b:b + 1, :, 0], o_ref) <= F32_BAR, (b, i)
         pos += 1   # the positions advance on the device
     Sg = S.cpu()
     for b in range(4):
-        assert rel_inf(Sg[b:b + 1], Sref[b]) <= 1e-4
+        assert rel_inf(Sg[b:b + 1], Sref[b]) <= F32_BAR
 
 
 def test_decode_step_at_equal_positions_is_the_plain_step():
@@ -127,7 +134,7 @@ def test_chunkwise_varlen_outputs_and_states(lengths, pos, path):
                                               chunk_parallel=path == "pair",
                                               segmented=path == "segmented")
     out, S = out.cpu(), S.cpu()
-    tol = 1e-4 if path == "generic" else 1e-2
+    tol = F32_BAR if path == "generic" else MFMA_BAR
     for b, (L, p) in enumerate(zip(lengths, pos)):
         sb = slice(b, b + 1)
         assert (out[sb, :, L:] == SENTINEL).all(), f"padded rows of sequence {b} written"
@@ -201,4 +208,4 @@ def test_prefill_then_decode_matches_recurrent_oracle():
                for n in ("q", "k", "v")}
         ref, _ = O.recurrent(cat["q"], cat["k"], cat["v"], x["gamma"], x["theta"], p)
         for i, (_, o) in enumerate(steps):
-            assert rel_inf(o[b:b + 1, :, 0], ref[:, :, L + i]) <= 1e-2, (b, i)
+            assert rel_inf(o[b:b + 1, :, 0], ref[:, :, L + i]) <= MFMA_BAR, (b, i)

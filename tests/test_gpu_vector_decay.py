@@ -5,13 +5,13 @@ Paths: the chunk-parallel MFMA pair (bf16 q/k/v, d_k 256, d_v 512; the decays fo
 the half operands per coordinate, the score tiles among a workgroup's own rows as bf16
 high/low parts), the generic float32 kernels, and the decode kernels.
 
-Tolerances, as for the per-head decay paths:
-  * MFMA pair: raw outputs and final states per (b, h) ||gpu - ref||_inf <= 1e-2
-    ||ref||_inf (operands rounded to half, relative 2^-11, summed over many terms; inside
+Tolerances, as for the per-head decay paths (about five times the largest measured error):
+  * MFMA pair: raw outputs and final states per (b, h) ||gpu - ref||_inf <= MFMA_BAR
+    ||ref||_inf (measured at most 6.8e-4; operands rounded to half, relative 2^-11, summed over many terms; inside
     the diagonal score tiles a decay below 2^-13 is taken as 2^-13, which moves a score
     term by less than 2^-13 of its undecayed size); after GroupNorm max-abs 2e-2, times
-    max(1, |swish(g)|) with the gate, plus half a bf16 ulp for bf16 output.
-  * float32 kernels (generic, decode): 1e-4 relative per (b, h).
+    max(1, |swish(g)|) with the gate, plus half a bf16 ulp for bf16 output (measured 2.6e-3).
+  * float32 kernels (generic, decode): F32_BAR relative per (b, h) (measured 1.0e-6).
 Decays: "pair_spread" draws them log-uniformly from 0.99999 down to 4.5e-5 with one pair
 at 1e-6 and one at exactly 1, so every fold limit is crossed; "pair_wide" is the
 RetNet-like range used at the 6.7B shape.
@@ -21,10 +21,13 @@ import pytest
 import torch
 
 import oracle as O
+from errlog import record
 import workloads as W
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+F32_BAR = 5e-6
+MFMA_BAR = 3e-3
 
 
 def rn():
@@ -36,7 +39,9 @@ def rel_inf(gpu, ref):
     g, r = O.to64(gpu), O.to64(ref)
     err = np.abs(g - r).reshape(r.shape[0], r.shape[1], -1).max(-1)
     nrm = np.abs(r).reshape(r.shape[0], r.shape[1], -1).max(-1)
-    return float((err / np.maximum(nrm, 1e-30)).max())
+    e = float((err / np.maximum(nrm, 1e-30)).max())
+    record("rel", e)
+    return e
 
 
 def dev(x):
@@ -58,6 +63,8 @@ def check_gated(out, ref, gate):
     sw = np.abs(O.swish(gate)) if gate is not None else 1.0
     bound = 2e-2 * np.maximum(1.0, sw)
     d = np.abs(O.to64(out) - ref)
+    record("gated", ((d - (np.abs(ref) * 2.0 ** -8 if out.dtype == torch.bfloat16 else 0.0))
+                     / np.maximum(1.0, sw)).max())
     if out.dtype == torch.bfloat16:
         bound = bound + np.abs(ref) * 2.0 ** -8
     assert (d <= bound).all(), float((d / bound).max())
@@ -74,8 +81,8 @@ def test_mfma_pair_raw_output_and_state(N, pos0, kind):
                                          out_dtype=torch.float32, pos0=pos0)
     ref, Sref = O.chunkwise_vec(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 64, pos0, 1.0,
                                 x["state"])
-    assert rel_inf(out.cpu(), ref) <= 1e-2
-    assert rel_inf(S.cpu(), Sref) <= 1e-2
+    assert rel_inf(out.cpu(), ref) <= MFMA_BAR
+    assert rel_inf(S.cpu(), Sref) <= MFMA_BAR
 
 
 def test_mfma_pair_gn_gate_affine_fp32_and_bf16_out():
@@ -104,8 +111,8 @@ def test_mfma_pair_equal_decays_match_the_per_head_path():
                                         x["theta"], 256, state_out=True, out_dtype=torch.float32)
     b, Sb = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"],
                                         x["theta"], 256, state_out=True, out_dtype=torch.float32)
-    assert rel_inf(a.cpu(), b.cpu()) <= 1e-2
-    assert rel_inf(Sa.cpu(), Sb.cpu()) <= 1e-2
+    assert rel_inf(a.cpu(), b.cpu()) <= MFMA_BAR
+    assert rel_inf(Sa.cpu(), Sb.cpu()) <= MFMA_BAR
 
 
 def test_mfma_pair_varlen_batch():
@@ -125,8 +132,8 @@ def test_mfma_pair_varlen_batch():
         sl = (slice(b, b + 1), slice(None), slice(0, L))
         ref, Sref = O.chunkwise_vec(x["q"][sl], x["k"][sl], x["v"][sl], x["gamma"], x["theta"],
                                     256, p0)
-        assert rel_inf(out[sl], ref) <= 1e-2, b
-        assert rel_inf(S[b:b + 1], Sref) <= 1e-2, b
+        assert rel_inf(out[sl], ref) <= MFMA_BAR, b
+        assert rel_inf(S[b:b + 1], Sref) <= MFMA_BAR, b
         assert (out[b, :, L:] == 0).all()
 
 
@@ -140,8 +147,8 @@ def test_generic_fp32_chunkwise(chunk, gn):
                                          state_out=True, gn=gn, pos0=9, qk_scale=0.7)
     ref, Sref = O.chunkwise_vec(x["q"], x["k"], x["v"], x["gamma"], x["theta"], chunk, 9, 0.7,
                                 x["state"])
-    assert rel_inf(out.cpu(), O.apply_epilogue(ref, gn=gn)) <= 1e-4
-    assert rel_inf(S.cpu(), Sref) <= 1e-4
+    assert rel_inf(out.cpu(), O.apply_epilogue(ref, gn=gn)) <= F32_BAR
+    assert rel_inf(S.cpu(), Sref) <= F32_BAR
 
 
 def test_generic_chunkwise_bf16_other_shape():
@@ -151,8 +158,8 @@ def test_generic_chunkwise_bf16_other_shape():
     out, S = rn().rn_retention_chunkwise(dev(x["q"]), dev(x["k"]), dev(x["v"]), gdev(x["gamma"]),
                                          x["theta"], 32, state_out=True, out_dtype=torch.float32)
     ref, Sref = O.chunkwise_vec(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 32)
-    assert rel_inf(out.cpu(), ref) <= 1e-4
-    assert rel_inf(S.cpu(), Sref) <= 1e-4
+    assert rel_inf(out.cpu(), ref) <= F32_BAR
+    assert rel_inf(S.cpu(), Sref) <= F32_BAR
 
 
 @pytest.mark.parametrize("norm_r", [False, True])
@@ -162,7 +169,7 @@ def test_generic_fp32_parallel(norm_r):
     out = rn().rn_retention_parallel(dev(x["q"]), dev(x["k"]), dev(x["v"]), gdev(x["gamma"]),
                                      x["theta"], norm_r=norm_r, qk_scale=0.5, pos0=3)
     ref = O.parallel_vec(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 3, 0.5, norm_r=norm_r)
-    assert rel_inf(out.cpu(), ref) <= 1e-4
+    assert rel_inf(out.cpu(), ref) <= F32_BAR
 
 
 @pytest.mark.parametrize("shape", [(256, 512, "bf16"), (16, 20, "f32"), (64, 128, "bf16")])
@@ -179,8 +186,8 @@ def test_decode_steps(shape):
                                                out_dtype=torch.float32)
         o_ref, Sref = O.recurrent_step_vec(y["q"], y["k"], y["v"], x["gamma"], x["theta"], 77 + st,
                                            1.0, Sref)
-        assert rel_inf(out.cpu()[:, :, 0], o_ref) <= 1e-4, st
-    assert rel_inf(S.cpu(), Sref) <= 1e-4
+        assert rel_inf(out.cpu()[:, :, 0], o_ref) <= F32_BAR, st
+    assert rel_inf(S.cpu(), Sref) <= F32_BAR
 
 
 def test_prefill_then_decode():
@@ -204,8 +211,8 @@ def test_prefill_then_decode():
     ka = torch.cat([x["k"], y["k"]], 2)
     va = torch.cat([x["v"], y["v"]], 2)
     ref, Sref = O.recurrent_vec(qa, ka, va, x["gamma"], x["theta"])
-    assert rel_inf(torch.cat(outs, 2), ref[:, :, 300:]) <= 1e-2
-    assert rel_inf(S.cpu(), Sref) <= 1e-2
+    assert rel_inf(torch.cat(outs, 2), ref[:, :, 300:]) <= MFMA_BAR
+    assert rel_inf(S.cpu(), Sref) <= MFMA_BAR
 
 
 def test_full_6p7b_pair_shape_sampled_heads():
@@ -225,4 +232,4 @@ def test_full_6p7b_pair_shape_sampled_heads():
                                     x["theta"])
         ref = O.groupnorm_gate(raw, x["gate"][sl], w.gn_eps)
         check_gated(out[sl], ref, x["gate"][sl])
-        assert rel_inf(S[sl], Sref) <= 1e-2, (b, h)
+        assert rel_inf(S[sl], Sref) <= MFMA_BAR, (b, h)
