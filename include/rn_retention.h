@@ -182,6 +182,25 @@ rn_status rn_retention_chunkwise(const rn_desc* desc, int32_t chunk, const void*
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * rn_retention_chunkwise without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the workspace is a 32 MiB buffer the library keeps in device memory, one per
+ * GPU, from the first call on that GPU until the process ends. The call allocates nothing.
+ * Arguments, routing and results are those of rn_retention_chunkwise (chunkwise equation
+ * of the hwhale notes, as above); a call whose rn_chunkwise_workspace_bytes exceeds 32 MiB
+ * is rejected with RN_ERR_UNSUPPORTED before any launch (the default sequential kernel
+ * with d_v = 512 needs at most 17 MiB, for any number of heads).
+ * Every call on one GPU shares its buffer: calls that overlap on one GPU (on different
+ * streams, or from several threads without ordering) race and their results are
+ * undefined; calls ordered on one stream are safe. The buffer keeps the last call's
+ * contents; the kernels clear what must start at zero themselves.
+ */
+rn_status rn_retention_chunkwise_noalloc(const rn_desc* desc, int32_t chunk, const void* q,
+                                         const void* k, const void* v, const void* gate,
+                                         const float* state_in, float* state_out, void* out,
+                                         void* stream);
+
+/*
  * Chunkwise form over a padded batch of sequences that start at positions of their own
  * and hold numbers of tokens of their own: the prompt (prefill) half of serving, whose
  * state_out the decode steps below continue from. (eepw translation, "inference cost"

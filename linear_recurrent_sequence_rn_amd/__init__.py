@@ -28,6 +28,7 @@ __all__ = [
     "rn_retention_chunkwise_varlen", "rn_retention_recurrent_step_at", "rn_groupnorm_gate",
     "rn_retention_chunkwise_backward", "rn_chunkwise_backward_workspace_bytes", "rn_chunkwise_workspace_bytes", "rn_parallel_workspace_bytes",
     "rn_version", "make_desc", "rn_msr_layer_forward", "rn_msr_layer_workspace_bytes",
+    "rn_retention_chunkwise_noalloc",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "librn_retention.so"
@@ -47,6 +48,7 @@ EXPORTED_SYMBOLS = (
     "rn_retention_recurrent_step_at", "rn_groupnorm_gate", "rn_status_str", "rn_last_error",
     "rn_version", "rn_retention_chunkwise_backward", "rn_chunkwise_backward_workspace_bytes",
     "rn_msr_layer_workspace_bytes", "rn_msr_layer_forward", "rn_chunkwise_check",
+    "rn_retention_chunkwise_noalloc",
 )
 
 
@@ -100,6 +102,8 @@ def _load():
     L.rn_msr_layer_forward.restype = i32
     L.rn_chunkwise_check.argtypes = [D, i32, vp, sz, vp]
     L.rn_chunkwise_check.restype = i32
+    L.rn_retention_chunkwise_noalloc.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.rn_retention_chunkwise_noalloc.restype = i32
     L.rn_groupnorm_gate.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                     ctypes.c_float, vp, vp]
     L.rn_groupnorm_gate.restype = i32
@@ -360,6 +364,33 @@ def _chunkwise(q, k, v, gamma, theta, chunk, pos, lengths, gate, state_in, state
         _check(lib.rn_retention_chunkwise_varlen(
             ctypes.byref(d), chunk, _seq_array(pos, B, torch.int64, "pos"),
             _seq_array(lengths, B, torch.int32, "lengths"), *args))
+    return out, state_out
+
+
+def rn_retention_chunkwise_noalloc(q, k, v, gamma, theta, chunk, *, gate=None, state_in=None,
+                                   state_out=None, out=None, out_dtype=None, pos0=0,
+                                   qk_scale=1.0, gn=False, gn_eps=1e-5, gn_weight=None,
+                                   gn_bias=None, force_generic=False, chunk_parallel=False,
+                                   segmented=False):
+    """rn_retention_chunkwise with the library's own device workspace (the C call allocates
+    nothing; pass ``out`` and a ``state_out`` tensor to keep this wrapper from allocating
+    them). Returns (out, state_out)."""
+    flags = _flags(False, False, gn, gate, force_generic, chunk_parallel, segmented)
+    d, keep, od = _qkv_desc(q, k, v, gamma, theta, out_dtype, flags, pos0, qk_scale, gn_eps,
+                            gn_weight, gn_bias, gate)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    out = _out(out, v.shape, od, v.device)
+    if state_out is True:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif state_out is False:
+        state_out = None
+    for s in (state_in, state_out):
+        if s is not None and (s.dtype != torch.float32 or tuple(s.shape) != (B, H, dk, dv)):
+            raise ValueError("states must be float32 [B,H,d_k,d_v]")
+    _check(lib.rn_retention_chunkwise_noalloc(ctypes.byref(d), chunk, _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(gate), _ptr(state_in), _ptr(state_out),
+                                              _ptr(out), _stream(q)))
     return out, state_out
 
 

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "rn_kernels.h"
 #include "rn_retention.h"
@@ -252,6 +253,64 @@ rn_status rn_retention_chunkwise(const rn_desc* desc, int32_t chunk, const void*
                                  size_t workspace_bytes, void* stream) {
   return chunkwise_call(desc, chunk, nullptr, nullptr, q, k, v, gate, state_in, state_out, out,
                         workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- chunkwise form without allocation --------------------------------------------------
+// A workspace the library holds in device memory, for callers that cannot allocate. Each
+// GPU the library runs on holds its own copy of the array until the process ends; host
+// code reaches it only through the address hipGetSymbolAddress returns for the current
+// device (the array's name on the host is not a device address).
+namespace {
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's scratch array, looked up once per device.
+rn_status scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RN_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(RN_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return RN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+rn_status rn_retention_chunkwise_noalloc(const rn_desc* desc, int32_t chunk, const void* q,
+                                         const void* k, const void* v, const void* gate,
+                                         const float* state_in, float* state_out, void* out,
+                                         void* stream) {
+  rn::CallArgs a;
+  rn_status s = check_desc(desc, Form::kChunkwise, &a);
+  if (s != RN_OK) return s;
+  if (chunk < 1) return fail(RN_ERR_INVALID_ARG, "chunk=%d must be >= 1", chunk);
+  const size_t need = rn_chunkwise_workspace_bytes(desc, chunk);
+  if (need > kScratchBytes)
+    return fail(RN_ERR_UNSUPPORTED, "this call needs %zu bytes of workspace; the library's "
+                "buffer for calls without allocation holds %zu", need, kScratchBytes);
+  void* ws = nullptr;
+  if ((s = scratch_for_current_device(&ws)) != RN_OK) return s;
+  return chunkwise_call(desc, chunk, nullptr, nullptr, q, k, v, gate, state_in, state_out,
+                        out, ws, kScratchBytes, stream);
 }
 
 rn_status rn_chunkwise_check(const rn_desc* desc, int32_t chunk, const void* workspace,

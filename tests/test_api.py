@@ -398,3 +398,18 @@ def test_binding_checks_gate_and_affine():
         rn.rn_groupnorm_gate(v, gate=torch.zeros(1, 2, 8, 32, dtype=torch.bfloat16, device="meta"))
     with pytest.raises(ValueError, match="gn_weight"):
         rn.rn_groupnorm_gate(v, weight=torch.ones(63))
+
+
+def test_noalloc_entry_point_validates_first():
+    """The call without allocation validates like rn_retention_chunkwise and rejects a
+    workspace beyond its 32 MiB buffer before any HIP call."""
+    f = rn.lib.rn_retention_chunkwise_noalloc
+    d, keep = desc(N=0)
+    assert f(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None) == rn.RN_ERR_INVALID_ARG
+    d, keep = desc()
+    assert f(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None) == rn.RN_ERR_INVALID_ARG
+    big = dict(d_k=256, d_v=256, theta=np.ones(128), H=16, gamma=np.full(16, 0.99), B=4, N=64)
+    d, keep = desc(**big)
+    assert rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(d), 64) > 32 << 20
+    assert f(ctypes.byref(d), 64, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None) == rn.RN_ERR_UNSUPPORTED
+    assert b"workspace" in rn.lib.rn_last_error()
