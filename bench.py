@@ -70,14 +70,14 @@ def profiled_traffic():
     return traffic
 
 
-def chunkwise_work(B, H, N, dk, dv, C):
+def chunkwise_work(B, H, N, dk, dv, C, gate=True):
     """Algorithmic flops and compulsory HBM bytes of one chunkwise forward with
-    GroupNorm + gate: causal intra-chunk pairs (C+1)(dk+dv) per token, cross term and
-    state carry 2*dk*dv each per token; bytes: q, k, v, gate read, out written (bf16),
-    final state written (fp32)."""
+    GroupNorm (+ gate): causal intra-chunk pairs (C+1)(dk+dv) per token, cross term and
+    state carry 2*dk*dv each per token; bytes: q, k, v (and gate) read, out written
+    (bf16), final state written (fp32)."""
     th = B * H * N
     flops = th * ((C + 1) * (dk + dv) + 4 * dk * dv)
-    bytes_ = th * 2 * (dk + dk + dv + dv + dv) + B * H * dk * dv * 4
+    bytes_ = th * 2 * (dk + dk + dv + (dv if gate else 0) + dv) + B * H * dk * dv * 4
     return flops, bytes_
 
 
@@ -110,8 +110,9 @@ def main():
     ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--source-hash", action="store_true",
                     help="print the chunkwise kernel's source hash (as recorded in its profile) and exit")
+    ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "backward", "pair", "layer",
-                                       "copy"],
+                                       "long", "copy"],
                     default=None,
                     help="run one workload only (for profiling); 'copy' times a plain 1 GiB "
                          "device copy, the reference for the HBM byte counters")
@@ -148,7 +149,7 @@ def main():
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "copy_GBs": 2 * src.numel() * 4 / dt / 1e9}))
         return
-    if args.only in ("decode", "parallel", "backward", "pair", "layer"):
+    if args.only in ("decode", "parallel", "backward", "pair", "layer", "long"):
         args.no_cpu_baseline = True
     w = W.WORKLOADS["chunkwise_6p7b"]
     x = W.make_inputs(w)
@@ -163,8 +164,10 @@ def main():
         rn.rn_retention_chunkwise(q, k, v, gamma, theta, w.chunk, gate=gate, gn=True,
                                   gn_eps=w.gn_eps, state_out=S_out, out=out, workspace=ws)
 
-    if args.only in ("decode", "parallel", "backward", "pair", "layer"):
+    if args.only in ("decode", "parallel", "backward", "pair", "layer", "long"):
         args.steps = args.warmup = 1
+    if args.only is not None and args.only != "long":
+        args.no_long = True
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -208,7 +211,7 @@ def main():
                      "frac": gbs / HBM_PEAK_GBS, "traffic": profiled_traffic(),
                      "kernel": "chunkwise_fused", "kernel_ms": kern_s * 1e3,
                      "algorithmic_bytes": bytes_, "algorithmic_flops": flops,
-                     "mfma_tflops": tfl, "mfma_frac": tfl / BF16_PEAK_TFLOPS},
+                     "effective_tflops": tfl, "effective_mfma_frac": tfl / BF16_PEAK_TFLOPS},
     }
 
     # ---- the other chunkwise schedules on the same workload (secondary record) ------------
@@ -246,7 +249,7 @@ def main():
     # tile products on matrix cores (f16 operands), the state scans in float32.
     # Algorithmic flops: twice the forward's (each product of the forward has two gradient
     # products of the same size).
-    if args.only in ("chunkwise", "decode", "parallel", "pair", "layer"):
+    if args.only in ("chunkwise", "decode", "parallel", "pair", "layer", "long"):
         args.no_backward = True
     if not args.no_backward:
         dout = torch.randn(v.shape, generator=torch.Generator(device=dev).manual_seed(5),
@@ -285,7 +288,7 @@ def main():
     # Chunk-parallel pair of kernels (state snapshots, then outputs) with the decays
     # folded into the operands per coordinate; same algorithmic bytes and flops as the
     # per-head-decay forward.
-    if args.only in ("chunkwise", "decode", "parallel", "layer"):
+    if args.only in ("chunkwise", "decode", "parallel", "layer", "long"):
         args.no_pair = True
     if args.only == "pair":
         args.no_parallel = True
@@ -330,7 +333,7 @@ def main():
     # x [2, 8192, 4096] -> projections (rocBLAS bf16 GEMMs) -> fused chunkwise retention
     # with GroupNorm + gate -> heads regrouped by token -> W_O. Algorithmic flops: the five
     # projections plus the retention's.
-    if args.only in ("chunkwise", "decode", "parallel"):
+    if args.only in ("chunkwise", "decode", "parallel", "long"):
         args.no_layer = True
     if args.only == "layer":
         args.no_parallel = True
@@ -373,7 +376,7 @@ def main():
         del xl, lt, outl, wsl
 
     # ---- parallel form, 1.3B shape (secondary record) --------------------------------
-    if args.only in ("chunkwise", "decode"):
+    if args.only in ("chunkwise", "decode", "long"):
         args.no_parallel = True
     if args.only == "parallel":
         args.no_decode = True
@@ -410,8 +413,59 @@ def main():
                            "hbm_frac": pby / ps / 1e9 / HBM_PEAK_GBS}
         del xp, qp, kp, vp, outp, wsp
 
+    # ---- long sequences (secondary record) ---------------------------------------------
+    # B=1, H=16, chunk 512, GroupNorm, bf16 in/out, fp32 final state, default schedule, at
+    # N = 16K, 32K and 64K tokens: time per call, roofline fractions and the peak device
+    # memory of the call's tensors (inputs, output, state and workspace; the workspace
+    # does not grow with N).
+    if not args.no_long:
+        if args.only == "long":
+            del q, k, v, gate, out, ws
+        wl_ = W.WORKLOADS["chunkwise_long"]
+        long_rec = {"workload": "chunkwise_long: B=1 H=16 d_k=256 d_v=512 chunk=512, bf16 in/out, "
+                                "GroupNorm, fp32 final state, default (sequential) schedule",
+                    "by_N": {}}
+        for Nl in (16384, 32768, 65536):
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats(dev)
+            base = torch.cuda.memory_allocated(dev)
+            xl_ = W.make_inputs(wl_, N=Nl)
+            ql, kl, vl = (xl_[n].to(dev) for n in ("q", "k", "v"))
+            outl_ = torch.empty_like(vl)
+            Sl = torch.empty(wl_.B, wl_.H, wl_.d_k, wl_.d_v, dtype=torch.float32, device=dev)
+            wsl_ = torch.empty(rn.rn_chunkwise_workspace_bytes(ql, vl, xl_["gamma"], xl_["theta"], wl_.chunk,
+                                                               gn=True), dtype=torch.uint8, device=dev)
+
+            def lgstep():
+                rn.rn_retention_chunkwise(ql, kl, vl, xl_["gamma"], xl_["theta"], wl_.chunk, gn=True,
+                                          gn_eps=wl_.gn_eps, state_out=Sl, out=outl_, workspace=wsl_)
+
+            for _ in range(3):
+                lgstep()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 10
+            e0.record(stream)
+            for _ in range(reps):
+                lgstep()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts = e0.elapsed_time(e1) / reps / 1e3
+            lfl, lby = chunkwise_work(wl_.B, wl_.H, Nl, wl_.d_k, wl_.d_v, wl_.chunk, gate=False)
+            long_rec["by_N"][str(Nl)] = {
+                "ms": ts * 1e3, "tokens_per_s": wl_.B * Nl / ts,
+                "achieved_GBs": lby / ts / 1e9, "hbm_frac": lby / ts / 1e9 / HBM_PEAK_GBS,
+                "effective_tflops": lfl / ts / 1e12,
+                "effective_mfma_frac": lfl / ts / 1e12 / BF16_PEAK_TFLOPS,
+                "algorithmic_bytes": lby, "algorithmic_flops": lfl,
+                "workspace_bytes": wsl_.numel(),
+                "max_memory_allocated_bytes": torch.cuda.max_memory_allocated(dev) - base}
+            del xl_, ql, kl, vl, outl_, Sl, wsl_
+        rec["long"] = long_rec
+
     # ---- decode step ---------------------------------------------------------------
-    if args.only in ("chunkwise", "parallel"):
+    if args.only in ("chunkwise", "parallel", "long"):
         args.no_decode = True
     if not args.no_decode:
         wd = W.WORKLOADS["decode_6p7b"]
@@ -450,11 +504,7 @@ def main():
     # oracle, repeated until at least 10 s of CPU time have been spent (at most 3 passes).
     if not args.no_cpu_baseline:
         import oracle as O
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:  # pragma: no cover
-            cores = len(os.sched_getaffinity(0))
+        cores = cpu_cores()
         heads = w.B * w.H
         passes, t_total = 0, 0.0
         while passes < 3 and (passes == 0 or t_total < 10.0):
@@ -472,7 +522,86 @@ def main():
                                "sample": f"the whole chunkwise_6p7b workload ({heads} heads x N={w.N}, "
                                          f"chunk {w.chunk}, GroupNorm+gate) in fp64, {passes} pass(es), "
                                          f"{t_pass:.2f} s per pass"}
+        secondary_cpu_baselines(rec, args, O, W, cores)
     print(json.dumps(rec))
+    teardown()
+
+
+def cpu_cores() -> int:
+    """Threads the oracle's numpy calls use on this host."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
+def secondary_cpu_baselines(rec, args, O, W, cores):
+    """The fp64 oracle on bounded samples of the secondary workloads (about 10 s each)."""
+    if "parallel" in rec:
+        wp = W.WORKLOADS["parallel_1p3b"]
+        xp = W.make_inputs(wp)
+        t0 = time.perf_counter()
+        for b in range(wp.B):
+            for hh in range(wp.H):
+                sl = (slice(b, b + 1), slice(hh, hh + 1))
+                raw = O.parallel(xp["q"][sl], xp["k"][sl], xp["v"][sl], xp["gamma"][hh:hh + 1],
+                                 xp["theta"], 0, wp.qk_scale, True, True)
+                O.group_norm(raw, wp.gn_eps)
+        t = time.perf_counter() - t0
+        rec["parallel"]["cpu_baseline"] = {
+            "value": wp.B * wp.N / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the whole parallel_1p3b workload ({wp.B * wp.H} heads x N={wp.N}, D and R "
+                      f"normalisation, GroupNorm) in fp64, {t:.2f} s"}
+    if "decode" in rec:
+        wd = W.WORKLOADS["decode_6p7b"]
+        S0 = W.initial_state(wd)
+        nsteps, nb = 4, 16
+        states = [S0[b0:b0 + nb] for b0 in range(0, wd.B, nb)]
+        g_d, th_d = wd.gamma(), wd.theta()
+        t = 0.0
+        for i in range(nsteps):
+            d = W.make_decode_step_inputs(wd, i)
+            t0 = time.perf_counter()
+            for j, b0 in enumerate(range(0, wd.B, nb)):
+                sl = (slice(b0, b0 + nb),)
+                _, states[j] = O.recurrent_step(d["q"][sl], d["k"][sl], d["v"][sl], g_d, th_d, i, 1.0,
+                                                states[j])
+            t += time.perf_counter() - t0
+        rec["decode"]["cpu_baseline"] = {
+            "value": wd.B * nsteps / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "step_us": t / nsteps * 1e6,
+            "sample": f"{nsteps} decode steps of the whole decode_6p7b batch ({wd.B} x {wd.H} heads, "
+                      f"256 x 512 states) in fp64, {t:.2f} s"}
+    if "long" in rec:
+        wl_ = W.WORKLOADS["chunkwise_long"]
+        heads = [0, 5, 11, 15]
+        x = W.make_inputs(wl_)
+        t0 = time.perf_counter()
+        for hh in heads:
+            sl = (slice(0, 1), slice(hh, hh + 1))
+            raw, _ = O.chunkwise(x["q"][sl], x["k"][sl], x["v"][sl], x["gamma"][hh:hh + 1], x["theta"],
+                                 wl_.chunk)
+            O.group_norm(raw, wl_.gn_eps)
+        t = (time.perf_counter() - t0) * wl_.H / len(heads)
+        rec["long"]["cpu_baseline"] = {
+            "value": wl_.B * wl_.N / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(heads)} of the {wl_.H} heads of chunkwise_long at N={wl_.N} (chunk "
+                      f"{wl_.chunk}, GroupNorm) in fp64, time scaled by {wl_.H // len(heads)} to the "
+                      f"whole workload: {t:.2f} s"}
+
+
+def teardown():
+    """Ends the run with every launch finished and every tensor released before the
+    interpreter exits (so nothing of the library's or torch's GPU state is freed while a
+    profiler that wraps the process finalises)."""
+    import gc
+
+    import torch
+    torch.cuda.synchronize()
+    gc.collect()
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":
