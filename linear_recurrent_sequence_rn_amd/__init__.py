@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import ctypes
 import math
+import os
 from pathlib import Path
 from typing import Optional, Sequence
 
@@ -31,7 +32,9 @@ __all__ = [
     "rn_retention_chunkwise_noalloc",
 ]
 
-LIB_PATH = Path(__file__).resolve().parent / "librn_retention.so"
+# The in-tree build; RN_LIB_PATH names another build of the same sources (the host-side
+# tests use it for a copy built with the sanitizers).
+LIB_PATH = Path(os.environ.get("RN_LIB_PATH") or Path(__file__).resolve().parent / "librn_retention.so")
 
 RN_OK, RN_ERR_INVALID_ARG, RN_ERR_UNSUPPORTED, RN_ERR_HIP, RN_ERR_WORKSPACE = 0, -1, -2, -3, -4
 RN_ERR_EXCHANGE, RN_ERR_NONFINITE = -5, -6

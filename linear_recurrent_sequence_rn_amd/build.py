@@ -6,6 +6,11 @@
 
 Every HIP source under csrc/ is compiled to an object under _build/ and linked into
 linear_recurrent_sequence_rn_amd/librn_retention.so. Always recompiles.
+
+build(sanitize=True, lib=path) makes a copy whose host code is built with
+AddressSanitizer and UndefinedBehaviorSanitizer (device code unchanged), for running
+the host-side tests under the sanitizers; the process that loads it must preload the
+ASan runtime (sanitizer_runtime() names it).
 """
 from __future__ import annotations
 
@@ -40,30 +45,50 @@ def sources():
     return sorted(list(CSRC.glob("*.hip")) + list(CSRC.glob("*.cpp")))
 
 
-def _compile(src: Path) -> Path:
-    obj = BUILD / (src.stem + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", str(src), "-o", str(obj)]
+# Host-only sanitizers: each -fsanitize= applies to the host pass alone.
+SANITIZE = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined".split() + [
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-g"]
+
+
+def _compile(src: Path, build_dir: Path = BUILD, extra=()) -> Path:
+    obj = build_dir / (src.stem + ".o")
+    cmd = [HIPCC, *COMMON, *extra, "-x", "hip", "-c", str(src), "-o", str(obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src.name}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> Path:
-    BUILD.mkdir(exist_ok=True)
+def sanitizer_runtime() -> str:
+    """Path of the ASan runtime of the compiler that builds the sanitized library."""
+    clang = Path(HIPCC).resolve().parent.parent / "llvm" / "bin" / "clang"
+    if not clang.exists():
+        clang = Path("/opt/rocm/llvm/bin/clang")
+    r = subprocess.run([str(clang), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def build(verbose: bool = False, sanitize: bool = False, lib: Path = LIB) -> Path:
+    build_dir = BUILD / "sanitize" if sanitize else BUILD
+    build_dir.mkdir(parents=True, exist_ok=True)
     srcs = sources()
+    extra = SANITIZE if sanitize else ()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB.with_suffix(".so.tmp")
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs),
-           "-lrocblas"]
+        objs = list(ex.map(lambda s: _compile(s, build_dir, extra), srcs))
+    lib = Path(lib)
+    tmp = lib.with_suffix(".so.tmp")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(
+        ["-Xarch_host", "-shared-libsan"] if sanitize else []), "-o", str(tmp), *map(str, objs),
+        "-lrocblas"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
-    return LIB
+        print(f"built {lib} from {len(srcs)} sources")
+    return lib
 
 
 if __name__ == "__main__":
