@@ -16,9 +16,16 @@
 //     accumulates the signed row sums for the R normalisation and writes the scores to
 //     LDS in half (two buffers: the scores of block kb+1 are computed while block kb is
 //     multiplied with V); every wave then multiplies all 128 score rows with its 64
-//     columns of V. At the end each row is scaled by c_t = 1/sqrt(sum_{m<=t} gamma^m)
-//     (D normalisation) and 1/max(c_t |rowsum|, 1) (R normalisation), then GroupNorm
-//     (+ gate) over the 512 columns, whose sums are combined across the waves in LDS.
+//     columns of V, whose fragments it loads in two halves of 32 keys: the first half
+//     of the next key block during the current product, so V's latency sits behind a
+//     half or a whole block of work. At the end each row is scaled by
+//     c_t = 1/sqrt(sum_{m<=t} gamma^m) (D normalisation) and 1/max(c_t |rowsum|, 1)
+//     (R normalisation), then GroupNorm (+ gate) over the 512 columns, whose sums are
+//     combined across the waves in LDS.
+// Register budget: the accumulators (128 rows x 64 columns per wave) take half of each
+// wave's 256 VGPRs and the rest is full; with fewer rows per workgroup (64) the loop's
+// LDS reads batch well but every key/value block is read twice as often, which was
+// measured slower (0.64 against 0.56 ms per call at the 1.3B shape).
 // Query blocks are launched from the last (most key blocks) to the first, and each head's
 // blocks all go to one XCD.
 #include "rn_device.h"
@@ -37,6 +44,12 @@ constexpr int kT = 64;      // rows per block
 constexpr int kDK = 256;
 constexpr int kDV = 512;
 constexpr int kPLd = 72;    // LDS row stride (half) of the score block
+
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8), issued through the builtin so that the compiler's own wait insertion sees it.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | (((vm >> 4) & 3) << 14);
+}
 
 __device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -304,40 +317,55 @@ parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
 #pragma unroll
     for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: key block 0 -> scores 0; key block 1 staged
+  // V^T fragments of a key block, in two halves of 32 keys (e = 0, 1): this wave's 64
+  // columns, B operand (col dv, k = keys in vt_pos order).
+  auto load_vh = [&](int kb, int e, f16x8* dst) {
+    const uint32_t vblk = static_cast<uint32_t>(kb) * kDV * kT;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int dv = 64 * w + 16 * n + l16;
+      dst[n] = as_f16x8(ld_b128(rv, (vblk + static_cast<uint32_t>(dv * kT + 32 * e + 8 * g)) * 2));
+    }
+  };
+  // O[:, this wave's columns] += P(kb)[:, half e] V(kb)[half e]
+  auto pv_half = [&](int buf, int e, const f16x8* vf) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const f16x8 pf = as_f16x8(*reinterpret_cast<const u32x4*>(&sm.p[buf][16 * m + l16][32 * e + 8 * g]));
+#pragma unroll
+      for (int n = 0; n < 4; ++n) acc[m][n] = mfma(pf, vf[n], acc[m][n]);
+    }
+  };
+
+  // prologue: key block 0 -> scores 0; key block 1 staged; first half of V(0) loaded
   stage_k(0, 0);
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   __syncthreads();
   if (kb_end >= 1) stage_k(1, 1);
   scores(0);
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  f16x8 vh0[4], vh1[4];
+  load_vh(0, 0, vh0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   __syncthreads();
 
+  // Per key block: the first half of V(kb) was loaded during the previous block; the
+  // second half is loaded at the top and used last, and the first half of V(kb+1) is
+  // loaded between the two halves of the product, so each V load has a half or a whole
+  // block of work in front of it.
   for (int kb = 0; kb <= kb_end; ++kb) {
     // scores(kb) are in sm.p[kb%2]; key block kb+1 is in sm.kh[(kb+1)%2]
+    const bool more = kb + 1 <= kb_end;
     if (kb + 2 <= kb_end) stage_k(kb + 2, kb & 1);
-    const uint32_t vblk = static_cast<uint32_t>(kb) * kDV * kT;
-    f16x8 vf[2][4];
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const int dv = 64 * w + 16 * n + l16;
-        vf[e][n] = as_f16x8(ld_b128(rv, (vblk + static_cast<uint32_t>(dv * kT + 32 * e + 8 * g)) * 2));
-      }
-    if (kb + 1 <= kb_end) scores(kb + 1);
-    // O[:, this wave's columns] += P(kb) V(kb): A = P (row t, k = s), B = V^T (col dv, k = s),
-    // both with the keys in vt_pos order
+    load_vh(kb, 1, vh1);
+    if (more) scores(kb + 1);
     const int buf = kb & 1;
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const f16x8 pf = as_f16x8(*reinterpret_cast<const u32x4*>(&sm.p[buf][16 * m + l16][32 * e + 8 * g]));
-#pragma unroll
-        for (int n = 0; n < 4; ++n) acc[m][n] = mfma(pf, vf[e][n], acc[m][n]);
-      }
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    pv_half(buf, 0, vh0);
+    if (more) load_vh(kb + 1, 0, vh0);
+    pv_half(buf, 1, vh1);
+    // key block kb+2 staged (and V's second half, used above); V(kb+1)'s first half
+    // stays in flight
+    if (more) __builtin_amdgcn_s_waitcnt(waitcnt_imm(4, 0));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __syncthreads();
   }
 
