@@ -469,7 +469,7 @@ bm_dout(CallArgs a, Heads Hd, const void* gate, const void* dout, uint16_t* DR, 
 }
 
 // dQh = [alpha (dO V^T) (.) D] Kh + alpha xi dO S_c^T, rotated back.
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bm_dq(CallArgs a, Heads Hd, const uint16_t* v, void* dq) {
   __shared__ TileSharedH sm;
   const int dk = a.dk, dv = a.dv, N = a.N, Np = Hd.Np;
@@ -493,7 +493,7 @@ bm_dq(CallArgs a, Heads Hd, const uint16_t* v, void* dq) {
 }
 
 // Tile rows are keys s; later rows t in [s, c1): dKh = [alpha (V dO^T) (.) D'] Qh + zeta V G^T.
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bm_dk(CallArgs a, Heads Hd, const uint16_t* v, void* dk_) {
   __shared__ TileSharedH sm;
   const int dk = a.dk, dv = a.dv, N = a.N, Np = Hd.Np;
