@@ -139,6 +139,10 @@ size_t rn_parallel_workspace_bytes(const rn_desc* desc);
  * else ignored); out: [B,H,N,d_v] in out_dtype. No state: the parallel form starts
  * from S = 0. workspace: device buffer of at least rn_parallel_workspace_bytes(desc)
  * bytes, 256-byte aligned (may be NULL when that size is 0); contents ignored.
+ * Precision and range. bf16 inputs with d_k = 256 and d_v = 512 take matrix-core
+ * products on IEEE-half operands with float32 accumulation: alpha*Qh, Kh, v and the
+ * decayed scores alpha*gamma^(t-s) Qh_t.Kh_s must stay below 65504 in magnitude (no
+ * decay factor is folded into the operands here); other inputs run float32 kernels.
  */
 rn_status rn_retention_parallel(const rn_desc* desc, const void* q, const void* k,
                                 const void* v, const void* gate, void* out,
@@ -279,7 +283,7 @@ size_t rn_chunkwise_backward_workspace_bytes(const rn_desc* desc, int32_t chunk)
  * dgn_weight, dgn_bias: DEVICE float32 [H*d_v] or NULL, written when RN_EPI_GN (sums over
  *             the batch and the rows); ignored otherwise.
  * workspace:  at least rn_chunkwise_backward_workspace_bytes(desc, chunk), 256-byte aligned.
- * Arithmetic: float32 inputs take float32 products throughout (held to 1e-4 relative).
+ * Arithmetic: float32 inputs take float32 products throughout.
  * bf16 inputs take matrix-core products (16x16x32 f16 MFMA, float32 accumulation): with
  * d_k and d_v multiples of 8 and v 16-byte, q and k 4-byte aligned, every operand is
  * rounded to IEEE half (so, as for the forward, operands must stay below 65504 in

@@ -46,7 +46,8 @@ hipError_t launch_chunkwise_seg(const CallArgs& a, int out_dt, const void* q, co
                                 const void* v, const void* gate, const float* s_in, float* s_out,
                                 void* out, void* ws, size_t ws_bytes, hipStream_t st);
 
-// Gradients of the chunkwise form (plain float32 kernels).
+// Gradients of the chunkwise form: f16-operand MFMA products with float32 accumulation for
+// bf16 inputs whose d_k and d_v are multiples of 8, float32 products otherwise.
 struct BwArgs {
   const void* q; const void* k; const void* v; const void* gate;
   const void* dout; const float* state_in; const float* dstate_out;
