@@ -55,10 +55,10 @@ typedef int32_t rn_status;
 #define RN_ERR_EXCHANGE    (-5) /* reported by rn_chunkwise_check: a wait between the workgroups of
                                    the sequential chunkwise kernel hit its time limit (1 s); the
                                    call's out and state_out hold NaN where they were written */
-#define RN_ERR_NONFINITE   (-6) /* reported by rn_chunkwise_check: the sequential chunkwise kernel
-                                   produced a non-finite output or final state: a non-finite input,
-                                   or a value beyond its half-precision operand range (see
-                                   rn_retention_chunkwise) */
+#define RN_ERR_NONFINITE   (-6) /* reported by rn_chunkwise_check: a matrix-core chunkwise
+                                   schedule produced a non-finite output or final state: a
+                                   non-finite input, or a value beyond its half-precision operand
+                                   range (see rn_retention_chunkwise) */
 
 typedef int32_t rn_dtype;
 #define RN_F32  0   /* IEEE float32 */
@@ -178,7 +178,7 @@ size_t rn_chunkwise_workspace_bytes(const rn_desc* desc, int32_t chunk);
  * since that kernel takes gamma^32 >= 2^-6), so |alpha q|, |k| < 1000 and |state| < 2^15
  * keep every operand in range; RetNet-scaled data sits many orders of magnitude below.
  * Outside that range the result is not finite; rn_chunkwise_check then reports
- * RN_ERR_NONFINITE for the sequential kernel.
+ * RN_ERR_NONFINITE (all three matrix-core schedules keep the status word).
  */
 rn_status rn_retention_chunkwise(const rn_desc* desc, int32_t chunk, const void* q,
                                  const void* k, const void* v, const void* gate,
@@ -348,8 +348,9 @@ rn_status rn_groupnorm_gate(int32_t B, int32_t H, int32_t N, int32_t d_v,
  * Status of a completed rn_retention_chunkwise / rn_retention_chunkwise_varlen call (same
  * desc and chunk), read from its workspace: RN_OK; RN_ERR_EXCHANGE if a wait between the
  * workgroups of the sequential kernel hit its time limit (its outputs are then NaN);
- * RN_ERR_NONFINITE if that kernel produced a non-finite output or final state. Other
- * schedules (segmented, chunk-parallel, float32) record nothing and give RN_OK.
+ * RN_ERR_NONFINITE if the call's matrix-core schedule (sequential, segmented or
+ * chunk-parallel) produced a non-finite output or final state. The float32 kernels
+ * record nothing and give RN_OK.
  * workspace: the call's device workspace, in which case `stream` (the call's stream) is
  * synchronised and the status word copied to the host; or a host copy of at least its
  * first 256 bytes, read directly. Must be called before the workspace is reused.

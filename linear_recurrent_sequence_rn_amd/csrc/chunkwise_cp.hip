@@ -150,6 +150,7 @@ struct StateParams {
   float* dst;         // window's final state, or null
   int dst_group;
   uint16_t* snap;     // [heads][kWin][kSnapHalves]
+  uint32_t* status;   // the call's status word (bit 1: a non-finite final state)
 };
 
 constexpr int kLoads1 = 8 + 32;   // vector loads per thread and block
@@ -359,6 +360,7 @@ __global__ void __launch_bounds__(256) cp_states(StateParams P) {
 
   if (P.dst) {
     float* dst = P.dst + size_t(P.dst_group ? hg : bh) * kDK * kDV;
+    uint32_t bad = 0u;   // set by a non-finite value of the caller's final state
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -367,7 +369,10 @@ __global__ void __launch_bounds__(256) cp_states(StateParams P) {
         for (int r = 0; r < 4; ++r) {
           const int d = 64 * kq + 16 * rt + 4 * g + r, c = 256 * vh + 64 * w + 16 * ct + l16;
           dst[size_t(d) * kDV + c] = acc[rt][ct][r];
+          bad |= __builtin_isfinite(acc[rt][ct][r]) ? 0u : 1u;
         }
+    if (!P.dst_group && __builtin_amdgcn_ballot_w64(bad != 0u) != 0 && l == 0)
+      __hip_atomic_fetch_or(P.status, kChunkwiseStatusNonFinite, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -394,6 +399,7 @@ struct OutParams {
   const uint16_t* gate;
   const uint16_t* snap;
   void* out;
+  uint32_t* status;   // the call's status word (bit 1: a non-finite output)
 };
 
 // Rows of the transposed-operand buffer hold 32 half values (4 chunks of 16 bytes);
@@ -800,6 +806,20 @@ cp_outputs(OutParams P) {
           }
     }
   }
+  {
+    // a class test per stored value of the sequence's rows
+    uint32_t bad = 0u;
+#pragma unroll
+    for (int mq = 0; mq < 2; ++mq) {
+      const bool vrow = t0 + 16 * mq + l16 < len;
+#pragma unroll
+      for (int tb = 0; tb < 8; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bad |= (vrow && !__builtin_isfinite(y[tb][mq][r])) ? 1u : 0u;
+    }
+    if (__builtin_amdgcn_ballot_w64(bad != 0u) != 0 && l == 0)
+      __hip_atomic_fetch_or(P.status, kChunkwiseStatusNonFinite, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 #pragma unroll
   for (int mq = 0; mq < 2; ++mq) {
     const int row = t0 + 16 * mq + l16;
@@ -825,6 +845,12 @@ cp_outputs(OutParams P) {
 
 int chunks_of(int N) { return (N + kC - 1) / kC; }
 
+__global__ void cp_status_clear(uint32_t* status) {
+  if (threadIdx.x == 0) status[0] = 0u;
+}
+
+constexpr size_t kStatusBytes = 256;   // the call's status word leads the workspace
+
 }  // namespace
 
 bool chunkwise_cp_supported(const CallArgs& a, int in_dt) {
@@ -836,7 +862,7 @@ bool chunkwise_cp_supported(const CallArgs& a, int in_dt) {
 // A full window of snapshots and the carried state per head of a group, whatever N is.
 size_t chunkwise_cp_ws_bytes(const CallArgs& a) {
   const int heads = min(a.B * a.H, kHeadsPerGroup);
-  return size_t(heads) * (kWin * kSnapHalves * sizeof(uint16_t) + size_t(kDK) * kDV * sizeof(float));
+  return kStatusBytes + size_t(heads) * (kWin * kSnapHalves * sizeof(uint16_t) + size_t(kDK) * kDV * sizeof(float));
 }
 
 hipError_t launch_chunkwise_cp(const CallArgs& a, int out_dt, const void* q, const void* k,
@@ -847,8 +873,10 @@ hipError_t launch_chunkwise_cp(const CallArgs& a, int out_dt, const void* q, con
   const int nwin = (nch + kWin - 1) / kWin;
   const size_t snap_bytes = size_t(min(total, kHeadsPerGroup)) * kWin * kSnapHalves * sizeof(uint16_t);
   if (chunkwise_cp_ws_bytes(a) > ws_bytes) return hipErrorInvalidValue;
-  uint16_t* snap = static_cast<uint16_t*>(ws);
-  float* carry = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + snap_bytes);
+  uint32_t* status = static_cast<uint32_t*>(ws);
+  uint16_t* snap = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + kStatusBytes);
+  float* carry = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kStatusBytes + snap_bytes);
+  hipLaunchKernelGGL(cp_status_clear, dim3(1), dim3(64), 0, st, status);
   for (int h0 = 0; h0 < total; h0 += kHeadsPerGroup) {
     const int heads = min(kHeadsPerGroup, total - h0);
     for (int win = 0; win < nwin; ++win) {
@@ -864,6 +892,7 @@ hipError_t launch_chunkwise_cp(const CallArgs& a, int out_dt, const void* q, con
       sp.dst = win + 1 == nwin ? s_out : carry;
       sp.dst_group = win + 1 == nwin ? 0 : 1;
       sp.snap = snap;
+      sp.status = status;
       if (a.gpair)
         hipLaunchKernelGGL(cp_states<true>, dim3(64 * ((heads + 7) / 8)), dim3(256), 0, st, sp);
       else
@@ -881,6 +910,7 @@ hipError_t launch_chunkwise_cp(const CallArgs& a, int out_dt, const void* q, con
       op.gate = static_cast<const uint16_t*>(gate);
       op.snap = snap;
       op.out = out;
+      op.status = status;
       const int inst = heads * kWin;
       const dim3 grid(64 * ((inst + 7) / 8));
       if (a.gpair) {

@@ -144,6 +144,7 @@ struct SegArgs {
   float* dst;              // state leaving the window, or null
   int dst_group;
   void* out;
+  uint32_t* status;        // the call's status word (bit 1: a non-finite output or final state)
 };
 
 // =================================== seg_states =========================================
@@ -384,8 +385,14 @@ __global__ void __launch_bounds__(256) seg_scan(SegArgs P) {
   }
   if (P.dst) {
     float* dst = P.dst + size_t(P.dst_group ? hl : gh) * kSnap;
+    uint32_t bad = 0u;   // set by a non-finite value of the caller's final state
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dst[size_t(8 * cb + i) * kDV + n] = S[i];
+    for (int i = 0; i < 8; ++i) {
+      dst[size_t(8 * cb + i) * kDV + n] = S[i];
+      bad |= __builtin_isfinite(S[i]) ? 0u : 1u;
+    }
+    if (!P.dst_group && __builtin_amdgcn_ballot_w64(bad != 0u) != 0 && (threadIdx.x & 63) == 0)
+      __hip_atomic_fetch_or(P.status, kChunkwiseStatusNonFinite, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -711,6 +718,20 @@ __global__ void __launch_bounds__(512) seg_outputs(SegArgs P) {
           acc[i][j][r] = y;
         }
   }
+  {
+    // a class test per stored value of the sequence's rows
+    uint32_t bad = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool vrow = t0 + 16 * i + r < len;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bad |= (vrow && !__builtin_isfinite(acc[i][j][r])) ? 1u : 0u;
+      }
+    if (__builtin_amdgcn_ballot_w64(bad != 0u) != 0 && (threadIdx.x & 63) == 0)
+      __hip_atomic_fetch_or(P.status, kChunkwiseStatusNonFinite, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -730,6 +751,12 @@ __global__ void __launch_bounds__(512) seg_outputs(SegArgs P) {
 
 int chunks_of(int N) { return (N + kC - 1) / kC; }
 
+__global__ void seg_status_clear(uint32_t* status) {
+  if (threadIdx.x == 0) status[0] = 0u;
+}
+
+constexpr size_t kStatusBytes = 256;   // the call's status word leads the workspace
+
 }  // namespace
 
 bool chunkwise_seg_supported(const CallArgs& a, int in_dt) {
@@ -742,7 +769,7 @@ bool chunkwise_seg_supported(const CallArgs& a, int in_dt) {
 size_t chunkwise_seg_ws_bytes(const CallArgs& a) {
   const int heads = min(a.B * a.H, kHeadsPerGroup);
   const size_t per_head = kWin * kSnap * 2 + kSegMax * kSnap * 4 + kSegMax * kSnap * 2 + kSnap * 4;
-  return size_t(heads) * per_head;
+  return kStatusBytes + size_t(heads) * per_head;
 }
 
 hipError_t launch_chunkwise_seg(const CallArgs& a, int out_dt, const void* q, const void* k,
@@ -753,7 +780,9 @@ hipError_t launch_chunkwise_seg(const CallArgs& a, int out_dt, const void* q, co
   const int group = min(total, kHeadsPerGroup);
   const int nch = chunks_of(a.N);
   const int nwin = (nch + kWin - 1) / kWin;
-  uint8_t* p = static_cast<uint8_t*>(ws);
+  uint32_t* status = static_cast<uint32_t*>(ws);
+  hipLaunchKernelGGL(seg_status_clear, dim3(1), dim3(64), 0, st, status);
+  uint8_t* p = static_cast<uint8_t*>(ws) + kStatusBytes;
   uint16_t* snap = reinterpret_cast<uint16_t*>(p);
   p += size_t(group) * kWin * kSnap * 2;
   float* ends = reinterpret_cast<float*>(p);
@@ -783,6 +812,7 @@ hipError_t launch_chunkwise_seg(const CallArgs& a, int out_dt, const void* q, co
       P.dst = win + 1 == nwin ? s_out : carry;
       P.dst_group = win + 1 == nwin ? 0 : 1;
       P.out = out;
+      P.status = status;
       const int g1 = (heads * P.nseg * 2 + 7) & ~7;
       hipLaunchKernelGGL(seg_states, dim3(g1), dim3(512), 0, st, P);
       hipError_t e = hipGetLastError();

@@ -319,11 +319,12 @@ rn_status rn_chunkwise_check(const rn_desc* desc, int32_t chunk, const void* wor
   rn_status s = check_desc(desc, Form::kChunkwise, &a);
   if (s != RN_OK) return s;
   if (chunk < 1) return fail(RN_ERR_INVALID_ARG, "chunk=%d must be >= 1", chunk);
-  if (chunk_path(desc, a) != ChunkPath::kSequential) return RN_OK;   // nothing recorded
+  const ChunkPath path = chunk_path(desc, a);
+  if (path == ChunkPath::kGeneric) return RN_OK;   // the float32 kernels record nothing
   if (!workspace) return fail(RN_ERR_INVALID_ARG, "workspace is NULL");
   if (workspace_bytes < sizeof(uint32_t))
     return fail(RN_ERR_WORKSPACE, "workspace %zu bytes holds no status word", workspace_bytes);
-  // The status word is the first word of the sequential kernel's workspace. A device
+  // The status word is the first word of the MFMA schedules' workspaces. A device
   // pointer is read after the call's stream has finished; anything else (a host copy of
   // the workspace) is read directly.
   uint32_t word = 0;
@@ -343,7 +344,9 @@ rn_status rn_chunkwise_check(const rn_desc* desc, int32_t chunk, const void* wor
     return fail(RN_ERR_EXCHANGE, "a cross-workgroup wait of the sequential chunkwise kernel "
                                  "hit its time limit; its outputs are NaN");
   if (word & rn::kChunkwiseStatusNonFinite)
-    return fail(RN_ERR_NONFINITE, "the sequential chunkwise kernel produced non-finite values");
+    return fail(RN_ERR_NONFINITE, "the %s chunkwise schedule produced non-finite values",
+                path == ChunkPath::kSequential ? "sequential"
+                : path == ChunkPath::kSegmented ? "segmented" : "chunk-parallel");
   return RN_OK;
 }
 

@@ -340,13 +340,20 @@ def test_chunkwise_check_reads_the_status_word():
     assert rn.lib.rn_chunkwise_check(None, 64, FAKE, n, None) == rn.RN_ERR_INVALID_ARG
 
 
-def test_chunkwise_check_other_schedules_record_nothing():
-    """Schedules other than the sequential kernel keep no status word: the check is RN_OK
-    whatever the workspace holds (their waits are kernel boundaries, not time-limited)."""
-    for flags in (rn.RN_CHUNK_PARALLEL, rn.RN_CHUNK_SEGMENTED, rn.RN_FORCE_GENERIC):
+def test_chunkwise_check_other_schedules():
+    """The segmented and chunk-parallel schedules keep the status word too (their waits are
+    kernel boundaries, so only the non-finite bit is ever set); the float32 kernels keep
+    none, and the check is RN_OK whatever the workspace holds."""
+    for flags in (rn.RN_CHUNK_PARALLEL, rn.RN_CHUNK_SEGMENTED):
         d, keep = desc(**SEQ, flags=flags)
-        assert chk_status(d, status_image(3, 1024)) == rn.RN_OK, flags
-    d, keep = desc(**dict(SEQ, gamma=np.full(2, 0.8)))       # gamma^32 < 2^-6: not sequential
+        assert chk_status(d, status_image(0, 1024)) == rn.RN_OK, flags
+        assert chk_status(d, status_image(2, 1024)) == rn.RN_ERR_NONFINITE, flags
+        assert b"segmented" in rn.lib.rn_last_error() or b"chunk-parallel" in rn.lib.rn_last_error()
+    d, keep = desc(**dict(SEQ, gamma=np.full(2, 0.8)))       # gamma^32 < 2^-6: segmented
+    assert chk_status(d, status_image(2, 1024)) == rn.RN_ERR_NONFINITE
+    d, keep = desc(**SEQ, flags=rn.RN_FORCE_GENERIC)
+    assert chk_status(d, status_image(3, 1024)) == rn.RN_OK
+    d, keep = desc(**dict(SEQ, in_dtype=rn.RN_F32))             # float32 inputs: generic
     assert chk_status(d, status_image(3, 1024)) == rn.RN_OK
 
 

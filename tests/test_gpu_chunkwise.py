@@ -68,7 +68,7 @@ def ws_for(q, v, gamma, theta, chunk, **kw):
     return torch.zeros(n, dtype=torch.uint8, device=DEV)
 
 
-STATUS_BYTES = 256   # the sequential kernel's call status word leads its workspace
+STATUS_BYTES = 256   # every matrix-core schedule's call status word leads its workspace
 
 
 def counters(ws, heads):
@@ -257,7 +257,7 @@ def test_chunk_parallel_snapshots_are_the_chunk_states():
                                 state_in=dev(x["state"]), workspace=ws, out_dtype=torch.float32,
                                 chunk_parallel=True)
     torch.cuda.synchronize()
-    snap = ws[: 2 * 32 * 256 * 512 * 2].view(torch.float16).reshape(2, 32, 8, 512, 32)
+    snap = ws[STATUS_BYTES: STATUS_BYTES + 2 * 32 * 256 * 512 * 2].view(torch.float16).reshape(2, 32, 8, 512, 32)
     for c in range(3):
         # [head, piece, d_v, 32] -> [head, piece, 32, d_v] -> S [head, d_k, d_v]
         got = snap[:, c].permute(0, 1, 3, 2).reshape(2, 256, 512).cpu().to(torch.float64).numpy()[None]
@@ -303,8 +303,8 @@ def test_segmented_states_in_the_workspace():
                                 segmented=True)
     torch.cuda.synchronize()
     heads, snap = 2, 256 * 512
-    L = ws[: heads * 32 * snap * 2].view(torch.float16).reshape(heads, 32, 512, 256)
-    off = heads * 32 * snap * 2 + heads * 4 * snap * 4
+    L = ws[STATUS_BYTES: STATUS_BYTES + heads * 32 * snap * 2].view(torch.float16).reshape(heads, 32, 512, 256)
+    off = STATUS_BYTES + heads * 32 * snap * 2 + heads * 4 * snap * 4
     T = ws[off: off + heads * 4 * snap * 2].view(torch.float16).reshape(heads, 4, 512, 256)
 
     def state_at(t):
@@ -403,22 +403,26 @@ def test_no_decay_constant_inputs_over_64k_tokens():
         print("gamma = 1, constant inputs, N = 65536: reported RN_ERR_NONFINITE")
 
 
-@pytest.mark.parametrize("mag", [2e3, 1e5])
-def test_large_inputs_match_or_are_reported(mag):
-    """q, k, v ~ N(0, mag^2): beyond the half-precision operand range the default schedule
-    reports RN_ERR_NONFINITE rather than returning unreported infinities or NaNs; within
-    it, the outputs match the oracle."""
+@pytest.mark.parametrize("cp", SCHEDULES)
+@pytest.mark.parametrize("mag", [1 / 16, 2e3, 1e5])
+def test_large_inputs_match_or_are_reported(mag, cp):
+    """q, k, v ~ N(0, mag^2): beyond the half-precision operand range each matrix-core
+    schedule reports RN_ERR_NONFINITE rather than returning unreported infinities or NaNs;
+    within it, the outputs match the oracle and the status is RN_OK."""
     w = wl(N=1000, H=2, qkv_std=mag, seed=41)
     x = W.make_inputs(w)
     q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
-    ws = ws_for(q, v, x["gamma"], x["theta"], 64)
+    ws = ws_for(q, v, x["gamma"], x["theta"], 64, **sk(cp))
     out, S = rn().rn_retention_chunkwise(q, k, v, x["gamma"], x["theta"], 64, state_out=True,
-                                         workspace=ws, out_dtype=torch.float32)
-    st = status(q, v, x["gamma"], x["theta"], 64, ws)
+                                         workspace=ws, out_dtype=torch.float32, **sk(cp))
+    st = status(q, v, x["gamma"], x["theta"], 64, ws, **sk(cp))
     if finite_or_reported(out, S, st):
         raw, Sref = O.chunkwise(x["q"], x["k"], x["v"], x["gamma"], x["theta"], 64)
         assert rel_inf(out.cpu(), raw) <= MFMA_BAR
-    print(f"inputs ~ N(0, {mag:g}^2): status {st}")
+        assert rel_inf(S.cpu(), Sref) <= STATE_BAR
+    if mag < 1:
+        assert st == rn().RN_OK
+    print(f"{cp}: inputs ~ N(0, {mag:g}^2): status {st}")
 
 
 def test_near_the_decay_and_operand_limits():
