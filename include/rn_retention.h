@@ -139,10 +139,11 @@ size_t rn_parallel_workspace_bytes(const rn_desc* desc);
  * else ignored); out: [B,H,N,d_v] in out_dtype. No state: the parallel form starts
  * from S = 0. workspace: device buffer of at least rn_parallel_workspace_bytes(desc)
  * bytes, 256-byte aligned (may be NULL when that size is 0); contents ignored.
- * Precision and range. bf16 inputs with d_k = 256 and d_v = 512 take matrix-core
- * products on IEEE-half operands with float32 accumulation: alpha*Qh, Kh, v and the
- * decayed scores alpha*gamma^(t-s) Qh_t.Kh_s must stay below 65504 in magnitude (no
- * decay factor is folded into the operands here); other inputs run float32 kernels.
+ * Precision and range. bf16 inputs with d_k = 256, d_v = 512 and N * 2048 < 2^31
+ * (N below 1,048,576) take matrix-core products on IEEE-half operands with float32
+ * accumulation: alpha*Qh, Kh, v and the decayed scores alpha*gamma^(t-s) Qh_t.Kh_s
+ * must stay below 65504 in magnitude (no decay factor is folded into the operands
+ * here); other inputs run float32 kernels.
  */
 rn_status rn_retention_parallel(const rn_desc* desc, const void* q, const void* k,
                                 const void* v, const void* gate, void* out,

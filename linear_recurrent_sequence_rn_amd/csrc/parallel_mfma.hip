@@ -61,6 +61,19 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   v[1] = static_cast<_Float16>(hi);
   return __builtin_bit_cast(uint32_t, v);
 }
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+// Sum over each row of 16 lanes, every lane receiving the row's sum (DPP moves, VALU
+// only): swap neighbours, swap pairs, mirror within 8 lanes, mirror within 16.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);    // lane ^ 1
+  x += dpp_mov<0x4E>(x);    // lane ^ 2
+  x += dpp_mov<0x141>(x);   // lane i <-> 7 - i within 8
+  x += dpp_mov<0x140>(x);   // lane i <-> 15 - i within 16
+  return x;
+}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
                                            static_cast<int>(bytes > 0 ? bytes : 0), 0x00020000);
@@ -201,6 +214,7 @@ __global__ void __launch_bounds__(256) parallel_prep(CallArgs a, const uint16_t*
 
 // ---- main -------------------------------------------------------------------------------
 constexpr int kQ = 128;       // query rows per workgroup
+constexpr int kStgLd = 68;    // LDS row stride (floats) of the epilogue's 16 x 64 tiles
 constexpr int kWaves = 8;     // 512 threads
 
 struct alignas(16) PShared {
@@ -217,7 +231,10 @@ struct alignas(16) PShared {
 // into 16 different 4-bank groups.
 __device__ __forceinline__ int kh_unit(int s, int u) { return 32 * s + (u ^ (s & 31)); }
 
-template <int OUT>
+// FACT: every head of the call has gamma^-127 in float's normal range, so the decay is
+// formed from per-lane, per-row and per-block factors; otherwise each score takes its own
+// exp2 (decided on the host, so the score loop has no branch on it).
+template <int OUT, bool FACT>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
   const int N = a.N, nb = (N + kT - 1) / kT, nq = (N + kQ - 1) / kQ;
@@ -269,8 +286,7 @@ parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
   // rl * gr[r] * bi[i]: rl = gamma^(16w + l16 - 4g) per lane (exponent in [-12, 127]),
   // gr[r] = gamma^-r (scalar registers), bi[i] = gamma^(128qb - 64kb - 16i) per wave and
   // key block. The factors stay in float's normal range when gamma^-127 does
-  // (gamma > 0.5035); below that every element takes its own exp2.
-  const bool factored = lg * 127.f >= -126.f;
+  // (gamma > 0.5035, FACT); below that every element takes its own exp2.
   const float rl = exp2f(lg * float(16 * w + l16 - 4 * g));
   float gr[4];
 #pragma unroll
@@ -301,7 +317,7 @@ parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int d = dq + 16 * w + l16 - 16 * i - 4 * g - r;
-        const float f = factored ? bl * gr[r] : exp2f(lg * float(d));
+        const float f = FACT ? bl * gr[r] : exp2f(lg * float(d));
         val[r] = (diag && d < 0) ? 0.f : sc[i][r] * f;
         rsum += val[r];
       }
@@ -415,10 +431,7 @@ parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
         float x = 0.f;
 #pragma unroll
         for (int n = 0; n < 4; ++n) x += f(acc[m][n][r], m, r);
-        x += __shfl_xor(x, 1, 64);
-        x += __shfl_xor(x, 2, 64);
-        x += __shfl_xor(x, 4, 64);
-        x += __shfl_xor(x, 8, 64);
+        x = row16_sum(x);
         if (l16 == 0) sm.red[w][16 * m + 4 * g + r] = x;
       }
   };
@@ -446,36 +459,86 @@ parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
     __syncthreads();
   }
 
-  // ---- epilogue: normalise, gate, store (each lane: 4 consecutive rows x 1 column) ----
+  // ---- epilogue: one 16-row tile at a time through this wave's LDS area, so that each
+  // lane ends with 16 consecutive columns of one row: normalise, gate, and store them as
+  // 16-byte runs. The key buffers are free by now (the loop's last barrier has passed).
+  float* stg = reinterpret_cast<float*>(&sm.kh[0][0]) + w * (16 * kStgLd);
+  const int er = l >> 2, ec = 16 * (l & 3);          // row in the tile, first column
+  const int col0 = 64 * w + ec;                      // first column of the lane's run
+  float gw[16], gb[16];
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
+  for (int j = 0; j < 16; ++j) {
+    gw[j] = (gn && a.gn_w) ? a.gn_w[h * kDV + col0 + j] : 1.f;
+    gb[j] = (gn && a.gn_b) ? a.gn_b[h * kDV + col0 + j] : 0.f;
+  }
+  constexpr int kEsz = OUT == RN_BF16 ? 2 : 4;      // output element bytes
+  const __amdgpu_buffer_rsrc_t rg =
+      range_rsrc(gt ? static_cast<const uint16_t*>(gate) + size_t(bh) * N * kDV : nullptr,
+                 gt ? int64_t(N) * kDV * 2 : 0);
+  const __amdgpu_buffer_rsrc_t ro =
+      range_rsrc(static_cast<uint8_t*>(out) + size_t(bh) * N * kDV * kEsz, int64_t(N) * kDV * kEsz);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int col = 64 * w + 16 * n + l16;
+  for (int m = 0; m < 8; ++m) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = qb * kQ + 16 * m + 4 * g + r;
-        if (t >= N) continue;
-        float y = acc[m][n][r];
-        const int64_t off = (int64_t(bh) * N + t) * kDV + col;
-        if (gn) {
-          const int tl = 16 * m + 4 * g + r;
-          y = (y - sm.mean[tl]) * sm.rstd[tl];
-          if (a.gn_w) y *= a.gn_w[h * kDV + col];
-          if (a.gn_b) y += a.gn_b[h * kDV + col];
-          if (gt) y *= swishf(Elem<RN_BF16>::load(gate, off));
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) stg[(4 * g + r) * kStgLd + 16 * n + l16] = acc[m][n][r];
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    float y[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 x4 = *reinterpret_cast<const f32x4*>(&stg[er * kStgLd + ec + 4 * i]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) y[4 * i + c] = x4[c];
+    }
+    const int tl = 16 * m + er, t = qb * kQ + tl;
+    // byte offsets within the head; rows past N go to an offset past the buffer's range,
+    // where loads return zero and stores are dropped
+    const uint32_t ooff = t < N ? static_cast<uint32_t>((t * kDV + col0) * kEsz) : 0x80000000u;
+    const uint32_t goff = t < N ? static_cast<uint32_t>((t * kDV + col0) * 2) : 0x80000000u;
+    if (gn) {
+      const float mu = sm.mean[tl], rs = sm.rstd[tl];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) y[j] = (y[j] - mu) * rs * gw[j] + gb[j];
+      if (gt) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const u32x4 gv = ld_b128(rg, goff + 16 * i);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            y[8 * i + 2 * c] *= swishf(__uint_as_float(gv[c] << 16));
+            y[8 * i + 2 * c + 1] *= swishf(__uint_as_float(gv[c] & 0xffff0000u));
+          }
         }
-        Elem<OUT>::store(out, off, y);
       }
     }
+    if (OUT == RN_BF16) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        u32x4 v;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = pack_bf16x2(y[8 * i + 2 * c], y[8 * i + 2 * c + 1]);
+        st_b128(ro, ooff + 16 * i, v);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x4 v;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = __float_as_uint(y[4 * i + c]);
+        st_b128(ro, ooff + 16 * i, v);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));   // tile read back before it is rewritten
+  }
 }
 
 }  // namespace
 
-// Buffer offsets within one head's rows are 32-bit: N d_v 2-byte elements must stay
-// below 2^31 bytes.
+// Buffer offsets within one head's rows are 32-bit: N d_v elements of up to 4 bytes (a
+// float32 output) must stay below 2^31 bytes.
 bool parallel_mfma_supported(const CallArgs& a, int in_dt) {
-  return in_dt == RN_BF16 && a.dk == kDK && a.dv == kDV && int64_t(a.N) * kDV * 2 < (int64_t(1) << 31);
+  return in_dt == RN_BF16 && a.dk == kDK && a.dv == kDV && int64_t(a.N) * kDV * 4 < (int64_t(1) << 31);
 }
 
 size_t parallel_mfma_ws_bytes(const CallArgs& a) {
@@ -495,10 +558,16 @@ hipError_t launch_parallel_mfma(const CallArgs& a, int out_dt, const void* q, co
   if (e != hipSuccess) return e;
   const int nq = (a.N + kQ - 1) / kQ;
   const dim3 grid(static_cast<unsigned>(nq) * 8 * ((BH + 7) / 8));
-  if (out_dt == RN_BF16)
-    hipLaunchKernelGGL((parallel_main<RN_BF16>), grid, dim3(kWaves * 64), 0, st, a, w, gate, out);
-  else
-    hipLaunchKernelGGL((parallel_main<RN_F32>), grid, dim3(kWaves * 64), 0, st, a, w, gate, out);
+  bool fact = true;
+  for (int h = 0; h < a.H; ++h) fact = fact && a.hp.log2g[h] * 127.f >= -126.f;
+  const dim3 blk(kWaves * 64);
+  if (out_dt == RN_BF16) {
+    if (fact) hipLaunchKernelGGL((parallel_main<RN_BF16, true>), grid, blk, 0, st, a, w, gate, out);
+    else hipLaunchKernelGGL((parallel_main<RN_BF16, false>), grid, blk, 0, st, a, w, gate, out);
+  } else {
+    if (fact) hipLaunchKernelGGL((parallel_main<RN_F32, true>), grid, blk, 0, st, a, w, gate, out);
+    else hipLaunchKernelGGL((parallel_main<RN_F32, false>), grid, blk, 0, st, a, w, gate, out);
+  }
   return hipGetLastError();
 }
 

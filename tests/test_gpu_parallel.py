@@ -69,6 +69,19 @@ def test_raw_output(N, pos0, alpha, nd, nr):
     assert rel_inf(out.cpu(), ref) <= MFMA_BAR
 
 
+def test_small_decay_per_element_exp():
+    """A head with gamma below 0.5035 (gamma^-127 outside float's normal range) makes the
+    whole call take the kernel instance that forms each decay with its own exp2; the
+    other head of the call goes through it too."""
+    x = W.make_inputs(wl(N=300, H=2))
+    gamma = np.array([0.3, 0.97], dtype=np.float32)
+    out = rn().rn_retention_parallel(dev(x["q"]), dev(x["k"]), dev(x["v"]), gamma, x["theta"],
+                                     out_dtype=torch.float32, qk_scale=1 / 16, norm_d=True,
+                                     norm_r=True)
+    ref = O.parallel(x["q"], x["k"], x["v"], gamma, x["theta"], 0, 1 / 16, True, True)
+    assert rel_inf(out.cpu(), ref) <= MFMA_BAR
+
+
 def test_gn_gate_affine_and_bf16_out():
     w = wl(N=190, gate=True, H=3)
     x = W.make_inputs(w)
