@@ -298,31 +298,35 @@ parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
   // 16w + l16, the keys 16i + 4g + r: four consecutive keys per tile i.
   auto scores = [&](int kb) {
     const int buf = kb & 1;
-    f32x4 sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = 16 * i + l16;        // key row (A operand row)
-      f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        z = mfma(as_f16x8(sm.kh[buf][kh_unit(s, 4 * c + g)]), qf[c], z);
-      sc[i] = z;
-    }
     const int dq = qb * kQ - kb * kT;                 // t - s without the in-block offsets
     const bool diag = kb >= 2 * qb;                   // only these blocks hold s > t
+    // two key tiles at a time: two independent accumulation chains, each pair decayed
+    // and written to LDS before the next pair starts (fewer live registers)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float bl = rl * exp2f(lg * float(dq - 16 * i));
-      float val[4];
+    for (int ip = 0; ip < 2; ++ip) {
+      f32x4 z[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d = dq + 16 * w + l16 - 16 * i - 4 * g - r;
-        const float f = FACT ? bl * gr[r] : exp2f(lg * float(d));
-        val[r] = (diag && d < 0) ? 0.f : sc[i][r] * f;
-        rsum += val[r];
+      for (int c = 0; c < 8; ++c) {
+        const f16x8 k0 = as_f16x8(sm.kh[buf][kh_unit(32 * ip + l16, 4 * c + g)]);
+        const f16x8 k1 = as_f16x8(sm.kh[buf][kh_unit(32 * ip + 16 + l16, 4 * c + g)]);
+        z[0] = mfma(k0, qf[c], z[0]);
+        z[1] = mfma(k1, qf[c], z[1]);
       }
-      *reinterpret_cast<u32x2*>(&sm.p[buf][16 * w + l16][vt_pos(16 * i + 4 * g)]) =
-          u32x2{pack_f16x2(val[0], val[1]), pack_f16x2(val[2], val[3])};
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * ip + ii;
+        const float bl = rl * exp2f(lg * float(dq - 16 * i));
+        float val[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = dq + 16 * w + l16 - 16 * i - 4 * g - r;
+          const float f = FACT ? bl * gr[r] : exp2f(lg * float(d));
+          val[r] = (diag && d < 0) ? 0.f : z[ii][r] * f;
+          rsum += val[r];
+        }
+        *reinterpret_cast<u32x2*>(&sm.p[buf][16 * w + l16][vt_pos(16 * i + 4 * g)]) =
+            u32x2{pack_f16x2(val[0], val[1]), pack_f16x2(val[2], val[3])};
+      }
     }
   };
 
