@@ -122,9 +122,9 @@ typedef struct rn_desc {
 
 /*
  * Bytes of device workspace rn_retention_parallel needs for `desc` (0 for an invalid
- * descriptor or when the call needs none). The MFMA path stores the rotated q and k
- * and the blocked, transposed v in half precision there: 2*B*H*ceil(N/64)*64*(2*d_k + d_v)
- * bytes, linear in N.
+ * descriptor or when the call needs none). The MFMA path stores the rotated k and the
+ * blocked, transposed v in half precision there: 2*B*H*ceil(N/64)*64*(d_k + d_v) bytes,
+ * linear in N (q is rotated where it is read).
  */
 size_t rn_parallel_workspace_bytes(const rn_desc* desc);
 

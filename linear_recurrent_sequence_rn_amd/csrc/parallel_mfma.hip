@@ -86,18 +86,18 @@ __device__ __forceinline__ void st_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, 
       __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, 0);
 }
 
-// Workspace per head: Qh [Np][256], Kh [Np][256], Vt [Np/64][512][64], all half,
-// with Np = N rounded up to 64 (rows past N are zero).
+// Workspace per head: Kh [Np][256], Vt [Np/64][512][64], both half, with Np = N rounded
+// up to 64 (rows past N are zero). (q is rotated by the main kernel itself: each query
+// row is read by one workgroup only.)
 struct Ws {
-  size_t q, k, v, head;   // element offsets within a head, and elements per head
+  size_t k, v, head;   // element offsets within a head, and elements per head
 };
 __host__ __device__ inline Ws ws_layout(int N) {
   const size_t np = size_t((N + kT - 1) / kT) * kT;
   Ws w;
-  w.q = 0;
-  w.k = np * kDK;
-  w.v = 2 * np * kDK;
-  w.head = 2 * np * kDK + np * kDV;
+  w.k = 0;
+  w.v = np * kDK;
+  w.head = np * kDK + np * kDV;
   return w;
 }
 
@@ -111,32 +111,29 @@ __host__ __device__ constexpr int vt_pos(int s) {
 }
 
 // ---- prep: one 256-thread block per (64-row block, head) ------------------------------
-// bf16 inputs only. q and k: thread = (group of 4 coordinate pairs = 16 bytes, group of
-// 8 rows); 16-byte loads, angles by recurrence along the rows. v: thread = 8 rows x 8
-// columns, transposed in registers, assembled as V^T (keys in vt_pos order) in LDS and
-// written out as one contiguous run.
-__global__ void __launch_bounds__(256) parallel_prep(CallArgs a, const uint16_t* q,
-                                                     const uint16_t* k, const uint16_t* v,
-                                                     uint16_t* ws) {
+// bf16 inputs only. k: thread = (group of 4 coordinate pairs = 16 bytes, group of 8 rows);
+// 16-byte loads, angles by recurrence along the rows. v: thread = 8 rows x 8 columns,
+// transposed in registers, assembled as V^T (keys in vt_pos order) in LDS and written
+// out as one contiguous run.
+__global__ void __launch_bounds__(256) parallel_prep(CallArgs a, const uint16_t* k,
+                                                     const uint16_t* v, uint16_t* ws) {
   const int jb = blockIdx.x, bh = blockIdx.y;
   const int N = a.N, tid = threadIdx.x;
   const Ws L = ws_layout(N);
   uint16_t* base = ws + size_t(bh) * L.head;
   const int row0 = jb * kT;
   const int64_t bytes_qk = int64_t(N) * kDK * 2, bytes_v = int64_t(N) * kDV * 2;
-  const __amdgpu_buffer_rsrc_t rq = range_rsrc(q + size_t(bh) * N * kDK, bytes_qk);
   const __amdgpu_buffer_rsrc_t rk = range_rsrc(k + size_t(bh) * N * kDK, bytes_qk);
   const __amdgpu_buffer_rsrc_t rv = range_rsrc(v + size_t(bh) * N * kDV, bytes_v);
   // Every load of the thread is issued before any store (the compiler cannot reorder a
   // load past a store to memory it cannot prove distinct), so the 32 loads are in
   // flight together.
-  const int pg = tid & 31, rg = tid >> 5;     // q/k: pairs 4pg..4pg+3, rows 8rg..8rg+7
-  u32x4 xq[8], xk[8], xv[2][8];
+  const int pg = tid & 31, rg = tid >> 5;     // k: pairs 4pg..4pg+3, rows 8rg..8rg+7
+  u32x4 xk[8], xv[2][8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const uint32_t off = static_cast<uint32_t>(((row0 + 8 * rg + u) * kDK + 8 * pg) * 2);
-    xq[u] = ld_b128(rq, off);   // zero past N
-    xk[u] = ld_b128(rk, off);
+    xk[u] = ld_b128(rk, off);   // zero past N
   }
   // v: 8x8 tiles; 64 x 512 block = 512 tiles, 2 per thread: columns 8cg..8cg+7, rows
   // 8sg..8sg+7 of tile tid + 256 rep
@@ -156,22 +153,18 @@ __global__ void __launch_bounds__(256) parallel_prep(CallArgs a, const uint16_t*
       angle_cs(1, th, &c1[i], &s1[i]);
       angle_cs(a.pos0 + row0 + 8 * rg, th, &cs[i], &sn[i]);
     }
-    const float al = a.alpha;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int t = row0 + 8 * rg + u;
-      u32x4 oq, ok;
+      u32x4 ok;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float q0 = __uint_as_float(xq[u][i] << 16), q1 = __uint_as_float(xq[u][i] & 0xffff0000u);
         const float k0 = __uint_as_float(xk[u][i] << 16), k1 = __uint_as_float(xk[u][i] & 0xffff0000u);
-        oq[i] = pack_f16x2(al * (q0 * cs[i] - q1 * sn[i]), al * (q0 * sn[i] + q1 * cs[i]));
         ok[i] = pack_f16x2(k0 * cs[i] - k1 * sn[i], k0 * sn[i] + k1 * cs[i]);
         const float cn = cs[i] * c1[i] - sn[i] * s1[i];
         sn[i] = cs[i] * s1[i] + sn[i] * c1[i];
         cs[i] = cn;
       }
-      *reinterpret_cast<u32x4*>(base + L.q + size_t(t) * kDK + 8 * pg) = oq;
       *reinterpret_cast<u32x4*>(base + L.k + size_t(t) * kDK + 8 * pg) = ok;
     }
   }
@@ -236,7 +229,7 @@ __device__ __forceinline__ int kh_unit(int s, int u) { return 32 * s + (u ^ (s &
 // exp2 (decided on the host, so the score loop has no branch on it).
 template <int OUT, bool FACT>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
+parallel_main(CallArgs a, const uint16_t* q, const uint16_t* ws, const void* gate, void* out) {
   const int N = a.N, nb = (N + kT - 1) / kT, nq = (N + kQ - 1) / kQ;
   const int BH = a.B * a.H;
   // Workgroups are dispatched round-robin over the 8 XCDs (id mod 8). XCD x owns the
@@ -253,7 +246,7 @@ parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
   const Ws L = ws_layout(N);
   const uint16_t* base = ws + size_t(bh) * L.head;
   const int64_t np = int64_t(nb) * kT;
-  const __amdgpu_buffer_rsrc_t rq = range_rsrc(base + L.q, np * kDK * 2);
+  const __amdgpu_buffer_rsrc_t rq = range_rsrc(q + size_t(bh) * N * kDK, int64_t(N) * kDK * 2);
   const __amdgpu_buffer_rsrc_t rk = range_rsrc(base + L.k, np * kDK * 2);
   const __amdgpu_buffer_rsrc_t rv = range_rsrc(base + L.v, np * kDV * 2);
   __shared__ PShared sm;
@@ -273,12 +266,31 @@ parallel_main(CallArgs a, const uint16_t* ws, const void* gate, void* out) {
     }
   };
 
-  // this wave's 16 query rows (A operand: row t, k = dk)
+  // this wave's 16 query rows (B operand of the transposed score product: column t,
+  // k = dk), rotated here and scaled by alpha: lane (l16, g) holds row t_row, coordinate
+  // pairs 16c + 4g .. +3 of fragment c (rows past N read as zeros)
   const int t_row = qb * kQ + 16 * w + l16;
   f16x8 qf[8];
+  {
+    u32x4 xq[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
-    qf[c] = as_f16x8(ld_b128(rq, static_cast<uint32_t>((t_row * kDK + 32 * c + 8 * g) * 2)));
+    for (int c = 0; c < 8; ++c)
+      xq[c] = ld_b128(rq, static_cast<uint32_t>((t_row * kDK + 32 * c + 8 * g) * 2));
+    const int64_t p = a.pos0 + t_row;
+    const float al = a.alpha;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float cs, sn;
+        angle_cs_fast(p, a.ap.theta[16 * c + 4 * g + i], &cs, &sn);
+        const float q0 = __uint_as_float(xq[c][i] << 16), q1 = __uint_as_float(xq[c][i] & 0xffff0000u);
+        o[i] = pack_f16x2(al * (q0 * cs - q1 * sn), al * (q0 * sn + q1 * cs));
+      }
+      qf[c] = as_f16x8(o);
+    }
+  }
 
   float rsum = 0.f;   // partial signed sum of the scores of row 16w + l16
 
@@ -556,8 +568,8 @@ hipError_t launch_parallel_mfma(const CallArgs& a, int out_dt, const void* q, co
   const int BH = a.B * a.H;
   uint16_t* w = static_cast<uint16_t*>(ws);
   hipLaunchKernelGGL(parallel_prep, dim3(nb, BH), dim3(256), 0, st, a,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), w);
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), w);
+  const uint16_t* qh = static_cast<const uint16_t*>(q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nq = (a.N + kQ - 1) / kQ;
@@ -566,11 +578,11 @@ hipError_t launch_parallel_mfma(const CallArgs& a, int out_dt, const void* q, co
   for (int h = 0; h < a.H; ++h) fact = fact && a.hp.log2g[h] * 127.f >= -126.f;
   const dim3 blk(kWaves * 64);
   if (out_dt == RN_BF16) {
-    if (fact) hipLaunchKernelGGL((parallel_main<RN_BF16, true>), grid, blk, 0, st, a, w, gate, out);
-    else hipLaunchKernelGGL((parallel_main<RN_BF16, false>), grid, blk, 0, st, a, w, gate, out);
+    if (fact) hipLaunchKernelGGL((parallel_main<RN_BF16, true>), grid, blk, 0, st, a, qh, w, gate, out);
+    else hipLaunchKernelGGL((parallel_main<RN_BF16, false>), grid, blk, 0, st, a, qh, w, gate, out);
   } else {
-    if (fact) hipLaunchKernelGGL((parallel_main<RN_F32, true>), grid, blk, 0, st, a, w, gate, out);
-    else hipLaunchKernelGGL((parallel_main<RN_F32, false>), grid, blk, 0, st, a, w, gate, out);
+    if (fact) hipLaunchKernelGGL((parallel_main<RN_F32, true>), grid, blk, 0, st, a, qh, w, gate, out);
+    else hipLaunchKernelGGL((parallel_main<RN_F32, false>), grid, blk, 0, st, a, qh, w, gate, out);
   }
   return hipGetLastError();
 }

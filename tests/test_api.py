@@ -163,7 +163,7 @@ def test_parallel_workspace():
     big = dict(d_k=256, d_v=512, theta=np.ones(128), H=8, gamma=np.full(8, 0.9), N=2048)
     d, keep = desc(**big)
     need = rn.lib.rn_parallel_workspace_bytes(ctypes.byref(d))
-    assert need == 8 * 2048 * (2 * 256 + 512) * 2          # q, k rotated + v transposed, half
+    assert need == 8 * 2048 * (256 + 512) * 2              # k rotated + v transposed, half
     assert par(d, ws_bytes=need - 1) == rn.RN_ERR_WORKSPACE
     assert par(d, ws=None) == rn.RN_ERR_WORKSPACE
     assert par(d, ws=ctypes.c_void_p(0x1010), ws_bytes=need) == rn.RN_ERR_INVALID_ARG   # misaligned
