@@ -85,8 +85,8 @@ __device__ __forceinline__ u32x4 raw8(__amdgpu_buffer_rsrc_t r, int64_t pitch, i
 // column n is row br0 + n of B, read from column bc0 on. Without FROMP, K is a multiple of
 // 8 and runs at or past K read as zeros; with FROMP the scores past the product's extent
 // are zero. The next slice is fetched into registers while the MFMAs of the current run.
-template <int NCT, bool FROMP, int NSET = 1>
-__device__ __forceinline__ void tmm16(float (&acc)[4][NCT], int K, TileSharedH& sm, const Src& A,
+template <int NCT, bool FROMP, int NSET = 1, class SM>
+__device__ __forceinline__ void tmm16(float (&acc)[4][NCT], int K, SM& sm, const Src& A,
                                       int ar0, float amul, float alg, int ae0, int aesg,
                                       const Src& B, int br0, int bc0) {
   constexpr int NRUN = NCT / 4;   // B runs of 8 per thread and slice (16 NCT columns x 4 runs)
@@ -159,6 +159,129 @@ __device__ __forceinline__ void tmm16(float (&acc)[4][NCT], int K, TileSharedH& 
   for (int j = 0; j < NCT; ++j)
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r][j] += t[j][r];
+}
+
+// ---- products with both operands copied straight into LDS -------------------------------
+// Shared memory of the tile kernels. A ring of NSLOT product slices (the copy path): a
+// slot holds A's 64 rows x 32 k-values (256 units of 16 bytes) and then B's columns x 32
+// k-values (up to BUNITS units), as 16-byte runs copied from the half sources by buffer
+// loads into LDS. Run q (k-values 8q..8q+7) of row (column) n sits at unit
+// 4n + (q ^ ((n >> 2) & 3)), so that the 16 rows a lane group reads at one q fall into 16
+// different 4-bank groups. The ring shares its space with the staging buffers of the
+// register path (As, Bs: operands that need a conversion), and, after the products, with
+// the rotation buffer and the GroupNorm backward's sums and dO tile.
+template <int NSLOT, int BUNITS, int DTROWS = 1>
+struct alignas(16) TileSharedD {
+  union {
+    struct {
+      union {
+        u32x4 ring[NSLOT][256 + BUNITS];
+        struct {
+          _Float16 As[kR][kLdH];
+          _Float16 Bs[kMaxDv][kLdH];
+        };
+      };
+      _Float16 P[kR][kLdPH];
+    } m;
+    float rot[kR][kMaxDk + 4];
+    struct {
+      float sw[16][kLdB];
+      float sb[16][kLdB];
+      uint16_t dtile[DTROWS][kMaxDv + 8];   // (bm_dout only: kR rows)
+    } gn;
+  };
+};
+template <int NS, int BU, int DT> __device__ __forceinline__ float* rot_buf(TileSharedD<NS, BU, DT>& sm) { return &sm.rot[0][0]; }
+template <int NS, int BU, int DT> __device__ __forceinline__ float* gn_sw(TileSharedD<NS, BU, DT>& sm) { return &sm.gn.sw[0][0]; }
+template <int NS, int BU, int DT> __device__ __forceinline__ float* gn_sb(TileSharedD<NS, BU, DT>& sm) { return &sm.gn.sb[0][0]; }
+
+__device__ __forceinline__ int ring_unit(int n, int q) { return 4 * n + (q ^ ((n >> 2) & 3)); }
+
+// Barrier for LDS traffic only: this wave's LDS operations are complete; copies into LDS
+// that are still in flight stay in flight (__syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+template <int VM>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(VM >= 0 && VM <= 63, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (15 << 8) | (((VM >> 4) & 3) << 14));
+  __asm__ volatile("" ::: "memory");
+}
+
+// acc += A B as tmm16 does, for half sources only (no conversion): both operands of slice
+// k (32 k-values) are copied into ring slot k % NSLOT while slices k - NSLOT + 1 .. k - 1
+// are multiplied, one barrier per slice. A's row scaling amul * gamma^(ae0 + aesg i) is
+// applied to the product's rows instead of A's (C = diag(f) A B). The caller has issued no
+// store that is still in flight (the copies are waited for by count, in issue order).
+template <int NCT, bool FROMP, int NSLOT, class SM>
+__device__ __forceinline__ void tmm16d(float (&acc)[4][NCT], int K, SM& sm, const Src& A,
+                                       int ar0, float amul, float alg, int ae0, int aesg,
+                                       const Src& B, int br0, int bc0) {
+  constexpr int NRUN = NCT / 4;                    // B copies per wave and slice
+  constexpr int NOPS = NRUN + (FROMP ? 0 : 1);     // copies per wave and slice
+  static_assert(NSLOT >= 2 && (NSLOT - 2) * NOPS <= 63, "ring depth");
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, g = l >> 4;
+  const __amdgpu_buffer_rsrc_t rsa = src_rsrc(A), rsb = src_rsrc(B);
+  const int nsl = (K + kKH - 1) / kKH;
+  // A copy of this lane: unit 64 w + l of the slot's A part
+  const int ap = 64 * w + l, arow = ap >> 2, aq = (ap & 3) ^ ((arow >> 2) & 3);
+  auto issue = [&](int k, int slot) __attribute__((always_inline)) {
+    const int k0 = k * kKH;
+    if constexpr (!FROMP) {
+      const int kq = k0 + 8 * aq;
+      const uint32_t off = kq < K ? static_cast<uint32_t>(((ar0 + arow) * A.pitch + kq) * 2) : kRunSink;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsa, (__attribute__((address_space(3))) void*)(&sm.m.ring[slot][64 * w]), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < NRUN; ++u) {
+      const int p = (NRUN * w + u) * 64 + l, n = p >> 2, q = (p & 3) ^ ((n >> 2) & 3);
+      const int kq = k0 + 8 * q;
+      const uint32_t off = kq < K ? static_cast<uint32_t>(((br0 + n) * B.pitch + bc0 + kq) * 2) : kRunSink;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsb, (__attribute__((address_space(3))) void*)(&sm.m.ring[slot][256 + (NRUN * w + u) * 64]), 16,
+          off, 0, 0, 0);
+    }
+  };
+  f32x4 t[NCT];
+#pragma unroll
+  for (int j = 0; j < NCT; ++j) t[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  lds_barrier();   // earlier reads of the ring (and of P's writes) are done
+#pragma unroll
+  for (int k = 0; k < NSLOT - 1; ++k)
+    if (k < nsl) issue(k, k);
+  int slot = 0;
+  for (int k = 0; k < nsl; ++k) {
+    // this wave's copies of slice k are complete (those of the next NSLOT-2 slices, when
+    // issued, may stay in flight)
+    if (k + NSLOT - 2 < nsl) wait_vm<(NSLOT - 2) * NOPS>();
+    else wait_vm<0>();
+    lds_barrier();   // every wave's copies of slice k landed; slice k-1's reads are done
+    if (k + NSLOT - 1 < nsl) issue(k + NSLOT - 1, slot == 0 ? NSLOT - 1 : slot - 1);
+    const u32x4* rs = sm.m.ring[slot];
+    f16x8 av;
+    if constexpr (FROMP) av = *reinterpret_cast<const f16x8*>(&sm.m.P[16 * w + l16][k * kKH + 8 * g]);
+    else av = __builtin_bit_cast(f16x8, rs[ring_unit(16 * w + l16, g)]);
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const f16x8 bv = __builtin_bit_cast(f16x8, rs[256 + ring_unit(16 * j + l16, g)]);
+      t[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, t[j], 0, 0, 0);
+    }
+    slot = slot + 1 == NSLOT ? 0 : slot + 1;
+  }
+  float f[4] = {1.f, 1.f, 1.f, 1.f};
+  if (!FROMP && (aesg != 0 || amul != 1.f)) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f[r] = amul * exp2f(alg * float(ae0 + aesg * (16 * w + 4 * g + r)));
+  }
+#pragma unroll
+  for (int j = 0; j < NCT; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r][j] += f[r] * t[j][r];
 }
 
 // Workspace (half), per head: row-major rotated q and k, their transposes, v transposed,
@@ -410,25 +533,225 @@ __global__ void __launch_bounds__(256) bm_scan(CallArgs a, const uint16_t* XT, c
   }
 }
 
-// ---- tile kernels (grid: (64-row tiles of the chunks, b*H + h)) ----------------------------
+// ---- tile kernels (1-D grid over (head, chunk, 64-row tile)) ----------------------------------
+// Workgroups are dispatched round-robin over the 8 XCDs (id mod 8). The four row tiles of
+// a chunk read the same chunk operands (its keys, values, state), so they are numbered to
+// run one after the other on one XCD, where the later ones find those operands in L2:
+// id = 8 (4 (P / 8) + tile) + P % 8 for chunk P = bh * nch + c.
+struct TileAt {
+  TileRows T;
+  int bh;
+  bool valid;
+};
+__device__ __forceinline__ TileAt tile_at(int N, int BH, int nch) {
+  const int id = blockIdx.x, j = id >> 3;
+  const int P = 8 * (j >> 2) + (id & 7), tile = j & 3;
+  TileAt r;
+  r.valid = P < BH * nch;
+  r.bh = r.valid ? P / nch : 0;
+  const int c = r.valid ? P % nch : 0;
+  r.T.c = c;
+  r.T.c0 = c * kBC;
+  r.T.c1 = min(N, r.T.c0 + kBC);
+  r.T.r0 = r.T.c0 + kR * tile;
+  r.T.r1 = min(r.T.c1, r.T.r0 + kR);
+  return r;
+}
 struct Heads {
   const uint16_t *QR, *KR, *QT, *KT, *VT, *DR, *DT, *S, *ST, *G, *GT;
   int Np, nch;
 };
+
+// ---- GroupNorm / gate backward of a bm_dout tile ----------------------------------------
+// Each wave takes the 16 rows it holds in its accumulators (rows 16w + 4g + r, columns
+// l16 + 16 j), staged through LDS in float32, and works through them one row at a time with
+// 8 consecutive columns per lane, so that dout, gate and dgate move in 16-byte pieces.
+// Per row: dO = rstd (dxh - mean(dxh) - xh mean(dxh xh)), dxh = dy w, dy = dout (* swish(g)),
+// written (half) over the row's own staging; the gate's gradient is stored; per-column
+// sums of dy xh and dy gather in LDS and are added to dgn_w, dgn_b once per tile.
+constexpr int kOLd = kMaxDv + 4;   // staging row pitch (floats); a dO row (half) fits in its first half
+__device__ __forceinline__ float lane_sum64(float x) {   // over the wave; every lane receives it
+  x = row16_sum(x);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+}
+template <int OUTD, bool AFF>
+__device__ __forceinline__ void gn_backward_rows(float* ost, const float (&o)[4][32],
+                                                 const CallArgs& a, int h, int bh, int r0, int r1,
+                                                 const void* gate, const void* dout, void* dgate,
+                                                 float* dgn_w, float* dgn_b) {
+  const int dv = a.dv, N = a.N;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, g = l >> 4;
+  const bool gt = a.flags & RN_EPI_GATE;
+  const bool sums = AFF && (dgn_w || dgn_b);
+  constexpr int esz = OUTD == RN_F32 ? 4 : 2;
+  const int64_t hoff = int64_t(bh) * N * dv;
+  const __amdgpu_buffer_rsrc_t rdo = head_rsrc(static_cast<const char*>(dout) + hoff * esz, int64_t(N) * dv * esz);
+  const __amdgpu_buffer_rsrc_t rga =
+      head_rsrc(gt ? static_cast<const char*>(gate) + hoff * 2 : nullptr, gt ? int64_t(N) * dv * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rdg =
+      head_rsrc(gt && dgate ? static_cast<char*>(dgate) + hoff * 2 : nullptr, gt && dgate ? int64_t(N) * dv * 2 : 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int j = 0; j < 32; ++j) ost[(16 * w + 4 * g + r) * kOLd + l16 + 16 * j] = o[r][j];
+  __syncthreads();
+  const int c0 = 8 * l;
+  const bool cl = c0 < dv;   // this lane has columns
+  float wv[8], bv[8], swa[8], sba[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    wv[c] = (AFF && a.gn_w && cl) ? a.gn_w[h * dv + c0 + c] : 1.f;
+    bv[c] = (AFF && a.gn_b && cl) ? a.gn_b[h * dv + c0 + c] : 0.f;
+    swa[c] = sba[c] = 0.f;
+  }
+  const float inv_dv = 1.0f / float(dv);
+  // dout / gate of row rr (16-byte pieces). Byte offsets within the head; rows past the
+  // tile and lanes past d_v use an offset past the buffers' ranges (loads read zeros,
+  // stores are dropped).
+  auto boff = [&](int rr, int bytes) -> uint32_t {
+    const int t = r0 + 16 * w + rr;
+    return (t < r1 && cl) ? static_cast<uint32_t>((t * dv + c0) * bytes) : 0x80000000u;
+  };
+  // all rows of a batch are loaded before the first is used (16 rows for bf16 dout, 8 for
+  // float32), so their latencies overlap
+  constexpr int RB = OUTD == RN_F32 ? 8 : 16;
+  constexpr int DW = OUTD == RN_F32 ? 2 : 1;   // 16-byte pieces of dout per row and lane
+#pragma unroll
+  for (int rb = 0; rb < 16; rb += RB) {
+    u32x4 dl[RB][DW], gl[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const uint32_t od = boff(rb + i, esz), og = boff(rb + i, 2);
+#pragma unroll
+      for (int p = 0; p < DW; ++p)
+        dl[i][p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rdo, od + 16 * p, 0, 0));
+      gl[i] = gt ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rga, og, 0, 0))
+                 : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int rr = rb + i;
+      float d0[8], gv[8];
+      if constexpr (OUTD == RN_F32) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          d0[c] = __uint_as_float(dl[i][0][c]);
+          d0[4 + c] = __uint_as_float(dl[i][DW - 1][c]);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          d0[2 * c] = __uint_as_float(dl[i][0][c] << 16);
+          d0[2 * c + 1] = __uint_as_float(dl[i][0][c] & 0xffff0000u);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        gv[2 * c] = __uint_as_float(gl[i][c] << 16);
+        gv[2 * c + 1] = __uint_as_float(gl[i][c] & 0xffff0000u);
+      }
+      const uint32_t og = boff(rr, 2);
+      const int row = 16 * w + rr;
+      float x[8];
+      {
+        const float4 x0 = *reinterpret_cast<const float4*>(&ost[row * kOLd + c0]);
+        const float4 x1 = *reinterpret_cast<const float4*>(&ost[row * kOLd + c0 + 4]);
+        x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+        x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+      }
+      float s1 = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s1 += cl ? x[c] : 0.f;
+      const float mean = lane_sum64(s1) * inv_dv;
+      float s2 = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float dd = x[c] - mean;
+        s2 += cl ? dd * dd : 0.f;
+      }
+      const float rstd = __builtin_amdgcn_rsqf(lane_sum64(s2) * inv_dv + a.eps);
+      float xh[8], dxh[8], dg[8];
+      float m1 = 0.f, m2 = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        xh[c] = (x[c] - mean) * rstd;
+        float dy = d0[c];
+        if (gt) {
+          const float gg = gv[c];
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gg));
+          dy = d0[c] * gg * sg;
+          dg[c] = d0[c] * (xh[c] * wv[c] + bv[c]) * sg * (1.0f + gg * (1.0f - sg));
+        }
+        dxh[c] = dy * wv[c];
+        m1 += dxh[c];
+        m2 += dxh[c] * xh[c];
+        if constexpr (AFF) {
+          swa[c] += dy * xh[c];
+          sba[c] += dy;
+        }
+      }
+      if (gt) {
+        const u32x4 pk{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]), pack_bf16x2(dg[4], dg[5]),
+                       pack_bf16x2(dg[6], dg[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, pk), rdg, og, 0, 0);
+      }
+      m1 = lane_sum64(m1) * inv_dv;
+      m2 = lane_sum64(m2) * inv_dv;
+      float od[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) od[c] = rstd * (dxh[c] - m1 - xh[c] * m2);
+      // the row's values were read above (this wave's LDS operations run in order)
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(&ost[row * kOLd]) + c0) =
+          u32x4{pack_h2(od[0], od[1]), pack_h2(od[2], od[3]), pack_h2(od[4], od[5]), pack_h2(od[6], od[7])};
+    }
+  }
+  // per-wave column sums go to the second halves of the wave's staging rows (the dO rows
+  // take the first halves): row 16w + 2c + s holds, from float kOLd / 2 on, sum s
+  // (0: dy xh, 1: dy) of column 8l + c at index l
+  auto part = [&](int ww, int c, int sidx) { return ost + (16 * ww + 2 * c + sidx) * kOLd + kOLd / 2; };
+  if (sums) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      part(w, c, 0)[l] = swa[c];
+      part(w, c, 1)[l] = sba[c];
+    }
+  }
+  __syncthreads();
+  if (sums)
+    for (int col = tid; col < dv; col += 256) {
+      const int lc = col >> 3, c = col & 7;
+      float xw = 0.f, xb = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        xw += part(ww, c, 0)[lc];
+        xb += part(ww, c, 1)[lc];
+      }
+      if (dgn_w) atomicAdd(&dgn_w[h * dv + col], xw);
+      if (dgn_b) atomicAdd(&dgn_b[h * dv + col], xb);
+    }
+}
 
 // o recomputed: alpha (Qh Kh^T (.) D) V + alpha xi Qh S_c, then the GroupNorm / gate backward.
 template <int OUTD, bool AFF>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bm_dout(CallArgs a, Heads Hd, const void* gate, const void* dout, uint16_t* DR, uint16_t* DT,
         void* dgate, float* dgn_w, float* dgn_b) {
-  __shared__ TileSharedH sm;
+  __shared__ TileSharedD<3, kMaxDv * 4> sm;
+  static_assert(sizeof(sm) >= kR * kOLd * sizeof(float), "staging fits");
   // dO of the tile in half (rows past the tile's end hold zeros), copied out at the end in
-  // 16-byte runs, row-major to DR and transposed to DT
-  __shared__ __attribute__((aligned(16))) uint16_t dtile[kR][kMaxDv + 8];
+  // 16-byte runs, row-major to DR and transposed to DT; row r at dt + r * kDtLd
+  float* ost = reinterpret_cast<float*>(&sm);
+  uint16_t* dt = reinterpret_cast<uint16_t*>(ost);
+  constexpr int kDtLd = 2 * kOLd;
   const int dk = a.dk, dv = a.dv, N = a.N, Np = Hd.Np;
-  const TileRows T = tile_rows(N);
-  if (T.r0 >= T.r1) return;
-  const int bh = blockIdx.y, h = bh % a.H;
+  const TileAt at = tile_at(N, a.B * a.H, Hd.nch);
+  const TileRows T = at.T;
+  if (!at.valid || T.r0 >= T.r1) return;
+  const int bh = at.bh, h = bh % a.H;
   const float lg = a.hp.log2g[h];
   const Src Q{Hd.QR + int64_t(bh) * N * dk, dk, N, false};
   const Src K{Hd.KR + int64_t(bh) * N * dk, dk, N, false};
@@ -436,16 +759,22 @@ bm_dout(CallArgs a, Heads Hd, const void* gate, const void* dout, uint16_t* DR, 
   const Src ST{Hd.ST + (int64_t(bh) * Hd.nch + T.c) * dk * dv, dk, dv, false};
   float m[4][16];
   zero_acc(m);
-  tmm16<16, false>(m, dk, sm, Q, T.r0, 1.f, 0.f, 0, 0, K, T.c0, 0);
+  tmm16d<16, false, 3>(m, dk, sm, Q, T.r0, 1.f, 0.f, 0, 0, K, T.c0, 0);
   store_scores<true>(sm, m, T.r0, T.r1, T.c0, T.r1, lg, a.alpha);
   float o[4][32];
   zero_acc(o);
-  tmm16<32, true>(o, T.r1 - T.c0, sm, Q, 0, 1.f, 0.f, 0, 0, VT, 0, T.c0);
-  tmm16<32, false>(o, dk, sm, Q, T.r0, a.alpha, lg, T.r0 - T.c0 + 1, 1, ST, 0, 0);
-  gn_backward_tile<RN_BF16, OUTD, AFF>(sm, o, a, h, bh, T.r0, T.r1, gate, dout, dgate, dgn_w, dgn_b,
-      [&](int64_t, int, bool ok, float x, int rloc, int col) __attribute__((always_inline)) {
-        dtile[rloc][col] = ok ? h_bits(x) : uint16_t(0);
-      });
+  tmm16d<32, true, 3>(o, T.r1 - T.c0, sm, Q, 0, 1.f, 0.f, 0, 0, VT, 0, T.c0);
+  tmm16d<32, false, 3>(o, dk, sm, Q, T.r0, a.alpha, lg, T.r0 - T.c0 + 1, 1, ST, 0, 0);
+  __syncthreads();   // the products' reads of the ring are done (the staging shares its space)
+  if (a.flags & RN_EPI_GN) {
+    gn_backward_rows<OUTD, AFF>(ost, o, a, h, bh, T.r0, T.r1, gate, dout, dgate,
+                                dgn_w, dgn_b);
+  } else {
+    gn_backward_tile<RN_BF16, OUTD, AFF>(sm, o, a, h, bh, T.r0, T.r1, gate, dout, dgate, dgn_w, dgn_b,
+        [&](int64_t, int, bool ok, float x, int rloc, int col) __attribute__((always_inline)) {
+          dt[rloc * kDtLd + col] = ok ? h_bits(x) : uint16_t(0);
+        });
+  }
   __syncthreads();
   // row-major: the tile's rows below its end
   const int rows = T.r1 - T.r0, runs = dv / 8;
@@ -453,7 +782,7 @@ bm_dout(CallArgs a, Heads Hd, const void* gate, const void* dout, uint16_t* DR, 
   for (int e = threadIdx.x; e < rows * runs; e += 256) {
     const int rr = e / runs, c8 = e - rr * runs;
     *reinterpret_cast<u32x4*>(DRh + int64_t(rr) * dv + 8 * c8) =
-        *reinterpret_cast<const u32x4*>(&dtile[rr][8 * c8]);
+        *reinterpret_cast<const u32x4*>(&dt[rr * kDtLd + 8 * c8]);
   }
   // transposed: 8 tokens of one column per run, all 64 columns of the tile (the rows past
   // the sequence's end are zeros, as the padded layout wants)
@@ -463,7 +792,7 @@ bm_dout(CallArgs a, Heads Hd, const void* gate, const void* dout, uint16_t* DR, 
     uint32_t wds[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      wds[k] = uint32_t(dtile[8 * tg + 2 * k][col]) | (uint32_t(dtile[8 * tg + 2 * k + 1][col]) << 16);
+      wds[k] = uint32_t(dt[(8 * tg + 2 * k) * kDtLd + col]) | (uint32_t(dt[(8 * tg + 2 * k + 1) * kDtLd + col]) << 16);
     *reinterpret_cast<u32x4*>(DTh + int64_t(col) * Np + 8 * tg) = u32x4{wds[0], wds[1], wds[2], wds[3]};
   }
 }
@@ -471,11 +800,12 @@ bm_dout(CallArgs a, Heads Hd, const void* gate, const void* dout, uint16_t* DR, 
 // dQh = [alpha (dO V^T) (.) D] Kh + alpha xi dO S_c^T, rotated back.
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bm_dq(CallArgs a, Heads Hd, const uint16_t* v, void* dq) {
-  __shared__ TileSharedH sm;
+  __shared__ TileSharedD<2, kMaxDv * 2> sm;
   const int dk = a.dk, dv = a.dv, N = a.N, Np = Hd.Np;
-  const TileRows T = tile_rows(N);
-  if (T.r0 >= T.r1) return;
-  const int bh = blockIdx.y, h = bh % a.H;
+  const TileAt at = tile_at(N, a.B * a.H, Hd.nch);
+  const TileRows T = at.T;
+  if (!at.valid || T.r0 >= T.r1) return;
+  const int bh = at.bh, h = bh % a.H;
   const float lg = a.hp.log2g[h];
   const Src D{Hd.DR + int64_t(bh) * N * dv, dv, N, false};
   const Src V{v + int64_t(bh) * N * dv, dv, N, true};
@@ -487,19 +817,20 @@ bm_dq(CallArgs a, Heads Hd, const uint16_t* v, void* dq) {
   store_scores<true>(sm, m, T.r0, T.r1, T.c0, T.r1, lg, a.alpha);
   float gq[4][16];
   zero_acc(gq);
-  tmm16<16, true, 2>(gq, T.r1 - T.c0, sm, D, 0, 1.f, 0.f, 0, 0, KT, 0, T.c0);
-  tmm16<16, false, 2>(gq, dv, sm, D, T.r0, a.alpha, lg, T.r0 - T.c0 + 1, 1, S, 0, 0);
+  tmm16d<16, true, 2>(gq, T.r1 - T.c0, sm, D, 0, 1.f, 0.f, 0, 0, KT, 0, T.c0);
+  tmm16d<16, false, 2>(gq, dv, sm, D, T.r0, a.alpha, lg, T.r0 - T.c0 + 1, 1, S, 0, 0);
   store_rotated<RN_BF16>(sm, gq, a, seq_pos0(a, bh / a.H), bh, T.r0, T.r1, dq);
 }
 
 // Tile rows are keys s; later rows t in [s, c1): dKh = [alpha (V dO^T) (.) D'] Qh + zeta V G^T.
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bm_dk(CallArgs a, Heads Hd, const uint16_t* v, void* dk_) {
-  __shared__ TileSharedH sm;
+  __shared__ TileSharedD<2, kMaxDv * 2> sm;
   const int dk = a.dk, dv = a.dv, N = a.N, Np = Hd.Np;
-  const TileRows T = tile_rows(N);
-  if (T.r0 >= T.r1) return;
-  const int bh = blockIdx.y, h = bh % a.H;
+  const TileAt at = tile_at(N, a.B * a.H, Hd.nch);
+  const TileRows T = at.T;
+  if (!at.valid || T.r0 >= T.r1) return;
+  const int bh = at.bh, h = bh % a.H;
   const float lg = a.hp.log2g[h];
   const Src V{v + int64_t(bh) * N * dv, dv, N, true};
   const Src D{Hd.DR + int64_t(bh) * N * dv, dv, N, false};
@@ -511,7 +842,7 @@ bm_dk(CallArgs a, Heads Hd, const uint16_t* v, void* dk_) {
   store_scores<false>(sm, m, T.r0, T.r1, T.r0, T.c1, lg, a.alpha);
   float gk[4][16];
   zero_acc(gk);
-  tmm16<16, true, 2>(gk, T.c1 - T.r0, sm, V, 0, 1.f, 0.f, 0, 0, QT, 0, T.r0);
+  tmm16d<16, true, 2>(gk, T.c1 - T.r0, sm, V, 0, 1.f, 0.f, 0, 0, QT, 0, T.r0);
   tmm16<16, false, 2>(gk, dv, sm, V, T.r0, 1.f, lg, T.c1 - 1 - T.r0, -1, G, 0, 0);
   store_rotated<RN_BF16>(sm, gk, a, seq_pos0(a, bh / a.H), bh, T.r0, T.r1, dk_);
 }
@@ -519,11 +850,12 @@ bm_dk(CallArgs a, Heads Hd, const uint16_t* v, void* dk_) {
 // dV = [alpha (Kh Qh^T) (.) D'] dO + zeta Kh G.
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bm_dv(CallArgs a, Heads Hd, void* dv_) {
-  __shared__ TileSharedH sm;
+  __shared__ TileSharedD<3, kMaxDv * 4> sm;
   const int dk = a.dk, dv = a.dv, N = a.N, Np = Hd.Np;
-  const TileRows T = tile_rows(N);
-  if (T.r0 >= T.r1) return;
-  const int bh = blockIdx.y, h = bh % a.H;
+  const TileAt at = tile_at(N, a.B * a.H, Hd.nch);
+  const TileRows T = at.T;
+  if (!at.valid || T.r0 >= T.r1) return;
+  const int bh = at.bh, h = bh % a.H;
   const float lg = a.hp.log2g[h];
   const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
   const Src K{Hd.KR + int64_t(bh) * N * dk, dk, N, false};
@@ -532,12 +864,12 @@ bm_dv(CallArgs a, Heads Hd, void* dv_) {
   const Src GT{Hd.GT + (int64_t(bh) * Hd.nch + T.c) * dk * dv, dk, dv, false};
   float m[4][16];
   zero_acc(m);
-  tmm16<16, false>(m, dk, sm, K, T.r0, 1.f, 0.f, 0, 0, Q, T.r0, 0);
+  tmm16d<16, false, 3>(m, dk, sm, K, T.r0, 1.f, 0.f, 0, 0, Q, T.r0, 0);
   store_scores<false>(sm, m, T.r0, T.r1, T.r0, T.c1, lg, a.alpha);
   float o[4][32];
   zero_acc(o);
-  tmm16<32, true>(o, T.c1 - T.r0, sm, K, 0, 1.f, 0.f, 0, 0, DT, 0, T.r0);
-  tmm16<32, false>(o, dk, sm, K, T.r0, 1.f, lg, T.c1 - 1 - T.r0, -1, GT, 0, 0);
+  tmm16d<32, true, 3>(o, T.c1 - T.r0, sm, K, 0, 1.f, 0.f, 0, 0, DT, 0, T.r0);
+  tmm16d<32, false, 3>(o, dk, sm, K, T.r0, 1.f, lg, T.c1 - 1 - T.r0, -1, GT, 0, 0);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int s = T.r0 + 4 * ty + r;
@@ -564,7 +896,7 @@ hipError_t launch_t(const CallArgs& a, const BwArgs& x, void* ws, hipStream_t st
            at(L.S), at(L.ST), at(L.G), at(L.GT), L.Np, L.nch};
   const dim3 gblk(L.Np / 64, BH);
   const dim3 gscan(((a.dk + 63) / 64) * ((a.dv + 127) / 128), BH);
-  const dim3 gtiles(L.nch * (kBC / kR), BH);
+  const dim3 gtiles(static_cast<unsigned>((BH * L.nch + 7) / 8) * 8 * (kBC / kR));
   hipLaunchKernelGGL(bm_prep, gblk, dim3(256), 0, st, a, static_cast<const uint16_t*>(x.q),
                      static_cast<const uint16_t*>(x.k), static_cast<const uint16_t*>(x.v), at(L.QR),
                      at(L.KR), at(L.QT), at(L.KT), at(L.VT), L.Np);

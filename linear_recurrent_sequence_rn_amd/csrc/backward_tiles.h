@@ -230,17 +230,23 @@ __device__ __forceinline__ void store_scores(SM& sm, const float (&m)[4][16], in
       const int dist = FORWARD ? row - key : key - row;
       const bool ok = row < row_end && key < key_end && dist >= 0;
       const float x = ok ? alpha * m[r][j] * gpow(lg, float(dist)) : 0.f;
-      if constexpr (__is_same(SM, TileSharedH)) sm.m.P[4 * ty + r][tx + 16 * j] = static_cast<_Float16>(x);
+      if constexpr (!__is_same(SM, TileShared)) sm.m.P[4 * ty + r][tx + 16 * j] = static_cast<_Float16>(x);
       else sm.P[tx + 16 * j][4 * ty + r] = x;
     }
 }
 
-// Sum over the 16 threads (tx) that share a row.
+// Sum over the 16 threads (tx = lanes 16k .. 16k+15) that share a row, every lane
+// receiving it: DPP moves (VALU only) swap neighbours, swap pairs, mirror within 8 lanes,
+// mirror within 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float row16_sum(float x) {
-  x += __shfl_xor(x, 1, 64);
-  x += __shfl_xor(x, 2, 64);
-  x += __shfl_xor(x, 4, 64);
-  x += __shfl_xor(x, 8, 64);
+  x += dpp_mov<0xB1>(x);    // lane ^ 1
+  x += dpp_mov<0x4E>(x);    // lane ^ 2
+  x += dpp_mov<0x141>(x);   // lane i <-> 7 - i within 8
+  x += dpp_mov<0x140>(x);   // lane i <-> 15 - i within 16
   return x;
 }
 
