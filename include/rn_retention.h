@@ -286,7 +286,8 @@ size_t rn_chunkwise_backward_workspace_bytes(const rn_desc* desc, int32_t chunk)
  * workspace:  at least rn_chunkwise_backward_workspace_bytes(desc, chunk), 256-byte aligned.
  * Arithmetic: float32 inputs take float32 products throughout.
  * bf16 inputs take matrix-core products (16x16x32 f16 MFMA, float32 accumulation): with
- * d_k and d_v multiples of 8 and v 16-byte, q and k 4-byte aligned, every operand is
+ * d_k and d_v multiples of 8, v, dv, dout, gate and dgate 16-byte aligned and q and k
+ * 4-byte aligned, every operand is
  * rounded to IEEE half (so, as for the forward, operands must stay below 65504 in
  * magnitude); other bf16 shapes stage float32 operands and take the same products. Every
  * shape and dtype the forward accepts is accepted.

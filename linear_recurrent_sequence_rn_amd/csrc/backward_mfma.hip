@@ -76,7 +76,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t src_rsrc(const Src& s) {
                                            static_cast<int>(bytes > 0x7fffffff ? 0x7fffffff : bytes), 0x00020000);
 }
 __device__ __forceinline__ u32x4 raw8(__amdgpu_buffer_rsrc_t r, int64_t pitch, int row, int64_t c, bool live) {
-  const uint32_t off = live ? static_cast<uint32_t>((row * pitch + c) * 2) : kRunSink;
+  const uint32_t off = live_off(static_cast<uint32_t>((row * pitch + c) * 2), live);
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
@@ -233,7 +233,7 @@ __device__ __forceinline__ void tmm16d(float (&acc)[4][NCT], int K, SM& sm, cons
     const int k0 = k * kKH;
     if constexpr (!FROMP) {
       const int kq = k0 + 8 * aq;
-      const uint32_t off = kq < K ? static_cast<uint32_t>(((ar0 + arow) * A.pitch + kq) * 2) : kRunSink;
+      const uint32_t off = live_off(static_cast<uint32_t>(((ar0 + arow) * A.pitch + kq) * 2), kq < K);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsa, (__attribute__((address_space(3))) void*)(&sm.m.ring[slot][64 * w]), 16, off, 0, 0, 0);
     }
@@ -241,7 +241,7 @@ __device__ __forceinline__ void tmm16d(float (&acc)[4][NCT], int K, SM& sm, cons
     for (int u = 0; u < NRUN; ++u) {
       const int p = (NRUN * w + u) * 64 + l, n = p >> 2, q = (p & 3) ^ ((n >> 2) & 3);
       const int kq = k0 + 8 * q;
-      const uint32_t off = kq < K ? static_cast<uint32_t>(((br0 + n) * B.pitch + bc0 + kq) * 2) : kRunSink;
+      const uint32_t off = live_off(static_cast<uint32_t>(((br0 + n) * B.pitch + bc0 + kq) * 2), kq < K);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsb, (__attribute__((address_space(3))) void*)(&sm.m.ring[slot][256 + (NRUN * w + u) * 64]), 16,
           off, 0, 0, 0);
@@ -422,12 +422,17 @@ __global__ void __launch_bounds__(256) bm_prep(CallArgs a, const uint16_t* q, co
 // REV = 1: G (gradients reaching the chunk ends) from X = Qh^T weighted by alpha xi, Y = dO^T,
 //          chunks in reverse, from dstate_out; the final value goes to dstate_in.
 // Workgroup: a 64 (d_k) x 128 (d_v) tile of the state in MFMA accumulators, wave w rows
-// 16w.. of the tile. Per 32-token slice: X^T rows (tokens weighted on staging) times Y^T
-// rows. Each chunk's boundary value is stored in half as [d_k][d_v] and [d_v][d_k].
+// 16w.. of the tile. Per 64-token slice: X^T rows (tokens weighted on staging) times Y^T
+// rows, staged in one of two LDS buffers (one barrier per slice). Each chunk's boundary
+// value is stored in half as [d_k][d_v] and [d_v][d_k].
+constexpr int kSK = 64;            // tokens per slice
+constexpr int kLdS = kSK + 8;      // LDS pitch (half) of a staged row
+constexpr int kLdT = 128 + 8;   // LDS pitch (half) of the staged boundary value
 struct alignas(16) ScanShared {
-  _Float16 As[64][kLdH];
-  _Float16 Bs[128][kLdH];
-  float wt[kBC];
+  _Float16 As[2][64][kLdS];
+  _Float16 Bs[2][128][kLdS];
+  float wt[2][kBC];               // token weights of a chunk (by chunk parity)
+  uint16_t bv[64][kLdT];          // the chunk's boundary value (half), for 16-byte row stores
 };
 
 template <int REV>
@@ -436,9 +441,14 @@ __global__ void __launch_bounds__(256) bm_scan(CallArgs a, const uint16_t* XT, c
                                                float* final_out, int Np) {
   __shared__ ScanShared sm;
   const int dk = a.dk, dv = a.dv, N = a.N;
-  const int nte = (dv + 127) / 128;
-  const int d0 = 64 * (blockIdx.x / nte), e0 = 128 * (blockIdx.x % nte);
-  const int bh = blockIdx.y, h = bh % a.H;
+  // 1-D grid: the state tiles of a head all run on one XCD (id mod 8), where the tiles that
+  // share rows of X^T or Y^T find them in L2
+  const int nte = (dv + 127) / 128, ntiles = ((dk + 63) / 64) * nte;
+  const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+  const int bh = 8 * (jx / ntiles) + xcd, tile = jx % ntiles;
+  if (bh >= a.B * a.H) return;
+  const int d0 = 64 * (tile / nte), e0 = 128 * (tile % nte);
+  const int h = bh % a.H;
   const float lg = a.hp.log2g[h];
   const int nch = (N + kBC - 1) / kBC;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, g = l >> 4;
@@ -453,22 +463,28 @@ __global__ void __launch_bounds__(256) bm_scan(CallArgs a, const uint16_t* XT, c
       const int d = d0 + 16 * w + 4 * g + r, e = e0 + 16 * j + l16;
       t[j][r] = (init && d < dk && e < dv) ? init[bh * nS + int64_t(d) * dv + e] : 0.f;
     }
-  const int arow = tid >> 2, aq = tid & 3;
-  // Slices of 32 tokens are numbered across chunks (slice u: chunk u >> 3 in scan order,
-  // tokens 32 (u & 7) .. of it) and loaded four ahead through a ring of register sets,
-  // branch-free: runs past a chunk's end or past the last chunk read as zeros.
+  // Slices of 64 tokens are numbered across chunks (slice u: chunk u >> 2 in scan order,
+  // tokens 64 (u & 3) .. of it) and loaded four ahead through a ring of register sets,
+  // branch-free: runs past a chunk's end or past the last chunk read as zeros. Thread tid
+  // stages runs tid + 256 v: X^T row (run >> 3) (two runs), Y^T row (run >> 3) (four
+  // runs), tokens 8 (run & 7) .. of the slice.
   constexpr int kSets = 4;
   const __amdgpu_buffer_rsrc_t rx = src_rsrc(X), ry = src_rsrc(Y);
-  u32x4 ra[kSets], rb[kSets][2];
+  u32x4 ra[kSets][2], rb[kSets][4];
   auto fetch = [&](int u, int set) __attribute__((always_inline)) {
-    const int cu = REV ? nch - 1 - (u >> 3) : (u >> 3);
-    const int c0u = cu * kBC, Lu = (u >> 3) < nch ? min(N, c0u + kBC) - c0u : 0;
-    const int k = kKH * (u & 7);
-    ra[set] = raw8(rx, X.pitch, d0 + arow, int64_t(c0u) + k + 8 * aq, k + 8 * aq < Lu);
+    const int ci = u >> 2;
+    const int cu = REV ? nch - 1 - ci : ci;
+    const int c0u = cu * kBC, Lu = ci < nch ? min(N, c0u + kBC) - c0u : 0;
+    const int k = kSK * (u & 3);
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
-      const int run = tid + 256 * v, kq = k + 8 * (run & 3);
-      rb[set][v] = raw8(ry, Y.pitch, e0 + (run >> 2), int64_t(c0u) + kq, kq < Lu);
+      const int run = tid + 256 * v, kq = k + 8 * (run & 7);
+      ra[set][v] = raw8(rx, X.pitch, d0 + (run >> 3), int64_t(c0u) + kq, kq < Lu);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int run = tid + 256 * v, kq = k + 8 * (run & 7);
+      rb[set][v] = raw8(ry, Y.pitch, e0 + (run >> 3), int64_t(c0u) + kq, kq < Lu);
     }
   };
   // chunk boundary values through buffer resources over the head's states: lanes past
@@ -476,6 +492,16 @@ __global__ void __launch_bounds__(256) bm_scan(CallArgs a, const uint16_t* XT, c
   const __amdgpu_buffer_rsrc_t rS = src_rsrc(Src{Sr + int64_t(bh) * nch * nS, 1, int(nch * nS), false});
   const __amdgpu_buffer_rsrc_t rST = src_rsrc(Src{St + int64_t(bh) * nch * nS, 1, int(nch * nS), false});
   for (int u = 0; u < kSets; ++u) fetch(u, u);
+  // token weights of chunk `step` (scan order): zeta_s = gamma^(L-1-s) for the states,
+  // alpha xi_s = alpha gamma^(s+1) for the gradients, zero past the chunk's end
+  auto weights = [&](int step, float* wt) {
+    const int cw = REV ? nch - 1 - step : step;
+    const int Lw = (step < nch) ? min(N, cw * kBC + kBC) - cw * kBC : 0;
+    for (int jj = tid; jj < kBC; jj += 256)
+      wt[jj] = jj < Lw ? (REV ? a.alpha * gpow(lg, float(jj + 1)) : gpow(lg, float(Lw - 1 - jj))) : 0.f;
+  };
+  weights(0, sm.wt[0]);
+  __syncthreads();
   for (int step = 0; step < nch; ++step) {
     const int c = REV ? nch - 1 - step : step;
     const int c0 = c * kBC, L = min(N, c0 + kBC) - c0;
@@ -485,40 +511,66 @@ __global__ void __launch_bounds__(256) bm_scan(CallArgs a, const uint16_t* XT, c
     for (int j = 0; j < 8; ++j) {
       const int e = e0 + 16 * j + l16, d = d0 + 16 * w + 4 * g;
       const bool ok = e < dv && d < dk;
-      const uint32_t ot = ok ? (cbase + uint32_t(e) * dk + d) * 2 : kRunSink;
+      const uint32_t ot = live_off((cbase + uint32_t(e) * dk + d) * 2, ok);
       __builtin_amdgcn_raw_buffer_store_b64(
           __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
                              u32x2{pack_h2(t[j][0], t[j][1]), pack_h2(t[j][2], t[j][3])}),
           rST, ot, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t orow = ok ? (cbase + uint32_t(d + r) * dv + e) * 2 : kRunSink;
-        __builtin_amdgcn_raw_buffer_store_b16(h_bits(t[j][r]), rS, orow, 0, 0);
-      }
+      for (int r = 0; r < 4; ++r) sm.bv[16 * w + 4 * g + r][16 * j + l16] = h_bits(t[j][r]);
+    }
+    // (the weights of the next chunk go in while the boundary value is staged)
+    weights(step + 1, sm.wt[(step + 1) & 1]);
+    __syncthreads();   // the staged boundary value is complete
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int run = tid + 256 * v, row = run >> 4, q = run & 15;
+      const bool ok = d0 + row < dk && e0 + 8 * q < dv;
+      const uint32_t orow = live_off((cbase + uint32_t(d0 + row) * dv + e0 + 8 * q) * 2, ok);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int,
+                             *reinterpret_cast<const u32x4*>(&sm.bv[row][8 * q])),
+          rS, orow, 0, 0);
     }
     const float gL = gpow(lg, float(L));
 #pragma unroll
     for (int j = 0; j < 8; ++j) t[j] *= gL;
-    __syncthreads();   // the previous chunk's reads of wt are done
-    for (int jj = tid; jj < kBC; jj += 256)
-      sm.wt[jj] = jj < L ? (REV ? a.alpha * gpow(lg, float(jj + 1)) : gpow(lg, float(L - 1 - jj))) : 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k0 = kKH * i;
-      __syncthreads();   // previous slice's reads done; the weights are written
-      *reinterpret_cast<u32x4*>(&sm.As[arow][8 * aq]) = scale8(ra[i % kSets], &sm.wt[k0 + 8 * aq]);
+    for (int i = 0; i < 4; ++i) {
+      const int buf = i & 1, k0 = kSK * i;
+      // stage slice i of the chunk: X^T runs weighted per token
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
-        const int run = tid + 256 * v;
-        *reinterpret_cast<u32x4*>(&sm.Bs[run >> 2][8 * (run & 3)]) = rb[i % kSets][v];
+        const int run = tid + 256 * v, kq = k0 + 8 * (run & 7);
+        float f[8];
+        {
+          const float4 f0 = *reinterpret_cast<const float4*>(&sm.wt[step & 1][kq]);
+          const float4 f1 = *reinterpret_cast<const float4*>(&sm.wt[step & 1][kq + 4]);
+          f[0] = f0.x; f[1] = f0.y; f[2] = f0.z; f[3] = f0.w;
+          f[4] = f1.x; f[5] = f1.y; f[6] = f1.z; f[7] = f1.w;
+        }
+        *reinterpret_cast<u32x4*>(&sm.As[buf][run >> 3][8 * (run & 7)]) = scale8(ra[i][v], f);
       }
-      __syncthreads();
-      fetch(8 * step + i + kSets, i % kSets);
-      const f16x8 av = *reinterpret_cast<const f16x8*>(&sm.As[16 * w + l16][8 * g]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const f16x8 bv = *reinterpret_cast<const f16x8*>(&sm.Bs[16 * j + l16][8 * g]);
-        t[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, t[j], 0, 0, 0);
+      for (int v = 0; v < 4; ++v) {
+        const int run = tid + 256 * v;
+        *reinterpret_cast<u32x4*>(&sm.Bs[buf][run >> 3][8 * (run & 7)]) = rb[i][v];
+      }
+      // the buffer staged here was last read two slices ago, before every wave's
+      // previous barrier
+      __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+      __asm__ volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+      fetch(4 * step + i + kSets, i);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const f16x8 av = *reinterpret_cast<const f16x8*>(&sm.As[buf][16 * w + l16][32 * e + 8 * g]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const f16x8 bv = *reinterpret_cast<const f16x8*>(&sm.Bs[buf][16 * j + l16][32 * e + 8 * g]);
+          t[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, t[j], 0, 0, 0);
+        }
       }
     }
   }
@@ -613,7 +665,7 @@ __device__ __forceinline__ void gn_backward_rows(float* ost, const float (&o)[4]
   // stores are dropped).
   auto boff = [&](int rr, int bytes) -> uint32_t {
     const int t = r0 + 16 * w + rr;
-    return (t < r1 && cl) ? static_cast<uint32_t>((t * dv + c0) * bytes) : 0x80000000u;
+    return live_off(static_cast<uint32_t>((t * dv + c0) * bytes), t < r1 && cl);
   };
   // all rows of a batch are loaded before the first is used (16 rows for bf16 dout, 8 for
   // float32), so their latencies overlap
@@ -870,14 +922,21 @@ bm_dv(CallArgs a, Heads Hd, void* dv_) {
   zero_acc(o);
   tmm16d<32, true, 3>(o, T.c1 - T.r0, sm, K, 0, 1.f, 0.f, 0, 0, DT, 0, T.r0);
   tmm16d<32, false, 3>(o, dk, sm, K, T.r0, 1.f, lg, T.c1 - 1 - T.r0, -1, GT, 0, 0);
+  // the tile (bf16) through LDS, then out in 16-byte runs of the rows below its end
+  constexpr int kStLd = kMaxDv + 8;
+  static_assert(sizeof(sm) >= kR * kStLd * sizeof(uint16_t), "tile staging fits");
+  uint16_t* stg = reinterpret_cast<uint16_t*>(&sm);
+  __syncthreads();   // the products' reads of shared memory are done
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int s = T.r0 + 4 * ty + r;
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const int col = tx + 16 * j;
-      if (s < T.r1 && col < dv) Elem<RN_BF16>::store(dv_, (int64_t(bh) * N + s) * dv + col, o[r][j]);
-    }
+    for (int j = 0; j < 32; ++j) stg[(4 * ty + r) * kStLd + tx + 16 * j] = f32_to_bf16(o[r][j]);
+  __syncthreads();
+  const int rows = T.r1 - T.r0, runs = dv / 8;
+  uint16_t* dst = static_cast<uint16_t*>(dv_) + (int64_t(bh) * N + T.r0) * dv;
+  for (int e = threadIdx.x; e < rows * runs; e += 256) {
+    const int rr = e / runs, c8 = e - rr * runs;
+    *reinterpret_cast<u32x4*>(dst + int64_t(rr) * dv + 8 * c8) = *reinterpret_cast<const u32x4*>(&stg[rr * kStLd + 8 * c8]);
   }
 }
 
@@ -895,7 +954,7 @@ hipError_t launch_t(const CallArgs& a, const BwArgs& x, void* ws, hipStream_t st
   Heads Hd{at(L.QR), at(L.KR), at(L.QT), at(L.KT), at(L.VT), at(L.DR), at(L.DT),
            at(L.S), at(L.ST), at(L.G), at(L.GT), L.Np, L.nch};
   const dim3 gblk(L.Np / 64, BH);
-  const dim3 gscan(((a.dk + 63) / 64) * ((a.dv + 127) / 128), BH);
+  const dim3 gscan(static_cast<unsigned>(((a.dk + 63) / 64) * ((a.dv + 127) / 128) * 8 * ((BH + 7) / 8)));
   const dim3 gtiles(static_cast<unsigned>((BH * L.nch + 7) / 8) * 8 * (kBC / kR));
   hipLaunchKernelGGL(bm_prep, gblk, dim3(256), 0, st, a, static_cast<const uint16_t*>(x.q),
                      static_cast<const uint16_t*>(x.k), static_cast<const uint16_t*>(x.v), at(L.QR),

@@ -235,6 +235,16 @@ __device__ __forceinline__ void store_scores(SM& sm, const float (&m)[4][16], in
     }
 }
 
+// Buffer offset `off` when `live`, else one past every buffer range (bit 31 set: loads
+// return zero, stores are dropped). Formed without a select: the compiler turned selects
+// on load offsets into branches around the loads, and at each join it waits for every
+// load in flight. (The empty statement only hides the value from the optimizer.)
+__device__ __forceinline__ uint32_t live_off(uint32_t off, bool live) {
+  uint32_t hi = static_cast<uint32_t>(!live) << 31;
+  __asm__("" : "+v"(hi));
+  return off | hi;
+}
+
 // Sum over the 16 threads (tx = lanes 16k .. 16k+15) that share a row, every lane
 // receiving it: DPP moves (VALU only) swap neighbours, swap pairs, mirror within 8 lanes,
 // mirror within 16.
@@ -309,9 +319,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, in
 template <int DT>
 __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int i, bool ok, float x) {
   if constexpr (DT == RN_F32) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, ok ? static_cast<uint32_t>(i) * 4 : kGnSink, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, live_off(static_cast<uint32_t>(i) * 4, ok), 0, 0);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), r, ok ? static_cast<uint32_t>(i) * 2 : kGnSink, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), r, live_off(static_cast<uint32_t>(i) * 2, ok), 0, 0);
   }
 }
 

@@ -435,8 +435,9 @@ rn_status rn_retention_chunkwise_backward(const rn_desc* desc, int32_t chunk, co
                (desc->flags & RN_EPI_GN) ? dgn_weight : nullptr,
                (desc->flags & RN_EPI_GN) ? dgn_bias : nullptr};
   g_err[0] = 0;
-  const bool mfma = rn::backward_mfma_supported(a, desc->in_dtype) &&
-                    reinterpret_cast<uintptr_t>(v) % 16 == 0 && reinterpret_cast<uintptr_t>(q) % 4 == 0 &&
+  auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  const bool mfma = rn::backward_mfma_supported(a, desc->in_dtype) && a16(v) && a16(dv) && a16(dout) &&
+                    a16(x.gate) && a16(x.dgate) && reinterpret_cast<uintptr_t>(q) % 4 == 0 &&
                     reinterpret_cast<uintptr_t>(k) % 4 == 0;
   if (mfma)
     return hip_status(rn::launch_backward_mfma(a, desc->out_dtype, x, workspace,

@@ -57,8 +57,8 @@ struct BwArgs {
 size_t backward_ws_bytes(const CallArgs& a);
 hipError_t launch_backward(const CallArgs& a, int in_dt, int out_dt, const BwArgs& x, void* ws,
                            hipStream_t st);
-// Matrix-core path of the gradients (bf16 inputs, d_k and d_v multiples of 8; v 16-byte
-// and q, k 4-byte aligned).
+// Matrix-core path of the gradients (bf16 inputs, d_k and d_v multiples of 8; v, dv, dout,
+// gate and dgate 16-byte and q, k 4-byte aligned).
 bool backward_mfma_supported(const CallArgs& a, int in_dt);
 size_t backward_mfma_ws_bytes(const CallArgs& a);
 hipError_t launch_backward_mfma(const CallArgs& a, int out_dt, const BwArgs& x, void* ws,
