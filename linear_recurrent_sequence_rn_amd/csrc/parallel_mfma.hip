@@ -383,21 +383,22 @@ parallel_main(CallArgs a, const uint16_t* q, const uint16_t* ws, const void* gat
   // Per key block: the first half of V(kb) was loaded during the previous block; the
   // second half is loaded at the top and used last, and the first half of V(kb+1) is
   // loaded between the two halves of the product, so each V load has a half or a whole
-  // block of work in front of it.
+  // block of work in front of it. That load is issued on every pass, also after the last
+  // key block (block nb lies just past the end of V's range: the lanes read zeros):
+  // issued under a condition, the compiler's waits before the second half of the product
+  // would have to cover it too, exposing its latency.
   for (int kb = 0; kb <= kb_end; ++kb) {
     // scores(kb) are in sm.p[kb%2]; key block kb+1 is in sm.kh[(kb+1)%2]
-    const bool more = kb + 1 <= kb_end;
     if (kb + 2 <= kb_end) stage_k(kb + 2, kb & 1);
     load_vh(kb, 1, vh1);
-    if (more) scores(kb + 1);
+    if (kb + 1 <= kb_end) scores(kb + 1);
     const int buf = kb & 1;
     pv_half(buf, 0, vh0);
-    if (more) load_vh(kb + 1, 0, vh0);
+    load_vh(kb + 1, 0, vh0);
     pv_half(buf, 1, vh1);
     // key block kb+2 staged (and V's second half, used above); V(kb+1)'s first half
     // stays in flight
-    if (more) __builtin_amdgcn_s_waitcnt(waitcnt_imm(4, 0));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(4, 0));
     __syncthreads();
   }
 
