@@ -58,8 +58,11 @@
 // Schedule of iteration i (both roles run iterations 0 .. nb+3, rounded up to a
 // multiple of 4; iterations past the end do only what is left of the last blocks):
 //   M: wait for its copies; read the fragments of block i; wait for block i+1 to be
-//      whole and copy it into its LDS region; wait for the statistics of block i-3 and
-//      copy them to LDS | B2 | poll the counts for the next iteration; compute block i.
+//      whole; wait for the statistics of block i-3 and copy them to LDS | B2 | copy
+//      block i+1 into its LDS region; poll the counts for the next iteration; compute
+//      block i. (The 16 copies per wave are issued after B2: issued before it, their
+//      issue, slowed by the HBM streams in the same memory pipeline, held up both
+//      roles at the barrier.)
 //   E: read the partial outputs of block i-1 | B2 | publish its statistics; rotate
 //      block i+3 into the ring; normalise, gate and store block i-4; stage V^T of
 //      block i+1; issue the loads of blocks i+5 (q, k), i+3 (v) and i-2 (gate); raise
@@ -424,10 +427,12 @@ chunkwise_fused(Params P) {
       __asm__ volatile("" ::: "memory");
       // block i+1 into the fragment region just read; statistics of block i-3
       if (i + 1 < nb) settle(poll_r, kReady + (i + 1) % kRing, ready_target(i + 1));
-      stage_frags(i + 1);
       if (use_gn && i >= 3 && i - 3 < nb) settle(poll_s, kStat + (i - 3) % kStatRing, stat_target(i - 3));
       stage_stats(i - 3, i & 1);
       lds_barrier();   // B2: the E waves have read the partial outputs of block i-1
+      // block i+1 into the fragment region read at the top (its copies then have this
+      // iteration's matrix work to complete in, and do not hold up the barrier)
+      stage_frags(i + 1);
       // counts for the next iteration: block i+2 whole, statistics of block i-2
       poll_r = poll(kReady + (i + 2) % kRing);
       poll_s = poll(kStat + ((i - 2) & (kStatRing - 1)));
