@@ -63,10 +63,12 @@
 //      block i. (The 16 copies per wave are issued after B2: issued before it, their
 //      issue, slowed by the HBM streams in the same memory pipeline, held up both
 //      roles at the barrier.)
-//   E: read the partial outputs of block i-1 | B2 | publish its statistics; rotate
-//      block i+3 into the ring; normalise, gate and store block i-4; stage V^T of
-//      block i+1; issue the loads of blocks i+5 (q, k), i+3 (v) and i-2 (gate); raise
-//      the counts once the ring and statistics stores have completed.
+//   E: read the partial outputs of block i-1 | B2 | form its statistics; rotate this
+//      slice's rows of block i+3; normalise and gate block i-4; stage V^T of block i+1;
+//      then store the statistics, the ring rows and the outputs, issue the loads of
+//      blocks i+5 (q, k), i+3 (v) and i-2 (gate), and raise the counts once the ring
+//      and statistics stores have completed. (The stores follow the arithmetic: issued
+//      right after B2 they wait behind the M waves' copies in the memory pipeline.)
 // Ring safety. At iteration i an E wave writes slot (i+3) mod 8 after its M waves saw
 // block i+1 whole, which means every slice has finished iteration i-2, so every copy
 // of the block previously held in that slot (block i-5, copied at iteration i-6) is
@@ -595,7 +597,7 @@ chunkwise_fused(Params P) {
     // Rotates and stores this workgroup's rows of block b. Blocks are produced in
     // order; the angles advance by 64 theta per block and are re-anchored from their
     // float64-reduced values every kReanchor blocks.
-    auto produce = [&](int b, const u32x4* sq, const u32x4* sk) {
+    auto produce_calc = [&](int b, const u32x4* sq, const u32x4* sk, u32x4* poq, u32x4* pok, uint32_t* pso) {
       const bool anchor = (b % kReanchor) == 0;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -620,12 +622,25 @@ chunkwise_fused(Params P) {
           ok[i] = pack_f16x2(k0 * ck - k1 * sk_, k0 * sk_ + k1 * ck);
         }
         // (blocks past the last: an offset past the end of the ring, store dropped)
-        const uint32_t so = b < nb ? static_cast<uint32_t>(
+        pso[u] = b < nb ? static_cast<uint32_t>(
             ((size_t(b & (kRing - 1)) * 2 * kSlotElems + size_t(r_lo + pr + 8 * u) * kDK + 8 * pq) * 2))
-                                   : kSink;
-        st_b128(r_ring, so, oq);
-        st_b128(r_ring, so + static_cast<uint32_t>(kSlotElems * 2), ok);
+                        : kSink;
+        poq[u] = oq;
+        pok[u] = ok;
       }
+    };
+    auto store_ring = [&](const u32x4* poq, const u32x4* pok, const uint32_t* pso) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        st_b128(r_ring, pso[u], poq[u]);
+        st_b128(r_ring, pso[u] + static_cast<uint32_t>(kSlotElems * 2), pok[u]);
+      }
+    };
+    auto produce = [&](int b, const u32x4* sq, const u32x4* sk) {
+      u32x4 poq[U], pok[U];
+      uint32_t pso[U];
+      produce_calc(b, sq, sk, poq, pok, pso);
+      store_ring(poq, pok, pso);
     };
 
     // V slice: thread loads rows vs0..vs0+3, columns vd0..vd0+3 (bf16) of the slice
@@ -680,7 +695,8 @@ chunkwise_fused(Params P) {
     // (blocks outside the sequence: offsets past the end, stores dropped).
     const float inv_dv = 1.0f / float(DV);
     uint32_t nonfinite = 0u;   // set by a non-finite output of the sequence
-    auto finalize = [&](int b, const float (*o)[8], const u32x4* gt, int sbuf) {
+    constexpr int kOutPieces = (OUT == RN_BF16) ? 2 : 4;   // 16-byte output pieces per thread
+    auto finalize_calc = [&](int b, const float (*o)[8], const u32x4* gt, int sbuf, u32x4* fo, uint32_t* foff) {
       float y[2][8];
       if (use_gn) {
         const u32x4 st = *reinterpret_cast<const u32x4*>(&sm.stat[sbuf][eb][2 * ea][0]);
@@ -724,13 +740,24 @@ chunkwise_fused(Params P) {
       }
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
-        const uint32_t ooff = static_cast<uint32_t>(((b * kT + 2 * ea + rr) * DV + 8 * eb) * osz);
+        foff[rr] = static_cast<uint32_t>(((b * kT + 2 * ea + rr) * DV + 8 * eb) * osz);
         if constexpr (OUT == RN_BF16) {
-          st_b128(r_o, ooff, u32x4{pack_bf16x2(y[rr][0], y[rr][1]), pack_bf16x2(y[rr][2], y[rr][3]),
-                                   pack_bf16x2(y[rr][4], y[rr][5]), pack_bf16x2(y[rr][6], y[rr][7])});
+          fo[rr] = u32x4{pack_bf16x2(y[rr][0], y[rr][1]), pack_bf16x2(y[rr][2], y[rr][3]),
+                         pack_bf16x2(y[rr][4], y[rr][5]), pack_bf16x2(y[rr][6], y[rr][7])};
         } else {
-          st_b128(r_o, ooff, __builtin_bit_cast(u32x4, f32x4{y[rr][0], y[rr][1], y[rr][2], y[rr][3]}));
-          st_b128(r_o, ooff + 16, __builtin_bit_cast(u32x4, f32x4{y[rr][4], y[rr][5], y[rr][6], y[rr][7]}));
+          fo[2 * rr] = __builtin_bit_cast(u32x4, f32x4{y[rr][0], y[rr][1], y[rr][2], y[rr][3]});
+          fo[2 * rr + 1] = __builtin_bit_cast(u32x4, f32x4{y[rr][4], y[rr][5], y[rr][6], y[rr][7]});
+        }
+      }
+    };
+    auto store_out = [&](const u32x4* fo, const uint32_t* foff) {
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        if constexpr (OUT == RN_BF16) {
+          st_b128(r_o, foff[rr], fo[rr]);
+        } else {
+          st_b128(r_o, foff[rr], fo[2 * rr]);
+          st_b128(r_o, foff[rr] + 16, fo[2 * rr + 1]);
         }
       }
     };
@@ -817,6 +844,8 @@ chunkwise_fused(Params P) {
       }
       lds_barrier();   // B2
       // (2) statistics of block i-1 (per row: mean, centred sum of squares) -> ring
+      uint32_t st_so;
+      u32x4 st_v;
       {
         float st[4];
 #pragma unroll
@@ -834,17 +863,26 @@ chunkwise_fused(Params P) {
           st[2 * rr] = mu;
           st[2 * rr + 1] = row8_sum(m2);
         }
-        const uint32_t so = (i >= 1 && i <= nb) ? static_cast<uint32_t>(
+        st_so = (i >= 1 && i <= nb) ? static_cast<uint32_t>(
             (((((i - 1) & (kStatRing - 1)) * 8 + sl) * kT + 2 * ea) * 2) * sizeof(float)) : kSink;
-        st_b128(r_stats, so, __builtin_bit_cast(u32x4, f32x4{st[0], st[1], st[2], st[3]}));
+        st_v = __builtin_bit_cast(u32x4, f32x4{st[0], st[1], st[2], st[3]});
       }
-      // (3) this workgroup's rows of block i+3 into the ring (raw rows loaded at i-2)
-      produce(i + kAhead, xq[(C + kAhead) & 1], xk[(C + kAhead) & 1]);
-      __asm__ volatile("" ::: "memory");
-      // (4) block i-4: normalise, gate, store (statistics copied by the M waves at i-1)
-      finalize(i - kLag, ob[C], gb[C], (i - 1) & 1);
+      // (3) this workgroup's rows of block i+3 for the ring (raw rows loaded at i-2)
+      u32x4 poq[U], pok[U];
+      uint32_t pso[U];
+      produce_calc(i + kAhead, xq[(C + kAhead) & 1], xk[(C + kAhead) & 1], poq, pok, pso);
+      // (4) block i-4: normalise, gate (statistics copied by the M waves at i-1)
+      u32x4 fo[kOutPieces];
+      uint32_t foff[2];
+      finalize_calc(i - kLag, ob[C], gb[C], (i - 1) & 1, fo, foff);
       // (5) V^T of block i+1 (loaded at i-2)
       stage_v((C + 1) & 1, vb[(C + 1) & 1]);
+      // (5b) the stores, after the arithmetic: issued right after B2 they would wait
+      // behind the M waves' fragment copies in the memory pipeline
+      st_b128(r_stats, st_so, st_v);
+      store_ring(poq, pok, pso);
+      store_out(fo, foff);
+      __asm__ volatile("" ::: "memory");
       // (6) prefetches: q/k rows of block i+5, V of block i+3, gate of block i-2
       load_raw(i + kAhead + 2, xq[(C + kAhead) & 1], xk[(C + kAhead) & 1]);
       load_v(i + 3, vb[(C + 3) & 1]);
