@@ -111,8 +111,11 @@ constexpr uint32_t kSink = 0x80000000u;
 // count per head would not do: a wave that is ahead adds its next publication to the
 // same count and can complete it while a slower slice has not yet published the block
 // being waited for.) The GroupNorm statistics use kStat + j%kStatRing the same way.
-// Words [8, 16) record the XCD of each slice (diagnostics).
-enum { kArrive = 2, kXccMask = 3, kError = 4, kXccOfSlice = 8, kReady = 16, kStat = 24 };
+// Words 2-3 form one 64-bit arrival word: each slice adds 1 << (4 x) for its XCD x, so
+// nibble x counts the slices on XCD x (at most 8 of a head: no carry between nibbles)
+// and the nibbles sum to the slices that have arrived. Words [8, 16) record the XCD of
+// each slice (diagnostics).
+enum { kArrive = 2, kError = 4, kXccOfSlice = 8, kReady = 16, kStat = 24 };
 
 __device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -234,17 +237,23 @@ __device__ __forceinline__ void raise_timeout(uint32_t* cnt, uint32_t* status) {
   __hip_atomic_fetch_or(status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Thread 0 waits until cnt[word] >= target, then the block synchronises. With `force`
-// (the RN_TEST_FORCE_TIMEOUT flag) the wait gives up at once, as if its limit had passed.
-__device__ __forceinline__ void wait_count(uint32_t* cnt, int word, uint32_t target,
-                                           uint32_t* status, bool force) {
+// Sum of the 16 nibbles of v.
+__device__ __forceinline__ uint32_t nibble_sum(uint64_t v) {
+  v = (v & 0x0F0F0F0F0F0F0F0Full) + ((v >> 4) & 0x0F0F0F0F0F0F0F0Full);   // byte sums
+  return static_cast<uint32_t>((v * 0x0101010101010101ull) >> 56);
+}
+
+// Thread 0 waits until nS slices have added to the arrival word, then the block
+// synchronises. With `force` (the RN_TEST_FORCE_TIMEOUT flag) the wait gives up at once,
+// as if its limit had passed.
+__device__ __forceinline__ void wait_arrivals(uint32_t* cnt, uint32_t nS, uint32_t* status, bool force) {
   if (threadIdx.x == 0) {
-    uint32_t* p = cnt + word;
+    uint64_t* p = reinterpret_cast<uint64_t*>(cnt + kArrive);
     if (force) {
       raise_timeout(cnt, status);
-    } else if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    } else if (nibble_sum(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < nS) {
       const uint64_t t0 = wall_clock64();
-      while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      while (nibble_sum(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < nS) {
         if (__hip_atomic_load(cnt + kError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
         __builtin_amdgcn_s_sleep(1);
         if (wall_clock64() - t0 > kWaitTicks) {
@@ -255,7 +264,6 @@ __device__ __forceinline__ void wait_count(uint32_t* cnt, int word, uint32_t tar
     }
   }
   __syncthreads();
-  __atomic_thread_fence(__ATOMIC_ACQUIRE);
 }
 
 struct Params {
@@ -307,17 +315,23 @@ chunkwise_fused(Params P) {
   const uint32_t stats_off = static_cast<uint32_t>((stats_base - P.ws) + size_t(hg) * kStatsPerHead);
 
   // ---- placement check: are all slices of this head on one XCD? ----------------
+  // One atomic per slice carries both its arrival and its XCD, so no fence is needed
+  // between the two (a device-scope fence here writes back the XCD's L2, which the
+  // previous call has filled with dirty lines: about 18 us per call).
   if (tid == 0) {
     const uint32_t x = xcc_id();
     __hip_atomic_store(cnt + kXccOfSlice + sl, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_or(cnt + kXccMask, 1u << x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __threadfence();
-    __hip_atomic_fetch_add(cnt + kArrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(cnt + kArrive), uint64_t(1) << (4 * x),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  wait_count(cnt, kArrive, nS, P.status, (a.flags & RN_TEST_FORCE_TIMEOUT) != 0);
+  wait_arrivals(cnt, nS, P.status, (a.flags & RN_TEST_FORCE_TIMEOUT) != 0);
   if (tid == 0) {
-    uint32_t m = __hip_atomic_load(cnt + kXccMask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.mode = (__builtin_popcount(m) == 1) ? 0u : 1u;
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(cnt + kArrive), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    bool one = false;   // every slice on one XCD: one nibble holds them all
+#pragma unroll
+    for (int x = 0; x < 16; ++x) one |= ((v >> (4 * x)) & 15u) == uint64_t(nS);
+    sm.mode = one ? 0u : 1u;
   }
   __syncthreads();
   const bool agent = sm.mode != 0;
@@ -800,12 +814,16 @@ chunkwise_fused(Params P) {
     // staged; then the loads the first two iterations consume: q/k rows of blocks 3
     // and 4, V of blocks 1 and 2 (the gate rows they would use belong to blocks before
     // the first, whose outputs are dropped) ---------------------------------------------
-    for (int b = 0; b < kAhead; ++b) {
-      load_raw(b, xq[0], xk[0]);
-      produce(b, xq[0], xk[0]);
+    {
+      // (all loads first: one memory latency rather than one per block)
+      u32x4 tq[kAhead][U], tk[kAhead][U];
+#pragma unroll
+      for (int b = 0; b < kAhead; ++b) load_raw(b, tq[b], tk[b]);
+      load_v(0, vb[0]);
+#pragma unroll
+      for (int b = 0; b < kAhead; ++b) produce(b, tq[b], tk[b]);
+      stage_v(0, vb[0]);
     }
-    load_v(0, vb[0]);
-    stage_v(0, vb[0]);
     if (agent) __threadfence();
     else wait_vm<0>();
     if (l == 0) {
