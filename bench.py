@@ -223,12 +223,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        # the type the matrix products compute in: bf16 inputs are rounded to IEEE half
+        # for every MFMA operand (3 more significand bits than bf16), fp32 accumulation
+        "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": "chunkwise_6p7b: B=2 H=16 N=8192 d_k=256 d_v=512 chunk=256, "
                                "bf16 in/out, GroupNorm+swish gate, fp32 final state",
                    "global_batch": w.B, "seq_len": w.N, "heads": w.H, "d_k": w.d_k, "d_v": w.d_v,
-                   "chunk": w.chunk},
+                   "chunk": w.chunk, "io_dtype": "bf16", "mfma_operands": "f16",
+                   "accumulate": "fp32"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": profiled_traffic(),
                      "kernel": "chunkwise_fused", "kernel_ms": kern_s * 1e3,
