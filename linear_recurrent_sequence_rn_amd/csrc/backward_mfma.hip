@@ -166,7 +166,10 @@ __device__ __forceinline__ void tmm16(float (&acc)[4][NCT], int K, SM& sm, const
 // slot holds A's 64 rows x 32 k-values (256 units of 16 bytes) and then B's columns x 32
 // k-values (up to BUNITS units), as 16-byte runs copied from the half sources by buffer
 // loads into LDS. Run q (k-values 8q..8q+7) of row (column) n sits at unit
-// 4n + (q ^ ((n >> 2) & 3)), so that the 16 rows a lane group reads at one q fall into 16
+// 4n + (q ^ ring_swz(n)). A 16-byte LDS read serves 16 lanes at a time, lanes
+// {0-3, 12-15, 20-23, 24-27} together (and the sets derived from them: lane bit 5 and
+// bits 2 ^ 3 ^ 4 fixed), over 64 banks of 4 bytes; with ring_swz(n) = 0, 2, 3, 1 for
+// (n >> 2) & 3 = 0..3 the 16 rows and four runs such a set reads at one q fall into 16
 // different 4-bank groups. The ring shares its space with the staging buffers of the
 // register path (As, Bs: operands that need a conversion), and, after the products, with
 // the rotation buffer and the GroupNorm backward's sums and dO tile.
@@ -195,7 +198,8 @@ template <int NS, int BU, int DT> __device__ __forceinline__ float* rot_buf(Tile
 template <int NS, int BU, int DT> __device__ __forceinline__ float* gn_sw(TileSharedD<NS, BU, DT>& sm) { return &sm.gn.sw[0][0]; }
 template <int NS, int BU, int DT> __device__ __forceinline__ float* gn_sb(TileSharedD<NS, BU, DT>& sm) { return &sm.gn.sb[0][0]; }
 
-__device__ __forceinline__ int ring_unit(int n, int q) { return 4 * n + (q ^ ((n >> 2) & 3)); }
+__device__ __forceinline__ int ring_swz(int n) { return (0x78 >> (2 * ((n >> 2) & 3))) & 3; }
+__device__ __forceinline__ int ring_unit(int n, int q) { return 4 * n + (q ^ ring_swz(n)); }
 
 // Barrier for LDS traffic only: this wave's LDS operations are complete; copies into LDS
 // that are still in flight stay in flight (__syncthreads would wait for them).
@@ -228,7 +232,7 @@ __device__ __forceinline__ void tmm16d(float (&acc)[4][NCT], int K, SM& sm, cons
   const __amdgpu_buffer_rsrc_t rsa = src_rsrc(A), rsb = src_rsrc(B);
   const int nsl = (K + kKH - 1) / kKH;
   // A copy of this lane: unit 64 w + l of the slot's A part
-  const int ap = 64 * w + l, arow = ap >> 2, aq = (ap & 3) ^ ((arow >> 2) & 3);
+  const int ap = 64 * w + l, arow = ap >> 2, aq = (ap & 3) ^ ring_swz(arow);
   auto issue = [&](int k, int slot) __attribute__((always_inline)) {
     const int k0 = k * kKH;
     if constexpr (!FROMP) {
@@ -239,7 +243,7 @@ __device__ __forceinline__ void tmm16d(float (&acc)[4][NCT], int K, SM& sm, cons
     }
 #pragma unroll
     for (int u = 0; u < NRUN; ++u) {
-      const int p = (NRUN * w + u) * 64 + l, n = p >> 2, q = (p & 3) ^ ((n >> 2) & 3);
+      const int p = (NRUN * w + u) * 64 + l, n = p >> 2, q = (p & 3) ^ ring_swz(n);
       const int kq = k0 + 8 * q;
       const uint32_t off = live_off(static_cast<uint32_t>(((br0 + n) * B.pitch + bc0 + kq) * 2), kq < K);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(

@@ -112,7 +112,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kKH = 32;             // reduction slice
 constexpr int kLdH = kKH + 8;       // LDS pitch (half) of As and Bs rows
-constexpr int kLdPH = kBC + 8;      // LDS pitch (half) of P rows
+constexpr int kLdPH = kBC + 16;     // LDS pitch (half) of P rows: 34 16-byte units, so the
+                                    // 16-byte reads of 16 rows x 4 runs are conflict-free
 
 struct alignas(16) TileSharedH {
   union {
