@@ -69,7 +69,12 @@ typedef int32_t rn_dtype;
 #define RN_NORM_R_ROW (1u << 1) /* parallel only: R_nm / max(|sum_{i<=n} R_ni|, 1) (hwhale notes, 3rd rescaling) */
 #define RN_EPI_GN     (1u << 2) /* per-(token, head) GroupNorm over d_v (hwhale notes, multi-head paragraph) */
 #define RN_EPI_GATE   (1u << 3) /* out = GN(.) * swish(gate); requires RN_EPI_GN (m0nads notes, swish gate) */
-#define RN_FORCE_GENERIC (1u << 8) /* use the plain (non-MFMA) kernels; for testing and unusual shapes */
+#define RN_FORCE_GENERIC (1u << 8) /* take the kernels that read their operands through
+                                      pointers with 64-bit offsets (no per-head size bound):
+                                      plain float32 arithmetic for the forward forms; for the
+                                      backward, float32 staging with half-operand MFMA
+                                      products when the inputs are bf16. For testing and for
+                                      shapes past the other kernels' bounds. */
 #define RN_CHUNK_PARALLEL (1u << 9) /* chunkwise: the two-kernel chunk-parallel pair (state
                                        snapshots per 256 tokens, then all chunks' outputs in
                                        parallel) instead of the single sequential kernel; same

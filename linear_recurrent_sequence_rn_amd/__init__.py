@@ -433,9 +433,9 @@ def rn_retention_recurrent_step_at(q, k, v, gamma, theta, state, pos, *, gate=No
 
 
 def rn_chunkwise_backward_workspace_bytes(q, v, gamma, theta, chunk, *, gn=False, gate=None,
-                                          out_dtype=None) -> int:
+                                          out_dtype=None, force_generic=False) -> int:
     B, H, N, dk = q.shape
-    flags = _flags(False, False, gn, gate, False)
+    flags = _flags(False, False, gn, gate, force_generic)
     od = q.dtype if out_dtype is None else out_dtype
     d, keep = make_desc(B, H, N, dk, v.shape[-1], _dtype_code(q.dtype), _dtype_code(od), gamma,
                         theta, flags=flags, device=q.device)
@@ -445,12 +445,13 @@ def rn_chunkwise_backward_workspace_bytes(q, v, gamma, theta, chunk, *, gn=False
 def rn_retention_chunkwise_backward(q, k, v, gamma, theta, chunk, dout, *, gate=None,
                                     state_in=None, dstate_out=None, want_dstate_in=False,
                                     pos0=0, qk_scale=1.0, gn=False, gn_eps=1e-5, gn_weight=None,
-                                    gn_bias=None, workspace=None):
+                                    gn_bias=None, workspace=None, force_generic=False):
     """Gradients of the chunkwise call with respect to q, k, v (and the gate, the initial
     state, the GroupNorm weight and bias). ``dout`` has the forward output's dtype.
     Returns a dict with dq, dk, dv and, when they apply, dgate, dstate_in, dgn_weight,
-    dgn_bias."""
-    flags = _flags(False, False, gn, gate, False)
+    dgn_bias. ``force_generic`` takes the kernels that stage operands through registers
+    (64-bit addressing) also where the copy-fed matrix-core kernels apply."""
+    flags = _flags(False, False, gn, gate, force_generic)
     d, keep, od = _qkv_desc(q, k, v, gamma, theta, dout.dtype, flags, pos0, qk_scale, gn_eps,
                             gn_weight, gn_bias, gate)
     B, H, N, dk = q.shape

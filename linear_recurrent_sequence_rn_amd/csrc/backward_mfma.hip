@@ -988,9 +988,10 @@ hipError_t launch_t(const CallArgs& a, const BwArgs& x, void* ws, hipStream_t st
 }  // namespace
 
 bool backward_mfma_supported(const CallArgs& a, int in_dt) {
-  // (every per-head operand array is read through a buffer resource: under 2 GB)
+  // (every per-head operand array is read through a buffer resource with 32-bit offsets:
+  // under 2 GB, float32 dout included)
   return in_dt == RN_BF16 && a.dk % 8 == 0 && a.dv % 8 == 0 &&
-         (int64_t(a.N) + 64) * max(a.dk, a.dv) * 2 < (int64_t(1) << 31);
+         (int64_t(a.N) + 64) * max(a.dk, a.dv) * 4 < (int64_t(1) << 31);
 }
 
 size_t backward_mfma_ws_bytes(const CallArgs& a) { return m_layout(a).total; }

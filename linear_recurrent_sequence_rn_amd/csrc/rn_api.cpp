@@ -394,7 +394,8 @@ rn_status rn_retention_recurrent_step_at(const rn_desc* desc, const int64_t* pos
 // call, by the pointers' alignment), never less than the float32 path's.
 static size_t backward_need(const rn_desc* desc, const rn::CallArgs& a) {
   size_t n = rn::backward_ws_bytes(a);
-  if (rn::backward_mfma_supported(a, desc->in_dtype)) n = std::max(n, rn::backward_mfma_ws_bytes(a));
+  if (!(desc->flags & RN_FORCE_GENERIC) && rn::backward_mfma_supported(a, desc->in_dtype))
+    n = std::max(n, rn::backward_mfma_ws_bytes(a));
   return align256(n);
 }
 
@@ -436,7 +437,8 @@ rn_status rn_retention_chunkwise_backward(const rn_desc* desc, int32_t chunk, co
                (desc->flags & RN_EPI_GN) ? dgn_bias : nullptr};
   g_err[0] = 0;
   auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
-  const bool mfma = rn::backward_mfma_supported(a, desc->in_dtype) && a16(v) && a16(dv) && a16(dout) &&
+  const bool mfma = !(desc->flags & RN_FORCE_GENERIC) && rn::backward_mfma_supported(a, desc->in_dtype) &&
+                    a16(v) && a16(dv) && a16(dout) &&
                     a16(x.gate) && a16(x.dgate) && reinterpret_cast<uintptr_t>(q) % 4 == 0 &&
                     reinterpret_cast<uintptr_t>(k) % 4 == 0;
   if (mfma)

@@ -159,6 +159,30 @@ def test_chunkwise_schedule_flags():
     assert len(set(sizes.values())) == 3, sizes
 
 
+def test_matrix_core_paths_stop_at_32_bit_head_extents():
+    """Each matrix-core path reads a head's arrays through buffer resources with 32-bit
+    offsets; past 2 GB per head (float32 outputs and dout included) the calls take the
+    generic kernels, whose workspace sizes differ."""
+    big = dict(d_k=256, d_v=512, theta=np.ones(128), H=1, gamma=[0.9])
+    # backward: (N + 64) * 512 * 4 < 2^31 <=> N < 2^20 - 64
+    def bw_ws(N, flags=0):
+        d, keep = desc(**big, N=N, flags=flags)
+        return rn.lib.rn_chunkwise_backward_workspace_bytes(ctypes.byref(d), 256)
+    lo, hi = (1 << 20) - 65, (1 << 20) - 64
+    assert bw_ws(lo) != bw_ws(lo, rn.RN_FORCE_GENERIC)         # matrix cores below the bound
+    assert bw_ws(hi) == bw_ws(hi, rn.RN_FORCE_GENERIC) > 0     # generic kernels from it on
+    # forward: the sequential kernel while N * 512 * 4 < 2^31, then another schedule
+    lo, keep_lo = desc(**big, N=(1 << 20) - 1)
+    hi, keep_hi = desc(**big, N=1 << 20)
+    assert rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(lo), 256) != \
+        rn.lib.rn_chunkwise_workspace_bytes(ctypes.byref(hi), 256)
+    # parallel: the matrix-core kernel needs its workspace, the generic one none
+    lo, keep_lo = desc(**big, N=(1 << 20) - 1)
+    hi, keep_hi = desc(**big, N=1 << 20)
+    assert rn.lib.rn_parallel_workspace_bytes(ctypes.byref(lo)) > 0
+    assert rn.lib.rn_parallel_workspace_bytes(ctypes.byref(hi)) == 0
+
+
 def test_parallel_workspace():
     big = dict(d_k=256, d_v=512, theta=np.ones(128), H=8, gamma=np.full(8, 0.9), N=2048)
     d, keep = desc(**big)

@@ -118,6 +118,25 @@ def test_bf16_state_positions_other_shapes(N, pos0, dk, dv):
     assert close(got["dstate_in"].cpu(), ref["dstate0"], rel=1e-2) <= 1.0
 
 
+def test_bf16_inputs_register_staged_kernels():
+    """bf16 inputs through the kernels that stage their operands through registers with
+    64-bit addressing (RN_FORCE_GENERIC; the path taken where a head's arrays pass the
+    copy-fed kernels' 2 GB buffer range): operands staged in float32 and rounded to IEEE
+    half for the MFMA products, float32 accumulation and scans. Bar: 2e-3 of the head's
+    norm plus the bf16 store (measured at most 3.5e-4 of the norm beyond the store's
+    rounding)."""
+    x = make("bf16", 1, 2, 130, 64, 96, seed=31, gate=True, state=True)
+    got = rn().rn_retention_chunkwise_backward(
+        dev(x["q"]), dev(x["k"]), dev(x["v"]), x["gamma"], x["theta"], 64, dev(x["dout"]),
+        gate=dev(x["gate"]), gn=True, state_in=dev(x["state"]), dstate_out=dev(x["dstate_out"]),
+        want_dstate_in=True, pos0=9, force_generic=True)
+    ref = O.backward(x["q"], x["k"], x["v"], x["gamma"], x["theta"], x["dout"], gate=x["gate"],
+                     gn=True, pos0=9, state0=x["state"], dstate_out=x["dstate_out"])
+    for n in ("dq", "dk", "dv", "dgate"):
+        assert close(got[n].cpu(), ref[n], bf16=True, rel=2e-3) <= 1.0, n
+    assert close(got["dstate_in"].cpu(), ref["dstate0"], rel=2e-3) <= 1.0
+
+
 def test_bf16_gn_affine_gradients():
     x = make("bf16", 1, 2, 300, 256, 512, seed=21, gate=True)
     H, dv = 2, 512
